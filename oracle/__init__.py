@@ -1,0 +1,182 @@
+"""CPU oracle for the FP8 rollout hot path (test infrastructure only).
+
+This package wraps ``fp8q_oracle.c``: a plain, slow, scalar C implementation of
+what the hot path computes, in fp64 where the method leaves precision open.  It
+exists to check the HIP library: only ``tests/``, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import it.  It
+shares no code with the HIP library and imports nothing from it.
+
+Every function takes numpy arrays (bf16 as ``uint16`` bit patterns, FP8 codes as
+``uint8``) and returns numpy arrays.  See ``fp8q_oracle.c`` for the page and
+section each computation follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp8q_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libfp8q_oracle.so")
+
+CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (fp-contract off, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+_u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
+_u16p = np.ctypeslib.ndpointer(dtype=np.uint16, flags="C_CONTIGUOUS")
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
+_i64 = ctypes.c_int64
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_scale.argtypes = [ctypes.c_float, ctypes.c_float]
+        L.oracle_scale.restype = ctypes.c_float
+        L.oracle_quantize_value.argtypes = [ctypes.c_float, ctypes.c_float]
+        L.oracle_quantize_value.restype = ctypes.c_uint8
+        L.oracle_quant_weight_blk128.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p]
+        L.oracle_quant_act_g128.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p, _i64]
+        L.oracle_gemm_w8a8.argtypes = [_u8p, _i64, _f32p, _i64, _u8p, _i64, _f32p, _f64p, _i64,
+                                       _i64, _i64, _i64]
+        L.oracle_grouped_gemm_w8a8.argtypes = [_u8p, _i64, _f32p, _i64, _u8p, _f32p, _i32p,
+                                               ctypes.c_int32, _f64p, _i64, _i64, _i64]
+        L.oracle_kv_quant.argtypes = [_u16p, _i64, _u16p, _i64, _i64, ctypes.c_int32,
+                                      ctypes.c_int32, _i64p, _u8p, _u8p, ctypes.c_int32, _i64,
+                                      _f32p, _f32p, ctypes.c_float, ctypes.c_int]
+        for f in ("oracle_quant_weight_blk128", "oracle_quant_act_g128", "oracle_gemm_w8a8",
+                  "oracle_grouped_gemm_w8a8", "oracle_kv_quant", "oracle_num_threads"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc == -1:
+        raise ValueError(f"{what}: non-finite input (inputs must be finite)")
+    if rc != 0:
+        raise ValueError(f"{what}: invalid shape or argument (rc={rc})")
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 inputs are passed as uint16 bit patterns")
+    return a
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().oracle_e4m3_decode(int(code))
+
+
+def e4m3_encode(u: float) -> int:
+    """Nearest E4M3FN code to the real number ``u`` (ties to even, saturating)."""
+    return int(lib().oracle_e4m3_encode(float(u)))
+
+
+def scale(amax: float, rng: float = 448.0) -> np.float32:
+    return np.float32(lib().oracle_scale(float(amax), float(rng)))
+
+
+def quantize_value(x: float, s: float) -> int:
+    """E4M3FN code of the exact quotient x / s (x and s as binary32)."""
+    return int(lib().oracle_quantize_value(float(np.float32(x)), float(np.float32(s))))
+
+
+def quant_weight_blk128(w_bits: np.ndarray):
+    """128x128 blockwise quantization of a bf16 [n, k] weight -> (codes [n,k], scales [n/128,k/128])."""
+    w = _u16(w_bits)
+    n, k = w.shape
+    q = np.empty((n, k), dtype=np.uint8)
+    s = np.empty((n // 128, k // 128), dtype=np.float32)
+    _check(lib().oracle_quant_weight_blk128(w, n, k, k, q, k, s), "quant_weight_blk128")
+    return q, s
+
+
+def quant_act_g128(x_bits: np.ndarray, ld_s: int | None = None):
+    """1x128 group quantization of bf16 [m, k] -> (codes [m,k], scales [k/128, ld_s])."""
+    x = _u16(x_bits)
+    m, k = x.shape
+    ld_s = m if ld_s is None else ld_s
+    q = np.empty((m, k), dtype=np.uint8)
+    s = np.zeros((k // 128, ld_s), dtype=np.float32)
+    _check(lib().oracle_quant_act_g128(x, m, k, k, q, k, s, ld_s), "quant_act_g128")
+    return q, s
+
+
+def gemm_w8a8(a: np.ndarray, a_s: np.ndarray, b: np.ndarray, b_s: np.ndarray) -> np.ndarray:
+    """fp64 block-scaled GEMM: a [m,k] codes, a_s [k/128, ld_as], b [n,k] codes, b_s [n/128,k/128]."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    a_s = np.ascontiguousarray(a_s, dtype=np.float32)
+    b_s = np.ascontiguousarray(b_s, dtype=np.float32)
+    m, k = a.shape
+    n = b.shape[0]
+    y = np.empty((m, n), dtype=np.float64)
+    _check(lib().oracle_gemm_w8a8(a, k, a_s, a_s.shape[1], b, k, b_s, y, n, m, n, k), "gemm_w8a8")
+    return y
+
+
+def grouped_gemm_w8a8(a, a_s, b, b_s, offsets) -> np.ndarray:
+    """fp64 grouped GEMM: rows [off[g], off[g+1]) of a use b[g] ([G, n, k]) and b_s[g]."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    a_s = np.ascontiguousarray(a_s, dtype=np.float32)
+    b_s = np.ascontiguousarray(b_s, dtype=np.float32)
+    off = np.ascontiguousarray(offsets, dtype=np.int32)
+    m, k = a.shape
+    g, n, _ = b.shape
+    y = np.zeros((m, n), dtype=np.float64)
+    _check(lib().oracle_grouped_gemm_w8a8(a, k, a_s, a_s.shape[1], b, b_s, off, g, y, n, n, k),
+           "grouped_gemm_w8a8")
+    return y
+
+
+def kv_quant(k_bits, v_bits, slot_mapping, k_cache, v_cache, page_size: int,
+             k_scale: float = 1.0, v_scale: float = 1.0, rng: float = 448.0,
+             recalibrate: bool = True):
+    """Quantize-on-write into copies of the paged caches.
+
+    k_bits, v_bits: bf16 [T, heads, head_dim]; caches: uint8 [pages, page_size, heads, head_dim].
+    Returns (k_cache', v_cache', k_scale', v_scale')."""
+    kx = _u16(k_bits)
+    vx = _u16(v_bits)
+    t, heads, hd = kx.shape
+    kc = np.array(k_cache, dtype=np.uint8, copy=True, order="C")
+    vc = np.array(v_cache, dtype=np.uint8, copy=True, order="C")
+    ks = np.array([k_scale], dtype=np.float32)
+    vs = np.array([v_scale], dtype=np.float32)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    num_pages = kc.shape[0]
+    _check(lib().oracle_kv_quant(kx.reshape(t, -1), heads * hd, vx.reshape(t, -1), heads * hd, t,
+                                 heads, hd, slots, kc, vc, page_size, num_pages, ks, vs,
+                                 float(rng), 1 if recalibrate else 0), "kv_quant")
+    return kc, vc, ks[0], vs[0]

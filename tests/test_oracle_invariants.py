@@ -1,0 +1,193 @@
+"""Oracle quantizers pinned by invariants and metamorphic relations.
+
+Rule: FP8-RL summary page, "Prerequisites / FP8 quantization format" (blockwise
+scale, W_hat = round(W/scale), E4M3 range +-448) and "Method step details" steps
+1 and 3 (weights per sync, activations per forward, KV scales recalibrated per
+step).  The paged cache layout follows "1T-parameter RL on 100 GPUs", 3.4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_block_scaled_weight_amd import synth
+
+
+def _f32(bits):
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _dec(codes):
+    """Decode through torch's float8_e4m3fn (a library routine, not the oracle's table)."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.double().numpy()
+
+
+def _ulp_e4m3(v):
+    v = np.abs(v)
+    e = np.floor(np.log2(np.where(v > 0, v, 1.0)))
+    return np.exp2(np.maximum(e, -6.0) - 3.0)
+
+
+def _blocks(a, rb, cb):
+    r, c = a.shape
+    return a.reshape(r // rb, rb, c // cb, cb).transpose(0, 2, 1, 3)
+
+
+def _check_quant_invariants(x_bits, q, s, rb, cb):
+    x = _f32(x_bits)
+    d = _dec(q)
+    xb, db = _blocks(x, rb, cb), _blocks(d, rb, cb)
+    qb = _blocks(q, rb, cb)
+    sb = s.astype(np.float64)
+    assert np.all(sb > 0)
+    for i in range(xb.shape[0]):
+        for j in range(xb.shape[1]):
+            blk, dq, sc, cq = xb[i, j], db[i, j], sb[i, j], qb[i, j]
+            amax = np.max(np.abs(blk))
+            if amax == 0:
+                assert sc == 1.0 and np.all((cq & 0x7F) == 0)
+                continue
+            # the amax element maps to the E4M3 maximum, nothing exceeds it
+            assert np.max(np.abs(dq)) == 448.0
+            assert np.all(np.abs(dq[np.abs(blk) == amax]) == 448.0)
+            # error within half an E4M3 ulp of the quotient, in x units
+            err = np.abs(dq * sc - blk)
+            assert np.all(err <= 0.5 * _ulp_e4m3(blk / sc) * sc)
+            # sign kept for nonzero codes
+            nz = dq != 0
+            assert np.all(np.sign(dq[nz]) == np.sign(blk[nz]))
+            # monotone
+            order = np.argsort(blk, axis=None, kind="stable")
+            assert np.all(np.diff(dq.reshape(-1)[order]) >= 0)
+
+
+def test_weight_invariants():
+    w = synth.weight(99, 0, 0, 384, 256, zero_block=(2, 1))
+    q, s = oracle.quant_weight_blk128(w)
+    assert s.shape == (3, 2) and s[2, 1] == 1.0
+    _check_quant_invariants(w, q, s, 128, 128)
+
+
+def test_activation_invariants():
+    x = synth.activation(99, 0, 1, 64, 512)
+    q, s = oracle.quant_act_g128(x)
+    # scales are stored group-major, rows contiguous: s[g, m]
+    _check_quant_invariants(x, q, s.T.copy(), 1, 128)
+
+
+def test_power_of_two_rescaling():
+    """x * 2^j (exact in bf16, scale stays normal) gives the same codes and scale * 2^j."""
+    w = synth.weight(99, 1, 0, 256, 256)
+    q0, s0 = oracle.quant_weight_blk128(w)
+    for j in (-3, 5):
+        wj = synth.to_bf16_bits(synth.bf16_bits_to_f32(w) * np.float32(2.0 ** j))
+        assert np.array_equal(synth.bf16_bits_to_f32(wj), synth.bf16_bits_to_f32(w) * np.float32(2.0 ** j))
+        qj, sj = oracle.quant_weight_blk128(wj)
+        assert np.array_equal(qj, q0)
+        assert np.array_equal(sj, s0 * np.float32(2.0 ** j))
+
+
+def test_permutation_within_block_permutes_codes():
+    x = synth.activation(99, 2, 0, 8, 256)
+    g = np.random.Generator(np.random.PCG64(5))
+    perm = g.permutation(128)
+    xp = x.copy()
+    xp[:, :128] = x[:, perm]
+    q, s = oracle.quant_act_g128(x)
+    qp, sp = oracle.quant_act_g128(xp)
+    assert np.array_equal(qp[:, :128], q[:, perm])
+    assert np.array_equal(qp[:, 128:], q[:, 128:])
+    assert np.array_equal(sp, s)
+
+
+def test_editing_one_block_leaves_others():
+    w = synth.weight(99, 3, 0, 256, 384)
+    q0, s0 = oracle.quant_weight_blk128(w)
+    w2 = w.copy()
+    w2[130, 260] = synth.to_bf16_bits(np.array([5.0], dtype=np.float32))[0]
+    q1, s1 = oracle.quant_weight_blk128(w2)
+    mask = np.ones_like(q0, dtype=bool)
+    mask[128:256, 256:384] = False
+    assert np.array_equal(q1[mask], q0[mask])
+    smask = np.ones_like(s0, dtype=bool)
+    smask[1, 2] = False
+    assert np.array_equal(s1[smask], s0[smask])
+    assert s1[1, 2] == np.float32(5.0) / np.float32(448.0)
+
+
+def test_scale_layout_with_padded_ld():
+    x = synth.activation(99, 4, 0, 5, 384)
+    q, s = oracle.quant_act_g128(x, ld_s=8)
+    q2, s2 = oracle.quant_act_g128(x)
+    assert np.array_equal(q, q2)
+    assert np.array_equal(s[:, :5], s2)
+    assert np.all(s[:, 5:] == 0)
+
+
+# ------------------------------------------------------------------------- KV
+def _kv_case(tokens=40, pages=6, page_size=16, heads=2, hd=128, seed=3):
+    g = np.random.Generator(np.random.PCG64(seed))
+    k = synth.to_bf16_bits(g.standard_normal((tokens, heads, hd), dtype=np.float32))
+    v = synth.to_bf16_bits(3 * g.standard_normal((tokens, heads, hd), dtype=np.float32))
+    slots = g.permutation(pages * page_size)[:tokens].astype(np.int64)
+    slots[[3, 17]] = -1
+    cache = np.full((pages, page_size, heads, hd), 0x7F, dtype=np.uint8)
+    return k, v, slots, cache
+
+
+def test_kv_recalibration_and_skip():
+    k, v, slots, cache = _kv_case()
+    # a huge value in a skipped token must not move the scale
+    k[3, 0, 0] = synth.to_bf16_bits(np.array([1e4], dtype=np.float32))[0]
+    kc, vc, ks, vs = oracle.kv_quant(k, v, slots, cache, cache, 16)
+    w = slots >= 0
+    ak = np.max(np.abs(synth.bf16_bits_to_f32(k[w])))
+    av = np.max(np.abs(synth.bf16_bits_to_f32(v[w])))
+    assert ks == np.float32(ak) / np.float32(448.0)
+    assert vs == np.float32(av) / np.float32(448.0)
+    flat_k = kc.reshape(-1, k.shape[1], k.shape[2])
+    flat_v = vc.reshape(-1, v.shape[1], v.shape[2])
+    # reading back through the slot mapping gives the per-token quantization
+    for t in np.nonzero(w)[0]:
+        for h in range(k.shape[1]):
+            for d in (0, 1, 77, 127):
+                assert flat_k[slots[t], h, d] == oracle.quantize_value(synth.bf16_bits_to_f32(k[t, h, d]), ks)
+                assert flat_v[slots[t], h, d] == oracle.quantize_value(synth.bf16_bits_to_f32(v[t, h, d]), vs)
+    # unwritten slots keep their sentinel bytes
+    written = np.zeros(flat_k.shape[0], dtype=bool)
+    written[slots[w]] = True
+    assert np.all(flat_k[~written] == 0x7F) and np.all(flat_v[~written] == 0x7F)
+    # the dequantized cache is within half an E4M3 ulp everywhere it was written
+    x = synth.bf16_bits_to_f32(k[w]).astype(np.float64)
+    dq = _dec(flat_k[slots[w]]) * float(ks)
+    assert np.all(np.abs(dq - x) <= 0.5 * _ulp_e4m3(x / float(ks)) * float(ks))
+    assert np.max(np.abs(_dec(flat_k[slots[w]]))) == 448.0
+
+
+def test_kv_stored_scale_saturates_and_keeps_scale():
+    k, v, slots, cache = _kv_case()
+    kc, vc, ks, vs = oracle.kv_quant(k, v, slots, cache, cache, 16, k_scale=2.0 ** -8,
+                                     v_scale=0.5, recalibrate=False)
+    assert ks == np.float32(2.0 ** -8) and vs == np.float32(0.5)
+    w = slots >= 0
+    flat_k = kc.reshape(-1, k.shape[1], k.shape[2])[slots[w]]
+    x = synth.bf16_bits_to_f32(k[w])
+    big = np.abs(x) * 256 >= 464
+    assert big.any()
+    assert np.all((flat_k[big] & 0x7F) == 0x7E)  # saturated, never NaN
+    assert not np.any((flat_k & 0x7F) == 0x7F)
+
+
+def test_kv_all_zero_gives_unit_scale():
+    k = np.zeros((4, 1, 128), dtype=np.uint16)
+    cache = np.zeros((1, 16, 1, 128), dtype=np.uint8)
+    kc, vc, ks, vs = oracle.kv_quant(k, k, np.arange(4), cache, cache, 16)
+    assert ks == 1.0 and vs == 1.0 and np.all(kc == 0)
+
+
+def test_nonfinite_input_rejected():
+    x = np.zeros((1, 128), dtype=np.uint16)
+    x[0, 5] = 0x7F80  # +inf
+    with pytest.raises(ValueError):
+        oracle.quant_act_g128(x)
