@@ -1,0 +1,198 @@
+"""fp8q: FP8 rollout hot path on MI355X (gfx950) — Python binding of libfp8q.
+
+Thin ctypes binding over the C ABI declared in ``include/fp8q.h``.  Each function
+has the name of the C entry point it calls and does argument marshalling only:
+tensors are turned into device pointers, leading dimensions and the current HIP
+stream; every step of the computation runs in libfp8q's HIP kernels.  PyTorch is
+used for device memory and streams.
+
+There is no fallback: if ``libfp8q.so`` is missing, or a call fails, an exception
+is raised.  Build the library with ``python -m fp8_block_scaled_weight_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8q.so")
+
+FP8Q_OK = 0
+FP8Q_ERR_NULL = 1
+FP8Q_ERR_SHAPE = 2
+FP8Q_ERR_STRIDE = 3
+FP8Q_ERR_ALIGN = 4
+FP8Q_ERR_LAUNCH = 5
+FP8Q_ERR_UNSUPPORTED = 6
+FP8Q_KV_RECALIBRATE = 1
+
+EXPORTED = (
+    "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version", "fp8q_quant_weight_blk128",
+    "fp8q_quant_act_g128", "fp8q_gemm_w8a8_blkscaled", "fp8q_grouped_gemm_w8a8", "fp8q_kv_quant",
+)
+
+
+class Fp8qError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}: {detail}")
+
+
+class WeightDesc(ctypes.Structure):
+    """Mirror of ``fp8q_weight_desc``."""
+    _fields_ = [("w", ctypes.c_void_p), ("q", ctypes.c_void_p), ("s", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("ld_w", ctypes.c_int64),
+                ("ld_q", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfp8q.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libfp8q.so not found at {LIB_PATH}; build it with "
+                              "`python -m fp8_block_scaled_weight_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, u32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
+        L.fp8q_status_string.argtypes = [ctypes.c_int]
+        L.fp8q_status_string.restype = ctypes.c_char_p
+        L.fp8q_last_error.argtypes = []
+        L.fp8q_last_error.restype = ctypes.c_char_p
+        L.fp8q_abi_version.argtypes = []
+        L.fp8q_abi_version.restype = ctypes.c_int
+        L.fp8q_quant_weight_blk128.argtypes = [ctypes.POINTER(WeightDesc), i32, vp]
+        L.fp8q_quant_act_g128.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp]
+        L.fp8q_gemm_w8a8_blkscaled.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp]
+        L.fp8q_grouped_gemm_w8a8.argtypes = [vp, i64, vp, i64, vp, vp, vp, i32, i64, vp, i64, i64, i64, vp]
+        L.fp8q_kv_quant.argtypes = [vp, i64, vp, i64, i64, i32, i32, vp, vp, vp, i32, i64, vp, vp, f32, u32, vp]
+        for name in EXPORTED[3:]:
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fp8q_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().fp8q_last_error().decode()
+
+
+def abi_version() -> int:
+    return int(lib().fp8q_abi_version())
+
+
+def _check(status: int, where: str) -> None:
+    if status != FP8Q_OK:
+        raise Fp8qError(status, where, last_error())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes: Sequence[torch.dtype]) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (libfp8q runs on the GPU only)")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {list(dtypes)}")
+    return t.data_ptr()
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Leading dimension (elements) of a 2-D row-major tensor with unit column stride."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+
+
+FP8 = (torch.float8_e4m3fn, torch.uint8)
+BF16 = (torch.bfloat16,)
+F32 = (torch.float32,)
+
+
+def fp8q_quant_weight_blk128(weights: Iterable[tuple], stream=None) -> None:
+    """Blockwise-quantize many bf16 weights in one call.
+
+    weights: iterable of (w [n,k] bf16, q [n,k] fp8, s [n/128,k/128] fp32) device tensors."""
+    items = list(weights)
+    arr = (WeightDesc * max(len(items), 1))()
+    for i, (w, q, s) in enumerate(items):
+        n, k = w.shape
+        if tuple(q.shape) != (n, k) or tuple(s.shape) != (n // 128, k // 128) or not s.is_contiguous():
+            raise ValueError(f"weight {i}: q must be [n,k] and s contiguous [n/128,k/128]")
+        arr[i] = WeightDesc(_dev(w, "w", BF16), _dev(q, "q", FP8), _dev(s, "s", F32), n, k,
+                            _rows(w, "w"), _rows(q, "q"))
+    _check(lib().fp8q_quant_weight_blk128(arr, len(items), _stream(stream)), "fp8q_quant_weight_blk128")
+
+
+def fp8q_quant_act_g128(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
+    """Per-token 1x128 group quantization: x [m,k] bf16 -> q [m,k] fp8, s [k/128, ld_s] fp32."""
+    m, k = x.shape
+    if tuple(q.shape) != (m, k) or s.dim() != 2 or s.shape[0] != k // 128 or s.stride(1) != 1:
+        raise ValueError("q must be [m,k] and s [k/128, ld_s] with unit column stride")
+    _check(lib().fp8q_quant_act_g128(_dev(x, "x", BF16), m, k, _rows(x, "x"), _dev(q, "q", FP8), _rows(q, "q"),
+                                     _dev(s, "s", F32), s.stride(0), _stream(stream)), "fp8q_quant_act_g128")
+
+
+def fp8q_gemm_w8a8_blkscaled(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
+                             y: torch.Tensor, stream=None) -> None:
+    """y [m,n] bf16 = block-scaled a [m,k] fp8 (scales a_s [k/128, ld_as]) x b [n,k] fp8 (b_s [n/128,k/128])^T."""
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or tuple(y.shape) != (m, n) or not b_s.is_contiguous() or a_s.stride(1) != 1:
+        raise ValueError("shape mismatch between a, b and y")
+    _check(lib().fp8q_gemm_w8a8_blkscaled(_dev(a, "a", FP8), _rows(a, "a"), _dev(a_s, "a_s", F32), a_s.stride(0),
+                                          _dev(b, "b", FP8), _rows(b, "b"), _dev(b_s, "b_s", F32),
+                                          _dev(y, "y", BF16), _rows(y, "y"), m, n, k, _stream(stream)),
+           "fp8q_gemm_w8a8_blkscaled")
+
+
+def fp8q_grouped_gemm_w8a8(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
+                           group_offsets: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """Grouped GEMM: rows [off[g], off[g+1]) of a [M,k] times b[g] ([G,n,k]) with scales b_s [G,n/128,k/128]."""
+    total_m, k = a.shape
+    g, n, kb = b.shape
+    if kb != k or tuple(y.shape) != (total_m, n) or not b.is_contiguous() or not b_s.is_contiguous():
+        raise ValueError("shape mismatch between a, b and y")
+    if group_offsets.numel() != g + 1:
+        raise ValueError("group_offsets must have G+1 entries")
+    _check(lib().fp8q_grouped_gemm_w8a8(_dev(a, "a", FP8), _rows(a, "a"), _dev(a_s, "a_s", F32), a_s.stride(0),
+                                        _dev(b, "b", FP8), _dev(b_s, "b_s", F32),
+                                        _dev(group_offsets, "group_offsets", (torch.int32,)), g, total_m,
+                                        _dev(y, "y", BF16), _rows(y, "y"), n, k, _stream(stream)),
+           "fp8q_grouped_gemm_w8a8")
+
+
+def fp8q_kv_quant(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                  v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                  fp8_range: float = 448.0, recalibrate: bool = False, stream=None) -> None:
+    """Quantize-on-write of k, v [T, H, 128] bf16 into paged caches [P, page, H, 128] fp8."""
+    t = k.shape[0]
+    heads, hd = k.shape[1], k.shape[2]
+    pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    if tuple(v.shape) != tuple(k.shape) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k/v and k_cache/v_cache shapes must match")
+    if k_cache.shape[2:] != (heads, hd) or not k_cache.is_contiguous() or not v_cache.is_contiguous():
+        raise ValueError("caches must be contiguous [pages, page_size, heads, head_dim]")
+    if k.stride(2) != 1 or k.stride(1) != hd or v.stride(2) != 1 or v.stride(1) != hd:
+        raise ValueError("k/v rows must be contiguous over (heads, head_dim)")
+    _check(lib().fp8q_kv_quant(_dev(k, "k", BF16), k.stride(0), _dev(v, "v", BF16), v.stride(0), t, heads, hd,
+                               _dev(slot_mapping, "slot_mapping", (torch.int64,)), _dev(k_cache, "k_cache", FP8),
+                               _dev(v_cache, "v_cache", FP8), page_size, pages, _dev(k_scale, "k_scale", F32),
+                               _dev(v_scale, "v_scale", F32), float(fp8_range),
+                               FP8Q_KV_RECALIBRATE if recalibrate else 0, _stream(stream)),
+           "fp8q_kv_quant")

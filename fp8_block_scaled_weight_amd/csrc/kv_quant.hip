@@ -1,0 +1,131 @@
+// FP8 KV-cache quantize-on-write with per-step K/V scale recalibration, gfx950.
+//
+// FP8-RL summary page, "Method step details" step 3: the KV cache is stored in FP8
+// and its K/V scales are recomputed from the data at the start of every RL step's
+// rollout.  "1T-parameter RL on 100 GPUs", 3.4: the cache is paged in fixed blocks
+// and K and V are quantized to FP8 separately.
+//
+// Recalibration is a global dependency (every code needs the final amax), so a
+// recalibrating call is two streaming passes: an amax pass (2 B/element read) and an
+// encode pass (2 B read + 1 B written per element).  Between them a one-thread
+// kernel turns the amax into the scale.  The amax is accumulated as the bit pattern
+// of a non-negative float with an unsigned atomic max: exact and order-independent.
+#include "e4m3.hpp"
+#include "launch.hpp"
+
+namespace fp8q {
+
+constexpr int kKvBlock = 256;                 // 4 waves
+constexpr int kElemsPerWavePass = 64 * 16;    // 64 lanes x 16 bf16
+
+__global__ void kv_reset_kernel(float* k_scale, float* v_scale) {
+  if (threadIdx.x == 0) {
+    reinterpret_cast<uint32_t*>(k_scale)[0] = 0u;
+    reinterpret_cast<uint32_t*>(v_scale)[0] = 0u;
+  }
+}
+
+// One wave per token (grid-stride); each wave reduces K and V rows of its tokens.
+__global__ __launch_bounds__(kKvBlock) void kv_amax_kernel(const uint16_t* __restrict__ k, int64_t ld_k,
+                                                           const uint16_t* __restrict__ v, int64_t ld_v,
+                                                           int64_t tokens, int64_t row,
+                                                           const int64_t* __restrict__ slots,
+                                                           float* k_scale, float* v_scale) {
+  __shared__ uint32_t red[2][kKvBlock / 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t waves = (int64_t)gridDim.x * (kKvBlock / 64);
+  uint32_t mk = 0, mv = 0;
+  for (int64_t t = (int64_t)blockIdx.x * (kKvBlock / 64) + wave; t < tokens; t += waves) {
+    if (slots[t] < 0) continue;  // uniform per wave
+    for (int64_t e = lane * 16; e < row; e += kElemsPerWavePass) {
+      const uint4* pk = reinterpret_cast<const uint4*>(k + t * ld_k + e);
+      const uint4* pv = reinterpret_cast<const uint4*>(v + t * ld_v + e);
+      mk = max(mk, absmax16(load_stream(pk), load_stream(pk + 1)));
+      mv = max(mv, absmax16(load_stream(pv), load_stream(pv + 1)));
+    }
+  }
+  mk = max_over_wave(mk);
+  mv = max_over_wave(mv);
+  if (lane == 0) {
+    red[0][wave] = mk;
+    red[1][wave] = mv;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0, b = 0;
+    for (int w = 0; w < kKvBlock / 64; ++w) {
+      a = max(a, red[0][w]);
+      b = max(b, red[1][w]);
+    }
+    // the bf16 magnitude bits shifted up are the fp32 bits of the magnitude
+    if (a) atomicMax(reinterpret_cast<unsigned int*>(k_scale), a << 16);
+    if (b) atomicMax(reinterpret_cast<unsigned int*>(v_scale), b << 16);
+  }
+}
+
+__global__ void kv_finalize_kernel(float* k_scale, float* v_scale, float range) {
+  if (threadIdx.x == 0) {
+    float ak = __uint_as_float(reinterpret_cast<uint32_t*>(k_scale)[0]);
+    float av = __uint_as_float(reinterpret_cast<uint32_t*>(v_scale)[0]);
+    k_scale[0] = scale_from_amax(ak, range);
+    v_scale[0] = scale_from_amax(av, range);
+  }
+}
+
+// One wave per token: K row then V row, 16 elements per lane per pass.
+__global__ __launch_bounds__(kKvBlock) void kv_write_kernel(const uint16_t* __restrict__ k, int64_t ld_k,
+                                                            const uint16_t* __restrict__ v, int64_t ld_v,
+                                                            int64_t tokens, int64_t row,
+                                                            const int64_t* __restrict__ slots,
+                                                            uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                                            const float* k_scale, const float* v_scale) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t waves = (int64_t)gridDim.x * (kKvBlock / 64);
+  const Quantizer qk = make_quantizer(k_scale[0]);
+  const Quantizer qv = make_quantizer(v_scale[0]);
+  for (int64_t t = (int64_t)blockIdx.x * (kKvBlock / 64) + wave; t < tokens; t += waves) {
+    const int64_t slot = slots[t];
+    if (slot < 0) continue;
+    for (int64_t e = lane * 16; e < row; e += kElemsPerWavePass) {
+      const uint4* pk = reinterpret_cast<const uint4*>(k + t * ld_k + e);
+      const uint4* pv = reinterpret_cast<const uint4*>(v + t * ld_v + e);
+      uint4 ka = load_stream(pk), kb = load_stream(pk + 1);
+      uint4 va = load_stream(pv), vb = load_stream(pv + 1);
+      uint4 ok = quant16<true>(ka, kb, qk);
+      uint4 ov = quant16<true>(va, vb, qv);
+      store_stream(kc + slot * row + e, ok);
+      store_stream(vc + slot * row + e, ov);
+    }
+  }
+}
+
+static unsigned kv_grid(int64_t tokens) {
+  // enough waves to fill 256 CUs several times over, never more than one per token
+  int64_t wgs = (tokens + 3) / 4;
+  const int64_t cap = 256 * 16;
+  return (unsigned)(wgs < cap ? (wgs < 1 ? 1 : wgs) : cap);
+}
+
+hipError_t launch_kv_quant(const void* k, int64_t ld_k, const void* v, int64_t ld_v, int64_t tokens,
+                           int32_t heads, const int64_t* slots, void* k_cache, void* v_cache,
+                           float* k_scale, float* v_scale, float range, bool recalibrate,
+                           hipStream_t stream) {
+  const int64_t row = (int64_t)heads * 128;
+  const unsigned grid = kv_grid(tokens);
+  const uint16_t* kk = reinterpret_cast<const uint16_t*>(k);
+  const uint16_t* vv = reinterpret_cast<const uint16_t*>(v);
+  if (recalibrate) {
+    hipLaunchKernelGGL(kv_reset_kernel, dim3(1), dim3(64), 0, stream, k_scale, v_scale);
+    hipLaunchKernelGGL(kv_amax_kernel, dim3(grid), dim3(kKvBlock), 0, stream, kk, ld_k, vv, ld_v, tokens,
+                       row, slots, k_scale, v_scale);
+    hipLaunchKernelGGL(kv_finalize_kernel, dim3(1), dim3(64), 0, stream, k_scale, v_scale, range);
+  }
+  hipLaunchKernelGGL(kv_write_kernel, dim3(grid), dim3(kKvBlock), 0, stream, kk, ld_k, vv, ld_v, tokens, row,
+                     slots, reinterpret_cast<uint8_t*>(k_cache), reinterpret_cast<uint8_t*>(v_cache),
+                     k_scale, v_scale);
+  return hipGetLastError();
+}
+
+}  // namespace fp8q

@@ -1,0 +1,46 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+// One weight tensor inside a batched weight-quantization launch.  Descriptors of one
+// launch travel by value in the kernel arguments (no device table, no allocation).
+struct WeightDescDev {
+  const void* w;
+  void* q;
+  float* s;
+  int64_t ld_w;
+  int64_t ld_q;
+  int32_t first_block;  // first block id of this tensor within the launch
+  int32_t kblocks;      // k / 128
+};
+
+constexpr int kWeightChunk = 64;  // descriptors per launch (3 KB of kernel arguments)
+
+struct WeightChunk {
+  int32_t count;
+  WeightDescDev d[kWeightChunk];
+};
+
+hipError_t launch_quant_weight_chunk(const WeightChunk& chunk, int64_t blocks, hipStream_t stream);
+
+hipError_t launch_quant_act(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q, int64_t ld_q,
+                            float* s, int64_t ld_s, hipStream_t stream);
+
+hipError_t launch_kv_quant(const void* k, int64_t ld_k, const void* v, int64_t ld_v, int64_t tokens,
+                           int32_t heads, const int64_t* slots, void* k_cache, void* v_cache,
+                           float* k_scale, float* v_scale, float range, bool recalibrate,
+                           hipStream_t stream);
+
+hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
+                       int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
+                       int64_t k, hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
+                               const void* b, const float* b_s, const int32_t* offsets, int32_t groups,
+                               int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k,
+                               hipStream_t stream);
+
+}  // namespace fp8q

@@ -1,0 +1,116 @@
+// Blockwise weight quantization (128x128 blocks) and dynamic 1x128 activation
+// quantization for gfx950.
+//
+// FP8-RL summary page: "Prerequisites / FP8 quantization format" (one scale per
+// 128x128 block, W_hat = round(W / scale)), "Method step details" step 1 (weights
+// quantized statically at every sync, activations dynamically on every forward)
+// and step 2 (the sync quantizes every linear of every layer).
+//
+// Both kernels are single-pass HBM streams: each bf16 element is read once, kept in
+// registers while the block/group amax is reduced, and written once as an E4M3 byte.
+#include "e4m3.hpp"
+#include "launch.hpp"
+
+namespace fp8q {
+
+// ----------------------------------------------------------------------------
+// Weights: one 256-thread workgroup per 128x128 block.  Thread t covers columns
+// 16*(t%8) .. +15 of rows t/8 + 32*i (i < 4): 8 x 16-byte loads, 4 x 16-byte stores.
+// A launch covers a chunk of descriptors; block ids are laid out descriptor after
+// descriptor, row-major over the block grid of each.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_weight_blk128_kernel(WeightChunk chunk) {
+  __shared__ uint32_t wave_max[4];
+  const int64_t blk = blockIdx.x;
+  // descriptor lookup: largest d with first_block[d] <= blk (uniform)
+  int lo = 0, hi = chunk.count - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (chunk.d[mid].first_block <= blk) lo = mid; else hi = mid - 1;
+  }
+  const WeightDescDev& d = chunk.d[lo];
+  const int64_t local = blk - d.first_block;
+  const int64_t bi = local / d.kblocks;
+  const int64_t bj = local - bi * d.kblocks;
+
+  const int t = threadIdx.x;
+  const int col = (t & 7) * 16;
+  const int row0 = t >> 3;
+  const uint16_t* w = reinterpret_cast<const uint16_t*>(d.w) + (bi * 128) * d.ld_w + bj * 128 + col;
+  uint8_t* q = reinterpret_cast<uint8_t*>(d.q) + (bi * 128) * d.ld_q + bj * 128 + col;
+
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4* p = reinterpret_cast<const uint4*>(w + (int64_t)(row0 + 32 * i) * d.ld_w);
+    v[2 * i] = load_stream(p);
+    v[2 * i + 1] = load_stream(p + 1);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, absmax16(v[2 * i], v[2 * i + 1]));
+  m = max_over_wave(m);
+  if ((t & 63) == 0) wave_max[t >> 6] = m;
+  __syncthreads();
+  m = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+  const float scale = scale_from_amax(bf16_bits_to_float(m), kE4M3Max);
+  if (t == 0) d.s[bi * d.kblocks + bj] = scale;
+  const Quantizer qz = make_quantizer(scale);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 o = quant16<false>(v[2 * i], v[2 * i + 1], qz);
+    store_stream(q + (int64_t)(row0 + 32 * i) * d.ld_q, o);
+  }
+}
+
+hipError_t launch_quant_weight_chunk(const WeightChunk& chunk, int64_t blocks, hipStream_t stream) {
+  hipLaunchKernelGGL(quant_weight_blk128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, chunk);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// Activations: 8 lanes per 1x128 group, 16 elements per lane.  A wave takes the
+// same group g of 8 consecutive rows, so its 8 scales s[g*ld_s + r .. r+7] form one
+// contiguous 32-byte store; the 4 waves of a workgroup take 4 consecutive groups.
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_act_g128_kernel(const uint16_t* __restrict__ x, int64_t m,
+                                                             int64_t groups, int64_t ld_x,
+                                                             uint8_t* __restrict__ q, int64_t ld_q,
+                                                             float* __restrict__ s, int64_t ld_s,
+                                                             int64_t group_tiles) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // workgroup -> (row block of 8, tile of 4 groups)
+  const int64_t rb = blockIdx.x / group_tiles;
+  const int64_t g = (blockIdx.x - rb * group_tiles) * 4 + wave;
+  const int64_t row = rb * 8 + (lane >> 3);
+  const int col = (lane & 7) * 16;
+  const bool live = (g < groups) && (row < m);
+  uint4 a = make_uint4(0, 0, 0, 0), b = a;
+  if (live) {
+    const uint4* p = reinterpret_cast<const uint4*>(x + row * ld_x + g * 128 + col);
+    a = load_stream(p);
+    b = load_stream(p + 1);
+  }
+  uint32_t mx = max_over_8_lanes(absmax16(a, b));
+  if (!live) return;
+  const float scale = scale_from_amax(bf16_bits_to_float(mx), kE4M3Max);
+  if ((lane & 7) == 0) s[g * ld_s + row] = scale;
+  const Quantizer qz = make_quantizer(scale);
+  uint4 o = quant16<false>(a, b, qz);
+  store_stream(q + row * ld_q + g * 128 + col, o);
+}
+
+hipError_t launch_quant_act(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q, int64_t ld_q,
+                            float* s, int64_t ld_s, hipStream_t stream) {
+  const int64_t groups = k / 128;
+  const int64_t group_tiles = (groups + 3) / 4;
+  const int64_t row_blocks = (m + 7) / 8;
+  const int64_t wgs = row_blocks * group_tiles;
+  hipLaunchKernelGGL(quant_act_g128_kernel, dim3((unsigned)wgs), dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(x), m, groups, ld_x,
+                     reinterpret_cast<uint8_t*>(q), ld_q, s, ld_s, group_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace fp8q

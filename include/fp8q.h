@@ -1,0 +1,201 @@
+/*
+ * fp8q.h: C ABI of libfp8q, the FP8 rollout hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The library implements, as hand-written HIP kernels for one GPU:
+ *   - 128x128 blockwise E4M3 weight quantization, run at every RL weight sync;
+ *   - dynamic 1x128 per-token-group activation quantization, run on every forward;
+ *   - the block-scaled W8A8 GEMM that consumes both, dense and MoE-grouped;
+ *   - FP8 KV-cache quantize-on-write with per-step K/V scale recalibration.
+ *
+ * Sources (page title, then section):
+ *   [FP8-RL]   "FP8-RL: A Practical and Stable Low-Precision Stack for LLM Reinforcement
+ *              Learning" (paper summary page): "Prerequisites / FP8 quantization format"
+ *              (E4M3 with range about +-448; one scale per 128x128 weight block,
+ *              W_hat = round(W / scale)); "Method step details" step 1 (W8A8 linears:
+ *              weights quantized statically at sync, activations dynamically per
+ *              forward; q/k/v/o, gate/up/down and MoE fc1/fc2 quantized, embedding,
+ *              norms and lm_head not), step 2 (three-stage weight sync: init, sync with
+ *              blockwise quantization, inference), step 3 (FP8 KV cache, scales
+ *              recalibrated before every RL step's rollout); "Experimental results"
+ *              (FP32 scale factors preferred over power-of-two ones).
+ *   [Rounding] "Where rounding happens matters" (BF16 rounding-location page), section
+ *              on rounding-location mismatch: keep fused arithmetic in FP32 and round
+ *              to BF16 once, at the output.
+ *   [1T-RL]    "1T-parameter RL on 100 GPUs", section 3.4: paged KV cache in fixed
+ *              blocks; K and V each quantized to FP8 separately.
+ *
+ * Number formats.  FP8 codes are OCP E4M3FN bytes (bias 7, max +-448 = 0x7E/0xFE,
+ * subnormals m * 2^-9, NaN 0x7F/0xFF never produced).  BF16 inputs/outputs are
+ * 16-bit brain floats.  Scales are IEEE binary32.
+ *
+ * Quantization rule (every quantizer in this header):
+ *   amax  = max |x| over the block, group or call (exact);
+ *   scale = fl32(amax / range), an IEEE binary32 division; 1.0 if amax == 0;
+ *           range = 448 except where a call takes it as an argument;
+ *   code  = the E4M3FN value nearest to the exact real quotient x / scale, ties to
+ *           the even code, saturating to +-448; the sign of -0 is kept (0x80).
+ * The results are unique: codes and scales are bit-exact and deterministic.
+ *
+ * Conventions for every call.
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *     buffer.  The library allocates no memory and keeps no state besides the
+ *     per-thread error string.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.  Every
+ *     call validates its arguments on the host, enqueues its kernels on `stream` and
+ *     returns without synchronizing.  Stream order is the only ordering.
+ *   - Leading dimensions (`ld_*`) count elements of the buffer's type (bytes for FP8,
+ *     2-byte units for BF16, floats for scales).
+ *   - On any error nothing is enqueued and the returned status says why;
+ *     fp8q_last_error() gives a readable detail.  Device-side faults surface at the
+ *     caller's next synchronization.
+ *   - Preconditions not checked (undefined behaviour if violated): inputs are finite;
+ *     outputs do not overlap inputs or each other; group offsets are nondecreasing
+ *     with offsets[0] = 0 and offsets[G] = total_m; every KV slot is below
+ *     num_pages * page_size.
+ *   - Calls are thread-safe.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8Q_ABI_VERSION 1
+
+typedef enum fp8q_status {
+  FP8Q_OK = 0,
+  FP8Q_ERR_NULL = 1,        /* a required pointer is NULL */
+  FP8Q_ERR_SHAPE = 2,       /* negative size, size not a multiple of 128 where required,
+                               count/num_groups < 1, head_dim != 128, page_size < 1 */
+  FP8Q_ERR_STRIDE = 3,      /* a leading dimension is smaller than the row length */
+  FP8Q_ERR_ALIGN = 4,       /* a data pointer or row pitch is not 16-byte aligned */
+  FP8Q_ERR_LAUNCH = 5,      /* the HIP runtime refused a launch */
+  FP8Q_ERR_UNSUPPORTED = 6  /* no gfx950 device is current */
+} fp8q_status;
+
+/* Static string naming a status code. */
+const char* fp8q_status_string(fp8q_status s);
+/* Detail of the last failure on the calling thread ("" if none).  Valid until the
+ * thread's next fp8q call. */
+const char* fp8q_last_error(void);
+/* FP8Q_ABI_VERSION of the loaded library. */
+int fp8q_abi_version(void);
+
+/* ------------------------------------------------------------------------------
+ * Blockwise weight quantization  [FP8-RL, "Prerequisites / FP8 quantization format";
+ * "Method step details" steps 1-2]
+ *
+ * One descriptor per nn.Linear weight, or per stack of expert weights viewed as one
+ * [E*n, k] matrix.  For every 128x128 block (bi, bj) of w (blocks aligned at (0,0)):
+ *   s[bi * (k/128) + bj] = scale of the block;  q[r * ld_q + c] = code of w[r * ld_w + c].
+ *   w: bf16 [n, k] row-major, row pitch ld_w elements (ld_w >= k, ld_w % 8 == 0).
+ *   q: e4m3fn [n, k] row-major, row pitch ld_q bytes (ld_q >= k, ld_q % 16 == 0).
+ *   s: fp32 [n/128][k/128] row-major, contiguous.
+ *   n % 128 == 0 and k % 128 == 0 (else FP8Q_ERR_SHAPE); n == 0 or k == 0 is a no-op
+ *   for that descriptor.  w and q 16-byte aligned (else FP8Q_ERR_ALIGN).
+ * descs is a HOST array of `count` descriptors (count >= 1), read during the call only:
+ * one call quantizes a whole weight sync (e.g. all linears of all layers).
+ * ---------------------------------------------------------------------------- */
+typedef struct fp8q_weight_desc {
+  const void* w;  /* bf16 [n][ld_w] (device) */
+  void* q;        /* e4m3fn [n][ld_q] (device) */
+  float* s;       /* fp32 [n/128][k/128] (device) */
+  int64_t n, k;   /* rows (output features), columns (input features) */
+  int64_t ld_w;   /* elements */
+  int64_t ld_q;   /* bytes */
+} fp8q_weight_desc;
+
+fp8q_status fp8q_quant_weight_blk128(const fp8q_weight_desc* descs /* host */, int32_t count,
+                                     void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Dynamic per-token-group activation quantization  [FP8-RL, "Method step details"
+ * step 1: activations quantized dynamically on every forward]
+ *
+ * For row r < m and group g < k/128 (128 consecutive columns):
+ *   s[g * ld_s + r] = scale of x[r, 128g .. 128g+127];
+ *   q[r * ld_q + c] = code of x[r * ld_x + c].
+ *   x: bf16 [m, k], ld_x >= k, ld_x % 8 == 0; q: e4m3fn [m, k], ld_q >= k, ld_q % 16 == 0;
+ *   s: fp32 [k/128][ld_s], ld_s >= m (scales of one group are contiguous over rows, the
+ *   layout the GEMM reads).  k % 128 == 0.  m == 0 is a no-op.
+ * ---------------------------------------------------------------------------- */
+fp8q_status fp8q_quant_act_g128(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q,
+                                int64_t ld_q, float* s, int64_t ld_s, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Block-scaled W8A8 GEMM  [FP8-RL, "Method step details" step 1; Rounding]
+ *
+ *   y[r, j] = bf16_rne( sum_{kb < k/128} a_s[kb * ld_as + r] * b_s[(j/128) * (k/128) + kb]
+ *                        * sum_{t in block kb} dec(a[r, t]) * dec(b[j, t]) )
+ * The per-block scale product is applied to each 128-wide partial sum in the fp32
+ * accumulator; the result is rounded to bf16 once (round to nearest even).
+ *   a:   e4m3fn [m, k] row-major (activations), ld_a bytes >= k, ld_a % 16 == 0;
+ *   a_s: fp32 [k/128][ld_as], ld_as >= m (as written by fp8q_quant_act_g128);
+ *   b:   e4m3fn [n, k] row-major (weights, nn.Linear [out, in]), ld_b >= k, ld_b % 16 == 0;
+ *   b_s: fp32 [n/128][k/128] contiguous (as written by fp8q_quant_weight_blk128);
+ *   y:   bf16 [m, n] row-major, ld_y elements >= n, ld_y % 8 == 0.
+ *   n % 128 == 0, k % 128 == 0, k >= 128.  m == 0 is a no-op.  No bias.
+ * Accuracy: every element within half a bf16 ulp of the exact value plus 2e-3 of the
+ * largest |y| (fp32 accumulation order differs from exact arithmetic).
+ * ---------------------------------------------------------------------------- */
+fp8q_status fp8q_gemm_w8a8_blkscaled(const void* a, int64_t ld_a, const float* a_s,
+                                     int64_t ld_as, const void* b, int64_t ld_b,
+                                     const float* b_s, void* y, int64_t ld_y, int64_t m,
+                                     int64_t n, int64_t k, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * MoE grouped block-scaled W8A8 GEMM  [FP8-RL, "Method step details" step 1 (MoE
+ * expert layers fc1, fc2); "Experimental results" (MoE gains)]
+ *
+ * Rows of `a` are sorted by expert: rows [offsets[g], offsets[g+1]) belong to expert g
+ * and are multiplied by that expert's weight b[g] with scales b_s[g], exactly as in
+ * fp8q_gemm_w8a8_blkscaled:
+ *   a:   e4m3fn [total_m, k], ld_a bytes; a_s: fp32 [k/128][ld_as], ld_as >= total_m;
+ *   b:   e4m3fn [G][n][k] contiguous; b_s: fp32 [G][n/128][k/128] contiguous;
+ *   group_offsets: int32 [G+1] (device), read on the device only (no host sync);
+ *   y:   bf16 [total_m, n], ld_y elements.
+ * Empty groups are allowed.  num_groups >= 1; n, k multiples of 128; total_m == 0 is a
+ * no-op.  Rows outside [offsets[0], offsets[G]) are not written.
+ * ---------------------------------------------------------------------------- */
+fp8q_status fp8q_grouped_gemm_w8a8(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
+                                   const void* b, const float* b_s,
+                                   const int32_t* group_offsets, int32_t num_groups,
+                                   int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------------
+ * FP8 KV cache quantize-on-write with per-step scale recalibration  [FP8-RL, "Method
+ * step details" step 3; 1T-RL, 3.4]
+ *
+ * For each token t < num_tokens with slot = slot_mapping[t] >= 0 (a negative slot skips
+ * the token), head h and dim d:
+ *   k_cache[((slot / page_size) * page_size + slot % page_size) * H * D + h * D + d]
+ *       = code of k[t * ld_k + h * D + d] / *k_scale,   and likewise for v.
+ * Caches are e4m3fn [num_pages][page_size][H][D]; bytes of slots not written stay as
+ * they were.  H = num_kv_heads >= 1, D = head_dim == 128.
+ *   k, v: bf16 [num_tokens][ld_k] / [num_tokens][ld_v], ld >= H*D, ld % 8 == 0.
+ *   slot_mapping: int64 [num_tokens] (device).
+ *   k_scale, v_scale: one fp32 each (device), in/out.
+ * flags & FP8Q_KV_RECALIBRATE: first set *k_scale = fl32(amax_K / fp8_range) and
+ *   *v_scale = fl32(amax_V / fp8_range), amax over every element this call writes
+ *   (1.0 when it is 0), then write with those scales (the first write of an RL step).
+ * flags == 0: write with the stored *k_scale, *v_scale (later decode steps); values
+ *   beyond the E4M3 range saturate to +-448.
+ * fp8_range > 0 and finite (448 maps amax onto the E4M3 maximum).
+ * ---------------------------------------------------------------------------- */
+#define FP8Q_KV_RECALIBRATE 1u
+
+fp8q_status fp8q_kv_quant(const void* k, int64_t ld_k, const void* v, int64_t ld_v,
+                          int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                          const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                          int32_t page_size, int64_t num_pages, float* k_scale, float* v_scale,
+                          float fp8_range, uint32_t flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

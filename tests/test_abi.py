@@ -1,0 +1,149 @@
+"""C ABI checks that need no GPU: the library loads, exports every function that
+include/fp8q.h declares, and rejects invalid arguments on the host before touching
+the device (nothing is launched in these tests)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import fp8_block_scaled_weight_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+A16 = 0x10000  # 16-byte-aligned fake address: never dereferenced, validation fails first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8q_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = _declared()
+    for n in ("fp8q_quant_weight_blk128", "fp8q_quant_act_g128", "fp8q_gemm_w8a8_blkscaled",
+              "fp8q_grouped_gemm_w8a8", "fp8q_kv_quant"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = fq.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (fp8q_\w+)", out))
+    assert set(_declared()) <= exported
+    assert set(fq.EXPORTED) == set(_declared())
+
+
+def test_version_and_status_strings():
+    assert fq.abi_version() == 1
+    for code, name in ((0, "FP8Q_OK"), (1, "FP8Q_ERR_NULL"), (2, "FP8Q_ERR_SHAPE"), (3, "FP8Q_ERR_STRIDE"),
+                       (4, "FP8Q_ERR_ALIGN"), (5, "FP8Q_ERR_LAUNCH"), (6, "FP8Q_ERR_UNSUPPORTED")):
+        assert fq.status_string(code) == name
+
+
+def _act(**kw):
+    a = dict(x=A16, m=4, k=256, ld_x=256, q=A16, ld_q=256, s=A16, ld_s=4, stream=None)
+    a.update(kw)
+    return fq.lib().fp8q_quant_act_g128(a["x"], a["m"], a["k"], a["ld_x"], a["q"], a["ld_q"], a["s"],
+                                        a["ld_s"], a["stream"])
+
+
+def test_act_quant_validation():
+    assert _act(m=-1) == fq.FP8Q_ERR_SHAPE
+    assert _act(k=100, ld_x=100, ld_q=100) == fq.FP8Q_ERR_SHAPE
+    assert _act(x=None) == fq.FP8Q_ERR_NULL
+    assert _act(s=None) == fq.FP8Q_ERR_NULL
+    assert _act(ld_x=128) == fq.FP8Q_ERR_STRIDE
+    assert _act(ld_s=3) == fq.FP8Q_ERR_STRIDE
+    assert _act(x=A16 + 2) == fq.FP8Q_ERR_ALIGN
+    assert _act(ld_q=264) == fq.FP8Q_ERR_ALIGN
+    assert _act(ld_x=260) == fq.FP8Q_ERR_ALIGN
+    assert "multiple of 128" in fq.last_error() or fq.last_error()
+
+
+def _gemm(**kw):
+    a = dict(a=A16, ld_a=256, a_s=A16, ld_as=8, b=A16, ld_b=256, b_s=A16, y=A16, ld_y=128, m=8, n=128, k=256)
+    a.update(kw)
+    return fq.lib().fp8q_gemm_w8a8_blkscaled(a["a"], a["ld_a"], a["a_s"], a["ld_as"], a["b"], a["ld_b"],
+                                             a["b_s"], a["y"], a["ld_y"], a["m"], a["n"], a["k"], None)
+
+
+def test_gemm_validation():
+    assert _gemm(n=100) == fq.FP8Q_ERR_SHAPE
+    assert _gemm(k=0) == fq.FP8Q_ERR_SHAPE
+    assert _gemm(m=-3) == fq.FP8Q_ERR_SHAPE
+    assert _gemm(b=None) == fq.FP8Q_ERR_NULL
+    assert _gemm(ld_as=7) == fq.FP8Q_ERR_STRIDE
+    assert _gemm(ld_y=64) == fq.FP8Q_ERR_STRIDE
+    assert _gemm(ld_a=272, a=A16 + 8) == fq.FP8Q_ERR_ALIGN
+    assert _gemm(ld_y=132) == fq.FP8Q_ERR_ALIGN
+
+
+def test_grouped_validation():
+    L = fq.lib()
+    f = L.fp8q_grouped_gemm_w8a8
+    assert f(A16, 256, A16, 64, A16, A16, A16, 0, 64, A16, 128, 128, 256, None) == fq.FP8Q_ERR_SHAPE
+    assert f(A16, 256, A16, 64, A16, A16, None, 4, 64, A16, 128, 128, 256, None) == fq.FP8Q_ERR_NULL
+    assert f(A16, 256, A16, 32, A16, A16, A16, 4, 64, A16, 128, 128, 256, None) == fq.FP8Q_ERR_STRIDE
+    assert f(A16, 256, A16, 64, A16, A16, A16, 4, 64, A16, 128, 192, 256, None) == fq.FP8Q_ERR_SHAPE
+
+
+def test_weight_validation():
+    L = fq.lib()
+    d = (fq.WeightDesc * 2)()
+    d[0] = fq.WeightDesc(A16, A16, A16, 256, 256, 256, 256)
+    d[1] = fq.WeightDesc(A16, A16, A16, 128, 384, 384, 384)
+    assert L.fp8q_quant_weight_blk128(d, 0, None) == fq.FP8Q_ERR_SHAPE
+    assert L.fp8q_quant_weight_blk128(None, 1, None) == fq.FP8Q_ERR_NULL
+    d[1] = fq.WeightDesc(A16, A16, A16, 100, 384, 384, 384)
+    assert L.fp8q_quant_weight_blk128(d, 2, None) == fq.FP8Q_ERR_SHAPE
+    d[1] = fq.WeightDesc(A16, None, A16, 128, 384, 384, 384)
+    assert L.fp8q_quant_weight_blk128(d, 2, None) == fq.FP8Q_ERR_NULL
+    d[1] = fq.WeightDesc(A16, A16, A16, 128, 384, 256, 384)
+    assert L.fp8q_quant_weight_blk128(d, 2, None) == fq.FP8Q_ERR_STRIDE
+    d[1] = fq.WeightDesc(A16, A16 + 4, A16, 128, 384, 384, 384)
+    assert L.fp8q_quant_weight_blk128(d, 2, None) == fq.FP8Q_ERR_ALIGN
+
+
+def test_kv_validation():
+    L = fq.lib()
+
+    def kv(**kw):
+        a = dict(k=A16, ld_k=1024, v=A16, ld_v=1024, t=16, h=8, d=128, slots=A16, kc=A16, vc=A16, page=16,
+                 pages=4, ks=A16, vs=A16, rng=448.0, flags=1)
+        a.update(kw)
+        return L.fp8q_kv_quant(a["k"], a["ld_k"], a["v"], a["ld_v"], a["t"], a["h"], a["d"], a["slots"],
+                               a["kc"], a["vc"], a["page"], a["pages"], a["ks"], a["vs"], a["rng"],
+                               a["flags"], None)
+
+    assert kv(d=64) == fq.FP8Q_ERR_SHAPE
+    assert kv(h=0) == fq.FP8Q_ERR_SHAPE
+    assert kv(page=0) == fq.FP8Q_ERR_SHAPE
+    assert kv(rng=0.0) == fq.FP8Q_ERR_SHAPE
+    assert kv(rng=float("inf")) == fq.FP8Q_ERR_SHAPE
+    assert kv(flags=2) == fq.FP8Q_ERR_SHAPE
+    assert kv(ks=None) == fq.FP8Q_ERR_NULL
+    assert kv(slots=None) == fq.FP8Q_ERR_NULL
+    assert kv(ld_k=512) == fq.FP8Q_ERR_STRIDE
+    assert kv(kc=A16 + 1) == fq.FP8Q_ERR_ALIGN
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful without a GPU")
+def test_valid_arguments_without_gpu_report_unsupported():
+    assert _act() == fq.FP8Q_ERR_UNSUPPORTED
+    assert _gemm() == fq.FP8Q_ERR_UNSUPPORTED
+    assert "device" in fq.last_error()
+
+
+def test_python_binding_refuses_host_tensors():
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    q = torch.zeros(4, 128, dtype=torch.uint8)
+    s = torch.zeros(1, 4, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        fq.fp8q_quant_act_g128(x, q, s, stream=0)

@@ -1,0 +1,182 @@
+"""GPU parity of the block-scaled W8A8 GEMM, dense and grouped, against the fp64 oracle
+(FP8-RL summary page, "Method step details" step 1; the output is rounded to bf16
+once, per "Where rounding happens matters").  Gate: every element within half a bf16
+ulp of the exact value plus 2e-3 of max|y|.  Operands are quantized by the oracle so
+the GEMM is tested on its own."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_block_scaled_weight_amd as fq
+from fp8_block_scaled_weight_amd import synth
+from tests._helpers import bf16_bits, gemm_gate
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def quantized_operands(m, n, k, cfg=2, layer=0, tensor=0):
+    w = synth.weight(cfg, layer, tensor, n, k)
+    x = synth.activation(cfg, layer, tensor + 50, m, k)
+    wq, ws = oracle.quant_weight_blk128(w)
+    xq, xs = oracle.quant_act_g128(x)
+    return xq, xs, wq, ws
+
+
+def gpu_gemm(xq, xs, wq, ws, ld_y=None):
+    m, k = xq.shape
+    n = wq.shape[0]
+    ld_y = n if ld_y is None else ld_y
+    yfull = torch.full((max(m, 1), ld_y), float("nan"), dtype=torch.bfloat16, device=DEV)[:m]
+    y = yfull[:, :n]
+    fq.fp8q_gemm_w8a8_blkscaled(_dev_u8(xq), _dev_f32(xs), _dev_u8(wq), _dev_f32(ws), y)
+    torch.cuda.synchronize()
+    return bf16_bits(y), bf16_bits(yfull)
+
+
+def check(xq, xs, wq, ws, rows=None, ld_y=None):
+    y, yfull = gpu_gemm(xq, xs, wq, ws, ld_y)
+    if rows is None:
+        ref = oracle.gemm_w8a8(xq, xs, wq, ws)
+        got = y
+    else:
+        ref = oracle.gemm_w8a8(xq[rows], xs[:, rows], wq, ws)
+        got = y[rows]
+    ok, ratio, nrm = gemm_gate(got, ref)
+    assert ok, f"gate exceeded: worst err/bound {ratio:.3f}, normwise {nrm:.2e}"
+    assert nrm < 4e-3
+    return yfull
+
+
+def test_tiny():
+    w, x = synth.tiny()
+    wq, ws = oracle.quant_weight_blk128(w)
+    xq, xs = oracle.quant_act_g128(x)
+    check(xq, xs, wq, ws)
+
+
+@pytest.mark.parametrize("m", [1, 5, 64, 130, 512])
+@pytest.mark.parametrize("n", [1024, 4096])
+def test_attention_shapes(m, n):
+    check(*quantized_operands(m, n, 4096, tensor=n))
+
+
+def test_m4096_sampled_rows():
+    g = np.random.Generator(np.random.PCG64(1))
+    rows = np.sort(g.choice(4096, size=96, replace=False))
+    rows[:2] = [0, 4095]
+    for n in (4096, 1024):
+        check(*quantized_operands(4096, n, 4096, tensor=n + 1), rows=rows)
+
+
+def test_mlp_shapes_sampled():
+    g = np.random.Generator(np.random.PCG64(2))
+    xq, xs, wq, ws = quantized_operands(64, 12288, 4096, cfg=3)
+    check(xq, xs, wq, ws)
+    xq, xs, wq, ws = quantized_operands(300, 4096, 12288, cfg=3, tensor=2)
+    check(xq, xs, wq, ws, rows=np.sort(g.choice(300, 40, replace=False)))
+
+
+def test_padded_output_pitch_untouched():
+    xq, xs, wq, ws = quantized_operands(40, 256, 384, tensor=9)
+    yfull = check(xq, xs, wq, ws, ld_y=264)
+    assert np.all(yfull[:, 256:] == 0x7FC0)  # NaN fill beyond n is untouched
+
+
+def test_zero_scales_and_zero_rows():
+    xq, xs, wq, ws = quantized_operands(48, 256, 256, tensor=11)
+    xq[3] = 0
+    ws[1, 0] = 0.0
+    check(xq, xs, wq, ws)
+
+
+def test_deterministic():
+    ops = quantized_operands(256, 1024, 2048, tensor=12)
+    a, _ = gpu_gemm(*ops)
+    b, _ = gpu_gemm(*ops)
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------------- grouped
+def grouped_case(sizes, n, k, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    G = len(sizes)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    m = int(off[-1])
+    bq = np.empty((G, n, k), np.uint8)
+    bs = np.empty((G, n // 128, k // 128), np.float32)
+    for e in range(G):
+        bq[e], bs[e] = oracle.quant_weight_blk128(synth.weight(4, 0, e, n, k, outlier_frac=0.0))
+    x = synth.to_bf16_bits(g.standard_normal((max(m, 1), k), dtype=np.float32))[:m]
+    aq, as_ = oracle.quant_act_g128(x) if m else (np.zeros((0, k), np.uint8), np.zeros((k // 128, 0), np.float32))
+    return aq, as_, bq, bs, off
+
+
+def gpu_grouped(aq, as_, bq, bs, off):
+    m, k = aq.shape
+    n = bq.shape[1]
+    y = torch.full((max(m, 1), n), float("nan"), dtype=torch.bfloat16, device=DEV)[:m]
+    fq.fp8q_grouped_gemm_w8a8(_dev_u8(aq), _dev_f32(as_), _dev_u8(bq), _dev_f32(bs),
+                              torch.from_numpy(off).to(DEV), y)
+    torch.cuda.synchronize()
+    return bf16_bits(y)
+
+
+def check_grouped(case, rows=None):
+    aq, as_, bq, bs, off = case
+    y = gpu_grouped(*case)
+    if rows is None:
+        ref = oracle.grouped_gemm_w8a8(aq, as_, bq, bs, off)
+        ok, ratio, nrm = gemm_gate(y, ref)
+        assert ok, f"worst err/bound {ratio:.3f}"
+        return
+    for gi in rows:
+        r0, r1 = off[gi], off[gi + 1]
+        if r1 == r0:
+            continue
+        ref = oracle.gemm_w8a8(aq[r0:r1], as_[:, r0:r1], bq[gi], bs[gi])
+        ok, ratio, nrm = gemm_gate(y[r0:r1], ref)
+        assert ok, f"group {gi}: worst err/bound {ratio:.3f}"
+
+
+def test_grouped_small_with_empty_groups():
+    check_grouped(grouped_case([3, 0, 130, 1, 0, 257, 64], 256, 384, 5))
+
+
+def test_grouped_all_empty_but_one():
+    check_grouped(grouped_case([0, 0, 200, 0], 128, 256, 6))
+
+
+def test_grouped_many_groups():
+    g = np.random.Generator(np.random.PCG64(7))
+    sizes = g.integers(0, 90, size=70)
+    check_grouped(grouped_case(list(sizes), 256, 256, 7))
+
+
+def test_grouped_moe_routing_fc2_subset():
+    """Zipf-skewed top-8 routing over 128 experts (4096 tokens); fc2 shape n=2048, k=768.
+    Checks a subset of groups (smallest, largest, a few others) against the oracle."""
+    row_token, off, _ = synth.moe_routing(0)
+    sizes = np.diff(off)
+    n, k = 2048, 768
+    G = 128
+    bq = np.empty((G, n, k), np.uint8)
+    bs = np.empty((G, n // 128, k // 128), np.float32)
+    rng = np.random.Generator(np.random.PCG64(9))
+    # expert weights: quantize a few distinct tensors and reuse them to keep the oracle fast
+    base = [oracle.quant_weight_blk128(synth.weight(4, 0, e, n, k, outlier_frac=0.0)) for e in range(4)]
+    for e in range(G):
+        bq[e], bs[e] = base[e % 4]
+    x = synth.to_bf16_bits(rng.standard_normal((int(off[-1]), k), dtype=np.float32))
+    aq, as_ = oracle.quant_act_g128(x)
+    pick = sorted({int(np.argmin(sizes)), int(np.argmax(sizes)), 0, 17, 64, 127})
+    check_grouped((aq, as_, bq, bs, off), rows=pick)
