@@ -1,0 +1,454 @@
+"""Benchmark of the FP8 rollout hot path on one MI355X.
+
+One step = one Qwen3-8B-like attention block at 4096 tokens through every hot-path
+call, inputs resident in HBM:
+  weight sync of q/k/v/o (128x128 blockwise quantization, one batched call)
+  -> 1x128 quantization of the block input X [4096, 4096]
+  -> block-scaled W8A8 GEMMs q (4096x4096), k and v (1024x4096)
+  -> FP8 KV-cache write of the k/v outputs (8 heads x 128) with scale recalibration
+  -> 1x128 quantization of the attention output stand-in [4096, 4096]
+  -> o GEMM (4096x4096).
+`value` is the step's GEMM FLOPs divided by the measured step time (TFLOP/s).
+Side legs (not in `value`) time the full 36-layer weight sync, one MoE layer's
+grouped GEMMs (128 experts, Zipf top-8 routing of 4096 tokens) and one layer of the
+20,000-token x 64-sequence FP8 KV step.  The CPU oracle is timed on a bounded sample
+of the same step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-legs] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+TOKENS = 4096
+HIDDEN = 4096
+KV_DIM = 1024
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-legs", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events on the stream every fp8q call is enqueued on (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ev = {}
+
+    def span(self, name):
+        torch = self.torch
+        timer = self
+
+        class _S:
+            def __enter__(self):
+                self.a = torch.cuda.Event(enable_timing=True)
+                self.b = torch.cuda.Event(enable_timing=True)
+                self.a.record()
+
+            def __exit__(self, *exc):
+                self.b.record()
+                timer.ev.setdefault(name, []).append((self.a, self.b))
+
+        return _S()
+
+    def ms(self, name):
+        return [a.elapsed_time(b) for a, b in self.ev[name]]
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "fp8_block_scaled_weight_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_tag: str, digest: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on
+    the current source; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        log("bench.py: only --gpus 1 is supported (single-GPU hot path; see the sharding notes)")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_block_scaled_weight_amd as fq
+    from fp8_block_scaled_weight_amd import synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (libfp8q runs on gfx950 only)")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fq.lib()
+
+    # ------------------------------------------------------------------ inputs
+    log("generating inputs")
+    W = {
+        "q": synth.device_normal_bf16((HIDDEN, HIDDEN), 0.02, dev, 2, 0, 0, outlier_p=1e-3, outlier_mult=20.0),
+        "k": synth.device_normal_bf16((KV_DIM, HIDDEN), 0.02, dev, 2, 0, 1, outlier_p=1e-3, outlier_mult=20.0),
+        "v": synth.device_normal_bf16((KV_DIM, HIDDEN), 0.02, dev, 2, 0, 2, outlier_p=1e-3, outlier_mult=20.0),
+        "o": synth.device_normal_bf16((HIDDEN, HIDDEN), 0.02, dev, 2, 0, 3, outlier_p=1e-3, outlier_mult=20.0),
+    }
+    WQ = {n: torch.empty(w.shape, dtype=torch.uint8, device=dev) for n, w in W.items()}
+    WS = {n: torch.empty((w.shape[0] // 128, w.shape[1] // 128), dtype=torch.float32, device=dev)
+          for n, w in W.items()}
+    X = synth.device_activation(TOKENS, HIDDEN, dev, 2, 0, 10)
+    O_in = synth.device_activation(TOKENS, HIDDEN, dev, 2, 0, 11)
+    Xq = torch.empty((TOKENS, HIDDEN), dtype=torch.uint8, device=dev)
+    Xs = torch.empty((HIDDEN // 128, TOKENS), dtype=torch.float32, device=dev)
+    Oq = torch.empty_like(Xq)
+    Os = torch.empty_like(Xs)
+    Y = {n: torch.empty((TOKENS, W[n].shape[0]), dtype=torch.bfloat16, device=dev) for n in W}
+    slots_np, pages = synth.kv_slot_mapping(2, 0, seqs=64, seq_len=TOKENS // 64)
+    slots = torch.from_numpy(slots_np).to(dev)
+    Kc = torch.empty((pages, 16, 8, 128), dtype=torch.uint8, device=dev)
+    Vc = torch.empty_like(Kc)
+    ks = torch.ones(1, dtype=torch.float32, device=dev)
+    vs = torch.ones(1, dtype=torch.float32, device=dev)
+    descs = [(W[n], WQ[n], WS[n]) for n in ("q", "k", "v", "o")]
+
+    T = Timer(torch)
+
+    def step(timed: bool):
+        def sp(name):
+            return T.span(name) if timed else _Null()
+        with sp("a1_weight_sync_qkvo"):
+            fq.fp8q_quant_weight_blk128(descs)
+        with sp("a2_act_quant_x"):
+            fq.fp8q_quant_act_g128(X, Xq, Xs)
+        with sp("a3_gemm_q"):
+            fq.fp8q_gemm_w8a8_blkscaled(Xq, Xs, WQ["q"], WS["q"], Y["q"])
+        with sp("a3_gemm_k"):
+            fq.fp8q_gemm_w8a8_blkscaled(Xq, Xs, WQ["k"], WS["k"], Y["k"])
+        with sp("a3_gemm_v"):
+            fq.fp8q_gemm_w8a8_blkscaled(Xq, Xs, WQ["v"], WS["v"], Y["v"])
+        with sp("a5a6_kv_recal_write"):
+            fq.fp8q_kv_quant(Y["k"].view(TOKENS, 8, 128), Y["v"].view(TOKENS, 8, 128), slots, Kc, Vc, ks, vs,
+                             448.0, recalibrate=True)
+        with sp("a2_act_quant_o"):
+            fq.fp8q_quant_act_g128(O_in, Oq, Os)
+        with sp("a3_gemm_o"):
+            fq.fp8q_gemm_w8a8_blkscaled(Oq, Os, WQ["o"], WS["o"], Y["o"])
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step(True)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+
+    gemm_flops = 2 * TOKENS * HIDDEN * (HIDDEN + 2 * KV_DIM + HIDDEN)
+    value = gemm_flops / (ms_step * 1e-3) / 1e12
+
+    # per-call breakdown and algorithmic bytes / flops
+    w_elems = sum(w.numel() for w in W.values())
+    bytes_of = {
+        "a1_weight_sync_qkvo": 3 * w_elems + 4 * w_elems / 16384,
+        "a2_act_quant_x": 3 * TOKENS * HIDDEN + 4 * TOKENS * HIDDEN / 128,
+        "a2_act_quant_o": 3 * TOKENS * HIDDEN + 4 * TOKENS * HIDDEN / 128,
+        "a5a6_kv_recal_write": 5 * 2 * TOKENS * KV_DIM + 8 * TOKENS,
+    }
+    flops_of = {f"a3_gemm_{n}": 2 * TOKENS * W[n].shape[0] * HIDDEN for n in W}
+    calls = {}
+    for name in T.ev:
+        ts = T.ms(name)
+        avg = sum(ts) / len(ts)
+        d = {"avg_us": round(avg * 1e3, 2)}
+        if name in bytes_of:
+            gbs = bytes_of[name] / (avg * 1e-3) / 1e9
+            d.update(GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBPS, 4))
+        if name in flops_of:
+            tf = flops_of[name] / (avg * 1e-3) / 1e12
+            d.update(TFLOPs=round(tf, 1), frac_fp8_peak=round(tf / FP8_PEAK_TFLOPS, 4))
+        calls[name] = d
+    q_bytes = sum(bytes_of.values())
+    q_ms = sum(sum(T.ms(n)) / args.steps for n in bytes_of)
+    g_ms = sum(sum(T.ms(n)) / args.steps for n in flops_of)
+
+    # dominant kernel: the 4096x4096x4096 GEMM (q and o projections)
+    dom = T.ms("a3_gemm_q") + T.ms("a3_gemm_o")
+    dom_avg_ms = sum(dom) / len(dom)
+    dom_flops = 2 * TOKENS * HIDDEN * HIDDEN
+    achieved = dom_flops / (dom_avg_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                "traffic": traffic_from_profile("gemm_w8a8_4096", source_digest("gemm.hip")),
+                "kernel": "gemm_w8a8_kernel M=N=K=4096", "avg_us": round(dom_avg_ms * 1e3, 2)}
+
+    out = {
+        "metric": "W8A8 block-scaled GEMM TFLOP/s (% FP8 peak) + quantizer GB/s (% HBM) at 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-in/fp32-acc/bf16-out",
+        "data": "synthetic (seeded; Qwen3-8B-like shapes, N(0,0.02) weights with 0.1% x20 outliers, "
+                "N(0,1) activations with 4 outlier channels x50)",
+        "config": {"workload": "attention block, Qwen3-8B-like: hidden 4096, q/o 4096x4096, k/v 1024x4096, "
+                               "4096 tokens; weight sync + act quant + 4 W8A8 GEMMs + FP8 KV write",
+                   "tokens": TOKENS, "hidden": HIDDEN, "kv_heads": 8, "head_dim": 128, "parallelism": "none"},
+        "gemm_TFLOPs": round(gemm_flops / (g_ms * 1e-3) / 1e12, 1),
+        "gemm_frac_fp8_peak": round(gemm_flops / (g_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "quantizer_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+        "quantizer_frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "calls": calls,
+        "roofline": roofline,
+    }
+
+    if not args.no_legs:
+        out["legs"] = legs(torch, fq, synth, dev)
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(torch, np, X, O_in, W, slots_np, value, gemm_flops)
+
+    print(json.dumps(out), flush=True)
+
+
+class _Null:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
+def _time(torch, fn, iters, warm=2):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(iters):
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def legs(torch, fq, synth, dev):
+    """Side measurements of the other hot-path workloads (not part of `value`)."""
+    res = {}
+    # full weight sync: 36 layers x {q, k, v, o, gate, up, down}
+    log("leg: 36-layer weight sync")
+    shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (12288, 4096), (12288, 4096), (4096, 12288)]
+    ws, qs, ss = [], [], []
+    for layer in range(36):
+        for t, (n, k) in enumerate(shapes):
+            ws.append(synth.device_normal_bf16((n, k), 0.02, dev, 3, layer, t, outlier_p=1e-3, outlier_mult=20.0))
+            qs.append(torch.empty((n, k), dtype=torch.uint8, device=dev))
+            ss.append(torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev))
+    descs = list(zip(ws, qs, ss))
+    el = sum(w.numel() for w in ws)
+    ms = _time(torch, lambda: fq.fp8q_quant_weight_blk128(descs), 5, 1)
+    gb = (3 * el + 4 * el / 16384) / 1e9
+    res["a1_sync_36_layers"] = {"tensors": len(ws), "params": el, "ms": round(ms, 3),
+                                "GBps": round(gb / ms * 1e3, 1), "frac_hbm": round(gb / ms * 1e3 / HBM_PEAK_GBPS, 4)}
+    del ws, qs, ss, descs
+    torch.cuda.empty_cache()
+
+    # MoE layer: expert weight quantization + grouped fc1 / fc2
+    log("leg: MoE layer")
+    E, H, I = 128, 2048, 768
+    row_token, off, _ = synth.moe_routing(0)
+    mrows = int(off[-1])
+    fc1 = synth.device_normal_bf16((E * 2 * I, H), 0.02, dev, 4, 0, 0)
+    fc2 = synth.device_normal_bf16((E * H, I), 0.02, dev, 4, 0, 1)
+    fc1q = torch.empty(fc1.shape, dtype=torch.uint8, device=dev)
+    fc2q = torch.empty(fc2.shape, dtype=torch.uint8, device=dev)
+    fc1s = torch.empty((E * 2 * I // 128, H // 128), dtype=torch.float32, device=dev)
+    fc2s = torch.empty((E * H // 128, I // 128), dtype=torch.float32, device=dev)
+    edescs = [(fc1, fc1q, fc1s), (fc2, fc2q, fc2s)]
+    el = fc1.numel() + fc2.numel()
+    ms = _time(torch, lambda: fq.fp8q_quant_weight_blk128(edescs), 5)
+    gb = (3 * el + 4 * el / 16384) / 1e9
+    res["a1_moe_expert_weights_layer"] = {"params": el, "ms": round(ms, 3), "GBps": round(gb / ms * 1e3, 1),
+                                          "frac_hbm": round(gb / ms * 1e3 / HBM_PEAK_GBPS, 4)}
+    x = synth.device_activation(4096, H, dev, 4, 0, 5)
+    xs_rows = x[torch.from_numpy(row_token).to(dev)]
+    a1q = torch.empty((mrows, H), dtype=torch.uint8, device=dev)
+    a1s = torch.empty((H // 128, mrows), dtype=torch.float32, device=dev)
+    fq.fp8q_quant_act_g128(xs_rows, a1q, a1s)
+    a2 = synth.device_activation(mrows, I, dev, 4, 0, 6, outlier_channels=0)
+    a2q = torch.empty((mrows, I), dtype=torch.uint8, device=dev)
+    a2s = torch.empty((I // 128, mrows), dtype=torch.float32, device=dev)
+    ms_aq = _time(torch, lambda: fq.fp8q_quant_act_g128(a2, a2q, a2s), 10)
+    offs = torch.from_numpy(off).to(dev)
+    y1 = torch.empty((mrows, 2 * I), dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty((mrows, H), dtype=torch.bfloat16, device=dev)
+    b1 = fc1q.view(E, 2 * I, H)
+    b1s = fc1s.view(E, 2 * I // 128, H // 128)
+    b2 = fc2q.view(E, H, I)
+    b2s = fc2s.view(E, H // 128, I // 128)
+    ms1 = _time(torch, lambda: fq.fp8q_grouped_gemm_w8a8(a1q, a1s, b1, b1s, offs, y1), 10)
+    ms2 = _time(torch, lambda: fq.fp8q_grouped_gemm_w8a8(a2q, a2s, b2, b2s, offs, y2), 10)
+    f1 = 2 * mrows * 2 * I * H
+    f2 = 2 * mrows * H * I
+    by1 = mrows * H + b1.numel() + 2 * mrows * 2 * I
+    by2 = mrows * I + b2.numel() + 2 * mrows * H
+    for name, f, by, ms_ in (("a4_moe_fc1", f1, by1, ms1), ("a4_moe_fc2", f2, by2, ms2)):
+        tf = f / (ms_ * 1e-3) / 1e12
+        ceil = min(FP8_PEAK_TFLOPS, f / by * HBM_PEAK_GBPS / 1e3)
+        res[name] = {"rows": mrows, "us": round(ms_ * 1e3, 1), "TFLOPs": round(tf, 1),
+                     "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4), "frac_roofline": round(tf / ceil, 4),
+                     "roofline_TFLOPs": round(ceil, 1)}
+    res["a2_moe_fc2_act_quant"] = {"us": round(ms_aq * 1e3, 1),
+                                   "GBps": round((3 * a2.numel() + 4 * a2.numel() / 128) / (ms_aq * 1e-3) / 1e9, 1)}
+    del fc1, fc2, fc1q, fc2q, x, xs_rows, a1q, a2, a2q, y1, y2
+    torch.cuda.empty_cache()
+
+    # KV: one layer of 64 sequences x 20,000 tokens, recalibrate + write; then a decode write
+    log("leg: KV layer")
+    slots_np, pages = synth.kv_slot_mapping()
+    T = len(slots_np)
+    k = synth.device_kv(T, dev, 5, 0, 0)
+    v = synth.device_kv(T, dev, 5, 0, 1)
+    sl = torch.from_numpy(slots_np).to(dev)
+    kc = torch.empty((pages, 16, 8, 128), dtype=torch.uint8, device=dev)
+    vc = torch.empty_like(kc)
+    ks = torch.ones(1, device=dev)
+    vs = torch.ones(1, device=dev)
+    ms = _time(torch, lambda: fq.fp8q_kv_quant(k, v, sl, kc, vc, ks, vs, 448.0, recalibrate=True), 5)
+    gb = (5 * 2 * T * 1024 + 8 * T) / 1e9
+    res["a5a6_kv_layer_recal_write"] = {"tokens": T, "ms": round(ms, 3), "GBps": round(gb / ms * 1e3, 1),
+                                        "frac_hbm": round(gb / ms * 1e3 / HBM_PEAK_GBPS, 4),
+                                        "step_36_layers_ms_est": round(36 * ms, 2)}
+    dec_idx = torch.arange(64, device=dev) * 20000 + 19999
+    kd, vd, sd = k[dec_idx].contiguous(), v[dec_idx].contiguous(), sl[dec_idx].contiguous()
+    ms = _time(torch, lambda: fq.fp8q_kv_quant(kd, vd, sd, kc, vc, ks, vs, 448.0, recalibrate=False), 20)
+    res["a6_kv_decode_write_64_tokens"] = {"us": round(ms * 1e3, 2)}
+    del k, v, kc, vc
+    torch.cuda.empty_cache()
+
+    # small-M GEMMs (decode / short prefill shapes)
+    log("leg: small-M GEMMs")
+    for m in (1, 64, 512):
+        for n in (4096, 1024):
+            a = torch.randint(0, 0x77, (m, 4096), dtype=torch.uint8, device=dev)
+            b = torch.randint(0, 0x77, (n, 4096), dtype=torch.uint8, device=dev)
+            asc = torch.rand((32, m), device=dev)
+            bsc = torch.rand((n // 128, 32), device=dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            ms = _time(torch, lambda: fq.fp8q_gemm_w8a8_blkscaled(a, asc, b, bsc, y), 20)
+            f = 2 * m * n * 4096
+            by = m * 4096 + n * 4096 + 2 * m * n
+            ceil = min(FP8_PEAK_TFLOPS, f / by * HBM_PEAK_GBPS / 1e3)
+            tf = f / (ms * 1e-3) / 1e12
+            res[f"a3_gemm_m{m}_n{n}"] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 2),
+                                         "frac_roofline": round(tf / ceil, 4)}
+    return res
+
+
+def cpu_baseline(torch, np, X, O_in, W, slots_np, gpu_value, gemm_flops):
+    """The oracle, as it stands, on a bounded sample of the step: 128 of the 4096 tokens
+    through act-quant, the q/k/v/o GEMMs (fp64) and the KV write, plus one 128-row block
+    row of each weight through blockwise quantization.  Each part is scaled to the full
+    step (x32 for the token parts, x20 for the weight sync) and the step's GEMM FLOPs are
+    divided by the estimated step time (TFLOP/s, like `value`)."""
+    import oracle
+
+    rows = 128
+    tok_scale = TOKENS / rows
+    h = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    xb, ob = h(X[:rows]), h(O_in[:rows])
+    wfull = {n: h(W[n]) for n in W}
+    wrow = {n: wfull[n][:128] for n in W}
+    w_scale = sum(w.shape[0] for w in wfull.values()) / (128 * len(W))
+    log(f"cpu baseline: oracle on {rows} tokens and {len(W)} weight block-rows "
+        f"({oracle.num_threads()} threads)")
+    wq = {n: oracle.quant_weight_blk128(wfull[n]) for n in wfull}  # operands of the sampled GEMMs (setup)
+
+    t0 = time.perf_counter()
+    for n in wrow:
+        oracle.quant_weight_blk128(wrow[n])
+    t_w = time.perf_counter() - t0
+
+    t1 = time.perf_counter()
+    xq, xs = oracle.quant_act_g128(xb)
+    yq = oracle.gemm_w8a8(xq, xs, *wq["q"])
+    yk = oracle.gemm_w8a8(xq, xs, *wq["k"])
+    yv = oracle.gemm_w8a8(xq, xs, *wq["v"])
+    t_gemm_kv_in = time.perf_counter() - t1
+    bf = lambda y: torch.from_numpy(y.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy() \
+        .view(np.uint16).reshape(rows, 8, 128)
+    kb, vb = bf(yk), bf(yv)
+    cache = np.zeros((int(slots_np[:rows].max()) // 16 + 1, 16, 8, 128), np.uint8)
+    t2 = time.perf_counter()
+    oracle.kv_quant(kb, vb, slots_np[:rows], cache, cache, 16)
+    oq, os_ = oracle.quant_act_g128(ob)
+    oracle.gemm_w8a8(oq, os_, *wq["o"])
+    t_rest = time.perf_counter() - t2
+
+    t_tok = t_gemm_kv_in + t_rest
+    sample_s = t_w + t_tok
+    est_step_s = t_w * w_scale + t_tok * tok_scale
+    value = gemm_flops / est_step_s / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{rows} of {TOKENS} tokens (act quant, q/k/v/o GEMMs in fp64, KV write; x{tok_scale:g}) "
+                      f"and one 128-row block row of each of q/k/v/o (blockwise quantization; x{w_scale:g}); "
+                      f"{sample_s:.1f} s measured, {est_step_s:.0f} s estimated per step",
+            "sample_seconds": round(sample_s, 2), "est_step_seconds": round(est_step_s, 1),
+            "gpu_over_cpu": round(gpu_value / value, 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -24,10 +24,12 @@ SOURCES = ["api.cpp", "quant.hip", "kv_quant.hip", "gemm.hip"]
 # No fast-math: fp32 division and the residual FMA must be IEEE; denormals are kept.
 # Packed fp32 instructions are disabled for all device code.
 HIPFLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fno-fast-math",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-fno-fast-math",
     "-fno-gpu-flush-denormals-to-zero", "-ffp-contract=fast",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function",
+    # MFMA results feed VALU promotion FMAs: keep them in VGPRs (no AGPR round trip)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

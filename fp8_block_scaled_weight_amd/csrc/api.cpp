@@ -27,6 +27,9 @@ fp8q_status ok() {
   return FP8Q_OK;
 }
 
+// The GEMM kernels address each operand with 32-bit byte offsets.
+constexpr int64_t kMaxOperandBytes = (int64_t)1 << 31;
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
@@ -157,6 +160,8 @@ static fp8q_status check_gemm_common(const void* a, int64_t ld_a, const float* a
   if (ld_a < k || ld_as < m || ld_y < n) return fail(FP8Q_ERR_STRIDE, "ld_a < k, ld_as < m or ld_y < n");
   if (!aligned16(a) || !aligned16(y) || ld_a % 16 || ld_y % 8 || !aligned4(a_s))
     return fail(FP8Q_ERR_ALIGN, "a/y must be 16-byte aligned with ld_a %% 16 == 0 and ld_y %% 8 == 0");
+  if (m * ld_a > kMaxOperandBytes || ld_as * 4 > kMaxOperandBytes)
+    return fail(FP8Q_ERR_SHAPE, "an operand spans more than 2 GiB");
   return FP8Q_OK;
 }
 
@@ -170,6 +175,7 @@ fp8q_status fp8q_gemm_w8a8_blkscaled(const void* a, int64_t ld_a, const float* a
     if (ld_b < k) return fail(FP8Q_ERR_STRIDE, "ld_b < k");
     if (!aligned16(b) || ld_b % 16 || !aligned4(b_s))
       return fail(FP8Q_ERR_ALIGN, "b must be 16-byte aligned with ld_b %% 16 == 0");
+    if (n * ld_b > kMaxOperandBytes) return fail(FP8Q_ERR_SHAPE, "b spans more than 2 GiB");
   }
   st = check_device();
   if (st != FP8Q_OK) return st;
@@ -189,6 +195,7 @@ fp8q_status fp8q_grouped_gemm_w8a8(const void* a, int64_t ld_a, const float* a_s
     if (!b || !b_s || !group_offsets) return fail(FP8Q_ERR_NULL, "NULL pointer");
     if (!aligned16(b) || !aligned4(b_s) || !aligned4(group_offsets))
       return fail(FP8Q_ERR_ALIGN, "b must be 16-byte aligned");
+    if (n * k > kMaxOperandBytes) return fail(FP8Q_ERR_SHAPE, "one expert's weight spans more than 2 GiB");
   }
   st = check_device();
   if (st != FP8Q_OK) return st;

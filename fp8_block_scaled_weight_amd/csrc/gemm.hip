@@ -8,22 +8,27 @@
 //   y[m, n] = bf16( sum_kb  sa[kb][m] * sb[n/128][kb] * P_kb[m, n] ),
 //   P_kb[m, n] = sum_{k in block kb} a[m, k] * b[n, k]   (FP8 x FP8, fp32 accumulate)
 //
-// Each 128-wide K block is exactly one v_mfma_f32_16x16x128_f8f6f4 per 16x16 output
-// tile, started from a zero accumulator, so P_kb comes out of the matrix core whole
-// and is folded into the running fp32 sum with one FMA per element (the "promotion").
+// Matrix core.  Each 128-wide K block is exactly one v_mfma_f32_16x16x128_f8f6f4 per
+// 16x16 output tile, started from a zero accumulator, so P_kb leaves the matrix core
+// whole and is folded into the running fp32 sum with one FMA per element.  The MFMA's
+// A operand is 16 weight rows (n) and its B operand 16 token rows (m); both are
+// K-contiguous and loaded the same way (lane l: row l%16, bytes 32*(l/16)..+31 of the
+// 128-byte K block), so whatever K order the matrix core uses applies to both.  The
+// result gives lane l the outputs m = l%16, n = 4*(l/16) + r (r < 4): one token scale
+// per lane and tile, four consecutive outputs per store.
 //
-// Operand roles: the MFMA's A operand is 16 weight rows (n) and its B operand 16
-// activation rows (m); both are K-contiguous, so both fragments are loaded the same
-// way (lane l: row l%16, 32 bytes at K offset 32*(l/16)) and any K order the matrix
-// core uses internally applies to both.  The 16x16 result then has lane l holding
-// m = l%16 and n = 4*(l/16) + r, r = 0..3: four consecutive outputs of one row
-// (an 8-byte store) and a single activation scale per lane and tile.
-//
-// Tiles: a 256-thread workgroup computes BN x BM outputs (weights x tokens) with 4
-// waves in a 2 x 2 grid; per K step both 128-byte-wide operand tiles are staged in
-// LDS, double-buffered.  LDS rows are 128 bytes; the 16-byte chunk c of row r is
-// stored at chunk c ^ (r & 7) so that 8 consecutive rows read at the same K offset
-// hit 8 different bank groups.
+// Data movement.  A workgroup owns a BM x BN output tile and walks K in 128-byte steps.
+// Each step's operand rows (BN weight rows, then BM token rows, 128 bytes each) are
+// copied HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a ring of
+// STAGES buffers, STAGES-1 steps ahead of the step being multiplied.  In LDS the
+// 16-byte chunk c of row r sits at chunk c ^ (r & 7): the copies write 1 KB (8 rows)
+// per wave instruction in lane order, so each lane fetches the chunk that belongs at
+// its slot, and fragment reads of 8 consecutive rows at one K offset hit 8 different
+// bank groups.  Fragment reads are issued as ds_read_b128 with explicit waits tied to
+// their registers, and each step is entered through one "wait for my copies, then
+// barrier" sequence, so copies for later steps stay in flight across the multiply.
+#include <utility>
+
 #include "launch.hpp"
 
 namespace fp8q {
@@ -31,6 +36,8 @@ namespace fp8q {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#define FP8Q_GLOBAL __attribute__((address_space(1)))
+#define FP8Q_LDS __attribute__((address_space(3)))
 
 __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b) {
   v4f zero = {0.f, 0.f, 0.f, 0.f};
@@ -45,141 +52,218 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return u >> 16;
 }
 
-template <int WN, int WM>  // MFMA tiles per wave along n and m
-struct TileCfg {
-  static constexpr int kWavesN = 2, kWavesM = 2;
-  static constexpr int BN = kWavesN * WN * 16;
-  static constexpr int BM = kWavesM * WM * 16;
-  static constexpr int kThreads = 256;
-  static constexpr int kTileBytesA = BN * 128;  // weights
-  static constexpr int kTileBytesB = BM * 128;  // activations
-  static constexpr int kLoadsA = kTileBytesA / (16 * kThreads);
-  static constexpr int kLoadsB = kTileBytesB / (16 * kThreads);
+template <int IMM>
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(IMM));
+  return v;
+}
+
+// Wait until at most N LDS reads are outstanding; ties the wait to x so that no use of
+// x can be scheduled before it.
+template <int N>
+__device__ __forceinline__ void lds_wait(v8i& x) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N));
+}
+
+__device__ __forceinline__ v8i join(u32x4 lo, u32x4 hi) {
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WM = BM / WAVES_M / 16;  // 16x16 tiles per wave along m (tokens)
+  static constexpr int WN = BN / WAVES_N / 16;  // along n (weights)
+  static constexpr int ROWS = BN + BM;          // rows staged per K step: weights, then tokens
+  static constexpr int A_BYTES = BN * 128;      // weight rows of a stage
+  static constexpr int SCALE_OFF = ROWS * 128;  // token scales of a stage (BM floats)
+  static constexpr int STAGE_BYTES = ((ROWS * 128 + BM * 4) + 1023) / 1024 * 1024;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int LOADS = ROWS / (8 * WAVES);    // 16-byte operand copies per thread per step
+  static constexpr int LOADS_W = BN / (8 * WAVES);    // of which weight rows
+  static constexpr int SCALES_PER_WAVE = BM / WAVES;  // 4-byte token-scale copies per wave per step
+  static_assert(ROWS % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "whole 1 KB copies per wave");
+  static_assert(BN / WAVES_N <= 128 && 128 % (BN / WAVES_N) == 0, "a wave's n range is one scale block");
+  static_assert(SCALES_PER_WAVE <= 64 && BM % WAVES == 0, "one scale copy per wave");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(STAGES >= 2 && WM >= 1 && WN >= 1 && WM % 2 == 0, "");
+  static_assert((STAGES - 2) * (LOADS + 1) <= 63, "vmcnt range");
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit dwords (gfx9 layout)
 
-// One output tile: rows [m0, m0+BM) of a (clipped to m_end), columns [n0, n0+BN).
-// b points at the weight matrix of this tile's group ([n][k]), bs at its scales.
-template <int WN, int WM>
-__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t ld_a,
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
+}
+
+// Two floats 16 dwords apart from LDS (token scales of tiles j and j+1).
+template <int OFF0, int OFF1>
+__device__ __forceinline__ void lds_read_pair(uint32_t addr, float& a, float& b) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  v2f v;
+  asm volatile("ds_read2_b32 %0, %1 offset0:%2 offset1:%3" : "=v"(v) : "v"(addr), "i"(OFF0), "i"(OFF1));
+  a = v.x;
+  b = v.y;
+}
+
+// Keep uses of x after the preceding wait (no code is emitted).
+template <class T>
+__device__ __forceinline__ void after_wait(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// One BM x BN output tile: token rows [m0, m_end) (m_end - m0 may be < BM), weight
+// rows [n0, n0 + BN).  b / bs describe this tile's weight matrix and its scales.
+// a_rows and b_rows bound the operand buffers (rows, row pitch ld_a / ld_b bytes).
+template <class C>
+__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t ld_a, int64_t a_rows,
                                           const float* __restrict__ as, int64_t ld_as,
                                           const uint8_t* __restrict__ b, int64_t ld_b,
-                                          const float* __restrict__ bs, uint16_t* __restrict__ y,
-                                          int64_t ld_y, int64_t m0, int64_t m_end, int64_t n0,
-                                          int64_t kblocks, uint8_t* lds) {
-  using C = TileCfg<WN, WM>;
+                                          const float* __restrict__ bs, int kblocks,
+                                          uint16_t* __restrict__ y, int64_t ld_y, int64_t m0, int64_t m_end,
+                                          int64_t n0, uint8_t FP8Q_LDS* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource builtins exist in the device pass only
+  constexpr int S = C::STAGES;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = (wave % C::kWavesN) * WN * 16;  // wave offset along n within the tile
-  const int wm = (wave / C::kWavesN) * WM * 16;  // wave offset along m
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = (wave / C::WAVES_N) * C::WM * 16;
+  const int wn = (wave % C::WAVES_N) * C::WN * 16;
 
-  // LDS stage s (s = 0, 1) holds the weight tile then the activation tile
-  constexpr int kStage = C::kTileBytesA + C::kTileBytesB;
-  auto ldsA = [&](int buf) { return lds + buf * kStage; };
-  auto ldsB = [&](int buf) { return lds + buf * kStage + C::kTileBytesA; };
-
-  // global -> LDS staging: thread covers chunk tid%8 of rows tid/8 + 32*i
-  const int ld_row = tid >> 3;
-  const int ld_chunk = tid & 7;
-  u32x4 ra[C::kLoadsA], rb[C::kLoadsB];
-
-  auto load_tiles = [&](int64_t kb) {
+  // ---- copy sources: lane byte offsets that stay fixed while K advances (token rows
+  // past m_end are clamped to the last row: valid memory, never stored)
+  uint32_t src[C::LOADS];
+  {
+    const int r_in = lane >> 3;
+    const int chunk = (lane & 7) ^ (r_in & 7);
 #pragma unroll
-    for (int i = 0; i < C::kLoadsA; ++i) {
-      const int r = ld_row + 32 * i;
-      ra[i] = *reinterpret_cast<const u32x4*>(b + (n0 + r) * ld_b + kb * 128 + ld_chunk * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < C::kLoadsB; ++i) {
-      const int r = ld_row + 32 * i;
-      const int64_t m = m0 + r;
-      rb[i] = (m < m_end) ? *reinterpret_cast<const u32x4*>(a + m * ld_a + kb * 128 + ld_chunk * 16)
-                          : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tiles = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::kLoadsA; ++i)
-      *reinterpret_cast<u32x4*>(ldsA(buf) + swz(ld_row + 32 * i, ld_chunk)) = ra[i];
-#pragma unroll
-    for (int i = 0; i < C::kLoadsB; ++i)
-      *reinterpret_cast<u32x4*>(ldsB(buf) + swz(ld_row + 32 * i, ld_chunk)) = rb[i];
-  };
-
-  // activation scale rows of this lane: m = m0 + wm + 16*j + lane%16
-  float sa_next[WM];
-  auto load_scales = [&](int64_t kb) {
-#pragma unroll
-    for (int j = 0; j < WM; ++j) {
-      const int64_t m = m0 + wm + 16 * j + (lane & 15);
-      sa_next[j] = (m < m_end) ? as[kb * ld_as + m] : 0.0f;
-    }
-  };
-
-  v4f acc[WN][WM];
-#pragma unroll
-  for (int i = 0; i < WN; ++i)
-#pragma unroll
-    for (int j = 0; j < WM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  const int64_t nb = n0 / 128;
-  const int frag_row = lane & 15;
-  const int frag_chunk = (lane >> 4) * 2;  // 32 bytes = chunks 2q, 2q+1
-
-  load_tiles(0);
-  load_scales(0);
-  store_tiles(0);
-  __syncthreads();
-
-  for (int64_t kb = 0; kb < kblocks; ++kb) {
-    const int buf = kb & 1;
-    float sa[WM];
-#pragma unroll
-    for (int j = 0; j < WM; ++j) sa[j] = sa_next[j];
-    const float sb = bs[nb * kblocks + kb];
-    if (kb + 1 < kblocks) {
-      load_tiles(kb + 1);
-      load_scales(kb + 1);
-    }
-    // B fragments (activations) for this wave's m tiles
-    v8i fb[WM];
-#pragma unroll
-    for (int j = 0; j < WM; ++j) {
-      const int r = wm + 16 * j + frag_row;
-      u32x4 lo = *reinterpret_cast<const u32x4*>(ldsB(buf) + swz(r, frag_chunk));
-      u32x4 hi = *reinterpret_cast<const u32x4*>(ldsB(buf) + swz(r, frag_chunk + 1));
-      fb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-    float sab[WM];
-#pragma unroll
-    for (int j = 0; j < WM; ++j) sab[j] = sa[j] * sb;
-#pragma unroll
-    for (int i = 0; i < WN; ++i) {
-      const int r = wn + 16 * i + frag_row;
-      u32x4 lo = *reinterpret_cast<const u32x4*>(ldsA(buf) + swz(r, frag_chunk));
-      u32x4 hi = *reinterpret_cast<const u32x4*>(ldsA(buf) + swz(r, frag_chunk + 1));
-      v8i fa = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-      for (int j = 0; j < WM; ++j) {
-        v4f p = mfma_fp8(fa, fb[j]);
-        acc[i][j] = p * sab[j] + acc[i][j];
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int r = (i * C::WAVES + wave) * 8 + r_in;
+      if (i < C::LOADS_W) {
+        src[i] = (uint32_t)((n0 + r) * ld_b) + chunk * 16;
+      } else {
+        int64_t m = m0 + (r - C::BN);
+        m = m < m_end ? m : m_end - 1;
+        src[i] = (uint32_t)(m * ld_a) + chunk * 16;
       }
     }
-    if (kb + 1 < kblocks) {
-      store_tiles(buf ^ 1);
+  }
+  // token-scale copy: wave w fetches scales of rows m0 + w*SCALES_PER_WAVE + lane
+  int64_t srow = m0 + wave * C::SCALES_PER_WAVE + lane;
+  srow = srow < m_end ? srow : m_end - 1;
+  const uint32_t ssrc = (uint32_t)(srow * 4);
+  const bool scale_lane = lane < C::SCALES_PER_WAVE;
+
+  const uint32_t a_bytes = (uint32_t)(a_rows * ld_a);
+  const uint32_t b_bytes = (uint32_t)((n0 + C::BN) * ld_b);
+  auto issue = [&](int kb) {
+    uint8_t FP8Q_LDS* dst = lds + (kb % S) * C::STAGE_BYTES;
+    const __amdgpu_buffer_rsrc_t rb = rsrc(b + (size_t)kb * 128, b_bytes - kb * 128);
+    const __amdgpu_buffer_rsrc_t ra = rsrc(a + (size_t)kb * 128, a_bytes - kb * 128);
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(i < C::LOADS_W ? rb : ra,
+                                               (FP8Q_LDS void*)(dst + (i * C::WAVES + wave) * 1024), 16, src[i], 0, 0,
+                                               0);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(as + (size_t)kb * ld_as, (uint32_t)(ld_as * 4));
+    if (scale_lane)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FP8Q_LDS void*)(dst + C::SCALE_OFF + wave * C::SCALES_PER_WAVE * 4),
+                                               4, ssrc, 0, 0, 0);
+  };
+
+  // ---- fragment read addresses (lane part; stage and tile offsets added per step)
+  const int x = lane & 7;
+  const int q2 = (lane >> 4) * 2;
+  const uint32_t rd_lo = (lane & 15) * 128 + ((q2 ^ x) << 4);
+  const uint32_t rd_hi = (lane & 15) * 128 + (((q2 + 1) ^ x) << 4);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  const int64_t sb_base = ((n0 + wn) / 128) * kblocks;
+
+  v4f acc[C::WN][C::WM];
+#pragma unroll
+  for (int i = 0; i < C::WN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: copies for steps 0 .. S-2
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < kblocks) issue(s);
+  float sb_next = bs[sb_base];
+
+  for (int kb = 0; kb < kblocks; ++kb) {
+    const float sb = sb_next;
+    if (kb + 1 < kblocks) sb_next = bs[sb_base + kb + 1];
+
+    // Wait until this thread's copies for step kb have landed (the copies of up to S-2
+    // later steps may stay in flight), then barrier: after it every thread's copies for
+    // kb are in LDS and no wave still reads the buffer of step kb-1, which the copy
+    // issued next reuses.
+    if (kb + S - 2 < kblocks) {
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((S - 2) * (C::LOADS + 1)) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    __syncthreads();
+    if (kb + S - 1 < kblocks) issue(kb + S - 1);
+
+    const uint32_t stage = lds_base + (uint32_t)((kb % S) * C::STAGE_BYTES);
+    const uint32_t a_lo = stage + wn * 128 + rd_lo, a_hi = stage + wn * 128 + rd_hi;
+    const uint32_t b_lo = stage + C::A_BYTES + wm * 128 + rd_lo, b_hi = stage + C::A_BYTES + wm * 128 + rd_hi;
+    const uint32_t s_addr = stage + C::SCALE_OFF + (wm + (lane & 15)) * 4;
+
+    v8i fa[C::WN];
+    v8i fb[3];
+    float sa[C::WM];
+    // weight fragments of all n tiles, token scales, token fragment 0
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((fa[I] = join(lds_read16<I * 2048>(a_lo), lds_read16<I * 2048>(a_hi))), ...);
+    }(std::make_integer_sequence<int, C::WN>{});
+    [&]<int... P>(std::integer_sequence<int, P...>) {
+      (lds_read_pair<32 * P, 32 * P + 16>(s_addr, sa[2 * P], sa[2 * P + 1]), ...);
+    }(std::make_integer_sequence<int, C::WM / 2>{});
+    fb[0] = join(lds_read16<0>(b_lo), lds_read16<0>(b_hi));
+
+    // token tile j: prefetch fragment j+1 (3 rotating registers keep a fragment's
+    // registers untouched until well after the MFMAs that read them), wait for j,
+    // then one MFMA per weight tile and its promotion FMA
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      (
+          [&] {
+            constexpr int j = J;
+            if constexpr (j + 1 < C::WM) {
+              fb[(j + 1) % 3] = join(lds_read16<(j + 1) * 2048>(b_lo), lds_read16<(j + 1) * 2048>(b_hi));
+              lds_wait<2>(fb[j % 3]);
+            } else {
+              lds_wait<0>(fb[j % 3]);
+            }
+            if constexpr (j == 0) {
+#pragma unroll
+              for (int i = 0; i < C::WN; ++i) after_wait(fa[i]);
+#pragma unroll
+              for (int jj = 0; jj < C::WM; ++jj) after_wait(sa[jj]);
+            }
+            const float sab = sa[j] * sb;
+#pragma unroll
+            for (int i = 0; i < C::WN; ++i) {
+              v4f p = mfma_fp8(fa[i], fb[j % 3]);
+              acc[i][j] = p * sab + acc[i][j];
+            }
+          }(),
+          ...);
+    }(std::make_integer_sequence<int, C::WM>{});
   }
 
-  // epilogue: lane holds y[m][n .. n+3], m = m0 + wm + 16j + lane%16, n = n0 + wn + 16i + 4*(lane/16)
+  // ---- epilogue: lane holds y[m][n .. n+3], m = m0 + wm + 16j + lane%16,
+  // n = n0 + wn + 16i + 4*(lane/16); one bf16 rounding per output
 #pragma unroll
-  for (int j = 0; j < WM; ++j) {
+  for (int j = 0; j < C::WM; ++j) {
     const int64_t m = m0 + wm + 16 * j + (lane & 15);
     if (m >= m_end) continue;
 #pragma unroll
-    for (int i = 0; i < WN; ++i) {
+    for (int i = 0; i < C::WN; ++i) {
       const int64_t n = n0 + wn + 16 * i + 4 * (lane >> 4);
       uint2 o;
       o.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
@@ -187,35 +271,75 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
       *reinterpret_cast<uint2*>(y + m * ld_y + n) = o;
     }
   }
+#endif
 }
 
-constexpr int kWN = 4, kWM = 4;
-using DenseCfg = TileCfg<kWN, kWM>;
-constexpr int kLdsBytes = 2 * (DenseCfg::kTileBytesA + DenseCfg::kTileBytesB);
+// Tile order.  Workgroups are dealt to the 8 XCDs round-robin, so consecutive tile
+// indices are given to one XCD: its L2 then serves a compact block of tiles
+// (GROUP_M token tiles x all weight tiles, walked weight-tile-major) that share
+// operand rows.
+constexpr int kXcds = 8;
 
-__global__ __launch_bounds__(256) void gemm_w8a8_kernel(const uint8_t* __restrict__ a, int64_t ld_a,
-                                                        const float* __restrict__ as, int64_t ld_as,
-                                                        const uint8_t* __restrict__ b, int64_t ld_b,
-                                                        const float* __restrict__ bs, uint16_t* __restrict__ y,
-                                                        int64_t ld_y, int64_t m, int64_t n, int64_t kblocks,
-                                                        int n_tiles) {
-  __shared__ __align__(16) uint8_t lds[kLdsBytes];
-  const int64_t tile_n = blockIdx.x % n_tiles;
-  const int64_t tile_m = blockIdx.x / n_tiles;
-  gemm_tile<kWN, kWM>(a, ld_a, as, ld_as, b, ld_b, bs, y, ld_y, tile_m * DenseCfg::BM, m,
-                      tile_n * DenseCfg::BN, kblocks, lds);
+__device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t tiles) {
+  const int64_t per = (tiles + kXcds - 1) / kXcds;
+  return (bid % kXcds) * per + bid / kXcds;
+}
+
+template <int GROUP_M>
+__device__ __forceinline__ void tile_coords(int64_t t, int64_t m_tiles, int64_t n_tiles, int64_t& tm, int64_t& tn) {
+  const int64_t span = (int64_t)GROUP_M * n_tiles;
+  const int64_t grp = t / span;
+  const int64_t first = grp * GROUP_M;
+  const int64_t gm = (m_tiles - first) < GROUP_M ? (m_tiles - first) : GROUP_M;
+  const int64_t r = t - grp * span;
+  tm = first + r % gm;
+  tn = r / gm;
+}
+
+using CfgLarge = GemmCfg<256, 128, 2, 2, 3>;   // 128 x 64 per wave, 144 KB LDS
+using CfgMid = GemmCfg<128, 128, 2, 2, 4>;     // 64 x 64 per wave, 128 KB LDS
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void gemm_w8a8_kernel(const uint8_t* __restrict__ a, int64_t ld_a,
+                                                                const float* __restrict__ as, int64_t ld_as,
+                                                                const uint8_t* __restrict__ b, int64_t ld_b,
+                                                                const float* __restrict__ bs,
+                                                                uint16_t* __restrict__ y, int64_t ld_y, int64_t m,
+                                                                int64_t m_tiles, int64_t n_tiles, int kblocks) {
+  __shared__ __align__(1024) uint8_t lds[C::LDS_BYTES];
+  const int64_t tiles = m_tiles * n_tiles;
+  const int64_t t = xcd_tile(blockIdx.x, tiles);
+  if (t >= tiles) return;
+  int64_t tm, tn;
+  tile_coords<4>(t, m_tiles, n_tiles, tm, tn);
+  const int64_t m0 = tm * C::BM;
+  const int64_t m_end = (m0 + C::BM) < m ? (m0 + C::BM) : m;
+  gemm_tile<C>(a, ld_a, m, as, ld_as, b, ld_b, bs, kblocks, y, ld_y, m0, m_end, tn * C::BN,
+               (uint8_t FP8Q_LDS*)lds);
+}
+
+template <class C>
+static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
+                               int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
+                               int64_t k, hipStream_t stream) {
+  const int64_t n_tiles = n / C::BN;
+  const int64_t m_tiles = (m + C::BM - 1) / C::BM;
+  const int64_t tiles = m_tiles * n_tiles;
+  const int64_t grid = ((tiles + kXcds - 1) / kXcds) * kXcds;
+  hipLaunchKernelGGL(gemm_w8a8_kernel<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
+                     reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b),
+                     ld_b, b_s, reinterpret_cast<uint16_t*>(y), ld_y, m, m_tiles, n_tiles, (int)(k / 128));
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                        int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream) {
-  const int n_tiles = (int)(n / DenseCfg::BN);
-  const int64_t m_tiles = (m + DenseCfg::BM - 1) / DenseCfg::BM;
-  hipLaunchKernelGGL(gemm_w8a8_kernel, dim3((unsigned)(n_tiles * m_tiles)), dim3(256), 0, stream,
-                     reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as,
-                     reinterpret_cast<const uint8_t*>(b), ld_b, b_s, reinterpret_cast<uint16_t*>(y), ld_y,
-                     m, n, k / 128, n_tiles);
-  return hipGetLastError();
+  // large tiles when they still give every CU at least two tiles
+  const int64_t large_tiles = ((m + CfgLarge::BM - 1) / CfgLarge::BM) * (n / CfgLarge::BN);
+  if (large_tiles >= 512)
+    return launch_dense<CfgLarge>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  return launch_dense<CfgMid>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
 }
 
 // ----------------------------------------------------------------------------
@@ -225,11 +349,14 @@ hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld
 // m-tiles of the groups before it to find its (group, m-tile) and exits if it has
 // none.  No host synchronization, no workspace.
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void grouped_gemm_w8a8_kernel(
+using CfgGrouped = CfgMid;
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void grouped_gemm_w8a8_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
     const uint8_t* __restrict__ b, const float* __restrict__ bs, const int32_t* __restrict__ off,
-    int32_t groups, uint16_t* __restrict__ y, int64_t ld_y, int64_t n, int64_t k, int n_tiles) {
-  __shared__ __align__(16) uint8_t lds[kLdsBytes];
+    int32_t groups, uint16_t* __restrict__ y, int64_t ld_y, int64_t n, int64_t k, int64_t n_tiles) {
+  __shared__ __align__(1024) uint8_t lds[C::LDS_BYTES];
   __shared__ int32_t sel[2];
   const int64_t tile_n = blockIdx.x % n_tiles;
   const int64_t tile_m = blockIdx.x / n_tiles;  // global m-tile index
@@ -242,8 +369,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_w8a8_kernel(
     for (int g0 = 0; g0 < groups && found_g < 0; g0 += 64) {
       const int g = g0 + lane;
       int64_t tiles = 0;
-      if (g < groups) tiles = (off[g + 1] - off[g] + DenseCfg::BM - 1) / DenseCfg::BM;
-      // inclusive scan across the wave
+      if (g < groups) tiles = (off[g + 1] - off[g] + C::BM - 1) / C::BM;
       int64_t incl = tiles;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -268,22 +394,26 @@ __global__ __launch_bounds__(256) void grouped_gemm_w8a8_kernel(
   __syncthreads();
   const int g = sel[0];
   if (g < 0) return;
-  const int64_t kblocks = k / 128;
-  const int64_t row0 = off[g] + (int64_t)sel[1] * DenseCfg::BM;
-  gemm_tile<kWN, kWM>(a, ld_a, as, ld_as, b + (int64_t)g * n * k, k, bs + (int64_t)g * (n / 128) * kblocks,
-                      y, ld_y, row0, off[g + 1], tile_n * DenseCfg::BN, kblocks, lds);
+  const int kblocks = (int)(k / 128);
+  const int64_t row0 = off[g] + (int64_t)sel[1] * C::BM;
+  const int64_t row_end = (row0 + C::BM) < off[g + 1] ? (row0 + C::BM) : off[g + 1];
+  const int64_t a_rows = off[groups];
+  const uint8_t* bg = b + (int64_t)g * n * k;
+  const float* bsg = bs + (int64_t)g * (n / 128) * kblocks;
+  gemm_tile<C>(a, ld_a, a_rows, as, ld_as, bg, k, bsg, kblocks, y, ld_y, row0, row_end, tile_n * C::BN,
+               (uint8_t FP8Q_LDS*)lds);
 }
 
 hipError_t launch_grouped_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
                                const void* b, const float* b_s, const int32_t* offsets, int32_t groups,
                                int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k,
                                hipStream_t stream) {
-  const int n_tiles = (int)(n / DenseCfg::BN);
-  const int64_t m_tiles = (total_m + DenseCfg::BM - 1) / DenseCfg::BM + groups;
-  hipLaunchKernelGGL(grouped_gemm_w8a8_kernel, dim3((unsigned)(n_tiles * m_tiles)), dim3(256), 0,
-                     stream, reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as,
-                     reinterpret_cast<const uint8_t*>(b), b_s, offsets, groups,
-                     reinterpret_cast<uint16_t*>(y), ld_y, n, k, n_tiles);
+  using C = CfgGrouped;
+  const int64_t n_tiles = n / C::BN;
+  const int64_t m_tiles = (total_m + C::BM - 1) / C::BM + groups;
+  hipLaunchKernelGGL(grouped_gemm_w8a8_kernel<C>, dim3((unsigned)(n_tiles * m_tiles)), dim3(C::THREADS), 0, stream,
+                     reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b), b_s,
+                     offsets, groups, reinterpret_cast<uint16_t*>(y), ld_y, n, k, n_tiles);
   return hipGetLastError();
 }
 

@@ -138,6 +138,8 @@ fp8q_status fp8q_quant_act_g128(const void* x, int64_t m, int64_t k, int64_t ld_
  *   b_s: fp32 [n/128][k/128] contiguous (as written by fp8q_quant_weight_blk128);
  *   y:   bf16 [m, n] row-major, ld_y elements >= n, ld_y % 8 == 0.
  *   n % 128 == 0, k % 128 == 0, k >= 128.  m == 0 is a no-op.  No bias.
+ *   Each operand (m * ld_a, n * ld_b, 4 * ld_as bytes) spans at most 2 GiB (else
+ *   FP8Q_ERR_SHAPE).
  * Accuracy: every element within half a bf16 ulp of the exact value plus 2e-3 of the
  * largest |y| (fp32 accumulation order differs from exact arithmetic).
  * ---------------------------------------------------------------------------- */
@@ -158,7 +160,8 @@ fp8q_status fp8q_gemm_w8a8_blkscaled(const void* a, int64_t ld_a, const float* a
  *   group_offsets: int32 [G+1] (device), read on the device only (no host sync);
  *   y:   bf16 [total_m, n], ld_y elements.
  * Empty groups are allowed.  num_groups >= 1; n, k multiples of 128; total_m == 0 is a
- * no-op.  Rows outside [offsets[0], offsets[G]) are not written.
+ * no-op.  Rows outside [offsets[0], offsets[G]) are not written.  As for the dense call,
+ * total_m * ld_a, n * k (one expert) and 4 * ld_as bytes are each at most 2 GiB.
  * ---------------------------------------------------------------------------- */
 fp8q_status fp8q_grouped_gemm_w8a8(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
                                    const void* b, const float* b_s,
