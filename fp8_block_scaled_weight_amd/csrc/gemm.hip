@@ -115,6 +115,9 @@ __device__ __forceinline__ void after_wait(T& x) {
   asm volatile("" : "+v"(x));
 }
 
+// LDS placement of 16-byte chunk c of staged row r: chunk c ^ swz(r).
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
 // One BM x BN output tile: token rows [m0, m_end) (m_end - m0 may be < BM), weight
 // rows [n0, n0 + BN).  b / bs describe this tile's weight matrix and its scales.
 // a_rows and b_rows bound the operand buffers (rows, row pitch ld_a / ld_b bytes).
@@ -138,10 +141,10 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
   uint32_t src[C::LOADS];
   {
     const int r_in = lane >> 3;
-    const int chunk = (lane & 7) ^ (r_in & 7);
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int r = (i * C::WAVES + wave) * 8 + r_in;
+      const int chunk = (lane & 7) ^ swz(r);
       if (i < C::LOADS_W) {
         src[i] = (uint32_t)((n0 + r) * ld_b) + chunk * 16;
       } else {
@@ -175,7 +178,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
   };
 
   // ---- fragment read addresses (lane part; stage and tile offsets added per step)
-  const int x = lane & 7;
+  const int x = swz(lane & 15);  // fragment rows start at multiples of 16
   const int q2 = (lane >> 4) * 2;
   const uint32_t rd_lo = (lane & 15) * 128 + ((q2 ^ x) << 4);
   const uint32_t rd_hi = (lane & 15) * 128 + (((q2 + 1) ^ x) << 4);
@@ -296,8 +299,11 @@ __device__ __forceinline__ void tile_coords(int64_t t, int64_t m_tiles, int64_t 
   tn = r / gm;
 }
 
-using CfgLarge = GemmCfg<256, 128, 2, 2, 3>;   // 128 x 64 per wave, 144 KB LDS
-using CfgMid = GemmCfg<128, 128, 2, 2, 4>;     // 64 x 64 per wave, 128 KB LDS
+// Two waves per SIMD (8 per workgroup): while one wave waits for LDS or a barrier, the
+// other keeps the matrix core busy, and one wave's promotion FMAs overlap the other's
+// MFMAs.
+using CfgLarge = GemmCfg<256, 256, 2, 4, 2>;   // 128 x 64 per wave, 130 KB LDS
+using CfgMid = GemmCfg<128, 128, 2, 4, 2>;     // 64 x 32 per wave, 66 KB LDS
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void gemm_w8a8_kernel(const uint8_t* __restrict__ a, int64_t ld_a,
@@ -335,9 +341,9 @@ static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, in
 hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                        int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream) {
-  // large tiles when they still give every CU at least two tiles
+  // large tiles when they still give every CU a tile
   const int64_t large_tiles = ((m + CfgLarge::BM - 1) / CfgLarge::BM) * (n / CfgLarge::BN);
-  if (large_tiles >= 512)
+  if (large_tiles >= 256)
     return launch_dense<CfgLarge>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   return launch_dense<CfgMid>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
 }
