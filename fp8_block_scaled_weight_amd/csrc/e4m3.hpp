@@ -20,7 +20,12 @@
 // `mid` comes from the fp32 bits of t: clearing all but three mantissa bits gives
 // the E4M3 value below t and setting the next bit gives the midpoint above it.  For
 // quotients below 2^-6 (E4M3 subnormals, spacing 2^-9) t is first shifted by 2^-6
-// into the binade [2^-6, 2^-5), whose spacing is the same 2^-9, and shifted back.
+// into the binade [2^-6, 2^-5), whose spacing is the same 2^-9, and shifted back; the
+// shift is folded into the FMA that forms t.  Which side of 2^-6 takes the shift is
+// decided by comparing |x| with lim = fl((2^-6 - 2^-20) * scale): the shifted path is
+// exact for t < 2^-6 - 2^-29 (t + 2^-6 stays below 2^-5) and the plain path for
+// t >= 2^-6 - 2^-11 (the nearest E4M3 midpoint below is 2^-6 - 2^-10), and the few-ulp
+// fuzz of the comparison stays well inside that overlap.
 //
 // The residual needs scale * mid to be representable down to its last bit: that
 // holds when scale >= 2^-116.  Smaller scales (data around 1e-33 and below) take a
@@ -33,22 +38,14 @@
 namespace fp8q {
 
 constexpr float kE4M3Max = 448.0f;
-// Largest float below 2^-6: quotients below it use the subnormal shift.
-constexpr float kSubnormalLimit = 0x1.fffffep-7f;
+constexpr float kSubnormalSwitch = 0x1.ffffcp-7f;  // 2^-6 - 2^-20
 constexpr float kTinyScale = 0x1p-116f;
 
 // bf16 bit patterns packed two per dword -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// |x| as an order-preserving integer for the packed pair (bf16 magnitude bits).
-__device__ __forceinline__ uint32_t bf16x2_absmax(uint32_t acc, uint32_t w) {
-  uint32_t lo = w & 0x7fffu;
-  uint32_t hi = (w >> 16) & 0x7fffu;
-  return max(acc, max(lo, hi));
-}
-
-// Scale from the amax magnitude bits (bf16): fl32(amax / range), 1 for amax == 0.
+// Scale from the amax: fl32(amax / range), 1 for amax == 0.
 __device__ __forceinline__ float scale_from_amax(float amax, float range) {
   return amax == 0.0f ? 1.0f : amax / range;
 }
@@ -56,6 +53,7 @@ __device__ __forceinline__ float scale_from_amax(float amax, float range) {
 struct Quantizer {
   float s;    // scale as used in the residual test (possibly x 2^64)
   float r;    // 1 / s
+  float lim;  // |x| below this takes the subnormal shift
   float xm;   // factor applied to x (1 or 2^64)
 };
 
@@ -69,7 +67,23 @@ __device__ __forceinline__ Quantizer make_quantizer(float scale) {
     q.xm = 1.0f;
   }
   q.r = 1.0f / q.s;
+  q.lim = kSubnormalSwitch * q.s;
   return q;
+}
+
+// fp32 bits with the mantissa cut to 3 bits and the next bit set: the midpoint above
+// the E4M3 value below (one bitfield insert).
+__device__ __forceinline__ uint32_t keep3_set_half(uint32_t bits) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(0xfff00000u), "v"(bits), "v"(0x00080000u));
+  return r;
+}
+
+// -1, 0 or +1 by the sign of a float's bit pattern read as an integer (+0 gives 0).
+__device__ __forceinline__ int sign_of(float v) {
+  int r;
+  asm("v_med3_i32 %0, %1, -1, 1" : "=v"(r) : "v"(__float_as_int(v)));
+  return r;
 }
 
 // The fp32 value whose round-to-nearest-even E4M3 conversion is the code of x/s.
@@ -77,14 +91,12 @@ __device__ __forceinline__ Quantizer make_quantizer(float scale) {
 // SAT: clamp the nudged value to 448 (needed only when x/s may exceed 464, i.e. with
 // a stored scale; with scale = amax/448 the quotient never exceeds 449.6).
 template <bool SAT>
-__device__ __forceinline__ float nudged_magnitude(float ax, float s, float r) {
-  float t = fminf(ax * r, kE4M3Max);
-  float off = (t < kSubnormalLimit) ? 0x1p-6f : 0.0f;
-  float tt = t + off;
-  float mid = __uint_as_float((__float_as_uint(tt) & 0xfff00000u) | 0x00080000u) - off;
-  float res = __builtin_fmaf(-mid, s, ax);
-  int side = min(max((int)__float_as_uint(res), -1), 1);  // sign of res: -1, 0, +1
-  float v = __uint_as_float(__float_as_uint(mid) + (uint32_t)side);
+__device__ __forceinline__ float nudged_magnitude(float ax, const Quantizer& q) {
+  const float off = (ax < q.lim) ? 0x1p-6f : 0.0f;
+  const float tt = fminf(__builtin_fmaf(ax, q.r, off), kE4M3Max);
+  const float mid = __uint_as_float(keep3_set_half(__float_as_uint(tt))) - off;
+  const float res = __builtin_fmaf(-mid, q.s, ax);
+  float v = __uint_as_float(__float_as_uint(mid) + (uint32_t)sign_of(res));
   if (SAT) v = fminf(v, kE4M3Max);
   return v;
 }
@@ -93,8 +105,8 @@ template <bool SAT>
 __device__ __forceinline__ float nudged(float x, const Quantizer& q, bool tiny) {
   float ax = fabsf(x);
   if (tiny) ax *= q.xm;
-  float v = nudged_magnitude<SAT>(ax, q.s, q.r);
-  return __uint_as_float(__float_as_uint(v) | (__float_as_uint(x) & 0x80000000u));
+  const float v = nudged_magnitude<SAT>(ax, q);
+  return __builtin_copysignf(v, x);  // v >= 0: takes x's sign, -0 included
 }
 
 // Four fp32 values (already nudged) -> four packed E4M3FN bytes, element 0 lowest.
@@ -130,17 +142,16 @@ __device__ __forceinline__ uint4 quant16(uint4 a, uint4 b, const Quantizer& q) {
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
+// Largest |x| of 16 bf16 values as magnitude bits (bf16 magnitudes order like
+// unsigned integers): packed 16-bit maxima of the sign-cleared pairs.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 mag2(uint32_t w) { return __builtin_bit_cast(u16x2, w & 0x7fff7fffu); }
 __device__ __forceinline__ uint32_t absmax16(uint4 a, uint4 b) {
-  uint32_t m = 0;
-  m = bf16x2_absmax(m, a.x);
-  m = bf16x2_absmax(m, a.y);
-  m = bf16x2_absmax(m, a.z);
-  m = bf16x2_absmax(m, a.w);
-  m = bf16x2_absmax(m, b.x);
-  m = bf16x2_absmax(m, b.y);
-  m = bf16x2_absmax(m, b.z);
-  m = bf16x2_absmax(m, b.w);
-  return m;
+  u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(mag2(a.x), mag2(a.y)),
+                                      __builtin_elementwise_max(mag2(a.z), mag2(a.w)));
+  m = __builtin_elementwise_max(m, __builtin_elementwise_max(__builtin_elementwise_max(mag2(b.x), mag2(b.y)),
+                                                             __builtin_elementwise_max(mag2(b.z), mag2(b.w))));
+  return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
 // Max over groups of 8 consecutive lanes (DPP: quad swaps then half-row mirror).

@@ -304,6 +304,7 @@ __device__ __forceinline__ void tile_coords(int64_t t, int64_t m_tiles, int64_t 
 // MFMAs.
 using CfgLarge = GemmCfg<256, 256, 2, 4, 2>;   // 128 x 64 per wave, 130 KB LDS
 using CfgMid = GemmCfg<128, 128, 2, 4, 2>;     // 64 x 32 per wave, 66 KB LDS
+using CfgSmall = GemmCfg<128, 64, 2, 2, 4>;    // 64 x 32 per wave, 4 waves: more tiles for mid-size M
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void gemm_w8a8_kernel(const uint8_t* __restrict__ a, int64_t ld_a,
@@ -338,9 +339,116 @@ static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, in
   return hipGetLastError();
 }
 
+// ----------------------------------------------------------------------------
+// Few tokens (decode, short prefill): the GEMM streams the weight matrix once and is
+// HBM-bound, so it is spread over as many CUs as possible.  A workgroup owns 16 weight
+// rows and up to 16*WM token rows; its 8 waves take the K blocks round-robin and load
+// their fragments straight into registers (weights read once, with a non-temporal
+// hint; token rows come from L2).  The 8 partial sums are added through LDS in a fixed
+// order, so the result does not depend on timing.
+// ----------------------------------------------------------------------------
+constexpr int kSmallWaves = 8;
+
+template <int WM>
+__global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
+    const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
+    const uint8_t* __restrict__ b, int64_t ld_b, const float* __restrict__ bs, uint16_t* __restrict__ y,
+    int64_t ld_y, int64_t m, int64_t n16, int kblocks) {
+  __shared__ v4f part[kSmallWaves][WM][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t tn = blockIdx.x % n16;
+  const int64_t m0 = (blockIdx.x / n16) * (16 * WM);
+  const int64_t n0 = tn * 16;
+  const int q = lane >> 4;
+  const uint8_t* brow = b + (n0 + (lane & 15)) * ld_b + q * 32;
+  const uint8_t* arow[WM];
+  int64_t srow[WM];  // token row of this lane (row 0 stands in for rows past m)
+  bool live[WM];
+#pragma unroll
+  for (int j = 0; j < WM; ++j) {
+    const int64_t r = m0 + 16 * j + (lane & 15);
+    live[j] = r < m;
+    srow[j] = live[j] ? r : 0;
+    arow[j] = a + srow[j] * ld_a + q * 32;
+  }
+  const float* bsrow = bs + (n0 / 128) * kblocks;
+  v4f acc[WM];
+#pragma unroll
+  for (int j = 0; j < WM; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int U = WM >= 4 ? 2 : 4;  // K blocks in flight per wave (register budget permitting)
+  for (int kb0 = wave; kb0 < kblocks; kb0 += kSmallWaves * U) {
+    v8i fw[U], ft[U][WM];
+    float sa[U][WM], sb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kb = kb0 + u * kSmallWaves;
+      if (kb < kblocks) {
+        const u32x4* pw = reinterpret_cast<const u32x4*>(brow + (int64_t)kb * 128);
+        fw[u] = join(__builtin_nontemporal_load(pw), __builtin_nontemporal_load(pw + 1));
+        sb[u] = bsrow[kb];
+#pragma unroll
+        for (int j = 0; j < WM; ++j) {
+          const u32x4* pt = reinterpret_cast<const u32x4*>(arow[j] + (int64_t)kb * 128);
+          ft[u][j] = live[j] ? join(pt[0], pt[1]) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          const float sv = as[(int64_t)kb * ld_as + srow[j]];
+          sa[u][j] = live[j] ? sv : 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kb = kb0 + u * kSmallWaves;
+      if (kb < kblocks) {
+#pragma unroll
+        for (int j = 0; j < WM; ++j) {
+          v4f p = mfma_fp8(fw[u], ft[u][j]);
+          acc[j] = p * (sa[u][j] * sb[u]) + acc[j];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < WM; ++j) part[wave][j][lane] = acc[j];
+  __syncthreads();
+  // wave j < WM adds the 8 partial sums of token tile j (fixed order) and stores it
+  if (wave < WM) {
+    const int j = wave;
+    v4f t = part[0][j][lane];
+#pragma unroll
+    for (int w = 1; w < kSmallWaves; ++w) t += part[w][j][lane];
+    const int64_t row = m0 + 16 * j + (lane & 15);
+    if (row < m) {
+      const int64_t col = n0 + 4 * q;
+      uint2 o;
+      o.x = bf16_rne(t[0]) | (bf16_rne(t[1]) << 16);
+      o.y = bf16_rne(t[2]) | (bf16_rne(t[3]) << 16);
+      *reinterpret_cast<uint2*>(y + row * ld_y + col) = o;
+    }
+  }
+}
+
+template <int WM>
+static hipError_t launch_smallm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
+                                int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
+                                int64_t k, hipStream_t stream) {
+  const int64_t n16 = n / 16;
+  const int64_t groups = (m + 16 * WM - 1) / (16 * WM);
+  hipLaunchKernelGGL(gemm_smallm_kernel<WM>, dim3((unsigned)(n16 * groups)), dim3(64 * kSmallWaves), 0, stream,
+                     reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b), ld_b,
+                     b_s, reinterpret_cast<uint16_t*>(y), ld_y, m, n16, (int)(k / 128));
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                        int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream) {
+  // few tokens: stream the weights over all CUs
+  if (m <= 16) return launch_smallm<1>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  if (m <= 32) return launch_smallm<2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  if (m <= 64) return launch_smallm<4>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  if (m < 1024) return launch_dense<CfgSmall>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   // large tiles when they still give every CU a tile
   const int64_t large_tiles = ((m + CfgLarge::BM - 1) / CfgLarge::BM) * (n / CfgLarge::BN);
   if (large_tiles >= 256)
