@@ -46,34 +46,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-legs", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only copy 1 GiB device-to-device 3 times (reference for HBM byte counters)")
     return p.parse_args()
-
-
-class Timer:
-    """HIP events on the stream every fp8q call is enqueued on (torch's current stream)."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.ev = {}
-
-    def span(self, name):
-        torch = self.torch
-        timer = self
-
-        class _S:
-            def __enter__(self):
-                self.a = torch.cuda.Event(enable_timing=True)
-                self.b = torch.cuda.Event(enable_timing=True)
-                self.a.record()
-
-            def __exit__(self, *exc):
-                self.b.record()
-                timer.ev.setdefault(name, []).append((self.a, self.b))
-
-        return _S()
-
-    def ms(self, name):
-        return [a.elapsed_time(b) for a, b in self.ev[name]]
 
 
 def source_digest(*names):
@@ -122,6 +97,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fq.lib()
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 1 << 30, "copies": 3}))
+        return
 
     # ------------------------------------------------------------------ inputs
     log("generating inputs")
@@ -149,49 +132,86 @@ def main():
     vs = torch.ones(1, dtype=torch.float32, device=dev)
     descs = [(W[n], WQ[n], WS[n]) for n in ("q", "k", "v", "o")]
 
-    T = Timer(torch)
+    calls = [
+        ("a1_weight_sync_qkvo", lambda: fq.fp8q_quant_weight_blk128(descs)),
+        ("a2_act_quant_x", lambda: fq.fp8q_quant_act_g128(X, Xq, Xs)),
+        ("a3_gemm_q", lambda: fq.fp8q_gemm_w8a8_blkscaled(Xq, Xs, WQ["q"], WS["q"], Y["q"])),
+        ("a3_gemm_k", lambda: fq.fp8q_gemm_w8a8_blkscaled(Xq, Xs, WQ["k"], WS["k"], Y["k"])),
+        ("a3_gemm_v", lambda: fq.fp8q_gemm_w8a8_blkscaled(Xq, Xs, WQ["v"], WS["v"], Y["v"])),
+        ("a5a6_kv_recal_write", lambda: fq.fp8q_kv_quant(Y["k"].view(TOKENS, 8, 128), Y["v"].view(TOKENS, 8, 128),
+                                                          slots, Kc, Vc, ks, vs, 448.0, recalibrate=True)),
+        ("a2_act_quant_o", lambda: fq.fp8q_quant_act_g128(O_in, Oq, Os)),
+        ("a3_gemm_o", lambda: fq.fp8q_gemm_w8a8_blkscaled(Oq, Os, WQ["o"], WS["o"], Y["o"])),
+    ]
+    outputs = [*WQ.values(), *WS.values(), Xq, Xs, Oq, Os, *Y.values(), Kc, Vc, ks, vs]
 
-    def step(timed: bool):
-        def sp(name):
-            return T.span(name) if timed else _Null()
-        with sp("a1_weight_sync_qkvo"):
-            fq.fp8q_quant_weight_blk128(descs)
-        with sp("a2_act_quant_x"):
-            fq.fp8q_quant_act_g128(X, Xq, Xs)
-        with sp("a3_gemm_q"):
-            fq.fp8q_gemm_w8a8_blkscaled(Xq, Xs, WQ["q"], WS["q"], Y["q"])
-        with sp("a3_gemm_k"):
-            fq.fp8q_gemm_w8a8_blkscaled(Xq, Xs, WQ["k"], WS["k"], Y["k"])
-        with sp("a3_gemm_v"):
-            fq.fp8q_gemm_w8a8_blkscaled(Xq, Xs, WQ["v"], WS["v"], Y["v"])
-        with sp("a5a6_kv_recal_write"):
-            fq.fp8q_kv_quant(Y["k"].view(TOKENS, 8, 128), Y["v"].view(TOKENS, 8, 128), slots, Kc, Vc, ks, vs,
-                             448.0, recalibrate=True)
-        with sp("a2_act_quant_o"):
-            fq.fp8q_quant_act_g128(O_in, Oq, Os)
-        with sp("a3_gemm_o"):
-            fq.fp8q_gemm_w8a8_blkscaled(Oq, Os, WQ["o"], WS["o"], Y["o"])
+    def step():
+        for _, fn in calls:
+            fn()
 
-    log(f"warmup {args.warmup} steps")
+    log(f"warmup {args.warmup} eager steps")
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
+    eager = [t.clone() for t in outputs]
+
+    # The step is captured once into a HIP graph and replayed: the timed region then
+    # measures the GPU, not Python's launch overhead.  A replay must reproduce the
+    # eager step byte for byte (every call is deterministic).
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    for t in outputs:
+        t.zero_()
+    for _ in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outputs, eager):
+            if not torch.equal(a.view(torch.uint8), b.view(torch.uint8)):
+                raise SystemExit("graph replay differs from the eager step")
+
     log(f"timing {args.steps} steps")
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for _ in range(args.steps):
-        step(True)
+        graph.replay()
     t1.record()
     torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    ms_step = total_ms / args.steps
+    ms_step = t0.elapsed_time(t1) / args.steps
 
     gemm_flops = 2 * TOKENS * HIDDEN * (HIDDEN + 2 * KV_DIM + HIDDEN)
     value = gemm_flops / (ms_step * 1e-3) / 1e12
 
-    # per-call breakdown and algorithmic bytes / flops
+    # Per-call times: each call captured REPS times into one graph (so the graph launch
+    # is amortized) and replayed back to back.
+    per_call_ms = {}
+    for name, fn in calls:
+        per_call_ms[name] = _time(torch, fn, 5, reps=20)
+    # The dominant kernel, launched directly (no graph), back to back on the current
+    # stream between two HIP events: its average duration.
+    dom_fn = calls[2][1]
+    for _ in range(3):
+        dom_fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    n_dom = max(20, args.steps)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n_dom):
+        dom_fn()
+    e1.record()
+    torch.cuda.synchronize()
+    dom_avg_ms = e0.elapsed_time(e1) / n_dom
+
+    # algorithmic bytes / flops per call
     w_elems = sum(w.numel() for w in W.values())
     bytes_of = {
         "a1_weight_sync_qkvo": 3 * w_elems + 4 * w_elems / 16384,
@@ -200,31 +220,27 @@ def main():
         "a5a6_kv_recal_write": 5 * 2 * TOKENS * KV_DIM + 8 * TOKENS,
     }
     flops_of = {f"a3_gemm_{n}": 2 * TOKENS * W[n].shape[0] * HIDDEN for n in W}
-    calls = {}
-    for name in T.ev:
-        ts = T.ms(name)
-        avg = sum(ts) / len(ts)
-        d = {"avg_us": round(avg * 1e3, 2)}
+    call_info = {}
+    for name, ms in per_call_ms.items():
+        d = {"avg_us": round(ms * 1e3, 2)}
         if name in bytes_of:
-            gbs = bytes_of[name] / (avg * 1e-3) / 1e9
+            gbs = bytes_of[name] / (ms * 1e-3) / 1e9
             d.update(GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBPS, 4))
         if name in flops_of:
-            tf = flops_of[name] / (avg * 1e-3) / 1e12
+            tf = flops_of[name] / (ms * 1e-3) / 1e12
             d.update(TFLOPs=round(tf, 1), frac_fp8_peak=round(tf / FP8_PEAK_TFLOPS, 4))
-        calls[name] = d
+        call_info[name] = d
     q_bytes = sum(bytes_of.values())
-    q_ms = sum(sum(T.ms(n)) / args.steps for n in bytes_of)
-    g_ms = sum(sum(T.ms(n)) / args.steps for n in flops_of)
+    q_ms = sum(per_call_ms[n] for n in bytes_of)
+    g_ms = sum(per_call_ms[n] for n in flops_of)
 
-    # dominant kernel: the 4096x4096x4096 GEMM (q and o projections)
-    dom = T.ms("a3_gemm_q") + T.ms("a3_gemm_o")
-    dom_avg_ms = sum(dom) / len(dom)
     dom_flops = 2 * TOKENS * HIDDEN * HIDDEN
     achieved = dom_flops / (dom_avg_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
                 "traffic": traffic_from_profile("gemm_w8a8_4096", source_digest("gemm.hip")),
-                "kernel": "gemm_w8a8_kernel M=N=K=4096", "avg_us": round(dom_avg_ms * 1e3, 2)}
+                "kernel": "gemm_w8a8_kernel<GemmCfg<256,256,2,4,2>> M=N=K=4096 (q/o projection)",
+                "avg_us": round(dom_avg_ms * 1e3, 2), "launches_timed": n_dom}
 
     out = {
         "metric": "W8A8 block-scaled GEMM TFLOP/s (% FP8 peak) + quantizer GB/s (% HBM) at 1 GPU",
@@ -247,7 +263,7 @@ def main():
         "gemm_frac_fp8_peak": round(gemm_flops / (g_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
         "quantizer_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
         "quantizer_frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "calls": calls,
+        "calls": call_info,
         "roofline": roofline,
     }
 
@@ -260,29 +276,36 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-class _Null:
-    def __enter__(self):
-        return self
-
-    def __exit__(self, *exc):
-        return False
-
-
-def _time(torch, fn, iters, warm=2):
-    for _ in range(warm):
-        fn()
+def _time_graph(torch, g, iters):
+    """Average time of a captured graph replayed `iters` times back to back."""
+    g.replay()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
-    ts = []
+    a.record()
     for _ in range(iters):
-        a.record()
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def _time(torch, fn, iters, warm=2, reps=10):
+    """Average time of one call of `fn`: `reps` calls captured into one graph, the graph
+    replayed `iters` times back to back."""
+    for _ in range(warm):
         fn()
-        b.record()
-        torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
-    ts.sort()
-    return ts[len(ts) // 2]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(reps):
+                fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return _time_graph(torch, g, iters) / reps
 
 
 def legs(torch, fq, synth, dev):
