@@ -185,3 +185,19 @@ def device_kv(tokens: int, device, *key: int, heads: int = KV_HEADS, head_dim: i
         dims = torch.randperm(head_dim, generator=gen, device=device)[:outlier_dims]
         x[:, h, dims] *= outlier_mult
     return x.to(torch.bfloat16)
+
+
+def device_fp8_codes(shape, device, *key: int) -> torch.Tensor:
+    """uint8 tensor on `device` of finite OCP E4M3FN byte codes, each drawn uniformly
+    from the 254 codes other than the two NaN patterns (0x7F, 0xFF)."""
+    gen = device_generator(device, *key)
+    c = torch.randint(0, 254, shape, generator=gen, device=device, dtype=torch.int16)
+    c = c + (c >= 0x7F).to(torch.int16)      # skip 0x7F
+    return c.to(torch.uint8)
+
+
+def device_scales(shape, device, *key: int) -> torch.Tensor:
+    """fp32 tensor on `device` of positive scale factors, log-uniform in [2^-12, 2^-4]."""
+    gen = device_generator(device, *key)
+    u = torch.rand(shape, generator=gen, device=device, dtype=torch.float32)
+    return torch.exp2(-12.0 + 8.0 * u)

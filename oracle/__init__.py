@@ -68,7 +68,8 @@ def lib():
         L.oracle_kv_quant.argtypes = [_u16p, _i64, _u16p, _i64, _i64, ctypes.c_int32,
                                       ctypes.c_int32, _i64p, _u8p, _u8p, ctypes.c_int32, _i64,
                                       _f32p, _f32p, ctypes.c_float, ctypes.c_int]
-        for f in ("oracle_quant_weight_blk128", "oracle_quant_act_g128", "oracle_gemm_w8a8",
+        L.oracle_kv_scales.argtypes = [_u16p, _i64, _u16p, _i64, _i64, _i64, _i64p, ctypes.c_float, _f32p, _f32p]
+        for f in ("oracle_kv_scales", "oracle_quant_weight_blk128", "oracle_quant_act_g128", "oracle_gemm_w8a8",
                   "oracle_grouped_gemm_w8a8", "oracle_kv_quant", "oracle_num_threads"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -160,6 +161,21 @@ def grouped_gemm_w8a8(a, a_s, b, b_s, offsets) -> np.ndarray:
     return y
 
 
+def kv_scales(k_bits, v_bits, slot_mapping, rng: float = 448.0):
+    """Recalibrated (k_scale, v_scale) of a KV write call: fl32(amax / rng) over the
+    tokens with slot >= 0 (1 when amax is 0).  k_bits, v_bits: bf16 [T, heads*head_dim]."""
+    kx = _u16(k_bits)
+    vx = _u16(v_bits)
+    t = kx.shape[0]
+    row = int(np.prod(kx.shape[1:])) if kx.ndim > 1 else 1
+    ks = np.zeros(1, np.float32)
+    vs = np.zeros(1, np.float32)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    _check(lib().oracle_kv_scales(kx.reshape(t, row), row, vx.reshape(t, row), row, t, row, slots, float(rng), ks, vs),
+           "kv_scales")
+    return ks[0], vs[0]
+
+
 def kv_quant(k_bits, v_bits, slot_mapping, k_cache, v_cache, page_size: int,
              k_scale: float = 1.0, v_scale: float = 1.0, rng: float = 448.0,
              recalibrate: bool = True):
@@ -176,7 +192,7 @@ def kv_quant(k_bits, v_bits, slot_mapping, k_cache, v_cache, page_size: int,
     vs = np.array([v_scale], dtype=np.float32)
     slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
     num_pages = kc.shape[0]
-    _check(lib().oracle_kv_quant(kx.reshape(t, -1), heads * hd, vx.reshape(t, -1), heads * hd, t,
+    _check(lib().oracle_kv_quant(kx.reshape(t, heads * hd), heads * hd, vx.reshape(t, heads * hd), heads * hd, t,
                                  heads, hd, slots, kc, vc, page_size, num_pages, ks, vs,
                                  float(rng), 1 if recalibrate else 0), "kv_quant")
     return kc, vc, ks[0], vs[0]

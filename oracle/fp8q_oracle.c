@@ -298,6 +298,31 @@ int oracle_kv_quant(const uint16_t* kx, int64_t ld_k, const uint16_t* vx, int64_
   return bad ? -1 : 0;
 }
 
+/* ---- a5 alone: the recalibrated K/V scales of a call, without writing the cache ----
+ * [FP8-RL, step 3]: scale = fl32(amax / range) over every element the call writes
+ * (tokens with slot >= 0), 1 when that amax is 0.  Same definition as the recalibrating
+ * branch of oracle_kv_quant, for inputs too large to encode in full on the host. */
+int oracle_kv_scales(const uint16_t* kx, int64_t ld_k, const uint16_t* vx, int64_t ld_v, int64_t tokens,
+                     int64_t row, const int64_t* slot_mapping, float range, float* k_scale, float* v_scale) {
+  if (tokens < 0 || row < 1 || ld_k < row || ld_v < row) return -2;
+  float ak = 0.0f, av = 0.0f;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(max : ak, av) reduction(| : bad)
+  for (int64_t t = 0; t < tokens; ++t) {
+    if (slot_mapping[t] < 0) continue;
+    for (int64_t e = 0; e < row; ++e) {
+      float xk = bf16_to_float(kx[t * ld_k + e]);
+      float xv = bf16_to_float(vx[t * ld_v + e]);
+      if (!isfinite(xk) || !isfinite(xv)) bad = 1;
+      if (fabsf(xk) > ak) ak = fabsf(xk);
+      if (fabsf(xv) > av) av = fabsf(xv);
+    }
+  }
+  *k_scale = oracle_scale(ak, range);
+  *v_scale = oracle_scale(av, range);
+  return bad ? -1 : 0;
+}
+
 /* Number of OpenMP threads the oracle uses (1 without OpenMP). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

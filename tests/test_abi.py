@@ -83,6 +83,10 @@ def test_gemm_validation():
     assert _gemm(ld_y=64) == fq.FP8Q_ERR_STRIDE
     assert _gemm(ld_a=272, a=A16 + 8) == fq.FP8Q_ERR_ALIGN
     assert _gemm(ld_y=132) == fq.FP8Q_ERR_ALIGN
+    # operands are addressed through 32-bit buffer ranges: at most 2 GiB each
+    assert _gemm(m=(1 << 31) // 256 + 1, ld_as=(1 << 31) // 256 + 1) == fq.FP8Q_ERR_SHAPE
+    big_n = (1 << 31) // 256 + 128
+    assert _gemm(n=big_n, ld_y=big_n) == fq.FP8Q_ERR_SHAPE
 
 
 def test_grouped_validation():

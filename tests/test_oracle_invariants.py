@@ -191,3 +191,16 @@ def test_nonfinite_input_rejected():
     x[0, 5] = 0x7F80  # +inf
     with pytest.raises(ValueError):
         oracle.quant_act_g128(x)
+
+
+def test_kv_scales_alone_match_recalibrating_write():
+    """The scale-only oracle (for inputs too large to encode on the host) gives the same
+    scales as the recalibrating write, skipped tokens and all."""
+    k, v, slots, cache = _kv_case(tokens=64, pages=8, heads=3)
+    k[5, 1, 7] = synth.to_bf16_bits(np.array([-900.0], dtype=np.float32))[0]
+    slots[5] = -1
+    _, _, ks, vs = oracle.kv_quant(k, v, slots, cache, cache, 16, rng=240.0)
+    ks2, vs2 = oracle.kv_scales(k.reshape(64, -1), v.reshape(64, -1), slots, rng=240.0)
+    assert ks2 == ks and vs2 == vs
+    ks3, vs3 = oracle.kv_scales(np.zeros((4, 128), np.uint16), np.zeros((4, 128), np.uint16), np.arange(4))
+    assert ks3 == 1.0 and vs3 == 1.0
