@@ -21,12 +21,19 @@
 // Each step's operand rows (BN weight rows, then BM token rows, 128 bytes each) are
 // copied HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a ring of
 // STAGES buffers, STAGES-1 steps ahead of the step being multiplied.  In LDS the
-// 16-byte chunk c of row r sits at chunk c ^ (r & 7): the copies write 1 KB (8 rows)
-// per wave instruction in lane order, so each lane fetches the chunk that belongs at
-// its slot, and fragment reads of 8 consecutive rows at one K offset hit 8 different
-// bank groups.  Fragment reads are issued as ds_read_b128 with explicit waits tied to
-// their registers, and each step is entered through one "wait for my copies, then
-// barrier" sequence, so copies for later steps stay in flight across the multiply.
+// 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7): the copies write 1 KB
+// (8 rows) per wave instruction in lane order, so each lane fetches the chunk that
+// belongs at its slot.  Fragments are read 8 bytes at a time (ds_read_b64, four per
+// lane and fragment): such a read is served a half-wave (32 lanes) at a time across
+// the 64 four-byte banks, the swizzle gives the 16 rows of a fragment 16 distinct
+// (row parity, chunk) bank groups, and lanes of odd 16-lane groups take the two
+// halves of each chunk in the opposite order, so every half-wave touches each bank
+// once (16-byte reads of the same data conflict two ways: the LDS bank-conflict
+// counter shows the difference).  The half swap permutes the K bytes of those lanes
+// identically for both operands, so the matrix core still pairs a[m][k] with b[n][k].
+// Reads carry explicit waits tied to their registers, and each step is entered
+// through one "wait for my copies, then barrier" sequence, so copies for later steps
+// stay in flight across the multiply.
 #include <utility>
 
 #include "launch.hpp"
@@ -59,6 +66,26 @@ __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
   return v;
 }
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <int IMM>
+__device__ __forceinline__ u32x2 lds_read8(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(IMM));
+  return v;
+}
+
+// One MFMA operand fragment (32 bytes per lane) as four 8-byte reads: chunk pair
+// (lo, hi), halves in the order hsw, hsw ^ 8 (hsw = 8 on odd 16-lane groups).
+constexpr int kReadsPerFragment = 4;
+
+template <int IMM>
+__device__ __forceinline__ v8i read_fragment(uint32_t lo, uint32_t hi, uint32_t hsw) {
+  const u32x2 p0 = lds_read8<IMM>(lo + hsw), p1 = lds_read8<IMM>(lo + (hsw ^ 8));
+  const u32x2 p2 = lds_read8<IMM>(hi + hsw), p3 = lds_read8<IMM>(hi + (hsw ^ 8));
+  return v8i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y, (int)p2.x, (int)p2.y, (int)p3.x, (int)p3.y};
+}
+
 // Wait until at most N LDS reads are outstanding; ties the wait to x so that no use of
 // x can be scheduled before it.
 template <int N>
@@ -88,6 +115,7 @@ struct GemmCfg {
   static_assert(ROWS % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "whole 1 KB copies per wave");
   static_assert(BN / WAVES_N <= 128 && 128 % (BN / WAVES_N) == 0, "a wave's n range is one scale block");
   static_assert(SCALES_PER_WAVE <= 64 && BM % WAVES == 0, "one scale copy per wave");
+  static_assert(WM % 4 == 0, "a lane's token scales are read 4 at a time");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(STAGES >= 2 && WM >= 1 && WN >= 1 && WM % 2 == 0, "");
   static_assert((STAGES - 2) * (LOADS + 1) <= 63, "vmcnt range");
@@ -97,16 +125,6 @@ constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit dwords (gfx9 layou
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
-}
-
-// Two floats 16 dwords apart from LDS (token scales of tiles j and j+1).
-template <int OFF0, int OFF1>
-__device__ __forceinline__ void lds_read_pair(uint32_t addr, float& a, float& b) {
-  typedef float v2f __attribute__((ext_vector_type(2)));
-  v2f v;
-  asm volatile("ds_read2_b32 %0, %1 offset0:%2 offset1:%3" : "=v"(v) : "v"(addr), "i"(OFF0), "i"(OFF1));
-  a = v.x;
-  b = v.y;
 }
 
 // Keep uses of x after the preceding wait (no code is emitted).
@@ -154,8 +172,13 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
       }
     }
   }
-  // token-scale copy: wave w fetches scales of rows m0 + w*SCALES_PER_WAVE + lane
-  int64_t srow = m0 + wave * C::SCALES_PER_WAVE + lane;
+  // token-scale copy: lane i of wave w fills scale slot p = w*SCALES_PER_WAVE + i.  A
+  // wave's token rows wm + 16j + r (j < WM, r < 16) sit at slots wm + r*WM + j, so the
+  // WM scales a lane needs are contiguous and come in with 16-byte reads (which, unlike
+  // broadcast 4-byte reads, cost no bank-conflict cycles).
+  const int slot = wave * C::SCALES_PER_WAVE + lane;
+  const int slab = slot / (16 * C::WM), within = slot % (16 * C::WM);
+  int64_t srow = m0 + slab * 16 * C::WM + (within % C::WM) * 16 + within / C::WM;
   srow = srow < m_end ? srow : m_end - 1;
   const uint32_t ssrc = (uint32_t)(srow * 4);
   const bool scale_lane = lane < C::SCALES_PER_WAVE;
@@ -182,6 +205,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
   const int q2 = (lane >> 4) * 2;
   const uint32_t rd_lo = (lane & 15) * 128 + ((q2 ^ x) << 4);
   const uint32_t rd_hi = (lane & 15) * 128 + (((q2 + 1) ^ x) << 4);
+  const uint32_t hsw = ((lane >> 4) & 1) * 8;
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
   const int64_t sb_base = ((n0 + wn) / 128) * kblocks;
 
@@ -215,19 +239,19 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
     const uint32_t stage = lds_base + (uint32_t)((kb % S) * C::STAGE_BYTES);
     const uint32_t a_lo = stage + wn * 128 + rd_lo, a_hi = stage + wn * 128 + rd_hi;
     const uint32_t b_lo = stage + C::A_BYTES + wm * 128 + rd_lo, b_hi = stage + C::A_BYTES + wm * 128 + rd_hi;
-    const uint32_t s_addr = stage + C::SCALE_OFF + (wm + (lane & 15)) * 4;
+    const uint32_t s_addr = stage + C::SCALE_OFF + (wm + (lane & 15) * C::WM) * 4;
 
     v8i fa[C::WN];
     v8i fb[3];
-    float sa[C::WM];
+    u32x4 sq[C::WM / 4];
     // weight fragments of all n tiles, token scales, token fragment 0
     [&]<int... I>(std::integer_sequence<int, I...>) {
-      ((fa[I] = join(lds_read16<I * 2048>(a_lo), lds_read16<I * 2048>(a_hi))), ...);
+      ((fa[I] = read_fragment<I * 2048>(a_lo, a_hi, hsw)), ...);
     }(std::make_integer_sequence<int, C::WN>{});
     [&]<int... P>(std::integer_sequence<int, P...>) {
-      (lds_read_pair<32 * P, 32 * P + 16>(s_addr, sa[2 * P], sa[2 * P + 1]), ...);
-    }(std::make_integer_sequence<int, C::WM / 2>{});
-    fb[0] = join(lds_read16<0>(b_lo), lds_read16<0>(b_hi));
+      ((sq[P] = lds_read16<16 * P>(s_addr)), ...);
+    }(std::make_integer_sequence<int, C::WM / 4>{});
+    fb[0] = read_fragment<0>(b_lo, b_hi, hsw);
 
     // token tile j: prefetch fragment j+1 (3 rotating registers keep a fragment's
     // registers untouched until well after the MFMAs that read them), wait for j,
@@ -237,8 +261,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
           [&] {
             constexpr int j = J;
             if constexpr (j + 1 < C::WM) {
-              fb[(j + 1) % 3] = join(lds_read16<(j + 1) * 2048>(b_lo), lds_read16<(j + 1) * 2048>(b_hi));
-              lds_wait<2>(fb[j % 3]);
+              fb[(j + 1) % 3] = read_fragment<(j + 1) * 2048>(b_lo, b_hi, hsw);
+              lds_wait<kReadsPerFragment>(fb[j % 3]);
             } else {
               lds_wait<0>(fb[j % 3]);
             }
@@ -246,9 +270,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
 #pragma unroll
               for (int i = 0; i < C::WN; ++i) after_wait(fa[i]);
 #pragma unroll
-              for (int jj = 0; jj < C::WM; ++jj) after_wait(sa[jj]);
+              for (int jj = 0; jj < C::WM / 4; ++jj) after_wait(sq[jj]);
             }
-            const float sab = sa[j] * sb;
+            const float sab = __uint_as_float(sq[j / 4][j % 4]) * sb;
 #pragma unroll
             for (int i = 0; i < C::WN; ++i) {
               v4f p = mfma_fp8(fa[i], fb[j % 3]);

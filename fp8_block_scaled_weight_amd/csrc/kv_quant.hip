@@ -7,44 +7,58 @@
 //
 // Recalibration is a global dependency (every code needs the final amax), so a
 // recalibrating call is two streaming passes: an amax pass (2 B/element read) and an
-// encode pass (2 B read + 1 B written per element).  Between them a one-thread
-// kernel turns the amax into the scale.  The amax is accumulated as the bit pattern
-// of a non-negative float with an unsigned atomic max: exact and order-independent.
+// encode pass (2 B read + 1 B written per element).  The amax is accumulated in the
+// scale slot itself as 0x80000000 | bits(amax) with an unsigned atomic max: exact,
+// order-independent, and marked as "not yet a scale" by the sign bit.  The encode
+// pass turns a marked value into the scale in every workgroup (all get the same
+// number) and workgroup 0 stores it back, so a workgroup reads either the marked amax
+// or the final scale and derives the same scale from both.
 #include "e4m3.hpp"
 #include "launch.hpp"
 
 namespace fp8q {
 
-constexpr int kKvBlock = 256;                 // 4 waves
+constexpr int kKvBlock = 256;                 // encode pass: 4 waves
+constexpr int kKvAmaxBlock = 1024;            // amax pass: 16 waves
 constexpr int kElemsPerWavePass = 64 * 16;    // 64 lanes x 16 bf16
+constexpr uint32_t kMarked = 0x80000000u;
 
 __global__ void kv_reset_kernel(float* k_scale, float* v_scale) {
   if (threadIdx.x == 0) {
-    reinterpret_cast<uint32_t*>(k_scale)[0] = 0u;
-    reinterpret_cast<uint32_t*>(v_scale)[0] = 0u;
+    reinterpret_cast<uint32_t*>(k_scale)[0] = kMarked;  // marked amax 0
+    reinterpret_cast<uint32_t*>(v_scale)[0] = kMarked;
   }
 }
 
-// One wave per token (grid-stride); each wave reduces K and V rows of its tokens.
-__global__ __launch_bounds__(kKvBlock) void kv_amax_kernel(const uint16_t* __restrict__ k, int64_t ld_k,
-                                                           const uint16_t* __restrict__ v, int64_t ld_v,
-                                                           int64_t tokens, int64_t row,
-                                                           const int64_t* __restrict__ slots,
-                                                           float* k_scale, float* v_scale) {
-  __shared__ uint32_t red[2][kKvBlock / 64];
+// One wave per token (grid-stride), two tokens in flight per wave; one atomic per
+// tensor per workgroup.  Few, wide workgroups keep the number of same-address atomics
+// small: they are performed past the per-XCD L2s and serialize there.
+__global__ __launch_bounds__(kKvAmaxBlock) void kv_amax_kernel(const uint16_t* __restrict__ k, int64_t ld_k,
+                                                               const uint16_t* __restrict__ v, int64_t ld_v,
+                                                               int64_t tokens, int64_t row,
+                                                               const int64_t* __restrict__ slots,
+                                                               float* k_scale, float* v_scale) {
+  constexpr int W = kKvAmaxBlock / 64;
+  __shared__ uint32_t red[2][W];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t waves = (int64_t)gridDim.x * (kKvBlock / 64);
+  const int64_t waves = (int64_t)gridDim.x * W;
   uint32_t mk = 0, mv = 0;
-  for (int64_t t = (int64_t)blockIdx.x * (kKvBlock / 64) + wave; t < tokens; t += waves) {
-    if (slots[t] < 0) continue;  // uniform per wave
+  auto token = [&](int64_t t) {
+    if (slots[t] < 0) return;  // uniform per wave
     for (int64_t e = lane * 16; e < row; e += kElemsPerWavePass) {
       const uint4* pk = reinterpret_cast<const uint4*>(k + t * ld_k + e);
       const uint4* pv = reinterpret_cast<const uint4*>(v + t * ld_v + e);
       mk = max(mk, absmax16(load_stream(pk), load_stream(pk + 1)));
       mv = max(mv, absmax16(load_stream(pv), load_stream(pv + 1)));
     }
+  };
+  int64_t t = (int64_t)blockIdx.x * W + wave;
+  for (; t + waves < tokens; t += 2 * waves) {
+    token(t);
+    token(t + waves);
   }
+  if (t < tokens) token(t);
   mk = max_over_wave(mk);
   mv = max_over_wave(mv);
   if (lane == 0) {
@@ -54,23 +68,19 @@ __global__ __launch_bounds__(kKvBlock) void kv_amax_kernel(const uint16_t* __res
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t a = 0, b = 0;
-    for (int w = 0; w < kKvBlock / 64; ++w) {
+    for (int w = 0; w < W; ++w) {
       a = max(a, red[0][w]);
       b = max(b, red[1][w]);
     }
     // the bf16 magnitude bits shifted up are the fp32 bits of the magnitude
-    if (a) atomicMax(reinterpret_cast<unsigned int*>(k_scale), a << 16);
-    if (b) atomicMax(reinterpret_cast<unsigned int*>(v_scale), b << 16);
+    if (a) atomicMax(reinterpret_cast<unsigned int*>(k_scale), kMarked | (a << 16));
+    if (b) atomicMax(reinterpret_cast<unsigned int*>(v_scale), kMarked | (b << 16));
   }
 }
 
-__global__ void kv_finalize_kernel(float* k_scale, float* v_scale, float range) {
-  if (threadIdx.x == 0) {
-    float ak = __uint_as_float(reinterpret_cast<uint32_t*>(k_scale)[0]);
-    float av = __uint_as_float(reinterpret_cast<uint32_t*>(v_scale)[0]);
-    k_scale[0] = scale_from_amax(ak, range);
-    v_scale[0] = scale_from_amax(av, range);
-  }
+// The scale a slot stands for: a marked amax becomes fl32(amax / range) (1 for 0).
+__device__ __forceinline__ float resolve_scale(uint32_t bits, float range) {
+  return (bits & kMarked) ? scale_from_amax(__uint_as_float(bits & ~kMarked), range) : __uint_as_float(bits);
 }
 
 // One wave per token: K row then V row, 16 elements per lane per pass.
@@ -79,12 +89,18 @@ __global__ __launch_bounds__(kKvBlock) void kv_write_kernel(const uint16_t* __re
                                                             int64_t tokens, int64_t row,
                                                             const int64_t* __restrict__ slots,
                                                             uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
-                                                            const float* k_scale, const float* v_scale) {
+                                                            float* k_scale, float* v_scale, float range) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t waves = (int64_t)gridDim.x * (kKvBlock / 64);
-  const Quantizer qk = make_quantizer(k_scale[0]);
-  const Quantizer qv = make_quantizer(v_scale[0]);
+  const float sk = resolve_scale(__atomic_load_n(reinterpret_cast<uint32_t*>(k_scale), __ATOMIC_RELAXED), range);
+  const float sv = resolve_scale(__atomic_load_n(reinterpret_cast<uint32_t*>(v_scale), __ATOMIC_RELAXED), range);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    __atomic_store_n(reinterpret_cast<uint32_t*>(k_scale), __float_as_uint(sk), __ATOMIC_RELAXED);
+    __atomic_store_n(reinterpret_cast<uint32_t*>(v_scale), __float_as_uint(sv), __ATOMIC_RELAXED);
+  }
+  const Quantizer qk = make_quantizer(sk);
+  const Quantizer qv = make_quantizer(sv);
   for (int64_t t = (int64_t)blockIdx.x * (kKvBlock / 64) + wave; t < tokens; t += waves) {
     const int64_t slot = slots[t];
     if (slot < 0) continue;
@@ -108,6 +124,12 @@ static unsigned kv_grid(int64_t tokens) {
   return (unsigned)(wgs < cap ? (wgs < 1 ? 1 : wgs) : cap);
 }
 
+static unsigned kv_amax_grid(int64_t tokens) {
+  // one wave per token up to 256 workgroups of 16 waves
+  const int64_t wgs = (tokens + 15) / 16;
+  return (unsigned)(wgs < 256 ? (wgs < 1 ? 1 : wgs) : 256);
+}
+
 hipError_t launch_kv_quant(const void* k, int64_t ld_k, const void* v, int64_t ld_v, int64_t tokens,
                            int32_t heads, const int64_t* slots, void* k_cache, void* v_cache,
                            float* k_scale, float* v_scale, float range, bool recalibrate,
@@ -118,13 +140,12 @@ hipError_t launch_kv_quant(const void* k, int64_t ld_k, const void* v, int64_t l
   const uint16_t* vv = reinterpret_cast<const uint16_t*>(v);
   if (recalibrate) {
     hipLaunchKernelGGL(kv_reset_kernel, dim3(1), dim3(64), 0, stream, k_scale, v_scale);
-    hipLaunchKernelGGL(kv_amax_kernel, dim3(grid), dim3(kKvBlock), 0, stream, kk, ld_k, vv, ld_v, tokens,
-                       row, slots, k_scale, v_scale);
-    hipLaunchKernelGGL(kv_finalize_kernel, dim3(1), dim3(64), 0, stream, k_scale, v_scale, range);
+    hipLaunchKernelGGL(kv_amax_kernel, dim3(kv_amax_grid(tokens)), dim3(kKvAmaxBlock), 0, stream, kk, ld_k, vv,
+                       ld_v, tokens, row, slots, k_scale, v_scale);
   }
   hipLaunchKernelGGL(kv_write_kernel, dim3(grid), dim3(kKvBlock), 0, stream, kk, ld_k, vv, ld_v, tokens, row,
                      slots, reinterpret_cast<uint8_t*>(k_cache), reinterpret_cast<uint8_t*>(v_cache),
-                     k_scale, v_scale);
+                     k_scale, v_scale, range);
   return hipGetLastError();
 }
 

@@ -185,8 +185,10 @@ fp8q_status fp8q_grouped_gemm_w8a8(const void* a, int64_t ld_a, const float* a_s
  * flags & FP8Q_KV_RECALIBRATE: first set *k_scale = fl32(amax_K / fp8_range) and
  *   *v_scale = fl32(amax_V / fp8_range), amax over every element this call writes
  *   (1.0 when it is 0), then write with those scales (the first write of an RL step).
- * flags == 0: write with the stored *k_scale, *v_scale (later decode steps); values
- *   beyond the E4M3 range saturate to +-448.
+ * flags == 0: write with the stored *k_scale, *v_scale (later decode steps), which
+ *   must be positive and finite; values beyond the E4M3 range saturate to +-448.
+ * While a recalibrating call runs, *k_scale and *v_scale hold an intermediate value
+ * (the amax with the sign bit set); the call's last kernel replaces it with the scale.
  * fp8_range > 0 and finite (448 maps amax onto the E4M3 maximum).
  * ---------------------------------------------------------------------------- */
 #define FP8Q_KV_RECALIBRATE 1u
