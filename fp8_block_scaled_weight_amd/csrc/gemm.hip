@@ -8,32 +8,27 @@
 //   y[m, n] = bf16( sum_kb  sa[kb][m] * sb[n/128][kb] * P_kb[m, n] ),
 //   P_kb[m, n] = sum_{k in block kb} a[m, k] * b[n, k]   (FP8 x FP8, fp32 accumulate)
 //
-// Matrix core.  Each 128-wide K block is exactly one v_mfma_f32_16x16x128_f8f6f4 per
-// 16x16 output tile, started from a zero accumulator, so P_kb leaves the matrix core
-// whole and is folded into the running fp32 sum with one FMA per element.  The MFMA's
-// A operand is 16 weight rows (n) and its B operand 16 token rows (m); both are
-// K-contiguous and loaded the same way (lane l: row l%16, bytes 32*(l/16)..+31 of the
-// 128-byte K block), so whatever K order the matrix core uses applies to both.  The
-// result gives lane l the outputs m = l%16, n = 4*(l/16) + r (r < 4): one token scale
-// per lane and tile, four consecutive outputs per store.
+// Matrix core.  A 128-wide K block of a 32x32 output tile is two chained
+// v_mfma_f32_32x32x64_f8f6f4 (K halves 0 and 1) started from a zero accumulator, so
+// P_kb leaves the matrix core whole and is folded into the running fp32 sum with one
+// FMA per element.  The MFMA's A operand is 32 weight rows (n) and its B operand 32
+// token rows (m); both are K-contiguous and loaded the same way (lane l: row l%32,
+// bytes 32*(l/32)..+31 of the K half), so whatever K order the matrix core uses applies
+// to both.  The result gives lane l the token m = l%32 and the weights
+// n = 8q + 4*(l/32) + r (q, r < 4): one token scale per lane and tile.
 //
 // Data movement.  A workgroup owns a BM x BN output tile and walks K in 128-byte steps.
-// Each step's operand rows (BN weight rows, then BM token rows, 128 bytes each) are
-// copied HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a ring of
-// STAGES buffers, STAGES-1 steps ahead of the step being multiplied.  In LDS the
-// 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7): the copies write 1 KB
-// (8 rows) per wave instruction in lane order, so each lane fetches the chunk that
-// belongs at its slot.  Fragments are read 8 bytes at a time (ds_read_b64, four per
-// lane and fragment): such a read is served a half-wave (32 lanes) at a time across
-// the 64 four-byte banks, the swizzle gives the 16 rows of a fragment 16 distinct
-// (row parity, chunk) bank groups, and lanes of odd 16-lane groups take the two
-// halves of each chunk in the opposite order, so every half-wave touches each bank
-// once (16-byte reads of the same data conflict two ways: the LDS bank-conflict
-// counter shows the difference).  The half swap permutes the K bytes of those lanes
-// identically for both operands, so the matrix core still pairs a[m][k] with b[n][k].
-// Reads carry explicit waits tied to their registers, and each step is entered
-// through one "wait for my copies, then barrier" sequence, so copies for later steps
-// stay in flight across the multiply.
+// Each step's operand rows (BN weight rows, then BM token rows, 128 bytes each) and
+// its scales are copied HBM -> LDS with buffer loads that write LDS directly (no VGPR
+// staging) into a ring of STAGES buffers, STAGES-1 steps ahead of the step being
+// multiplied.  In LDS the 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7):
+// the copies write 1 KB (8 rows) per wave instruction in lane order, so each lane
+// fetches the chunk that belongs at its slot; a 16-byte fragment read then gives the
+// 16 lanes served together 16 distinct (row parity, chunk) bank groups.  The copies
+// are issued in inline asm so that the compiler, which does not see them, schedules
+// and counts the LDS fragment reads on its own; each step is entered through one
+// "wait for my copies, then barrier" sequence, so copies for later steps stay in
+// flight across the multiply.
 #include <utility>
 
 #include "launch.hpp"
@@ -43,12 +38,12 @@ namespace fp8q {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-#define FP8Q_GLOBAL __attribute__((address_space(1)))
 #define FP8Q_LDS __attribute__((address_space(3)))
 
+// 16x16x128 FP8 MFMA from a zero accumulator (scale operands 0 select the unscaled
+// FP8 x FP8 -> fp32 instruction)
 __device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b) {
   v4f zero = {0.f, 0.f, 0.f, 0.f};
-  // scale operands 0 select the unscaled FP8 x FP8 -> fp32 instruction
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
@@ -59,42 +54,18 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return u >> 16;
 }
 
-template <int IMM>
-__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
-  u32x4 v;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(IMM));
-  return v;
-}
-
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-template <int IMM>
-__device__ __forceinline__ u32x2 lds_read8(uint32_t addr) {
-  u32x2 v;
-  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(IMM));
-  return v;
-}
-
-// One MFMA operand fragment (32 bytes per lane) as four 8-byte reads: chunk pair
-// (lo, hi), halves in the order hsw, hsw ^ 8 (hsw = 8 on odd 16-lane groups).
-constexpr int kReadsPerFragment = 4;
-
-template <int IMM>
-__device__ __forceinline__ v8i read_fragment(uint32_t lo, uint32_t hi, uint32_t hsw) {
-  const u32x2 p0 = lds_read8<IMM>(lo + hsw), p1 = lds_read8<IMM>(lo + (hsw ^ 8));
-  const u32x2 p2 = lds_read8<IMM>(hi + hsw), p3 = lds_read8<IMM>(hi + (hsw ^ 8));
-  return v8i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y, (int)p2.x, (int)p2.y, (int)p3.x, (int)p3.y};
-}
-
-// Wait until at most N LDS reads are outstanding; ties the wait to x so that no use of
-// x can be scheduled before it.
-template <int N>
-__device__ __forceinline__ void lds_wait(v8i& x) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N));
-}
 
 __device__ __forceinline__ v8i join(u32x4 lo, u32x4 hi) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// 32x32x64 FP8 MFMA accumulating into c (unscaled form, as above)
+__device__ __forceinline__ v16f mfma32(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
@@ -102,43 +73,58 @@ struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int WM = BM / WAVES_M / 16;  // 16x16 tiles per wave along m (tokens)
-  static constexpr int WN = BN / WAVES_N / 16;  // along n (weights)
-  static constexpr int ROWS = BN + BM;          // rows staged per K step: weights, then tokens
-  static constexpr int A_BYTES = BN * 128;      // weight rows of a stage
-  static constexpr int SCALE_OFF = ROWS * 128;  // token scales of a stage (BM floats)
-  static constexpr int STAGE_BYTES = ((ROWS * 128 + BM * 4) + 1023) / 1024 * 1024;
+  static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // wave tile: tokens x weights
+  static constexpr int JM = TM / 32, IN = TN / 32;            // 32x32 sub-tiles per wave
+  static constexpr int ROWS = BN + BM;                        // staged rows: weights, then tokens
+  static constexpr int SCALE_OFF = ROWS * 128;
+  static constexpr int SPW = BM / WAVES;                      // token scales copied per wave
+  static constexpr int NWS = BN >= 128 ? BN / 128 : 1;        // weight scales per step
+  static constexpr int WSC_OFF = SCALE_OFF + BM * 4;            // per-wave weight scales
+  static constexpr int STAGE_BYTES = ((WSC_OFF + WAVES * NWS * 4) + 1023) / 1024 * 1024;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int LOADS = ROWS / (8 * WAVES);    // 16-byte operand copies per thread per step
-  static constexpr int LOADS_W = BN / (8 * WAVES);    // of which weight rows
-  static constexpr int SCALES_PER_WAVE = BM / WAVES;  // 4-byte token-scale copies per wave per step
+  static constexpr int LOADS = ROWS / (8 * WAVES);
+  static constexpr int LOADS_W = BN / (8 * WAVES);
+  static constexpr int VM_PER_STEP = LOADS + 2;  // copies per thread and step
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "32x32 sub-tiles");
   static_assert(ROWS % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "whole 1 KB copies per wave");
-  static_assert(BN / WAVES_N <= 128 && 128 % (BN / WAVES_N) == 0, "a wave's n range is one scale block");
-  static_assert(SCALES_PER_WAVE <= 64 && BM % WAVES == 0, "one scale copy per wave");
-  static_assert(WM % 4 == 0, "a lane's token scales are read 4 at a time");
+  static_assert(TN <= 128 && 128 % TN == 0, "a wave's weight rows lie in one scale block");
+  static_assert(SPW >= 1 && SPW + NWS <= 64 && BM % WAVES == 0, "scale copies");
+  static_assert(JM == 1 || JM == 2 || JM == 4, "token scales per lane");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert(STAGES >= 2 && WM >= 1 && WN >= 1 && WM % 2 == 0, "");
-  static_assert((STAGES - 2) * (LOADS + 1) <= 63, "vmcnt range");
+  static_assert(STAGES >= 2 && (STAGES - 2) * VM_PER_STEP <= 63, "vmcnt range");
 };
 
-constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit dwords (gfx9 layout)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
+// Copies global -> LDS: lane i's 16 (or 4) bytes at rsrc base + voff + soff land at LDS
+// address m0 + 16i (4i).  Issued in asm so that the compiler's own wait counting for
+// LDS reads is not tied to these copies; the s_nop covers the one wait state an M0
+// write needs before an LDS-writing buffer load.
+__device__ __forceinline__ void dma16(v4i rs, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr) : "memory");
 }
-
-// Keep uses of x after the preceding wait (no code is emitted).
-template <class T>
-__device__ __forceinline__ void after_wait(T& x) {
-  asm volatile("" : "+v"(x));
+__device__ __forceinline__ void dma4(v4i rs, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds_addr) : "memory");
+}
+// Raw buffer resource (stride 0, 32-bit data format) over [base, base + bytes).
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  v4i r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000;
+  return r;
 }
 
 // LDS placement of 16-byte chunk c of staged row r: chunk c ^ swz(r).
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-// One BM x BN output tile: token rows [m0, m_end) (m_end - m0 may be < BM), weight
-// rows [n0, n0 + BN).  b / bs describe this tile's weight matrix and its scales.
-// a_rows and b_rows bound the operand buffers (rows, row pitch ld_a / ld_b bytes).
+template <class T>
+__device__ __forceinline__ T lds_ld(const uint8_t FP8Q_LDS* base, uint32_t off) {
+  return *reinterpret_cast<const T FP8Q_LDS*>(base + off);
+}
+
 template <class C>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t ld_a, int64_t a_rows,
                                           const float* __restrict__ as, int64_t ld_as,
@@ -146,159 +132,208 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
                                           const float* __restrict__ bs, int kblocks,
                                           uint16_t* __restrict__ y, int64_t ld_y, int64_t m0, int64_t m_end,
                                           int64_t n0, uint8_t FP8Q_LDS* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource builtins exist in the device pass only
-  constexpr int S = C::STAGES;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = (wave / C::WAVES_N) * C::WM * 16;
-  const int wn = (wave % C::WAVES_N) * C::WN * 16;
+  const int wm = (wave / C::WAVES_N) * C::TM;
+  const int wn = (wave % C::WAVES_N) * C::TN;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
-  // ---- copy sources: lane byte offsets that stay fixed while K advances (token rows
-  // past m_end are clamped to the last row: valid memory, never stored)
+  // ---- copy sources (fixed while K advances; K enters through the scalar offset)
   uint32_t src[C::LOADS];
-  {
-    const int r_in = lane >> 3;
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int r = (i * C::WAVES + wave) * 8 + r_in;
-      const int chunk = (lane & 7) ^ swz(r);
-      if (i < C::LOADS_W) {
-        src[i] = (uint32_t)((n0 + r) * ld_b) + chunk * 16;
-      } else {
-        int64_t m = m0 + (r - C::BN);
-        m = m < m_end ? m : m_end - 1;
-        src[i] = (uint32_t)(m * ld_a) + chunk * 16;
-      }
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int r = (i * C::WAVES + wave) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(r);
+    if (i < C::LOADS_W) {
+      src[i] = (uint32_t)((n0 + r) * ld_b) + chunk * 16;
+    } else {
+      int64_t m = m0 + (r - C::BN);
+      m = m < m_end ? m : m_end - 1;
+      src[i] = (uint32_t)(m * ld_a) + chunk * 16;
     }
   }
-  // token-scale copy: lane i of wave w fills scale slot p = w*SCALES_PER_WAVE + i.  A
-  // wave's token rows wm + 16j + r (j < WM, r < 16) sit at slots wm + r*WM + j, so the
-  // WM scales a lane needs are contiguous and come in with 16-byte reads (which, unlike
-  // broadcast 4-byte reads, cost no bank-conflict cycles).
-  const int slot = wave * C::SCALES_PER_WAVE + lane;
-  const int slab = slot / (16 * C::WM), within = slot % (16 * C::WM);
-  int64_t srow = m0 + slab * 16 * C::WM + (within % C::WM) * 16 + within / C::WM;
+  // token scales: slot p of the stage's scale area holds token
+  // (p / TM) * TM + 32 * (p % TM % JM) + (p % TM / JM), so a lane's JM scales are contiguous
+  const int slot = wave * C::SPW + lane;
+  const int seg = slot / C::TM, q = slot % C::TM;
+  int64_t srow = m0 + seg * C::TM + 32 * (q % C::JM) + q / C::JM;
   srow = srow < m_end ? srow : m_end - 1;
   const uint32_t ssrc = (uint32_t)(srow * 4);
-  const bool scale_lane = lane < C::SCALES_PER_WAVE;
+  const bool tok_lane = lane < C::SPW;
+  // weight scales: every wave copies the tile's NWS weight scales (lanes SPW ..
+  // SPW+NWS-1) into its own slots, so that each wave issues the same number of copies
+  const bool wsc_lane = lane >= C::SPW && lane < C::SPW + C::NWS;
+  const uint32_t wsrc = (uint32_t)(((n0 / 128) + (lane - C::SPW)) * kblocks * 4);
 
-  const uint32_t a_bytes = (uint32_t)(a_rows * ld_a);
-  const uint32_t b_bytes = (uint32_t)((n0 + C::BN) * ld_b);
-  auto issue = [&](int kb) {
-    uint8_t FP8Q_LDS* dst = lds + (kb % S) * C::STAGE_BYTES;
-    const __amdgpu_buffer_rsrc_t rb = rsrc(b + (size_t)kb * 128, b_bytes - kb * 128);
-    const __amdgpu_buffer_rsrc_t ra = rsrc(a + (size_t)kb * 128, a_bytes - kb * 128);
+  const v4i ra = make_rsrc(a, (uint32_t)(a_rows * ld_a));
+  const v4i rb = make_rsrc(b, (uint32_t)((n0 + C::BN) * ld_b));
+  const v4i rsa = make_rsrc(as, (uint32_t)(ld_as * kblocks * 4));
+  const v4i rsb = make_rsrc(bs, (uint32_t)((n0 / 128 + C::NWS) * kblocks * 4));
+
+  auto issue = [&](int kb, int stage) {
+    const uint32_t dst = lds_base + (uint32_t)(stage * C::STAGE_BYTES);
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(i < C::LOADS_W ? rb : ra,
-                                               (FP8Q_LDS void*)(dst + (i * C::WAVES + wave) * 1024), 16, src[i], 0, 0,
-                                               0);
-    const __amdgpu_buffer_rsrc_t rs = rsrc(as + (size_t)kb * ld_as, (uint32_t)(ld_as * 4));
-    if (scale_lane)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FP8Q_LDS void*)(dst + C::SCALE_OFF + wave * C::SCALES_PER_WAVE * 4),
-                                               4, ssrc, 0, 0, 0);
+      dma16(i < C::LOADS_W ? rb : ra, src[i], (uint32_t)kb * 128u, dst + (uint32_t)((i * C::WAVES + wave) * 1024));
+    const uint32_t sdst = dst + C::SCALE_OFF + (uint32_t)(wave * C::SPW * 4);
+    if (tok_lane) dma4(rsa, ssrc, (uint32_t)(kb * ld_as * 4), sdst);
+    if (wsc_lane) dma4(rsb, wsrc, (uint32_t)kb * 4u, dst + C::WSC_OFF + (uint32_t)((wave * C::NWS - C::SPW) * 4));
   };
 
-  // ---- fragment read addresses (lane part; stage and tile offsets added per step)
-  const int x = swz(lane & 15);  // fragment rows start at multiples of 16
-  const int q2 = (lane >> 4) * 2;
-  const uint32_t rd_lo = (lane & 15) * 128 + ((q2 ^ x) << 4);
-  const uint32_t rd_hi = (lane & 15) * 128 + (((q2 + 1) ^ x) << 4);
-  const uint32_t hsw = ((lane >> 4) & 1) * 8;
-  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
-  const int64_t sb_base = ((n0 + wn) / 128) * kblocks;
-
-  v4f acc[C::WN][C::WM];
+  // ---- fragment offsets: lane l reads row l%32 of a 32-row tile, 16-byte chunks
+  // 4h + 2(l/32) + e (e = 0, 1) for the MFMA of K half h
+  const int r32 = lane & 31, g = lane >> 5;
+  uint32_t fo[2][2];
 #pragma unroll
-  for (int i = 0; i < C::WN; ++i)
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int j = 0; j < C::WM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 2; ++e) fo[h][e] = (uint32_t)(r32 * 128 + (((4 * h + 2 * g + e) ^ swz(r32)) << 4));
+  const uint32_t so = (uint32_t)(C::SCALE_OFF + (wm + r32 * C::JM) * 4);
+  const uint32_t wso = (uint32_t)(C::WSC_OFF + (wave * C::NWS + wn / 128) * 4);
 
-  // prologue: copies for steps 0 .. S-2
+  v16f acc[C::IN][C::JM];
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < kblocks) issue(s);
-  float sb_next = bs[sb_base];
+  for (int i = 0; i < C::IN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::JM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // Software pipeline.  The 32x32 sub-tiles of a step are taken as chains c = j*IN + i
+  // (two MFMAs each: K halves 0 and 1).  Each chain's MFMAs are issued before the
+  // previous chain's promotion FMAs.  The last chain of a step is issued after the next
+  // step's barrier, so the matrix core has work while that step's first fragment reads
+  // are in flight; its operands stay in registers the new step's first reads do not touch.
+  constexpr int CH = C::IN * C::JM;
+  static_assert(CH % 2 == 0, "chains alternate between two result registers");
+  v16f P[2];
+  v8i fa[C::IN][2];
+  v8i fb[2][2];
+  float pc = 0.0f;   // scale product of the deferred chain
+  auto promote = [&](int slot, int i, int j, float c) { acc[i][j] = P[slot] * c + acc[i][j]; };
+  auto chain = [&](int slot, int i, int bslot) {
+    P[slot] = mfma32(fa[i][0], fb[bslot][0], v16f{});
+    P[slot] = mfma32(fa[i][1], fb[bslot][1], P[slot]);
+  };
+
+  constexpr int S = C::STAGES;
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < kblocks) issue(p, p);
+  int cur = 0;  // stage of step kb
   for (int kb = 0; kb < kblocks; ++kb) {
-    const float sb = sb_next;
-    if (kb + 1 < kblocks) sb_next = bs[sb_base + kb + 1];
-
-    // Wait until this thread's copies for step kb have landed (the copies of up to S-2
-    // later steps may stay in flight), then barrier: after it every thread's copies for
-    // kb are in LDS and no wave still reads the buffer of step kb-1, which the copy
-    // issued next reuses.
+    // this thread's copies for step kb have landed (those of up to S-2 later steps may
+    // still be in flight); after the barrier every thread's have, and no wave still
+    // reads the stage the copies issued next overwrite
     if (kb + S - 2 < kblocks) {
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((S - 2) * (C::LOADS + 1)) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((S - 2) * C::VM_PER_STEP) : "memory");
     } else {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    if (kb + S - 1 < kblocks) issue(kb + S - 1);
-
-    const uint32_t stage = lds_base + (uint32_t)((kb % S) * C::STAGE_BYTES);
-    const uint32_t a_lo = stage + wn * 128 + rd_lo, a_hi = stage + wn * 128 + rd_hi;
-    const uint32_t b_lo = stage + C::A_BYTES + wm * 128 + rd_lo, b_hi = stage + C::A_BYTES + wm * 128 + rd_hi;
-    const uint32_t s_addr = stage + C::SCALE_OFF + (wm + (lane & 15) * C::WM) * 4;
-
-    v8i fa[C::WN];
-    v8i fb[3];
-    u32x4 sq[C::WM / 4];
-    // weight fragments of all n tiles, token scales, token fragment 0
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      ((fa[I] = read_fragment<I * 2048>(a_lo, a_hi, hsw)), ...);
-    }(std::make_integer_sequence<int, C::WN>{});
-    [&]<int... P>(std::integer_sequence<int, P...>) {
-      ((sq[P] = lds_read16<16 * P>(s_addr)), ...);
-    }(std::make_integer_sequence<int, C::WM / 4>{});
-    fb[0] = read_fragment<0>(b_lo, b_hi, hsw);
-
-    // token tile j: prefetch fragment j+1 (3 rotating registers keep a fragment's
-    // registers untouched until well after the MFMAs that read them), wait for j,
-    // then one MFMA per weight tile and its promotion FMA
-    [&]<int... J>(std::integer_sequence<int, J...>) {
-      (
-          [&] {
-            constexpr int j = J;
-            if constexpr (j + 1 < C::WM) {
-              fb[(j + 1) % 3] = read_fragment<(j + 1) * 2048>(b_lo, b_hi, hsw);
-              lds_wait<kReadsPerFragment>(fb[j % 3]);
-            } else {
-              lds_wait<0>(fb[j % 3]);
-            }
-            if constexpr (j == 0) {
+    const uint8_t FP8Q_LDS* st = lds + cur * C::STAGE_BYTES;
+    const uint8_t FP8Q_LDS* stw = st + wn * 128;
+    const uint8_t FP8Q_LDS* stt = st + (C::BN + wm) * 128;
+    auto read_a = [&](int i) {
 #pragma unroll
-              for (int i = 0; i < C::WN; ++i) after_wait(fa[i]);
+      for (int h = 0; h < 2; ++h)
+        fa[i][h] = join(lds_ld<u32x4>(stw, fo[h][0] + i * 4096), lds_ld<u32x4>(stw, fo[h][1] + i * 4096));
+    };
+    auto read_b = [&](int j) {
 #pragma unroll
-              for (int jj = 0; jj < C::WM / 4; ++jj) after_wait(sq[jj]);
-            }
-            const float sab = __uint_as_float(sq[j / 4][j % 4]) * sb;
+      for (int h = 0; h < 2; ++h)
+        fb[j & 1][h] = join(lds_ld<u32x4>(stt, fo[h][0] + j * 4096), lds_ld<u32x4>(stt, fo[h][1] + j * 4096));
+    };
+    read_b(0);
 #pragma unroll
-            for (int i = 0; i < C::WN; ++i) {
-              v4f p = mfma_fp8(fa[i], fb[j % 3]);
-              acc[i][j] = p * sab + acc[i][j];
-            }
-          }(),
-          ...);
-    }(std::make_integer_sequence<int, C::WM>{});
+    for (int i = 0; i + 1 < C::IN; ++i) read_a(i);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb > 0) chain(1, C::IN - 1, (C::JM - 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(C::IN - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb + S - 1 < kblocks) issue(kb + S - 1, cur == 0 ? S - 1 : cur - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    float sa[C::JM];
+    if constexpr (C::JM == 4) {
+      const u32x4 t = lds_ld<u32x4>(st, so);
+      sa[0] = __uint_as_float(t.x); sa[1] = __uint_as_float(t.y);
+      sa[2] = __uint_as_float(t.z); sa[3] = __uint_as_float(t.w);
+    } else if constexpr (C::JM == 2) {
+      const u32x2 t = lds_ld<u32x2>(st, so);
+      sa[0] = __uint_as_float(t.x); sa[1] = __uint_as_float(t.y);
+    } else {
+      sa[0] = lds_ld<float>(st, so);
+    }
+    const float sb = lds_ld<float>(st, wso);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float c_prev = pc;
+#pragma unroll
+    for (int j = 0; j < C::JM; ++j) {
+      const float c = sa[j] * sb;
+#pragma unroll
+      for (int i = 0; i < C::IN; ++i) {
+        const int ch = j * C::IN + i;
+        if (ch == CH - 1) break;  // deferred to the next step
+        chain(ch & 1, i, j & 1);
+        if (i == 0 && j + 1 < C::JM) read_b(j + 1);
+        if (ch > 0) {
+          const int pi = (i == 0) ? C::IN - 1 : i - 1;
+          const int pj = (i == 0) ? j - 1 : j;
+          promote((ch - 1) & 1, pi, pj, (i == 0) ? c_prev : c);
+        } else if (kb > 0) {
+          promote(1, C::IN - 1, C::JM - 1, pc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      c_prev = c;
+    }
+    // the deferred chain's operands fa[IN-1], fb[(JM-1)&1] are already in flight
+    pc = sa[C::JM - 1] * sb;
+    if (CH >= 2) promote((CH - 2) & 1, (CH - 2) % C::IN, (CH - 2) / C::IN, (C::IN == 1) ? sa[C::JM - 2] * sb : pc);
+    __builtin_amdgcn_sched_barrier(0);
+    cur = (cur + 1 == S) ? 0 : cur + 1;
+  }
+  if (kblocks > 0) {
+    chain(1, C::IN - 1, (C::JM - 1) & 1);
+    promote(1, C::IN - 1, C::JM - 1, pc);
   }
 
-  // ---- epilogue: lane holds y[m][n .. n+3], m = m0 + wm + 16j + lane%16,
-  // n = n0 + wn + 16i + 4*(lane/16); one bf16 rounding per output
+  // ---- epilogue.  A lane holds y[m][n .. n+3] for m = wm + 32j + l%32 and
+  // n = wn + 32i + 8q + 4(l/32): four outputs of one row per 8 bytes.  Each wave
+  // rounds them to bf16 (once) into its own TM x TN row-major block of LDS, then reads
+  // the block back in 16-byte row pieces, so that each global store instruction writes
+  // whole row segments of 2*TN bytes.  16-byte chunks are XOR-swizzled per row so that
+  // both the 8-byte writes and the 16-byte reads touch every LDS bank once per pass.
+  constexpr int CPR = C::TN / 8;          // 16-byte chunks per row
+  constexpr int RPW = 16 / CPR;           // rows per 256-byte bank window
+  constexpr int RPI = 64 / CPR;           // rows per wave store instruction
+  static_assert(C::WAVES * C::TM * C::TN * 2 <= C::LDS_BYTES, "epilogue staging fits in LDS");
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  uint8_t FP8Q_LDS* ep = lds + wave * (C::TM * C::TN * 2);
 #pragma unroll
-  for (int j = 0; j < C::WM; ++j) {
-    const int64_t m = m0 + wm + 16 * j + (lane & 15);
-    if (m >= m_end) continue;
+  for (int j = 0; j < C::JM; ++j)
 #pragma unroll
-    for (int i = 0; i < C::WN; ++i) {
-      const int64_t n = n0 + wn + 16 * i + 4 * (lane >> 4);
-      uint2 o;
-      o.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
-      o.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
-      *reinterpret_cast<uint2*>(y + m * ld_y + n) = o;
-    }
+    for (int i = 0; i < C::IN; ++i)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int row = 32 * j + r32;
+        const int chunk = (4 * i + q4) ^ ((row / RPW) & (CPR - 1));
+        u32x2 o;
+        o.x = bf16_rne(acc[i][j][4 * q4 + 0]) | (bf16_rne(acc[i][j][4 * q4 + 1]) << 16);
+        o.y = bf16_rne(acc[i][j][4 * q4 + 2]) | (bf16_rne(acc[i][j][4 * q4 + 3]) << 16);
+        *reinterpret_cast<u32x2 FP8Q_LDS*>(ep + row * (C::TN * 2) + chunk * 16 + 8 * g) = o;
+      }
+  const int c_in = lane % CPR;
+#pragma unroll
+  for (int t = 0; t < C::TM / RPI; ++t) {
+    const int row = t * RPI + lane / CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4 FP8Q_LDS*>(ep + row * (C::TN * 2) +
+                                                           ((c_in ^ ((row / RPW) & (CPR - 1))) * 16));
+    const int64_t m = m0 + wm + row;
+    if (m < m_end) *reinterpret_cast<u32x4*>(y + m * ld_y + n0 + wn + 8 * c_in) = v;
   }
-#endif
 }
 
 // Tile order.  Workgroups are dealt to the 8 XCDs round-robin, so consecutive tile
@@ -326,9 +361,14 @@ __device__ __forceinline__ void tile_coords(int64_t t, int64_t m_tiles, int64_t 
 // Two waves per SIMD (8 per workgroup): while one wave waits for LDS or a barrier, the
 // other keeps the matrix core busy, and one wave's promotion FMAs overlap the other's
 // MFMAs.
-using CfgLarge = GemmCfg<256, 256, 2, 4, 2>;   // 128 x 64 per wave, 130 KB LDS
-using CfgMid = GemmCfg<128, 128, 2, 4, 2>;     // 64 x 32 per wave, 66 KB LDS
-using CfgSmall = GemmCfg<128, 64, 2, 2, 4>;    // 64 x 32 per wave, 4 waves: more tiles for mid-size M
+// Tile shapes.  Two waves per SIMD (8 per workgroup; 4 for the smallest tile): one
+// wave's promotion FMAs and fragment reads overlap the other's MFMAs.  The large tile
+// halves operand traffic per FLOP but leaves room in LDS for only two stages; the
+// smaller tiles keep three steps of copies in flight, which their shorter steps need.
+using CfgLarge = GemmCfg<256, 256, 2, 4, 2>;   // 128 x 64 per wave, 132 KB LDS
+using CfgMid = GemmCfg<128, 128, 2, 4, 4>;     // 64 x 32 per wave, 132 KB LDS
+using CfgMid2 = GemmCfg<128, 128, 2, 4, 2>;    // two workgroups per CU when tiles are plenty
+using CfgSmall = GemmCfg<128, 64, 2, 2, 4>;    // 64 x 32 per wave, 100 KB LDS
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void gemm_w8a8_kernel(const uint8_t* __restrict__ a, int64_t ld_a,
@@ -477,6 +517,11 @@ hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld
   const int64_t large_tiles = ((m + CfgLarge::BM - 1) / CfgLarge::BM) * (n / CfgLarge::BN);
   if (large_tiles >= 256)
     return launch_dense<CfgLarge>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  // with at least two tiles per CU, two co-resident workgroups hide each other's waits
+  // better than deeper copy rings
+  const int64_t mid_tiles = ((m + CfgMid::BM - 1) / CfgMid::BM) * (n / CfgMid::BN);
+  if (mid_tiles >= 512)
+    return launch_dense<CfgMid2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   return launch_dense<CfgMid>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
 }
 
@@ -487,7 +532,9 @@ hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld
 // m-tiles of the groups before it to find its (group, m-tile) and exits if it has
 // none.  No host synchronization, no workspace.
 // ----------------------------------------------------------------------------
-using CfgGrouped = CfgMid;
+// Grouped: the MoE layers give thousands of 128x128 tiles, so two co-resident
+// workgroups per CU (measured faster than the four-stage ring here).
+using CfgGrouped = CfgMid2;
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_w8a8_kernel(
@@ -556,3 +603,4 @@ hipError_t launch_grouped_gemm(const void* a, int64_t ld_a, const float* a_s, in
 }
 
 }  // namespace fp8q
+
