@@ -89,7 +89,8 @@ struct GemmCfg {
   static_assert(ROWS % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "whole 1 KB copies per wave");
   static_assert(TN <= 128 && 128 % TN == 0, "a wave's weight rows lie in one scale block");
   static_assert(SPW >= 1 && SPW + NWS <= 64 && BM % WAVES == 0, "scale copies");
-  static_assert(JM == 1 || JM == 2 || JM == 4, "token scales per lane");
+  static_assert(JM == 2 || JM == 4, "token scales per lane; the deferred chain's token "
+                "fragment must not be the one the next step reads first");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(STAGES >= 2 && (STAGES - 2) * VM_PER_STEP <= 63, "vmcnt range");
 };
@@ -508,10 +509,16 @@ static hipError_t launch_smallm(const void* a, int64_t ld_a, const float* a_s, i
 hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                        int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                        int64_t k, hipStream_t stream) {
-  // few tokens: stream the weights over all CUs
-  if (m <= 16) return launch_smallm<1>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-  if (m <= 32) return launch_smallm<2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-  if (m <= 64) return launch_smallm<4>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  // few tokens: stream the weights over all CUs.  A workgroup takes 16*WM tokens; WM
+  // shrinks (more workgroups, each re-reading its weight rows from L2) until the grid
+  // covers every CU
+  if (m <= 64) {
+    const int64_t n16 = n / 16;
+    if (m > 32 && n16 >= 256) return launch_smallm<4>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+    if (m > 16 && n16 * ((m + 31) / 32) >= 256)
+      return launch_smallm<2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+    return launch_smallm<1>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  }
   if (m < 1024) return launch_dense<CfgSmall>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   // large tiles when they still give every CU a tile
   const int64_t large_tiles = ((m + CfgLarge::BM - 1) / CfgLarge::BM) * (n / CfgLarge::BN);
