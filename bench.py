@@ -48,6 +48,15 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only copy 1 GiB device-to-device 3 times (reference for HBM byte counters)")
+    p.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                   help="no GPU: turn four rocprofv3 --pmc output directories (FETCH_SIZE and WRITE_SIZE of a "
+                        "bench run, then of a --calibrate-copy run) into the traffic summaries under profiles/")
+    p.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                   help="no GPU: matrix-core utilisation of the GEMM kernels from a rocprofv3 --pmc run of "
+                        "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY SQ_INSTS_MFMA "
+                        "SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS GRBM_GUI_ACTIVE")
+    p.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                   help="no GPU: per-kernel table from a rocprofv3 --kernel-trace --stats output directory")
     return p.parse_args()
 
 
@@ -78,8 +87,163 @@ def traffic_from_profile(kernel_tag: str, digest: str):
         return None
 
 
+def _counter_rows(d):
+    """(kernel name, counter, value) of every row of the rocprofv3 counter CSVs under d."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def _per_launch(rows, counter, match):
+    v = [x for k, c, x in rows if c.startswith(counter) and match(k)]
+    return (sum(v) / len(v), len(v)) if v else (None, 0)
+
+
+def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
+    """Write profiles/gemm_w8a8_4096_traffic.txt and profiles/quantizers_traffic.md from
+    FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch), each scaled by what the same counter
+    reads for a plain 1 GiB device copy."""
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    cf, cw = _counter_rows(cal_fetch_dir), _counter_rows(cal_write_dir)
+    kib = (1 << 30) / 1024
+    cal_f = max(x for _, c, x in cf if c.startswith("FETCH_SIZE"))
+    cal_w = max(x for _, c, x in cw if c.startswith("WRITE_SIZE"))
+    fs, ws = kib / cal_f, kib / cal_w
+    dom = lambda k: "GemmCfg<256, 256" in k and "gemm_w8a8_kernel" in k
+    f_raw, nf = _per_launch(fr, "FETCH_SIZE", dom)
+    w_raw, nw = _per_launch(wr, "WRITE_SIZE", dom)
+    fb, wb = f_raw * 1024 * fs, w_raw * 1024 * ws
+    alg = TOKENS * HIDDEN + HIDDEN * HIDDEN + 2 * TOKENS * HIDDEN + 4 * (HIDDEN // 128) * TOKENS \
+        + 4 * (HIDDEN // 128) ** 2
+    cmd = "rocprofv3 --pmc {c} --output-format csv -d <out>/{d} -o {o} -- python3 bench.py {a}"
+    lines = [
+        "# HBM traffic of the dominant kernel (M=N=K=4096 block-scaled GEMM, 256x256 tiles)",
+        "#",
+        "# Counters, one pass each, on one MI355X from the repository root:",
+        "#   " + cmd.format(c="FETCH_SIZE", d="pmc_FETCH_SIZE", o="bench", a="--steps 5 --warmup 2 --no-legs --no-cpu"),
+        "#   " + cmd.format(c="WRITE_SIZE", d="pmc_WRITE_SIZE", o="bench", a="--steps 5 --warmup 2 --no-legs --no-cpu"),
+        "# Calibration with a plain device copy of 1 GiB (torch copy_, 3 times):",
+        "#   " + cmd.format(c="FETCH_SIZE", d="cal_FETCH_SIZE", o="cal", a="--calibrate-copy"),
+        "#   " + cmd.format(c="WRITE_SIZE", d="cal_WRITE_SIZE", o="cal", a="--calibrate-copy"),
+        "# Summary written by:",
+        "#   python3 bench.py --summarize-counters <out>/pmc_FETCH_SIZE <out>/pmc_WRITE_SIZE "
+        "<out>/cal_FETCH_SIZE <out>/cal_WRITE_SIZE",
+        f"# The copy reads and writes {kib:.0f} KiB; the counters report {cal_f:.0f} KiB fetched and "
+        f"{cal_w:.0f} KiB written, so FETCH_SIZE is scaled by {fs:.4f} and WRITE_SIZE by {ws:.4f}.",
+        f"# Averages over every launch of the kernel in the run ({nf} and {nw} dispatches; KiB per dispatch).",
+        "# bench.py uses hbm_bytes_per_launch only while source_digest matches gemm.hip.",
+        f"source_digest: {source_digest('gemm.hip')}",
+        f"fetch_kib_per_launch_raw: {f_raw:.1f}",
+        f"write_kib_per_launch_raw: {w_raw:.1f}",
+        f"fetch_scale: {fs:.4f}",
+        f"write_scale: {ws:.4f}",
+        f"fetch_bytes_per_launch: {fb:.0f}",
+        f"write_bytes_per_launch: {wb:.0f}",
+        f"hbm_bytes_per_launch: {fb + wb:.0f}",
+        f"algorithmic_bytes_per_launch: {alg}",
+        f"# fetched / algorithmic operand bytes (A, B, scales): {fb / (alg - 2 * TOKENS * HIDDEN):.2f}x; "
+        f"written / output bytes: {wb / (2 * TOKENS * HIDDEN):.2f}x",
+    ]
+    with open(os.path.join(ROOT, "profiles", "gemm_w8a8_4096_traffic.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    w_el = 2 * HIDDEN * HIDDEN + 2 * KV_DIM * HIDDEN
+    quant = [("quant_weight_blk128_kernel", 2 * w_el, w_el + 4 * w_el // 16384),
+             ("quant_act_g128_kernel", 2 * TOKENS * HIDDEN, TOKENS * HIDDEN + 4 * TOKENS * HIDDEN // 128),
+             ("kv_amax_kernel", 2 * 2 * TOKENS * KV_DIM, 0),
+             ("kv_write_kernel", 2 * 2 * TOKENS * KV_DIM + 8 * TOKENS, 2 * TOKENS * KV_DIM)]
+    md = ["# HBM traffic of the quantizers in the benchmark step", "",
+          f"Same counter runs and calibration as `gemm_w8a8_4096_traffic.txt` (FETCH_SIZE x{fs:.4f}, "
+          f"WRITE_SIZE x{ws:.4f}), summarized by the same `bench.py --summarize-counters` command.", "",
+          "| kernel | fetched (MB) | algorithmic read (MB) | written (MB) | algorithmic write (MB) |",
+          "|---|---|---|---|---|"]
+    for name, rd, wrt in quant:
+        f_, _ = _per_launch(fr, "FETCH_SIZE", lambda k, n=name: n in k)
+        w_, _ = _per_launch(wr, "WRITE_SIZE", lambda k, n=name: n in k)
+        if f_ is None or w_ is None:
+            continue
+        md.append(f"| `{name}` | {f_ * 1024 * fs / 1e6:.2f} | {rd / 1e6:.2f} | {w_ * 1024 * ws / 1e6:.2f} | "
+                  f"{wrt / 1e6:.2f} |")
+    md += ["", "Figures are per launch (`quant_act_g128_kernel` runs twice per step, for the block input and",
+           "the attention output; the KV write also reads each token's 8-byte slot)."]
+    with open(os.path.join(ROOT, "profiles", "quantizers_traffic.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_mfma(d):
+    """Per GEMM instantiation: dispatches, average duration, matrix-core busy fraction
+    (SQ_VALU_MFMA_BUSY_CYCLES summed over the 1024 SIMDs, against the kernel duration at
+    the nominal 2.4 GHz and against GRBM_GUI_ACTIVE / 8 cycles per XCD) and the fraction
+    of wave time spent waiting on counters (s_waitcnt)."""
+    import csv
+    import glob
+    per = {}
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            k = r["Kernel_Name"]
+            if "gemm_w8a8_kernel" not in k:
+                continue
+            key = k.split("(")[0].replace("void fp8q::", "")
+            e = per.setdefault(key, {})
+            disp = e.setdefault(r["Dispatch_Id"], {"ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+            disp[r["Counter_Name"]] = disp.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    for key, disps in per.items():
+        ds = list(disps.values())[2:] or list(disps.values())
+        avg = lambda c: sum(x.get(c, 0.0) for x in ds) / len(ds)
+        ns = avg("ns")
+        gpu_cycles = avg("GRBM_GUI_ACTIVE") / 8
+        util = avg("SQ_VALU_MFMA_BUSY_CYCLES") / (gpu_cycles * 1024) if gpu_cycles else float("nan")
+        wait = avg("SQ_WAIT_INST_ANY") / avg("SQ_WAVE_CYCLES") if avg("SQ_WAVE_CYCLES") else float("nan")
+        print(f"[{key}]")
+        print(f"dispatches: {len(ds)}")
+        print(f"duration_us: {ns / 1e3:.2f}")
+        nominal = avg("SQ_VALU_MFMA_BUSY_CYCLES") / (1024 * ns * 2.4)
+        print(f"grbm_gui_active_per_xcd: {gpu_cycles:.0f}")
+        print(f"mfma_instructions: {avg('SQ_INSTS_MFMA'):.0f}")
+        print(f"mfma_busy_cycles_total: {avg('SQ_VALU_MFMA_BUSY_CYCLES'):.0f}")
+        print(f"mfma_utilisation_at_2.4GHz: {nominal:.3f}   (busy cycles / (1024 SIMDs x duration x 2.4 GHz))")
+        print(f"mfma_utilisation_vs_grbm_cycles: {util:.3f}")
+        print(f"wave_time_waiting_on_counters: {wait:.3f}")
+        print(f"lds_instructions: {avg('SQ_INSTS_LDS'):.0f}")
+        print(f"lds_bank_conflict_cycles: {avg('SQ_LDS_BANK_CONFLICT'):.0f}")
+        print()
+
+
+def summarize_trace(d):
+    """Markdown table of per-kernel statistics from a rocprofv3 --stats output directory."""
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(files[0])))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    print("| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |")
+    print("|---|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        if "fp8q" not in r["Name"]:
+            continue
+        print(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+              f"{float(r['MaxNs']) / 1e3:.2f} | {100 * float(r['TotalDurationNs']) / total:.1f} % |")
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))

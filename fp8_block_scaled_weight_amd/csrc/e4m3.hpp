@@ -174,7 +174,8 @@ __device__ __forceinline__ uint32_t max_over_wave(uint32_t v) {
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
 
-// 16-byte streaming (non-temporal) global accesses: data touched once is not kept.
+// 16-byte global accesses.  The streaming (non-temporal) forms keep data touched once
+// out of the caches; the plain forms let it stay for a consumer that follows.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream(const void* p) {
   u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -183,6 +184,13 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
 __device__ __forceinline__ void store_stream(void* p, uint4 v) {
   u32x4 w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ uint4 load_plain(const void* p) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_plain(void* p, uint4 v) {
+  *reinterpret_cast<u32x4*>(p) = u32x4{v.x, v.y, v.z, v.w};
 }
 
 }  // namespace fp8q

@@ -520,9 +520,9 @@ hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld
     return launch_smallm<1>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   }
   if (m < 1024) return launch_dense<CfgSmall>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-  // large tiles when they still give every CU a tile
+  // large tiles when they cover n exactly and still give every CU a tile
   const int64_t large_tiles = ((m + CfgLarge::BM - 1) / CfgLarge::BM) * (n / CfgLarge::BN);
-  if (large_tiles >= 256)
+  if (n % CfgLarge::BN == 0 && large_tiles >= 256)
     return launch_dense<CfgLarge>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   // with at least two tiles per CU, two co-resident workgroups hide each other's waits
   // better than deeper copy rings

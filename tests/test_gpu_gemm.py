@@ -86,6 +86,21 @@ def test_mlp_shapes_sampled():
     check(xq, xs, wq, ws, rows=np.sort(g.choice(300, 40, replace=False)))
 
 
+@pytest.mark.parametrize("m,n,k", [
+    (4000, 4096, 1024),   # 256x256 tiles, ragged last token tile
+    (2000, 4096, 512),    # 128x128 tiles, two workgroups per CU, ragged
+    (1000, 1024, 512),    # 128x128 tiles, four-stage copy ring, ragged
+    (700, 1024, 640),     # 128x64 tiles, ragged
+    (65536, 384, 256),    # n not a multiple of 256 with enough rows for 256x256 tiles
+])
+def test_tile_configs_ragged(m, n, k):
+    g = np.random.Generator(np.random.PCG64(m + n))
+    xq, xs, wq, ws = quantized_operands(m, n, k, tensor=20 + n // 128)
+    edges = [0, 1, 127, 128, 255, 256, m - 129, m - 128, m - 2, m - 1]
+    rows = np.unique(np.concatenate([np.array([r for r in edges if 0 <= r < m]), g.choice(m, 40, replace=False)]))
+    check(xq, xs, wq, ws, rows=rows)
+
+
 def test_padded_output_pitch_untouched():
     xq, xs, wq, ws = quantized_operands(40, 256, 384, tensor=9)
     yfull = check(xq, xs, wq, ws, ld_y=264)
