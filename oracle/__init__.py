@@ -59,8 +59,12 @@ def lib():
         L.oracle_scale.restype = ctypes.c_float
         L.oracle_quantize_value.argtypes = [ctypes.c_float, ctypes.c_float]
         L.oracle_quantize_value.restype = ctypes.c_uint8
-        L.oracle_quant_weight_blk128.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p]
-        L.oracle_quant_act_g128.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p, _i64]
+        L.oracle_scale_ue8m0.argtypes = [ctypes.c_float, ctypes.c_float]
+        L.oracle_scale_ue8m0.restype = ctypes.c_float
+        for f in ("oracle_quant_weight_blk128", "oracle_quant_weight_blk128_ue8m0"):
+            getattr(L, f).argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p]
+        for f in ("oracle_quant_act_g128", "oracle_quant_act_g128_ue8m0"):
+            getattr(L, f).argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p, _i64]
         L.oracle_gemm_w8a8.argtypes = [_u8p, _i64, _f32p, _i64, _u8p, _i64, _f32p, _f64p, _i64,
                                        _i64, _i64, _i64]
         L.oracle_grouped_gemm_w8a8.argtypes = [_u8p, _i64, _f32p, _i64, _u8p, _f32p, _i32p,
@@ -70,6 +74,7 @@ def lib():
                                       _f32p, _f32p, ctypes.c_float, ctypes.c_int]
         L.oracle_kv_scales.argtypes = [_u16p, _i64, _u16p, _i64, _i64, _i64, _i64p, ctypes.c_float, _f32p, _f32p]
         for f in ("oracle_kv_scales", "oracle_quant_weight_blk128", "oracle_quant_act_g128", "oracle_gemm_w8a8",
+                  "oracle_quant_weight_blk128_ue8m0", "oracle_quant_act_g128_ue8m0",
                   "oracle_grouped_gemm_w8a8", "oracle_kv_quant", "oracle_num_threads"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -107,29 +112,38 @@ def scale(amax: float, rng: float = 448.0) -> np.float32:
     return np.float32(lib().oracle_scale(float(amax), float(rng)))
 
 
+def scale_ue8m0(amax: float, rng: float = 448.0) -> np.float32:
+    """Power-of-two scale: the smallest 2^e with rng * 2^e >= amax (e in [-127, 127]); 1 for 0."""
+    return np.float32(lib().oracle_scale_ue8m0(float(amax), float(rng)))
+
+
 def quantize_value(x: float, s: float) -> int:
     """E4M3FN code of the exact quotient x / s (x and s as binary32)."""
     return int(lib().oracle_quantize_value(float(np.float32(x)), float(np.float32(s))))
 
 
-def quant_weight_blk128(w_bits: np.ndarray):
-    """128x128 blockwise quantization of a bf16 [n, k] weight -> (codes [n,k], scales [n/128,k/128])."""
+def quant_weight_blk128(w_bits: np.ndarray, ue8m0: bool = False):
+    """128x128 blockwise quantization of a bf16 [n, k] weight -> (codes [n,k], scales [n/128,k/128]).
+    ue8m0=True takes power-of-two scales instead of fl32(amax/448)."""
     w = _u16(w_bits)
     n, k = w.shape
     q = np.empty((n, k), dtype=np.uint8)
     s = np.empty((n // 128, k // 128), dtype=np.float32)
-    _check(lib().oracle_quant_weight_blk128(w, n, k, k, q, k, s), "quant_weight_blk128")
+    f = lib().oracle_quant_weight_blk128_ue8m0 if ue8m0 else lib().oracle_quant_weight_blk128
+    _check(f(w, n, k, k, q, k, s), "quant_weight_blk128")
     return q, s
 
 
-def quant_act_g128(x_bits: np.ndarray, ld_s: int | None = None):
-    """1x128 group quantization of bf16 [m, k] -> (codes [m,k], scales [k/128, ld_s])."""
+def quant_act_g128(x_bits: np.ndarray, ld_s: int | None = None, ue8m0: bool = False):
+    """1x128 group quantization of bf16 [m, k] -> (codes [m,k], scales [k/128, ld_s]).
+    ue8m0=True takes power-of-two scales instead of fl32(amax/448)."""
     x = _u16(x_bits)
     m, k = x.shape
     ld_s = m if ld_s is None else ld_s
     q = np.empty((m, k), dtype=np.uint8)
     s = np.zeros((k // 128, ld_s), dtype=np.float32)
-    _check(lib().oracle_quant_act_g128(x, m, k, k, q, k, s, ld_s), "quant_act_g128")
+    f = lib().oracle_quant_act_g128_ue8m0 if ue8m0 else lib().oracle_quant_act_g128
+    _check(f(x, m, k, k, q, k, s, ld_s), "quant_act_g128")
     return q, s
 
 

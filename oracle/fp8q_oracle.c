@@ -35,6 +35,11 @@
  *   - GEMM: exact dequantize, fp64 accumulation, fp64 output.
  *   - KV: one fp32 scale per tensor (K, V) per call; amax over the tokens the
  *     call writes (slot >= 0).
+ *   - Power-of-two (UE8M0) scale variant, the alternative the "Experimental
+ *     results" ablation compares with FP32 scales: scale = the smallest power
+ *     of two 2^e with 448 * 2^e >= amax (the block maximum still fits the E4M3
+ *     range), e limited to the E8M0 exponent range [-127, 127]; 1 for amax 0.
+ *     The quotient x / 2^e is then exact and only the E4M3 rounding remains.
  *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC.
  * Every entry point returns 0 on success, -1 on non-finite input, -2 on a bad
@@ -120,6 +125,22 @@ float oracle_scale(float amax, float range) {
   return amax / range;
 }
 
+/* Power-of-two (UE8M0) scale [FP8-RL, "Experimental results", scale-format
+ * ablation]: 2^e for the smallest integer e with range * 2^e >= amax, found by
+ * exact comparisons (range * 2^e is exact in binary32 here), then limited to
+ * [-127, 127]; 1 for amax == 0.  2^-127 is a binary32 subnormal, still exact. */
+float oracle_scale_ue8m0(float amax, float range) {
+  if (amax == 0.0f) return 1.0f;
+  int e = ilogbf(amax) - ilogbf(range);
+  while ((double)range * ldexp(1.0, e) < (double)amax) ++e;
+  while ((double)range * ldexp(1.0, e - 1) >= (double)amax) --e;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return ldexpf(1.0f, e);
+}
+
+typedef float (*scale_rule_fn)(float amax, float range);
+
 /* One element: the fp64 quotient x/s decides every E4M3 rounding exactly as
  * the real quotient would (x has 8 and s 24 significant bits, so x/s is either
  * exactly a midpoint or at least ~2^-29 relative away from it). */
@@ -128,8 +149,8 @@ uint8_t oracle_quantize_value(float x, float s) {
 }
 
 /* ---- a1: 128x128 blockwise weight quantization [FP8-RL, FP8 format] ---- */
-int oracle_quant_weight_blk128(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
-                               uint8_t* q, int64_t ld_q, float* s) {
+static int quant_weight_rule(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
+                             uint8_t* q, int64_t ld_q, float* s, scale_rule_fn rule) {
   if (n < 0 || k < 0 || n % 128 || k % 128 || ld_w < k || ld_q < k) return -2;
   int64_t nb = n / 128, kb = k / 128;
   int bad = 0;
@@ -145,7 +166,7 @@ int oracle_quant_weight_blk128(const uint16_t* w, int64_t n, int64_t k, int64_t 
           if (a > amax) amax = a;
         }
       }
-      float sc = oracle_scale(amax, (float)E4M3_MAX);
+      float sc = rule(amax, (float)E4M3_MAX);
       s[bi * kb + bj] = sc;
       for (int64_t r = 0; r < 128; ++r) {
         for (int64_t c = 0; c < 128; ++c) {
@@ -158,10 +179,20 @@ int oracle_quant_weight_blk128(const uint16_t* w, int64_t n, int64_t k, int64_t 
   return bad ? -1 : 0;
 }
 
+int oracle_quant_weight_blk128(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
+                               uint8_t* q, int64_t ld_q, float* s) {
+  return quant_weight_rule(w, n, k, ld_w, q, ld_q, s, oracle_scale);
+}
+
+int oracle_quant_weight_blk128_ue8m0(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
+                                     uint8_t* q, int64_t ld_q, float* s) {
+  return quant_weight_rule(w, n, k, ld_w, q, ld_q, s, oracle_scale_ue8m0);
+}
+
 /* ---- a2: dynamic 1x128 activation quantization [FP8-RL, step 1] ----
  * Scale of row m, group g is stored at s[g*ld_s + m]. */
-int oracle_quant_act_g128(const uint16_t* x, int64_t m, int64_t k, int64_t ld_x,
-                          uint8_t* q, int64_t ld_q, float* s, int64_t ld_s) {
+static int quant_act_rule(const uint16_t* x, int64_t m, int64_t k, int64_t ld_x,
+                          uint8_t* q, int64_t ld_q, float* s, int64_t ld_s, scale_rule_fn rule) {
   if (m < 0 || k < 0 || k % 128 || ld_x < k || ld_q < k || ld_s < m) return -2;
   int64_t groups = k / 128;
   int bad = 0;
@@ -175,7 +206,7 @@ int oracle_quant_act_g128(const uint16_t* x, int64_t m, int64_t k, int64_t ld_x,
         float a = fabsf(v);
         if (a > amax) amax = a;
       }
-      float sc = oracle_scale(amax, (float)E4M3_MAX);
+      float sc = rule(amax, (float)E4M3_MAX);
       s[g * ld_s + row] = sc;
       for (int64_t c = 0; c < 128; ++c) {
         float v = bf16_to_float(x[row * ld_x + g * 128 + c]);
@@ -184,6 +215,16 @@ int oracle_quant_act_g128(const uint16_t* x, int64_t m, int64_t k, int64_t ld_x,
     }
   }
   return bad ? -1 : 0;
+}
+
+int oracle_quant_act_g128(const uint16_t* x, int64_t m, int64_t k, int64_t ld_x,
+                          uint8_t* q, int64_t ld_q, float* s, int64_t ld_s) {
+  return quant_act_rule(x, m, k, ld_x, q, ld_q, s, ld_s, oracle_scale);
+}
+
+int oracle_quant_act_g128_ue8m0(const uint16_t* x, int64_t m, int64_t k, int64_t ld_x,
+                                uint8_t* q, int64_t ld_q, float* s, int64_t ld_s) {
+  return quant_act_rule(x, m, k, ld_x, q, ld_q, s, ld_s, oracle_scale_ue8m0);
 }
 
 /* ---- a3: block-scaled W8A8 GEMM [FP8-RL, step 1; Rounding] ----
