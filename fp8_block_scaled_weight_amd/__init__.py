@@ -32,6 +32,8 @@ FP8Q_KV_RECALIBRATE = 1
 EXPORTED = (
     "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version", "fp8q_quant_weight_blk128",
     "fp8q_quant_act_g128", "fp8q_gemm_w8a8_blkscaled", "fp8q_grouped_gemm_w8a8", "fp8q_kv_quant",
+    "fp8q_quant_weight_blk128_ue8m0", "fp8q_quant_act_g128_ue8m0", "fp8q_gemm_w8a8_ue8m0",
+    "fp8q_grouped_gemm_w8a8_ue8m0",
 )
 
 
@@ -66,10 +68,13 @@ def lib() -> ctypes.CDLL:
         L.fp8q_last_error.restype = ctypes.c_char_p
         L.fp8q_abi_version.argtypes = []
         L.fp8q_abi_version.restype = ctypes.c_int
-        L.fp8q_quant_weight_blk128.argtypes = [ctypes.POINTER(WeightDesc), i32, vp]
-        L.fp8q_quant_act_g128.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp]
+        for sfx in ("", "_ue8m0"):
+            getattr(L, "fp8q_quant_weight_blk128" + sfx).argtypes = [ctypes.POINTER(WeightDesc), i32, vp]
+            getattr(L, "fp8q_quant_act_g128" + sfx).argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp]
+            getattr(L, "fp8q_grouped_gemm_w8a8" + sfx).argtypes = [vp, i64, vp, i64, vp, vp, vp, i32, i64, vp, i64,
+                                                                   i64, i64, vp]
         L.fp8q_gemm_w8a8_blkscaled.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp]
-        L.fp8q_grouped_gemm_w8a8.argtypes = [vp, i64, vp, i64, vp, vp, vp, i32, i64, vp, i64, i64, i64, vp]
+        L.fp8q_gemm_w8a8_ue8m0.argtypes = L.fp8q_gemm_w8a8_blkscaled.argtypes
         L.fp8q_kv_quant.argtypes = [vp, i64, vp, i64, i64, i32, i32, vp, vp, vp, i32, i64, vp, vp, f32, u32, vp]
         for name in EXPORTED[3:]:
             getattr(L, name).restype = ctypes.c_int
@@ -128,6 +133,15 @@ def fp8q_quant_weight_blk128(weights: Iterable[tuple], stream=None) -> None:
     """Blockwise-quantize many bf16 weights in one call.
 
     weights: iterable of (w [n,k] bf16, q [n,k] fp8, s [n/128,k/128] fp32) device tensors."""
+    _quant_weight("fp8q_quant_weight_blk128", weights, stream)
+
+
+def fp8q_quant_weight_blk128_ue8m0(weights: Iterable[tuple], stream=None) -> None:
+    """As fp8q_quant_weight_blk128, with power-of-two (UE8M0) scales."""
+    _quant_weight("fp8q_quant_weight_blk128_ue8m0", weights, stream)
+
+
+def _quant_weight(fn: str, weights: Iterable[tuple], stream) -> None:
     items = list(weights)
     arr = (WeightDesc * max(len(items), 1))()
     for i, (w, q, s) in enumerate(items):
@@ -136,45 +150,72 @@ def fp8q_quant_weight_blk128(weights: Iterable[tuple], stream=None) -> None:
             raise ValueError(f"weight {i}: q must be [n,k] and s contiguous [n/128,k/128]")
         arr[i] = WeightDesc(_dev(w, "w", BF16), _dev(q, "q", FP8), _dev(s, "s", F32), n, k,
                             _rows(w, "w"), _rows(q, "q"))
-    _check(lib().fp8q_quant_weight_blk128(arr, len(items), _stream(stream)), "fp8q_quant_weight_blk128")
+    _check(getattr(lib(), fn)(arr, len(items), _stream(stream)), fn)
 
 
 def fp8q_quant_act_g128(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
     """Per-token 1x128 group quantization: x [m,k] bf16 -> q [m,k] fp8, s [k/128, ld_s] fp32."""
+    _quant_act("fp8q_quant_act_g128", x, q, s, stream)
+
+
+def fp8q_quant_act_g128_ue8m0(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
+    """As fp8q_quant_act_g128, with power-of-two (UE8M0) scales."""
+    _quant_act("fp8q_quant_act_g128_ue8m0", x, q, s, stream)
+
+
+def _quant_act(fn: str, x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream) -> None:
     m, k = x.shape
     if tuple(q.shape) != (m, k) or s.dim() != 2 or s.shape[0] != k // 128 or s.stride(1) != 1:
         raise ValueError("q must be [m,k] and s [k/128, ld_s] with unit column stride")
-    _check(lib().fp8q_quant_act_g128(_dev(x, "x", BF16), m, k, _rows(x, "x"), _dev(q, "q", FP8), _rows(q, "q"),
-                                     _dev(s, "s", F32), s.stride(0), _stream(stream)), "fp8q_quant_act_g128")
+    _check(getattr(lib(), fn)(_dev(x, "x", BF16), m, k, _rows(x, "x"), _dev(q, "q", FP8), _rows(q, "q"),
+                              _dev(s, "s", F32), s.stride(0), _stream(stream)), fn)
 
 
 def fp8q_gemm_w8a8_blkscaled(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
                              y: torch.Tensor, stream=None) -> None:
     """y [m,n] bf16 = block-scaled a [m,k] fp8 (scales a_s [k/128, ld_as]) x b [n,k] fp8 (b_s [n/128,k/128])^T."""
+    _gemm("fp8q_gemm_w8a8_blkscaled", a, a_s, b, b_s, y, stream)
+
+
+def fp8q_gemm_w8a8_ue8m0(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
+                         y: torch.Tensor, stream=None) -> None:
+    """As fp8q_gemm_w8a8_blkscaled for power-of-two scales, applied by the matrix core."""
+    _gemm("fp8q_gemm_w8a8_ue8m0", a, a_s, b, b_s, y, stream)
+
+
+def _gemm(fn, a, a_s, b, b_s, y, stream) -> None:
     m, k = a.shape
     n = b.shape[0]
     if b.shape[1] != k or tuple(y.shape) != (m, n) or not b_s.is_contiguous() or a_s.stride(1) != 1:
         raise ValueError("shape mismatch between a, b and y")
-    _check(lib().fp8q_gemm_w8a8_blkscaled(_dev(a, "a", FP8), _rows(a, "a"), _dev(a_s, "a_s", F32), a_s.stride(0),
-                                          _dev(b, "b", FP8), _rows(b, "b"), _dev(b_s, "b_s", F32),
-                                          _dev(y, "y", BF16), _rows(y, "y"), m, n, k, _stream(stream)),
-           "fp8q_gemm_w8a8_blkscaled")
+    _check(getattr(lib(), fn)(_dev(a, "a", FP8), _rows(a, "a"), _dev(a_s, "a_s", F32), a_s.stride(0),
+                              _dev(b, "b", FP8), _rows(b, "b"), _dev(b_s, "b_s", F32),
+                              _dev(y, "y", BF16), _rows(y, "y"), m, n, k, _stream(stream)), fn)
 
 
 def fp8q_grouped_gemm_w8a8(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
                            group_offsets: torch.Tensor, y: torch.Tensor, stream=None) -> None:
     """Grouped GEMM: rows [off[g], off[g+1]) of a [M,k] times b[g] ([G,n,k]) with scales b_s [G,n/128,k/128]."""
+    _grouped("fp8q_grouped_gemm_w8a8", a, a_s, b, b_s, group_offsets, y, stream)
+
+
+def fp8q_grouped_gemm_w8a8_ue8m0(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
+                                 group_offsets: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """As fp8q_grouped_gemm_w8a8 for power-of-two scales, applied by the matrix core."""
+    _grouped("fp8q_grouped_gemm_w8a8_ue8m0", a, a_s, b, b_s, group_offsets, y, stream)
+
+
+def _grouped(fn, a, a_s, b, b_s, group_offsets, y, stream) -> None:
     total_m, k = a.shape
     g, n, kb = b.shape
     if kb != k or tuple(y.shape) != (total_m, n) or not b.is_contiguous() or not b_s.is_contiguous():
         raise ValueError("shape mismatch between a, b and y")
     if group_offsets.numel() != g + 1:
         raise ValueError("group_offsets must have G+1 entries")
-    _check(lib().fp8q_grouped_gemm_w8a8(_dev(a, "a", FP8), _rows(a, "a"), _dev(a_s, "a_s", F32), a_s.stride(0),
-                                        _dev(b, "b", FP8), _dev(b_s, "b_s", F32),
-                                        _dev(group_offsets, "group_offsets", (torch.int32,)), g, total_m,
-                                        _dev(y, "y", BF16), _rows(y, "y"), n, k, _stream(stream)),
-           "fp8q_grouped_gemm_w8a8")
+    _check(getattr(lib(), fn)(_dev(a, "a", FP8), _rows(a, "a"), _dev(a_s, "a_s", F32), a_s.stride(0),
+                              _dev(b, "b", FP8), _dev(b_s, "b_s", F32),
+                              _dev(group_offsets, "group_offsets", (torch.int32,)), g, total_m,
+                              _dev(y, "y", BF16), _rows(y, "y"), n, k, _stream(stream)), fn)
 
 
 def fp8q_kv_quant(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,

@@ -84,7 +84,7 @@ const char* fp8q_last_error(void) { return g_err; }
 
 int fp8q_abi_version(void) { return FP8Q_ABI_VERSION; }
 
-fp8q_status fp8q_quant_weight_blk128(const fp8q_weight_desc* descs, int32_t count, void* stream) {
+static fp8q_status quant_weight(const fp8q_weight_desc* descs, int32_t count, void* stream, bool pow2) {
   if (count < 1) return fail(FP8Q_ERR_SHAPE, "count must be >= 1 (got %d)", count);
   if (!descs) return fail(FP8Q_ERR_NULL, "descs is NULL");
   int64_t total = 0;
@@ -113,7 +113,7 @@ fp8q_status fp8q_quant_weight_blk128(const fp8q_weight_desc* descs, int32_t coun
     if (d.n == 0 || d.k == 0) continue;
     const int64_t nblk = (d.n / 128) * (d.k / 128);
     if (chunk.count == fp8q::kWeightChunk || blocks + nblk > (int64_t)0x7fffffff) {
-      st = launched(fp8q::launch_quant_weight_chunk(chunk, blocks, s), "quant_weight_blk128");
+      st = launched(fp8q::launch_quant_weight_chunk(chunk, blocks, pow2, s), "quant_weight_blk128");
       if (st != FP8Q_OK) return st;
       chunk.count = 0;
       blocks = 0;
@@ -128,11 +128,19 @@ fp8q_status fp8q_quant_weight_blk128(const fp8q_weight_desc* descs, int32_t coun
     e.kblocks = (int32_t)(d.k / 128);
     blocks += nblk;
   }
-  return launched(fp8q::launch_quant_weight_chunk(chunk, blocks, s), "quant_weight_blk128");
+  return launched(fp8q::launch_quant_weight_chunk(chunk, blocks, pow2, s), "quant_weight_blk128");
 }
 
-fp8q_status fp8q_quant_act_g128(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q, int64_t ld_q,
-                                float* s, int64_t ld_s, void* stream) {
+fp8q_status fp8q_quant_weight_blk128(const fp8q_weight_desc* descs, int32_t count, void* stream) {
+  return quant_weight(descs, count, stream, false);
+}
+
+fp8q_status fp8q_quant_weight_blk128_ue8m0(const fp8q_weight_desc* descs, int32_t count, void* stream) {
+  return quant_weight(descs, count, stream, true);
+}
+
+static fp8q_status quant_act(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q, int64_t ld_q, float* s,
+                             int64_t ld_s, void* stream, bool pow2) {
   if (m < 0 || k < 0) return fail(FP8Q_ERR_SHAPE, "negative shape");
   if (k % 128) return fail(FP8Q_ERR_SHAPE, "k=%lld must be a multiple of 128", (long long)k);
   if (m == 0 || k == 0) {
@@ -145,8 +153,18 @@ fp8q_status fp8q_quant_act_g128(const void* x, int64_t m, int64_t k, int64_t ld_
     return fail(FP8Q_ERR_ALIGN, "x/q must be 16-byte aligned with ld_x %% 8 == 0 and ld_q %% 16 == 0");
   fp8q_status st = check_device();
   if (st != FP8Q_OK) return st;
-  return launched(fp8q::launch_quant_act(x, m, k, ld_x, q, ld_q, s, ld_s, reinterpret_cast<hipStream_t>(stream)),
+  return launched(fp8q::launch_quant_act(x, m, k, ld_x, q, ld_q, s, ld_s, pow2, reinterpret_cast<hipStream_t>(stream)),
                   "quant_act_g128");
+}
+
+fp8q_status fp8q_quant_act_g128(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q, int64_t ld_q,
+                                float* s, int64_t ld_s, void* stream) {
+  return quant_act(x, m, k, ld_x, q, ld_q, s, ld_s, stream, false);
+}
+
+fp8q_status fp8q_quant_act_g128_ue8m0(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q, int64_t ld_q,
+                                      float* s, int64_t ld_s, void* stream) {
+  return quant_act(x, m, k, ld_x, q, ld_q, s, ld_s, stream, true);
 }
 
 static fp8q_status check_gemm_common(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
@@ -165,9 +183,9 @@ static fp8q_status check_gemm_common(const void* a, int64_t ld_a, const float* a
   return FP8Q_OK;
 }
 
-fp8q_status fp8q_gemm_w8a8_blkscaled(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
-                                     const void* b, int64_t ld_b, const float* b_s, void* y, int64_t ld_y,
-                                     int64_t m, int64_t n, int64_t k, void* stream) {
+static fp8q_status gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b, int64_t ld_b,
+                        const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n, int64_t k, void* stream,
+                        bool pow2) {
   fp8q_status st = check_gemm_common(a, ld_a, a_s, ld_as, y, ld_y, m, n, k);
   if (st != FP8Q_OK) return st;
   if (m > 0) {
@@ -180,14 +198,26 @@ fp8q_status fp8q_gemm_w8a8_blkscaled(const void* a, int64_t ld_a, const float* a
   st = check_device();
   if (st != FP8Q_OK) return st;
   if (m == 0) return ok();
-  return launched(fp8q::launch_gemm(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k,
+  return launched(fp8q::launch_gemm(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, pow2,
                                     reinterpret_cast<hipStream_t>(stream)),
                   "gemm_w8a8_blkscaled");
 }
 
-fp8q_status fp8q_grouped_gemm_w8a8(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
-                                   const float* b_s, const int32_t* group_offsets, int32_t num_groups,
-                                   int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k, void* stream) {
+fp8q_status fp8q_gemm_w8a8_blkscaled(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
+                                     const void* b, int64_t ld_b, const float* b_s, void* y, int64_t ld_y,
+                                     int64_t m, int64_t n, int64_t k, void* stream) {
+  return gemm(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream, false);
+}
+
+fp8q_status fp8q_gemm_w8a8_ue8m0(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
+                                 int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
+                                 int64_t k, void* stream) {
+  return gemm(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream, true);
+}
+
+static fp8q_status grouped_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
+                                const float* b_s, const int32_t* group_offsets, int32_t num_groups, int64_t total_m,
+                                void* y, int64_t ld_y, int64_t n, int64_t k, void* stream, bool pow2) {
   if (num_groups < 1) return fail(FP8Q_ERR_SHAPE, "num_groups must be >= 1 (got %d)", num_groups);
   fp8q_status st = check_gemm_common(a, ld_a, a_s, ld_as, y, ld_y, total_m, n, k);
   if (st != FP8Q_OK) return st;
@@ -201,8 +231,21 @@ fp8q_status fp8q_grouped_gemm_w8a8(const void* a, int64_t ld_a, const float* a_s
   if (st != FP8Q_OK) return st;
   if (total_m == 0) return ok();
   return launched(fp8q::launch_grouped_gemm(a, ld_a, a_s, ld_as, b, b_s, group_offsets, num_groups, total_m, y,
-                                            ld_y, n, k, reinterpret_cast<hipStream_t>(stream)),
+                                            ld_y, n, k, pow2, reinterpret_cast<hipStream_t>(stream)),
                   "grouped_gemm_w8a8");
+}
+
+fp8q_status fp8q_grouped_gemm_w8a8(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
+                                   const float* b_s, const int32_t* group_offsets, int32_t num_groups,
+                                   int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k, void* stream) {
+  return grouped_gemm(a, ld_a, a_s, ld_as, b, b_s, group_offsets, num_groups, total_m, y, ld_y, n, k, stream, false);
+}
+
+fp8q_status fp8q_grouped_gemm_w8a8_ue8m0(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
+                                         const void* b, const float* b_s, const int32_t* group_offsets,
+                                         int32_t num_groups, int64_t total_m, void* y, int64_t ld_y, int64_t n,
+                                         int64_t k, void* stream) {
+  return grouped_gemm(a, ld_a, a_s, ld_as, b, b_s, group_offsets, num_groups, total_m, y, ld_y, n, k, stream, true);
 }
 
 fp8q_status fp8q_kv_quant(const void* k, int64_t ld_k, const void* v, int64_t ld_v, int64_t num_tokens,

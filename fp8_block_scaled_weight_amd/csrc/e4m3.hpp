@@ -50,6 +50,28 @@ __device__ __forceinline__ float scale_from_amax(float amax, float range) {
   return amax == 0.0f ? 1.0f : amax / range;
 }
 
+// Power-of-two (UE8M0) scale variant: the smallest 2^e with range * 2^e >= amax, e in
+// the E8M0 exponent range [-127, 127]; 1 for amax == 0.  range * 2^e is exact in binary32
+// for every e reached from a bf16 amax, so the comparisons decide exactly.
+__device__ __forceinline__ float scale_pow2_from_amax(float amax, float range) {
+  if (amax == 0.0f) return 1.0f;
+  const int biased = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+  int e = (biased ? biased - 127 : -127) - 8;  // within a few steps of the answer
+  while (range * __builtin_ldexpf(1.0f, e) < amax) ++e;
+  while (range * __builtin_ldexpf(1.0f, e - 1) >= amax) --e;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  return __builtin_ldexpf(1.0f, e);
+}
+
+template <bool POW2>
+__device__ __forceinline__ float block_scale(float amax, float range) {
+  if constexpr (POW2) {
+    return scale_pow2_from_amax(amax, range);
+  } else {
+    return scale_from_amax(amax, range);
+  }
+}
+
 struct Quantizer {
   float s;    // scale as used in the residual test (possibly x 2^64)
   float r;    // 1 / s

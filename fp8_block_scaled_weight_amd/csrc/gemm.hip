@@ -68,6 +68,15 @@ __device__ __forceinline__ v16f mfma32(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// The same with block scales applied by the matrix core: lane l passes the E8M0
+// exponent (bias 127) of row l%32 of the A operand and of column l%32 of the B operand
+// for the 32-wide K group the lane's data belong to.  A power-of-two binary32 scale
+// 2^e (e >= -127) has E8M0 code bits >> 23.
+__device__ __forceinline__ v16f mfma32_scaled(v8i a, v8i b, v16f c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+}
+__device__ __forceinline__ int e8m0_of(float pow2_scale) { return (int)(__float_as_uint(pow2_scale) >> 23); }
+
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
@@ -126,7 +135,7 @@ __device__ __forceinline__ T lds_ld(const uint8_t FP8Q_LDS* base, uint32_t off) 
   return *reinterpret_cast<const T FP8Q_LDS*>(base + off);
 }
 
-template <class C>
+template <class C, bool POW2>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t ld_a, int64_t a_rows,
                                           const float* __restrict__ as, int64_t ld_as,
                                           const uint8_t* __restrict__ b, int64_t ld_b,
@@ -201,6 +210,56 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  if constexpr (POW2) {
+    // Power-of-two scales: the matrix core applies them, so a K step is two chained
+    // scaled MFMAs per 32x32 sub-tile accumulating straight into the running sum, with
+    // no promotion.  Weight fragments are read at the step start, token fragments one
+    // sub-tile ahead.
+    constexpr int S = C::STAGES;
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p)
+      if (p < kblocks) issue(p, p);
+    int cur = 0;
+    for (int kb = 0; kb < kblocks; ++kb) {
+      if (kb + S - 2 < kblocks) {
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((S - 2) * C::VM_PER_STEP) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+      if (kb + S - 1 < kblocks) issue(kb + S - 1, cur == 0 ? S - 1 : cur - 1);
+      const uint8_t FP8Q_LDS* st = lds + cur * C::STAGE_BYTES;
+      const uint8_t FP8Q_LDS* stw = st + wn * 128;
+      const uint8_t FP8Q_LDS* stt = st + (C::BN + wm) * 128;
+      v8i fa[C::IN][2];
+#pragma unroll
+      for (int i = 0; i < C::IN; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          fa[i][h] = join(lds_ld<u32x4>(stw, fo[h][0] + i * 4096), lds_ld<u32x4>(stw, fo[h][1] + i * 4096));
+      int eb[C::JM];
+      if constexpr (C::JM == 4) {
+        const u32x4 t = lds_ld<u32x4>(st, so);
+        eb[0] = (int)(t.x >> 23); eb[1] = (int)(t.y >> 23); eb[2] = (int)(t.z >> 23); eb[3] = (int)(t.w >> 23);
+      } else {
+        const u32x2 t = lds_ld<u32x2>(st, so);
+        eb[0] = (int)(t.x >> 23); eb[1] = (int)(t.y >> 23);
+      }
+      const int ea = e8m0_of(lds_ld<float>(st, wso));
+#pragma unroll
+      for (int j = 0; j < C::JM; ++j) {
+        v8i fb[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          fb[h] = join(lds_ld<u32x4>(stt, fo[h][0] + j * 4096), lds_ld<u32x4>(stt, fo[h][1] + j * 4096));
+#pragma unroll
+        for (int i = 0; i < C::IN; ++i) {
+          acc[i][j] = mfma32_scaled(fa[i][0], fb[0], acc[i][j], ea, eb[j]);
+          acc[i][j] = mfma32_scaled(fa[i][1], fb[1], acc[i][j], ea, eb[j]);
+        }
+      }
+      cur = (cur + 1 == S) ? 0 : cur + 1;
+    }
+  } else {
   // Software pipeline.  The 32x32 sub-tiles of a step are taken as chains c = j*IN + i
   // (two MFMAs each: K halves 0 and 1).  Each chain's MFMAs are issued before the
   // previous chain's promotion FMAs.  The last chain of a step is issued after the next
@@ -301,6 +360,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
     promote(1, C::IN - 1, C::JM - 1, pc);
   }
 
+  }
   // ---- epilogue.  A lane holds y[m][n .. n+3] for m = wm + 32j + l%32 and
   // n = wn + 32i + 8q + 4(l/32): four outputs of one row per 8 bytes.  Each wave
   // rounds them to bf16 (once) into its own TM x TN row-major block of LDS, then reads
@@ -371,7 +431,7 @@ using CfgMid = GemmCfg<128, 128, 2, 4, 4>;     // 64 x 32 per wave, 132 KB LDS
 using CfgMid2 = GemmCfg<128, 128, 2, 4, 2>;    // two workgroups per CU when tiles are plenty
 using CfgSmall = GemmCfg<128, 64, 2, 2, 4>;    // 64 x 32 per wave, 100 KB LDS
 
-template <class C>
+template <class C, bool POW2>
 __global__ __launch_bounds__(C::THREADS) void gemm_w8a8_kernel(const uint8_t* __restrict__ a, int64_t ld_a,
                                                                 const float* __restrict__ as, int64_t ld_as,
                                                                 const uint8_t* __restrict__ b, int64_t ld_b,
@@ -386,11 +446,11 @@ __global__ __launch_bounds__(C::THREADS) void gemm_w8a8_kernel(const uint8_t* __
   tile_coords<4>(t, m_tiles, n_tiles, tm, tn);
   const int64_t m0 = tm * C::BM;
   const int64_t m_end = (m0 + C::BM) < m ? (m0 + C::BM) : m;
-  gemm_tile<C>(a, ld_a, m, as, ld_as, b, ld_b, bs, kblocks, y, ld_y, m0, m_end, tn * C::BN,
+  gemm_tile<C, POW2>(a, ld_a, m, as, ld_as, b, ld_b, bs, kblocks, y, ld_y, m0, m_end, tn * C::BN,
                (uint8_t FP8Q_LDS*)lds);
 }
 
-template <class C>
+template <class C, bool POW2 = false>
 static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                                int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                                int64_t k, hipStream_t stream) {
@@ -398,7 +458,7 @@ static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, in
   const int64_t m_tiles = (m + C::BM - 1) / C::BM;
   const int64_t tiles = m_tiles * n_tiles;
   const int64_t grid = ((tiles + kXcds - 1) / kXcds) * kXcds;
-  hipLaunchKernelGGL(gemm_w8a8_kernel<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
+  hipLaunchKernelGGL((gemm_w8a8_kernel<C, POW2>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream,
                      reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b),
                      ld_b, b_s, reinterpret_cast<uint16_t*>(y), ld_y, m, m_tiles, n_tiles, (int)(k / 128));
   return hipGetLastError();
@@ -506,9 +566,29 @@ static hipError_t launch_smallm(const void* a, int64_t ld_a, const float* a_s, i
   return hipGetLastError();
 }
 
+// Tile shape for M > 64 (POW2: the matrix core applies power-of-two block scales).
+template <bool POW2>
+static hipError_t launch_tiles(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
+                               int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
+                               int64_t k, hipStream_t stream) {
+  if (m < 1024) return launch_dense<CfgSmall, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  // large tiles when they cover n exactly and still give every CU a tile
+  const int64_t large_tiles = ((m + CfgLarge::BM - 1) / CfgLarge::BM) * (n / CfgLarge::BN);
+  if (n % CfgLarge::BN == 0 && large_tiles >= 256)
+    return launch_dense<CfgLarge, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  // with at least two tiles per CU, two co-resident workgroups hide each other's waits
+  // better than deeper copy rings
+  const int64_t mid_tiles = ((m + CfgMid::BM - 1) / CfgMid::BM) * (n / CfgMid::BN);
+  if (mid_tiles >= 512)
+    return launch_dense<CfgMid2, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  return launch_dense<CfgMid, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+}
+
 hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                        int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
-                       int64_t k, hipStream_t stream) {
+                       int64_t k, bool pow2, hipStream_t stream) {
+  if (pow2 && m > 64) return launch_tiles<true>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  // (up to 64 tokens, power-of-two scales take the promotion path below: same result)
   // few tokens: stream the weights over all CUs.  A workgroup takes 16*WM tokens; WM
   // shrinks (more workgroups, each re-reading its weight rows from L2) until the grid
   // covers every CU
@@ -519,17 +599,7 @@ hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld
       return launch_smallm<2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
     return launch_smallm<1>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   }
-  if (m < 1024) return launch_dense<CfgSmall>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-  // large tiles when they cover n exactly and still give every CU a tile
-  const int64_t large_tiles = ((m + CfgLarge::BM - 1) / CfgLarge::BM) * (n / CfgLarge::BN);
-  if (n % CfgLarge::BN == 0 && large_tiles >= 256)
-    return launch_dense<CfgLarge>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-  // with at least two tiles per CU, two co-resident workgroups hide each other's waits
-  // better than deeper copy rings
-  const int64_t mid_tiles = ((m + CfgMid::BM - 1) / CfgMid::BM) * (n / CfgMid::BN);
-  if (mid_tiles >= 512)
-    return launch_dense<CfgMid2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-  return launch_dense<CfgMid>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  return launch_tiles<false>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
 }
 
 // ----------------------------------------------------------------------------
@@ -543,7 +613,7 @@ hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld
 // workgroups per CU (measured faster than the four-stage ring here).
 using CfgGrouped = CfgMid2;
 
-template <class C>
+template <class C, bool POW2>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_w8a8_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
     const uint8_t* __restrict__ b, const float* __restrict__ bs, const int32_t* __restrict__ off,
@@ -592,18 +662,19 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_w8a8_kernel(
   const int64_t a_rows = off[groups];
   const uint8_t* bg = b + (int64_t)g * n * k;
   const float* bsg = bs + (int64_t)g * (n / 128) * kblocks;
-  gemm_tile<C>(a, ld_a, a_rows, as, ld_as, bg, k, bsg, kblocks, y, ld_y, row0, row_end, tile_n * C::BN,
+  gemm_tile<C, POW2>(a, ld_a, a_rows, as, ld_as, bg, k, bsg, kblocks, y, ld_y, row0, row_end, tile_n * C::BN,
                (uint8_t FP8Q_LDS*)lds);
 }
 
 hipError_t launch_grouped_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
                                const void* b, const float* b_s, const int32_t* offsets, int32_t groups,
-                               int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k,
+                               int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k, bool pow2,
                                hipStream_t stream) {
   using C = CfgGrouped;
   const int64_t n_tiles = n / C::BN;
   const int64_t m_tiles = (total_m + C::BM - 1) / C::BM + groups;
-  hipLaunchKernelGGL(grouped_gemm_w8a8_kernel<C>, dim3((unsigned)(n_tiles * m_tiles)), dim3(C::THREADS), 0, stream,
+  auto kernel = pow2 ? grouped_gemm_w8a8_kernel<C, true> : grouped_gemm_w8a8_kernel<C, false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)(n_tiles * m_tiles)), dim3(C::THREADS), 0, stream,
                      reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b), b_s,
                      offsets, groups, reinterpret_cast<uint16_t*>(y), ld_y, n, k, n_tiles);
   return hipGetLastError();

@@ -24,23 +24,24 @@ struct WeightChunk {
   WeightDescDev d[kWeightChunk];
 };
 
-hipError_t launch_quant_weight_chunk(const WeightChunk& chunk, int64_t blocks, hipStream_t stream);
+hipError_t launch_quant_weight_chunk(const WeightChunk& chunk, int64_t blocks, bool pow2, hipStream_t stream);
 
 hipError_t launch_quant_act(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q, int64_t ld_q,
-                            float* s, int64_t ld_s, hipStream_t stream);
+                            float* s, int64_t ld_s, bool pow2, hipStream_t stream);
 
 hipError_t launch_kv_quant(const void* k, int64_t ld_k, const void* v, int64_t ld_v, int64_t tokens,
                            int32_t heads, const int64_t* slots, void* k_cache, void* v_cache,
                            float* k_scale, float* v_scale, float range, bool recalibrate,
                            hipStream_t stream);
 
+// pow2: the scales are powers of two (UE8M0 variant) and are applied by the matrix core
 hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                        int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
-                       int64_t k, hipStream_t stream);
+                       int64_t k, bool pow2, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
                                const void* b, const float* b_s, const int32_t* offsets, int32_t groups,
-                               int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k,
+                               int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k, bool pow2,
                                hipStream_t stream);
 
 }  // namespace fp8q

@@ -16,12 +16,17 @@
 
 namespace fp8q {
 
+// POW2 selects the power-of-two (UE8M0) scale variant of the same quantizers (FP8-RL
+// summary page, "Experimental results": the scale-format ablation); the encoding is the
+// same, and with a power-of-two scale the quotient it rounds is exact.
+//
 // ----------------------------------------------------------------------------
 // Weights: one 256-thread workgroup per 128x128 block.  Thread t covers columns
 // 16*(t%8) .. +15 of rows t/8 + 32*i (i < 4): 8 x 16-byte loads, 4 x 16-byte stores.
 // A launch covers a chunk of descriptors; block ids are laid out descriptor after
 // descriptor, row-major over the block grid of each.
 // ----------------------------------------------------------------------------
+template <bool POW2>
 __global__ __launch_bounds__(256) void quant_weight_blk128_kernel(WeightChunk chunk) {
   __shared__ uint32_t wave_max[4];
   const int64_t blk = blockIdx.x;
@@ -56,7 +61,7 @@ __global__ __launch_bounds__(256) void quant_weight_blk128_kernel(WeightChunk ch
   if ((t & 63) == 0) wave_max[t >> 6] = m;
   __syncthreads();
   m = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
-  const float scale = scale_from_amax(bf16_bits_to_float(m), kE4M3Max);
+  const float scale = block_scale<POW2>(bf16_bits_to_float(m), kE4M3Max);
   if (t == 0) d.s[bi * d.kblocks + bj] = scale;
   const Quantizer qz = make_quantizer(scale);
 #pragma unroll
@@ -66,8 +71,11 @@ __global__ __launch_bounds__(256) void quant_weight_blk128_kernel(WeightChunk ch
   }
 }
 
-hipError_t launch_quant_weight_chunk(const WeightChunk& chunk, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL(quant_weight_blk128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, chunk);
+hipError_t launch_quant_weight_chunk(const WeightChunk& chunk, int64_t blocks, bool pow2, hipStream_t stream) {
+  if (pow2)
+    hipLaunchKernelGGL(quant_weight_blk128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, chunk);
+  else
+    hipLaunchKernelGGL(quant_weight_blk128_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, chunk);
   return hipGetLastError();
 }
 
@@ -76,6 +84,7 @@ hipError_t launch_quant_weight_chunk(const WeightChunk& chunk, int64_t blocks, h
 // same group g of 8 consecutive rows, so its 8 scales s[g*ld_s + r .. r+7] form one
 // contiguous 32-byte store; the 4 waves of a workgroup take 4 consecutive groups.
 // ----------------------------------------------------------------------------
+template <bool POW2>
 __global__ __launch_bounds__(256) void quant_act_g128_kernel(const uint16_t* __restrict__ x, int64_t m,
                                                              int64_t groups, int64_t ld_x,
                                                              uint8_t* __restrict__ q, int64_t ld_q,
@@ -97,7 +106,7 @@ __global__ __launch_bounds__(256) void quant_act_g128_kernel(const uint16_t* __r
   }
   uint32_t mx = max_over_8_lanes(absmax16(a, b));
   if (!live) return;
-  const float scale = scale_from_amax(bf16_bits_to_float(mx), kE4M3Max);
+  const float scale = block_scale<POW2>(bf16_bits_to_float(mx), kE4M3Max);
   if ((lane & 7) == 0) s[g * ld_s + row] = scale;
   const Quantizer qz = make_quantizer(scale);
   uint4 o = quant16<false>(a, b, qz);
@@ -105,14 +114,14 @@ __global__ __launch_bounds__(256) void quant_act_g128_kernel(const uint16_t* __r
 }
 
 hipError_t launch_quant_act(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q, int64_t ld_q,
-                            float* s, int64_t ld_s, hipStream_t stream) {
+                            float* s, int64_t ld_s, bool pow2, hipStream_t stream) {
   const int64_t groups = k / 128;
   const int64_t group_tiles = (groups + 3) / 4;
   const int64_t row_blocks = (m + 7) / 8;
   const int64_t wgs = row_blocks * group_tiles;
-  hipLaunchKernelGGL(quant_act_g128_kernel, dim3((unsigned)wgs), dim3(256), 0, stream,
-                     reinterpret_cast<const uint16_t*>(x), m, groups, ld_x,
-                     reinterpret_cast<uint8_t*>(q), ld_q, s, ld_s, group_tiles);
+  auto kernel = pow2 ? quant_act_g128_kernel<true> : quant_act_g128_kernel<false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(256), 0, stream, reinterpret_cast<const uint16_t*>(x), m,
+                     groups, ld_x, reinterpret_cast<uint8_t*>(q), ld_q, s, ld_s, group_tiles);
   return hipGetLastError();
 }
 

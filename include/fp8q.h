@@ -36,6 +36,13 @@
  *           the even code, saturating to +-448; the sign of -0 is kept (0x80).
  * The results are unique: codes and scales are bit-exact and deterministic.
  *
+ * Power-of-two (UE8M0) scale variant, the entry points named *_ue8m0 [FP8-RL,
+ * "Experimental results": the scale-format ablation compares FP32 scales with UE8M0
+ * (power-of-two) ones]: scale = the smallest power of two 2^e with 448 * 2^e >= amax,
+ * e limited to the E8M0 exponent range [-127, 127] (2^-127 is a binary32 subnormal);
+ * 1.0 if amax == 0.  Codes follow the same rule (the quotient x / 2^e is exact).  Scales
+ * are still stored as binary32 values, in the same layouts.
+ *
  * Conventions for every call.
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns every
  *     buffer.  The library allocates no memory and keeps no state besides the
@@ -111,6 +118,10 @@ typedef struct fp8q_weight_desc {
 fp8q_status fp8q_quant_weight_blk128(const fp8q_weight_desc* descs /* host */, int32_t count,
                                      void* stream);
 
+/* The same with power-of-two (UE8M0) scales; arguments, layouts and errors as above. */
+fp8q_status fp8q_quant_weight_blk128_ue8m0(const fp8q_weight_desc* descs /* host */,
+                                           int32_t count, void* stream);
+
 /* ------------------------------------------------------------------------------
  * Dynamic per-token-group activation quantization  [FP8-RL, "Method step details"
  * step 1: activations quantized dynamically on every forward]
@@ -124,6 +135,10 @@ fp8q_status fp8q_quant_weight_blk128(const fp8q_weight_desc* descs /* host */, i
  * ---------------------------------------------------------------------------- */
 fp8q_status fp8q_quant_act_g128(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q,
                                 int64_t ld_q, float* s, int64_t ld_s, void* stream);
+
+/* The same with power-of-two (UE8M0) scales; arguments, layouts and errors as above. */
+fp8q_status fp8q_quant_act_g128_ue8m0(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q,
+                                      int64_t ld_q, float* s, int64_t ld_s, void* stream);
 
 /* ------------------------------------------------------------------------------
  * Block-scaled W8A8 GEMM  [FP8-RL, "Method step details" step 1; Rounding]
@@ -148,6 +163,15 @@ fp8q_status fp8q_gemm_w8a8_blkscaled(const void* a, int64_t ld_a, const float* a
                                      const float* b_s, void* y, int64_t ld_y, int64_t m,
                                      int64_t n, int64_t k, void* stream);
 
+/* The block-scaled GEMM for power-of-two scales (as written by the *_ue8m0 quantizers):
+ * same arguments, layouts, errors and accuracy bound as fp8q_gemm_w8a8_blkscaled.  The
+ * matrix core applies the scales (E8M0 block-scaled MFMA) and accumulates across K
+ * blocks directly.  Precondition (not checked): every a_s and b_s value is 2^e with
+ * -127 <= e <= 127; other values are read as 2^(biased exponent field - 127). */
+fp8q_status fp8q_gemm_w8a8_ue8m0(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
+                                 const void* b, int64_t ld_b, const float* b_s, void* y,
+                                 int64_t ld_y, int64_t m, int64_t n, int64_t k, void* stream);
+
 /* ------------------------------------------------------------------------------
  * MoE grouped block-scaled W8A8 GEMM  [FP8-RL, "Method step details" step 1 (MoE
  * expert layers fc1, fc2); "Experimental results" (MoE gains)]
@@ -168,6 +192,14 @@ fp8q_status fp8q_grouped_gemm_w8a8(const void* a, int64_t ld_a, const float* a_s
                                    const int32_t* group_offsets, int32_t num_groups,
                                    int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k,
                                    void* stream);
+
+/* The grouped GEMM for power-of-two scales; arguments as fp8q_grouped_gemm_w8a8, scale
+ * precondition as fp8q_gemm_w8a8_ue8m0. */
+fp8q_status fp8q_grouped_gemm_w8a8_ue8m0(const void* a, int64_t ld_a, const float* a_s,
+                                         int64_t ld_as, const void* b, const float* b_s,
+                                         const int32_t* group_offsets, int32_t num_groups,
+                                         int64_t total_m, void* y, int64_t ld_y, int64_t n,
+                                         int64_t k, void* stream);
 
 /* ------------------------------------------------------------------------------
  * FP8 KV cache quantize-on-write with per-step scale recalibration  [FP8-RL, "Method

@@ -151,3 +151,19 @@ def test_python_binding_refuses_host_tensors():
     s = torch.zeros(1, 4, dtype=torch.float32)
     with pytest.raises(ValueError):
         fq.fp8q_quant_act_g128(x, q, s, stream=0)
+
+
+def test_ue8m0_entry_points_validate_like_the_fp32_ones():
+    L = fq.lib()
+    assert L.fp8q_quant_act_g128_ue8m0(A16, -1, 256, 256, A16, 256, A16, 4, None) == fq.FP8Q_ERR_SHAPE
+    assert L.fp8q_quant_act_g128_ue8m0(None, 4, 256, 256, A16, 256, A16, 4, None) == fq.FP8Q_ERR_NULL
+    assert L.fp8q_gemm_w8a8_ue8m0(A16, 256, A16, 64, A16, 256, A16, A16, 100, 64, 100, 256, None) == \
+        fq.FP8Q_ERR_SHAPE
+    assert L.fp8q_gemm_w8a8_ue8m0(A16, 256, A16, 7, A16, 256, A16, A16, 128, 64, 128, 256, None) == \
+        fq.FP8Q_ERR_STRIDE
+    assert L.fp8q_grouped_gemm_w8a8_ue8m0(A16, 256, A16, 64, A16, A16, A16, 0, 64, A16, 128, 128, 256, None) == \
+        fq.FP8Q_ERR_SHAPE
+    d = (fq.WeightDesc * 1)()
+    d[0] = fq.WeightDesc(A16, A16, A16, 100, 256, 256, 256)
+    assert L.fp8q_quant_weight_blk128_ue8m0(d, 1, None) == fq.FP8Q_ERR_SHAPE
+    assert L.fp8q_quant_weight_blk128_ue8m0(d, 0, None) == fq.FP8Q_ERR_SHAPE

@@ -1,0 +1,140 @@
+"""GPU parity of the power-of-two (UE8M0) scale variant against the oracle.
+
+FP8-RL summary page, "Experimental results" (scale-format ablation: FP32 versus UE8M0
+scales).  Quantizers: codes and scales bit-exact.  GEMMs (the matrix core applies the
+E8M0 block scales): every element within half a bf16 ulp of the exact value plus 2e-3
+of max|y|, as for the FP32-scale GEMM.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_block_scaled_weight_amd as fq
+from fp8_block_scaled_weight_amd import synth
+from tests._helpers import bf16_bits, f32, gemm_gate, to_dev_bf16, u8
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _gpu_weight(w_bits):
+    n, k = w_bits.shape
+    w = to_dev_bf16(w_bits)
+    q = torch.empty((n, k), dtype=torch.uint8, device=DEV)
+    s = torch.empty((n // 128, k // 128), dtype=torch.float32, device=DEV)
+    fq.fp8q_quant_weight_blk128_ue8m0([(w, q, s)])
+    torch.cuda.synchronize()
+    return u8(q), f32(s)
+
+
+def _gpu_act(x_bits, ld_s=None):
+    m, k = x_bits.shape
+    ld_s = m if ld_s is None else ld_s
+    q = torch.empty((m, k), dtype=torch.uint8, device=DEV)
+    s = torch.full((k // 128, ld_s), -7.0, dtype=torch.float32, device=DEV)
+    fq.fp8q_quant_act_g128_ue8m0(to_dev_bf16(x_bits), q, s)
+    torch.cuda.synchronize()
+    return u8(q), f32(s)
+
+
+def _same(got, ref):
+    (gq, gs), (rq, rs) = got, ref
+    assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32)), "scales differ"
+    assert np.array_equal(gq, rq), f"{int(np.sum(gq != rq))} codes differ"
+
+
+def test_weight_tiny_and_projection():
+    w, _ = synth.tiny()
+    _same(_gpu_weight(w), oracle.quant_weight_blk128(w, ue8m0=True))
+    w = synth.weight(2, 0, 0, 4096, 4096)
+    _same(_gpu_weight(w), oracle.quant_weight_blk128(w, ue8m0=True))
+
+
+def test_weight_scale_edges():
+    """All-zero block (scale 1), amax below the E8M0 range (clamped to 2^-127), the
+    largest bf16 (2^120), an exact 448 * 2^k maximum, and blocks of subnormal bf16."""
+    w = synth.weight(3, 0, 5, 256, 640)
+    w[:128, :128] = 0
+    w[:128, 128:256] = synth.to_bf16_bits(np.full((128, 128), 2.0 ** -133, np.float32))
+    w[128:, 128:256] = synth.to_bf16_bits(np.linspace(-3e38, 3e38, 128 * 128, dtype=np.float32).reshape(128, 128))
+    w[:128, 256:384] = synth.to_bf16_bits((np.arange(128 * 128, dtype=np.float32).reshape(128, 128) % 7) * 2.0 ** -130)
+    w[128:, 256] = synth.to_bf16_bits(np.full(128, 448.0 * 2.0 ** -5, np.float32))
+    ref = oracle.quant_weight_blk128(w, ue8m0=True)
+    assert ref[1][0, 0] == 1.0 and ref[1][0, 1] == np.float32(2.0 ** -127) and ref[1][1, 1] == np.float32(2.0 ** 120)
+    _same(_gpu_weight(w), ref)
+
+
+@pytest.mark.parametrize("m,k", [(16, 256), (1, 4096), (77, 1024), (4096, 4096)])
+def test_activation(m, k):
+    x = synth.activation(2, 0, 60 + m, m, k)
+    got = _gpu_act(x, ld_s=m + 3)
+    ref = oracle.quant_act_g128(x, ld_s=m + 3, ue8m0=True)
+    assert np.all(got[1][:, m:] == -7.0)  # padding of the scale rows untouched
+    _same((got[0], got[1][:, :m]), (ref[0], ref[1][:, :m]))
+
+
+def _operands(m, n, k, tensor):
+    w = synth.weight(2, 0, tensor, n, k)
+    x = synth.activation(2, 0, tensor + 50, m, k)
+    wq, ws = oracle.quant_weight_blk128(w, ue8m0=True)
+    xq, xs = oracle.quant_act_g128(x, ue8m0=True)
+    return xq, xs, wq, ws
+
+
+def _gpu_gemm(fn, xq, xs, wq, ws):
+    m, k = xq.shape
+    n = wq.shape[0]
+    y = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    fn(torch.from_numpy(xq).to(DEV), torch.from_numpy(xs).to(DEV), torch.from_numpy(wq).to(DEV),
+       torch.from_numpy(ws).to(DEV), y)
+    torch.cuda.synchronize()
+    return bf16_bits(y)
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (16, 256, 256),      # few tokens: promotion path
+    (130, 1024, 512),    # 128x64 tiles, ragged
+    (1000, 1024, 1024),  # 128x128 tiles, four-stage ring, ragged
+    (2000, 4096, 512),   # 128x128 tiles, two workgroups per CU, ragged
+    (4000, 4096, 1024),  # 256x256 tiles, ragged
+])
+def test_gemm_matches_oracle(m, n, k):
+    xq, xs, wq, ws = _operands(m, n, k, tensor=n // 128 + m % 7)
+    y = _gpu_gemm(fq.fp8q_gemm_w8a8_ue8m0, xq, xs, wq, ws)
+    g = np.random.Generator(np.random.PCG64(m))
+    rows = np.unique(np.concatenate([[0, m - 1], g.choice(m, min(m, 48), replace=False)]))
+    ref = oracle.gemm_w8a8(xq[rows], xs[:, rows], wq, ws)
+    ok, ratio, nrm = gemm_gate(y[rows], ref)
+    assert ok, f"worst err/bound {ratio:.3f}"
+    assert nrm < 4e-3
+
+
+def test_gemm_agrees_with_fp32_scale_path():
+    """Power-of-two scales are valid FP32 scales: both GEMMs pass the same gate."""
+    xq, xs, wq, ws = _operands(512, 1024, 2048, tensor=3)
+    ref = oracle.gemm_w8a8(xq, xs, wq, ws)
+    for fn in (fq.fp8q_gemm_w8a8_ue8m0, fq.fp8q_gemm_w8a8_blkscaled):
+        ok, ratio, _ = gemm_gate(_gpu_gemm(fn, xq, xs, wq, ws), ref)
+        assert ok, f"{fn.__name__}: worst err/bound {ratio:.3f}"
+
+
+def test_grouped_with_empty_groups():
+    sizes = [3, 0, 130, 1, 0, 257, 64]
+    n, k = 256, 384
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    m = int(off[-1])
+    G = len(sizes)
+    bq = np.empty((G, n, k), np.uint8)
+    bs = np.empty((G, n // 128, k // 128), np.float32)
+    for e in range(G):
+        bq[e], bs[e] = oracle.quant_weight_blk128(synth.weight(4, 0, e, n, k, outlier_frac=0.0), ue8m0=True)
+    aq, as_ = oracle.quant_act_g128(synth.activation(4, 0, 99, m, k), ue8m0=True)
+    y = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    fq.fp8q_grouped_gemm_w8a8_ue8m0(torch.from_numpy(aq).to(DEV), torch.from_numpy(as_).to(DEV),
+                                    torch.from_numpy(bq).to(DEV), torch.from_numpy(bs).to(DEV),
+                                    torch.from_numpy(off).to(DEV), y)
+    torch.cuda.synchronize()
+    ref = oracle.grouped_gemm_w8a8(aq, as_, bq, bs, off)
+    ok, ratio, _ = gemm_gate(bf16_bits(y), ref)
+    assert ok, f"worst err/bound {ratio:.3f}"
