@@ -55,8 +55,9 @@ def parse():
                    help="no GPU: matrix-core utilisation of the GEMM kernels from a rocprofv3 --pmc run of "
                         "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY SQ_INSTS_MFMA "
                         "SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS GRBM_GUI_ACTIVE")
-    p.add_argument("--summarize-trace", metavar="TRACE_DIR",
-                   help="no GPU: per-kernel table from a rocprofv3 --kernel-trace --stats output directory")
+    p.add_argument("--summarize-trace", nargs="+", metavar="TRACE_DIR [BENCH_JSON]",
+                   help="no GPU: per-kernel table from a rocprofv3 --kernel-trace --stats output directory "
+                        "(optionally with the JSON line of a bench.py run of the same source)")
     return p.parse_args()
 
 
@@ -180,7 +181,8 @@ def summarize_mfma(d):
     """Per GEMM instantiation: dispatches, average duration, matrix-core busy fraction
     (SQ_VALU_MFMA_BUSY_CYCLES summed over the 1024 SIMDs, against the kernel duration at
     the nominal 2.4 GHz and against GRBM_GUI_ACTIVE / 8 cycles per XCD) and the fraction
-    of wave time spent waiting on counters (s_waitcnt)."""
+    of wave time spent waiting on counters (s_waitcnt).  Writes
+    profiles/gemm_mfma_utilisation.txt."""
     import csv
     import glob
     per = {}
@@ -193,6 +195,23 @@ def summarize_mfma(d):
             e = per.setdefault(key, {})
             disp = e.setdefault(r["Dispatch_Id"], {"ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
             disp[r["Counter_Name"]] = disp.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = [
+        "# Matrix-core utilisation of the block-scaled GEMMs in the benchmark step",
+        "#",
+        "# One counter pass on one MI355X from the repository root (TMPDIR=/tmp):",
+        "#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY SQ_INSTS_MFMA "
+        "SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS GRBM_GUI_ACTIVE --output-format csv -d <out>/pmc_mfma -o bench -- "
+        "python3 bench.py --steps 5 --warmup 2 --no-legs --no-cpu",
+        "# Summary written by:",
+        "#   python3 bench.py --summarize-mfma <out>/pmc_mfma",
+        "# Averages per dispatch (the first two dispatches of each kernel skipped).  Each",
+        "# v_mfma_f32_32x32x64_f8f6f4 counts 64 busy cycles: 131072 FLOP per 64 cycles per SIMD is the FP8",
+        "# dense peak rate.  SQ_WAVE_CYCLES and SQ_WAIT_INST_ANY count in the same unit, so their ratio is",
+        "# the share of wave time spent in s_waitcnt (mostly the wait for a step's global-to-LDS copies).",
+        "# GRBM_GUI_ACTIVE / 8 over the duration gives the mean shader clock of the run.",
+        f"# gemm.hip source_digest: {source_digest('gemm.hip')}",
+        "",
+    ]
     for key, disps in per.items():
         ds = list(disps.values())[2:] or list(disps.values())
         avg = lambda c: sum(x.get(c, 0.0) for x in ds) / len(ds)
@@ -200,23 +219,31 @@ def summarize_mfma(d):
         gpu_cycles = avg("GRBM_GUI_ACTIVE") / 8
         util = avg("SQ_VALU_MFMA_BUSY_CYCLES") / (gpu_cycles * 1024) if gpu_cycles else float("nan")
         wait = avg("SQ_WAIT_INST_ANY") / avg("SQ_WAVE_CYCLES") if avg("SQ_WAVE_CYCLES") else float("nan")
-        print(f"[{key}]")
-        print(f"dispatches: {len(ds)}")
-        print(f"duration_us: {ns / 1e3:.2f}")
         nominal = avg("SQ_VALU_MFMA_BUSY_CYCLES") / (1024 * ns * 2.4)
-        print(f"grbm_gui_active_per_xcd: {gpu_cycles:.0f}")
-        print(f"mfma_instructions: {avg('SQ_INSTS_MFMA'):.0f}")
-        print(f"mfma_busy_cycles_total: {avg('SQ_VALU_MFMA_BUSY_CYCLES'):.0f}")
-        print(f"mfma_utilisation_at_2.4GHz: {nominal:.3f}   (busy cycles / (1024 SIMDs x duration x 2.4 GHz))")
-        print(f"mfma_utilisation_vs_grbm_cycles: {util:.3f}")
-        print(f"wave_time_waiting_on_counters: {wait:.3f}")
-        print(f"lds_instructions: {avg('SQ_INSTS_LDS'):.0f}")
-        print(f"lds_bank_conflict_cycles: {avg('SQ_LDS_BANK_CONFLICT'):.0f}")
-        print()
+        out += [
+            f"[{key}]",
+            f"dispatches: {len(ds)}",
+            f"duration_us: {ns / 1e3:.2f}",
+            f"grbm_gui_active_per_xcd: {gpu_cycles:.0f}",
+            f"mean_clock_GHz: {gpu_cycles / ns:.2f}",
+            f"mfma_instructions: {avg('SQ_INSTS_MFMA'):.0f}",
+            f"mfma_busy_cycles_total: {avg('SQ_VALU_MFMA_BUSY_CYCLES'):.0f}",
+            f"mfma_utilisation_at_2.4GHz: {nominal:.3f}   (busy cycles / (1024 SIMDs x duration x 2.4 GHz))",
+            f"mfma_utilisation_vs_grbm_cycles: {util:.3f}",
+            f"wave_time_waiting_on_counters: {wait:.3f}",
+            f"lds_instructions: {avg('SQ_INSTS_LDS'):.0f}",
+            f"lds_bank_conflict_cycles: {avg('SQ_LDS_BANK_CONFLICT'):.0f}",
+            "",
+        ]
+    with open(os.path.join(ROOT, "profiles", "gemm_mfma_utilisation.txt"), "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
 
 
-def summarize_trace(d):
-    """Markdown table of per-kernel statistics from a rocprofv3 --stats output directory."""
+def summarize_trace(d, bench_json=None):
+    """Markdown table of per-kernel statistics from a rocprofv3 --stats output directory,
+    written to profiles/bench_step_kernel_trace.md (with the live HIP-event duration of
+    the dominant GEMM from a bench.py JSON line of the same source, when given)."""
     import csv
     import glob
     files = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
@@ -224,13 +251,42 @@ def summarize_trace(d):
         raise SystemExit(f"no kernel_stats.csv under {d}")
     rows = list(csv.DictReader(open(files[0])))
     total = sum(float(r["TotalDurationNs"]) for r in rows)
-    print("| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |")
-    print("|---|---|---|---|---|---|")
+    md = [
+        "# Kernel trace of the benchmark step (Qwen3-8B-like attention block, 4096 tokens)",
+        "",
+        "Command (on one MI355X, from the repository root, TMPDIR=/tmp):",
+        "",
+        "    rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace -o bench -- "
+        "python3 bench.py --steps 30 --no-legs --no-cpu",
+        "",
+        "Table written by `python3 bench.py --summarize-trace <out>/trace [<bench json line>]` from "
+        "`bench_kernel_stats.csv` (all",
+        "launches in the run: warm-up, graph replays, per-call timing graphs and the direct launches that time",
+        "the dominant GEMM).",
+        "",
+        "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+        "|---|---|---|---|---|---|",
+    ]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         if "fp8q" not in r["Name"]:
             continue
-        print(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
-              f"{float(r['MaxNs']) / 1e3:.2f} | {100 * float(r['TotalDurationNs']) / total:.1f} % |")
+        md.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                  f"{100 * float(r['TotalDurationNs']) / total:.1f} % |")
+    live = ""
+    if bench_json:
+        line = [l for l in open(bench_json) if l.startswith("{")][-1]
+        live = f" ({json.loads(line)['roofline']['avg_us']} us in the run of the same source)"
+    md += [
+        "",
+        "The 256x256-tile GEMM instantiation runs only the two M=N=K=4096 projections (q, o) in this command,",
+        "so its average is the dominant kernel's duration under the tracer; bench.py measures the same kernel",
+        f"live with HIP events on its launch stream (`roofline.avg_us`{live}).",
+        f"gemm.hip source_digest: {source_digest('gemm.hip')}",
+    ]
+    with open(os.path.join(ROOT, "profiles", "bench_step_kernel_trace.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
 
 
 def main():
@@ -239,7 +295,7 @@ def main():
         summarize_counters(*args.summarize_counters)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(*args.summarize_trace)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)
@@ -564,6 +620,37 @@ def legs(torch, fq, synth, dev):
     ms = _time(torch, lambda: fq.fp8q_kv_quant(kd, vd, sd, kc, vc, ks, vs, 448.0, recalibrate=False), 20)
     res["a6_kv_decode_write_64_tokens"] = {"us": round(ms * 1e3, 2)}
     del k, v, kc, vc
+    torch.cuda.empty_cache()
+
+    # power-of-two (UE8M0) scale variant of the attention block's calls: quantizers and
+    # the GEMMs whose block scales the matrix core applies
+    log("leg: UE8M0 variant")
+    X = synth.device_activation(TOKENS, HIDDEN, dev, 2, 0, 10)
+    Wq = synth.device_normal_bf16((HIDDEN, HIDDEN), 0.02, dev, 2, 0, 0, outlier_p=1e-3, outlier_mult=20.0)
+    Wk = synth.device_normal_bf16((KV_DIM, HIDDEN), 0.02, dev, 2, 0, 1, outlier_p=1e-3, outlier_mult=20.0)
+    xq = torch.empty((TOKENS, HIDDEN), dtype=torch.uint8, device=dev)
+    xs = torch.empty((HIDDEN // 128, TOKENS), dtype=torch.float32, device=dev)
+    wq = {n: torch.empty(w.shape, dtype=torch.uint8, device=dev) for n, w in (("q", Wq), ("k", Wk))}
+    wsc = {n: torch.empty((w.shape[0] // 128, HIDDEN // 128), dtype=torch.float32, device=dev)
+           for n, w in (("q", Wq), ("k", Wk))}
+    wd = [(Wq, wq["q"], wsc["q"]), (Wk, wq["k"], wsc["k"])]
+    ms_w = _time(torch, lambda: fq.fp8q_quant_weight_blk128_ue8m0(wd), 10)
+    ms_a = _time(torch, lambda: fq.fp8q_quant_act_g128_ue8m0(X, xq, xs), 10)
+    yq = torch.empty((TOKENS, HIDDEN), dtype=torch.bfloat16, device=dev)
+    yk = torch.empty((TOKENS, KV_DIM), dtype=torch.bfloat16, device=dev)
+    ms_q = _time(torch, lambda: fq.fp8q_gemm_w8a8_ue8m0(xq, xs, wq["q"], wsc["q"], yq), 10)
+    ms_k = _time(torch, lambda: fq.fp8q_gemm_w8a8_ue8m0(xq, xs, wq["k"], wsc["k"], yk), 10)
+    fq_, fk_ = 2 * TOKENS * HIDDEN * HIDDEN, 2 * TOKENS * KV_DIM * HIDDEN
+    el = Wq.numel() + Wk.numel()
+    res["f2_ue8m0"] = {
+        "weight_quant_qk_us": round(ms_w * 1e3, 2),
+        "weight_quant_GBps": round((3 * el + 4 * el / 16384) / (ms_w * 1e-3) / 1e9, 1),
+        "act_quant_x_us": round(ms_a * 1e3, 2),
+        "gemm_q_us": round(ms_q * 1e3, 2), "gemm_q_TFLOPs": round(fq_ / (ms_q * 1e-3) / 1e12, 1),
+        "gemm_q_frac_fp8_peak": round(fq_ / (ms_q * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "gemm_k_us": round(ms_k * 1e3, 2), "gemm_k_TFLOPs": round(fk_ / (ms_k * 1e-3) / 1e12, 1),
+    }
+    del X, Wq, Wk, xq, wq, yq, yk
     torch.cuda.empty_cache()
 
     # small-M GEMMs (decode / short prefill shapes)
