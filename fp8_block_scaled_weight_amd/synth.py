@@ -93,23 +93,36 @@ def tiny():
 
 
 # ---------------------------------------------------------------- MoE routing
-def moe_routing(layer: int, tokens: int = 4096, experts: int = MOE_EXPERTS, topk: int = MOE_TOPK,
-                zipf_s: float = 1.1):
-    """Skewed top-k routing: expert e gets popularity rank r_e (a seeded permutation
-    of 1..E); logits[t, e] = -s ln(r_e) + Gumbel(0, 1); each token takes its top-k
-    logits (ties to the lower expert id).  This samples k experts without
-    replacement with probability proportional to r_e^-s.
+def moe_topk(layer: int, tokens: int = 4096, experts: int = MOE_EXPERTS, topk: int = MOE_TOPK,
+             zipf_s: float = 1.1):
+    """Skewed top-k routing as a router would record it: expert e gets popularity rank
+    r_e (a seeded permutation of 1..E); logits[t, e] = -s ln(r_e) + Gumbel(0, 1); each
+    token takes its top-k logits (ties to the lower expert id), which samples k experts
+    without replacement with probability proportional to r_e^-s.  The routing weights
+    are the softmax of the k chosen logits.
 
-    Returns (row_token [tokens*topk] int64: token feeding each expert-sorted row,
-    offsets [experts+1] int32, expert_of_row [tokens*topk] int32)."""
+    Returns (topk_ids int16 [tokens, topk], topk_weights fp32 [tokens, topk])."""
     g = rng(4, layer, 1000)
     rank = g.permutation(experts) + 1
     logits = -zipf_s * np.log(rank.astype(np.float64))[None, :] + g.gumbel(size=(tokens, experts))
     # top-k with ties to the lower id: stable sort on -logit keeps id order for equal keys
     order = np.argsort(-logits, axis=1, kind="stable")[:, :topk]
+    chosen = np.take_along_axis(logits, order, axis=1)
+    w = np.exp(chosen - chosen.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    return order.astype(np.int16), w.astype(np.float32)
+
+
+def moe_routing(layer: int, tokens: int = 4096, experts: int = MOE_EXPERTS, topk: int = MOE_TOPK,
+                zipf_s: float = 1.1):
+    """The routing of moe_topk laid out for a grouped GEMM that takes pre-sorted rows
+    (rows sorted by expert, stable by token id).
+
+    Returns (row_token [tokens*topk] int64: token feeding each expert-sorted row,
+    offsets [experts+1] int32, expert_of_row [tokens*topk] int32)."""
+    ids, _ = moe_topk(layer, tokens, experts, topk, zipf_s)
     tok = np.repeat(np.arange(tokens, dtype=np.int64), topk)
-    exp = order.reshape(-1).astype(np.int32)
-    # rows sorted by expert, stable by token id
+    exp = ids.reshape(-1).astype(np.int32)
     perm = np.lexsort((tok, exp))
     row_token = tok[perm]
     expert_of_row = exp[perm]

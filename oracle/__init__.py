@@ -73,7 +73,11 @@ def lib():
                                       ctypes.c_int32, _i64p, _u8p, _u8p, ctypes.c_int32, _i64,
                                       _f32p, _f32p, ctypes.c_float, ctypes.c_int]
         L.oracle_kv_scales.argtypes = [_u16p, _i64, _u16p, _i64, _i64, _i64, _i64p, ctypes.c_float, _f32p, _f32p]
+        L.oracle_swiglu_quant_g128.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p, _i64, _f64p]
+        L.oracle_silu_times_up.argtypes = [ctypes.c_double, ctypes.c_double]
+        L.oracle_silu_times_up.restype = ctypes.c_double
         for f in ("oracle_kv_scales", "oracle_quant_weight_blk128", "oracle_quant_act_g128", "oracle_gemm_w8a8",
+                  "oracle_swiglu_quant_g128",
                   "oracle_quant_weight_blk128_ue8m0", "oracle_quant_act_g128_ue8m0",
                   "oracle_grouped_gemm_w8a8", "oracle_kv_quant", "oracle_num_threads"):
             getattr(L, f).restype = ctypes.c_int
@@ -210,3 +214,70 @@ def kv_quant(k_bits, v_bits, slot_mapping, k_cache, v_cache, page_size: int,
                                  heads, hd, slots, kc, vc, page_size, num_pages, ks, vs,
                                  float(rng), 1 if recalibrate else 0), "kv_quant")
     return kc, vc, ks[0], vs[0]
+
+
+# ---------------------------------------------------------------- MoE layer around the grouped GEMM
+# MoE routing-replay page, "Rollout Routing Replay" (section 4) and its cost analysis
+# (section 5): the rollout keeps each token's top-k expert indices (int16) and tokens are
+# dispatched to exactly those experts; [FP8-RL] step 1 quantizes fc1/fc2's inputs.
+
+def moe_dispatch(xq: np.ndarray, xs: np.ndarray, topk_ids: np.ndarray, num_experts: int):
+    """Dispatch quantized tokens to their recorded experts.
+
+    xq: FP8 codes [T, K]; xs: fp32 scales [K/128, ld_s >= T]; topk_ids: int16 [T, topk].
+    Entry f = t*topk + j (token t's j-th expert) is valid when 0 <= id < num_experts;
+    invalid entries are dropped.  Valid entries are ordered by expert, and within an
+    expert by f (a stable sort).  Returns (aq [R, K], as [K/128, R], offsets int32
+    [E+1], row_of int32 [T, topk] = the sorted row of entry (t, j), -1 if dropped),
+    R = number of valid entries."""
+    ids = np.asarray(topk_ids).astype(np.int64)
+    t, topk = ids.shape
+    flat = ids.reshape(-1)
+    valid = np.nonzero((flat >= 0) & (flat < num_experts))[0]
+    order = valid[np.argsort(flat[valid], kind="stable")]
+    counts = np.bincount(flat[valid], minlength=num_experts)
+    offsets = np.zeros(num_experts + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    row_of = np.full(t * topk, -1, dtype=np.int32)
+    row_of[order] = np.arange(order.size, dtype=np.int32)
+    tok = order // topk
+    aq = np.ascontiguousarray(np.asarray(xq)[tok])
+    as_ = np.ascontiguousarray(np.asarray(xs)[:, tok])
+    return aq, as_, offsets, row_of.reshape(t, topk)
+
+
+def swiglu_quant_g128(h_bits: np.ndarray, ld_s: int | None = None, with_amax: bool = False):
+    """silu(gate) * up of a bf16 fc1 output [m, 2n] (gate = first n columns), quantized
+    in 1x128 groups -> (codes [m, n], scales [n/128, ld_s]) and, with_amax, the fp64
+    group maxima [n/128, m]."""
+    h = _u16(h_bits)
+    m, n2 = h.shape
+    n = n2 // 2
+    ld_s = m if ld_s is None else ld_s
+    q = np.empty((m, n), dtype=np.uint8)
+    s = np.zeros((n // 128, ld_s), dtype=np.float32)
+    amax = np.zeros((n // 128, m), dtype=np.float64)
+    _check(lib().oracle_swiglu_quant_g128(h, m, n, n2, q, n, s, ld_s, amax), "swiglu_quant_g128")
+    return (q, s, amax) if with_amax else (q, s)
+
+
+def silu_times_up(g: float, u: float) -> float:
+    """The fp64 value silu(g) * u that swiglu_quant_g128 quantizes."""
+    return float(lib().oracle_silu_times_up(float(g), float(u)))
+
+
+def moe_combine(y_bits: np.ndarray, row_of: np.ndarray, weights: np.ndarray) -> np.ndarray:
+    """out[t] = sum_j weights[t, j] * y[row_of[t, j]] in fp64, skipping row_of = -1.
+    y: bf16 [R, H] (fc2 output rows in dispatch order); weights: fp32 [T, topk]."""
+    y = np.asarray(y_bits)
+    if y.dtype != np.uint16:
+        raise TypeError("bf16 inputs are passed as uint16 bit patterns")
+    yf = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    rows = np.asarray(row_of).astype(np.int64)
+    w = np.asarray(weights, dtype=np.float32).astype(np.float64)
+    t, topk = rows.shape
+    out = np.zeros((t, yf.shape[1]), dtype=np.float64)
+    for j in range(topk):
+        live = rows[:, j] >= 0
+        out[live] += w[live, j][:, None] * yf[rows[live, j]]
+    return out

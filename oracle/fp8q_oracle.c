@@ -23,6 +23,9 @@
  *       bits; keep fused math in FP32 and round once at the output.
  *   [1T-RL] "1T-parameter RL on 100 GPUs", section 3.4: paged KV cache in
  *       fixed-size blocks, K and V each quantized to FP8 separately.
+ *   [R3] MoE routing-replay page ("Rollout Routing Replay", section 4, and the
+ *       cost analysis, section 5): each token's top-8 expert indices are kept
+ *       as int16 and tokens are dispatched to those recorded experts.
  *
  * Readings where the pages are silent (each listed in the design notes):
  *   - E4M3 is OCP E4M3FN: bias 7, max 448 (0x7E), subnormals m*2^-9, NaN 0x7F.
@@ -40,6 +43,11 @@
  *     of two 2^e with 448 * 2^e >= amax (the block maximum still fits the E4M3
  *     range), e limited to the E8M0 exponent range [-127, 127]; 1 for amax 0.
  *     The quotient x / 2^e is then exact and only the E4M3 rounding remains.
+ *   - SwiGLU before MoE fc2 ([Rounding], SwiGLU fusion region): silu(gate)*up in
+ *     fp64, quantized once per 1x128 group with the rule above (scale
+ *     fl32(fl64(amax / 448))).
+ *   - MoE dispatch and combine ([R3]) are integer gathers and an fp64 sum;
+ *     they are written in numpy in __init__.py.
  *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC.
  * Every entry point returns 0 on success, -1 on non-finite input, -2 on a bad
@@ -226,6 +234,49 @@ int oracle_quant_act_g128_ue8m0(const uint16_t* x, int64_t m, int64_t k, int64_t
                                 uint8_t* q, int64_t ld_q, float* s, int64_t ld_s) {
   return quant_act_rule(x, m, k, ld_x, q, ld_q, s, ld_s, oracle_scale_ue8m0);
 }
+
+/* ---- SwiGLU fused with the 1x128 quantization between MoE fc1 and fc2 ----
+ * [Rounding], the SwiGLU fusion region: the fused form keeps SiLU's result
+ * unrounded and multiplies it by the up projection before the one rounding;
+ * [FP8-RL] step 1: fc2's input is quantized dynamically in 1x128 groups.
+ * h is the bf16 fc1 output [m, 2*n]: gate = columns [0, n), up = [n, 2n).
+ * Reading: a = g / (1 + exp(-g)) * u evaluated in fp64 (finer than fp32, so the
+ * E4M3 encoding is the only rounding that matters); per row and 128-column
+ * group, amax = max |a| (exact), s = fl32(fl64(amax / 448)), 1 for amax 0;
+ * code = E4M3 nearest of the fp64 quotient a / s.  Precondition: amax / 448
+ * fits binary32.  amax_out (may be NULL) receives the fp64 amax of group g of
+ * row r at amax_out[g*m + r], so that a caller can see how close a scale was
+ * to an fp32 rounding boundary. */
+static double silu_times_up(double g, double u) { return g / (1.0 + exp(-g)) * u; }
+
+int oracle_swiglu_quant_g128(const uint16_t* h, int64_t m, int64_t n, int64_t ld_h, uint8_t* q,
+                             int64_t ld_q, float* s, int64_t ld_s, double* amax_out) {
+  if (m < 0 || n < 0 || n % 128 || ld_h < 2 * n || ld_q < n || ld_s < m) return -2;
+  int64_t groups = n / 128;
+  int bad = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(| : bad)
+  for (int64_t row = 0; row < m; ++row) {
+    for (int64_t g = 0; g < groups; ++g) {
+      double a[128];
+      double amax = 0.0;
+      for (int64_t c = 0; c < 128; ++c) {
+        float gv = bf16_to_float(h[row * ld_h + g * 128 + c]);
+        float uv = bf16_to_float(h[row * ld_h + n + g * 128 + c]);
+        if (!isfinite(gv) || !isfinite(uv)) bad = 1;
+        a[c] = silu_times_up((double)gv, (double)uv);
+        if (fabs(a[c]) > amax) amax = fabs(a[c]);
+      }
+      float sc = (amax == 0.0) ? 1.0f : (float)(amax / E4M3_MAX);
+      s[g * ld_s + row] = sc;
+      if (amax_out) amax_out[g * m + row] = amax;
+      for (int64_t c = 0; c < 128; ++c) q[row * ld_q + g * 128 + c] = oracle_e4m3_encode(a[c] / (double)sc);
+    }
+  }
+  return bad ? -1 : 0;
+}
+
+/* SiLU(g) * u of one element, as above (exposed for the tests' pins). */
+double oracle_silu_times_up(double g, double u) { return silu_times_up(g, u); }
 
 /* ---- a3: block-scaled W8A8 GEMM [FP8-RL, step 1; Rounding] ----
  * y[i][j] = sum_kb (sa[kb][i] * sb[j/128][kb]) * sum_{t in kb} dec(a[i][t]) dec(b[j][t])
