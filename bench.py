@@ -596,6 +596,49 @@ def legs(torch, fq, synth, dev):
                      "roofline_TFLOPs": round(ceil, 1)}
     res["a2_moe_fc2_act_quant"] = {"us": round(ms_aq * 1e3, 1),
                                    "GBps": round((3 * a2.numel() + 4 * a2.numel() / 128) / (ms_aq * 1e-3) / 1e9, 1)}
+
+    # the layer's data movement around the grouped GEMMs: dispatch of the quantized tokens
+    # by their recorded top-8 expert ids, SwiGLU + 1x128 quantization of fc1's output,
+    # weighted combine of fc2's output; then the whole layer as one sequence
+    log("leg: MoE dispatch / SwiGLU-quant / combine")
+    ids_np, rw_np = synth.moe_topk(0)
+    T, topk = ids_np.shape
+    n = T * topk
+    ids = torch.from_numpy(ids_np).to(dev)
+    rw = torch.from_numpy(rw_np).to(dev)
+    xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    xsc = torch.empty((H // 128, T), dtype=torch.float32, device=dev)
+    fq.fp8q_quant_act_g128(x, xq, xsc)
+    dq = torch.empty((n, H), dtype=torch.uint8, device=dev)
+    dsc = torch.empty((H // 128, n), dtype=torch.float32, device=dev)
+    doff = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_of = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    q2 = torch.empty((n, I), dtype=torch.uint8, device=dev)
+    s2 = torch.empty((I // 128, n), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ms_d = _time(torch, lambda: fq.fp8q_moe_dispatch(xq, xsc, ids, E, dq, dsc, doff, row_of), 10)
+    ms_sw = _time(torch, lambda: fq.fp8q_swiglu_quant_g128(y1, q2, s2), 10)
+    ms_c = _time(torch, lambda: fq.fp8q_moe_combine(y2, row_of, rw, out), 10)
+
+    def layer():
+        fq.fp8q_moe_dispatch(xq, xsc, ids, E, dq, dsc, doff, row_of)
+        fq.fp8q_grouped_gemm_w8a8(dq, dsc, b1, b1s, doff, y1)
+        fq.fp8q_swiglu_quant_g128(y1, q2, s2)
+        fq.fp8q_grouped_gemm_w8a8(q2, s2, b2, b2s, doff, y2)
+        fq.fp8q_moe_combine(y2, row_of, rw, out)
+
+    ms_l = _time(torch, layer, 5, reps=2)
+    by_d = T * H + 4 * T * H / 128 + 2 * n + n * H + 4 * n * H / 128 + 4 * n + 4 * (E + 1)
+    by_sw = n * 2 * I * 2 + n * I + 4 * n * I / 128
+    by_c = n * H * 2 + 8 * n + T * H * 2
+    for name, by, ms_ in (("f1_moe_dispatch", by_d, ms_d), ("f1_swiglu_quant", by_sw, ms_sw),
+                          ("f1_moe_combine", by_c, ms_c)):
+        res[name] = {"us": round(ms_ * 1e3, 1), "GBps": round(by / (ms_ * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(by / (ms_ * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    res["f1_moe_layer"] = {"tokens": T, "rows": n, "us": round(ms_l * 1e3, 1),
+                           "TFLOPs": round((f1 + f2) / (ms_l * 1e-3) / 1e12, 1),
+                           "steps": "dispatch, fc1, swiglu-quant, fc2, combine"}
+    del xq, dq, q2, out
     del fc1, fc2, fc1q, fc2q, x, xs_rows, a1q, a2, a2q, y1, y2
     torch.cuda.empty_cache()
 

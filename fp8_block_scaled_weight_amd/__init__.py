@@ -33,7 +33,7 @@ EXPORTED = (
     "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version", "fp8q_quant_weight_blk128",
     "fp8q_quant_act_g128", "fp8q_gemm_w8a8_blkscaled", "fp8q_grouped_gemm_w8a8", "fp8q_kv_quant",
     "fp8q_quant_weight_blk128_ue8m0", "fp8q_quant_act_g128_ue8m0", "fp8q_gemm_w8a8_ue8m0",
-    "fp8q_grouped_gemm_w8a8_ue8m0",
+    "fp8q_grouped_gemm_w8a8_ue8m0", "fp8q_moe_dispatch", "fp8q_swiglu_quant_g128", "fp8q_moe_combine",
 )
 
 
@@ -76,6 +76,9 @@ def lib() -> ctypes.CDLL:
         L.fp8q_gemm_w8a8_blkscaled.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp]
         L.fp8q_gemm_w8a8_ue8m0.argtypes = L.fp8q_gemm_w8a8_blkscaled.argtypes
         L.fp8q_kv_quant.argtypes = [vp, i64, vp, i64, i64, i32, i32, vp, vp, vp, i32, i64, vp, vp, f32, u32, vp]
+        L.fp8q_moe_dispatch.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i64, vp, i64, vp, i64, vp, vp, vp]
+        L.fp8q_swiglu_quant_g128.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp]
+        L.fp8q_moe_combine.argtypes = [vp, i64, vp, vp, i64, i32, i64, vp, i64, vp]
         for name in EXPORTED[3:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -237,3 +240,50 @@ def fp8q_kv_quant(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, 
                                _dev(v_scale, "v_scale", F32), float(fp8_range),
                                FP8Q_KV_RECALIBRATE if recalibrate else 0, _stream(stream)),
            "fp8q_kv_quant")
+
+
+def fp8q_moe_dispatch(xq: torch.Tensor, xs: torch.Tensor, topk_ids: torch.Tensor, num_experts: int,
+                      aq: torch.Tensor, a_s: torch.Tensor, offsets: torch.Tensor, row_of: torch.Tensor,
+                      stream=None) -> None:
+    """Dispatch quantized tokens xq [T,k] fp8 (scales xs [k/128, ld_xs]) to the experts recorded in
+    topk_ids [T,topk] int16: aq [>=T*topk, k] fp8, a_s [k/128, >=T*topk], offsets [E+1] int32 and
+    row_of [T,topk] int32 (row of each entry, -1 if dropped)."""
+    t, k = xq.shape
+    topk = topk_ids.shape[1] if topk_ids.dim() == 2 else 1
+    if topk_ids.shape[0] != t or not topk_ids.is_contiguous() or not row_of.is_contiguous():
+        raise ValueError("topk_ids and row_of must be contiguous [T, topk]")
+    if row_of.numel() != t * topk or offsets.numel() != num_experts + 1:
+        raise ValueError("row_of must have T*topk entries and offsets E+1")
+    if aq.shape[1] != k or aq.shape[0] < t * topk or a_s.shape[0] != k // 128 or a_s.stride(1) != 1 \
+            or xs.stride(1) != 1:
+        raise ValueError("aq must be [>=T*topk, k] and a_s [k/128, >=T*topk] with unit column stride")
+    _check(lib().fp8q_moe_dispatch(_dev(xq, "xq", FP8), _rows(xq, "xq"), _dev(xs, "xs", F32), xs.stride(0),
+                                   _dev(topk_ids, "topk_ids", (torch.int16,)), t, topk, int(num_experts), k,
+                                   _dev(aq, "aq", FP8), _rows(aq, "aq"), _dev(a_s, "a_s", F32), a_s.stride(0),
+                                   _dev(offsets, "offsets", (torch.int32,)), _dev(row_of, "row_of", (torch.int32,)),
+                                   _stream(stream)), "fp8q_moe_dispatch")
+
+
+def fp8q_swiglu_quant_g128(h: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
+    """silu(gate) * up of h = [gate | up] ([m, 2n] bf16), quantized per 1x128 group:
+    q [m, n] fp8, s [n/128, ld_s] fp32."""
+    m, n2 = h.shape
+    n = n2 // 2
+    if tuple(q.shape) != (m, n) or s.dim() != 2 or s.shape[0] != n // 128 or s.stride(1) != 1:
+        raise ValueError("q must be [m, n] and s [n/128, ld_s] with unit column stride")
+    _check(lib().fp8q_swiglu_quant_g128(_dev(h, "h", BF16), m, n, _rows(h, "h"), _dev(q, "q", FP8), _rows(q, "q"),
+                                        _dev(s, "s", F32), s.stride(0), _stream(stream)), "fp8q_swiglu_quant_g128")
+
+
+def fp8q_moe_combine(y: torch.Tensor, row_of: torch.Tensor, weights: torch.Tensor, out: torch.Tensor,
+                     stream=None) -> None:
+    """out [T, hidden] bf16 = sum_j weights[t, j] * y[row_of[t, j]] (rows -1 skipped), fp32 sum, one rounding."""
+    t, topk = row_of.shape
+    hidden = out.shape[1]
+    if out.shape[0] != t or y.shape[1] != hidden or tuple(weights.shape) != (t, topk):
+        raise ValueError("shape mismatch between y, row_of, weights and out")
+    if not row_of.is_contiguous() or not weights.is_contiguous():
+        raise ValueError("row_of and weights must be contiguous [T, topk]")
+    _check(lib().fp8q_moe_combine(_dev(y, "y", BF16), _rows(y, "y"), _dev(row_of, "row_of", (torch.int32,)),
+                                  _dev(weights, "weights", F32), t, topk, hidden, _dev(out, "out", BF16),
+                                  _rows(out, "out"), _stream(stream)), "fp8q_moe_combine")

@@ -276,4 +276,71 @@ fp8q_status fp8q_kv_quant(const void* k, int64_t ld_k, const void* v, int64_t ld
                   "kv_quant");
 }
 
+fp8q_status fp8q_moe_dispatch(const void* xq, int64_t ld_xq, const float* xs, int64_t ld_xs, const int16_t* topk_ids,
+                              int64_t num_tokens, int32_t topk, int32_t num_experts, int64_t k, void* aq,
+                              int64_t ld_aq, float* as, int64_t ld_as, int32_t* offsets, int32_t* row_of,
+                              void* stream) {
+  if (num_tokens < 0 || k < 0) return fail(FP8Q_ERR_SHAPE, "negative shape");
+  if (topk < 1) return fail(FP8Q_ERR_SHAPE, "topk must be >= 1 (got %d)", topk);
+  if (num_experts < 1 || num_experts > 32767)
+    return fail(FP8Q_ERR_SHAPE, "num_experts must be in [1, 32767] (got %d)", num_experts);
+  if (k == 0 || k % 128) return fail(FP8Q_ERR_SHAPE, "k=%lld must be a positive multiple of 128", (long long)k);
+  const int64_t n = num_tokens * (int64_t)topk;
+  if (n > 0x7fffffffLL) return fail(FP8Q_ERR_SHAPE, "num_tokens * topk must be below 2^31");
+  if (!offsets) return fail(FP8Q_ERR_NULL, "offsets is NULL");
+  if (!aligned4(offsets)) return fail(FP8Q_ERR_ALIGN, "offsets must be 4-byte aligned");
+  if (n > 0) {
+    if (!xq || !xs || !topk_ids || !aq || !as || !row_of) return fail(FP8Q_ERR_NULL, "NULL pointer");
+    if (ld_xq < k || ld_aq < k || ld_xs < num_tokens || ld_as < n)
+      return fail(FP8Q_ERR_STRIDE, "ld_xq/ld_aq < k, ld_xs < num_tokens or ld_as < num_tokens*topk");
+    if (!aligned16(xq) || !aligned16(aq) || ld_xq % 16 || ld_aq % 16 || !aligned16(topk_ids) || !aligned4(xs) ||
+        !aligned4(as) || !aligned4(row_of))
+      return fail(FP8Q_ERR_ALIGN, "xq/aq/topk_ids must be 16-byte aligned with ld_xq, ld_aq multiples of 16");
+  }
+  fp8q_status st = check_device();
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_moe_dispatch(xq, ld_xq, xs, ld_xs, topk_ids, num_tokens, topk, num_experts, k, aq,
+                                            ld_aq, as, ld_as, offsets, row_of, reinterpret_cast<hipStream_t>(stream)),
+                  "moe_dispatch");
+}
+
+fp8q_status fp8q_swiglu_quant_g128(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q, int64_t ld_q,
+                                   float* s, int64_t ld_s, void* stream) {
+  if (m < 0 || n < 0) return fail(FP8Q_ERR_SHAPE, "negative shape");
+  if (n % 128) return fail(FP8Q_ERR_SHAPE, "n=%lld must be a multiple of 128", (long long)n);
+  if (m == 0 || n == 0) {
+    fp8q_status st = check_device();
+    return st == FP8Q_OK ? ok() : st;
+  }
+  if (!h || !q || !s) return fail(FP8Q_ERR_NULL, "NULL pointer");
+  if (ld_h < 2 * n || ld_q < n || ld_s < m) return fail(FP8Q_ERR_STRIDE, "ld_h < 2n, ld_q < n or ld_s < m");
+  if (!aligned16(h) || !aligned16(q) || ld_h % 8 || ld_q % 16 || !aligned4(s))
+    return fail(FP8Q_ERR_ALIGN, "h/q must be 16-byte aligned with ld_h %% 8 == 0 and ld_q %% 16 == 0");
+  fp8q_status st = check_device();
+  if (st != FP8Q_OK) return st;
+  return launched(fp8q::launch_swiglu_quant(h, m, n, ld_h, q, ld_q, s, ld_s, reinterpret_cast<hipStream_t>(stream)),
+                  "swiglu_quant_g128");
+}
+
+fp8q_status fp8q_moe_combine(const void* y, int64_t ld_y, const int32_t* row_of, const float* weights,
+                             int64_t num_tokens, int32_t topk, int64_t hidden, void* out, int64_t ld_out,
+                             void* stream) {
+  if (num_tokens < 0 || hidden < 0) return fail(FP8Q_ERR_SHAPE, "negative shape");
+  if (topk < 1) return fail(FP8Q_ERR_SHAPE, "topk must be >= 1 (got %d)", topk);
+  if (hidden == 0 || hidden % 8)
+    return fail(FP8Q_ERR_SHAPE, "hidden=%lld must be a positive multiple of 8", (long long)hidden);
+  if (num_tokens > 0) {
+    if (!y || !row_of || !weights || !out) return fail(FP8Q_ERR_NULL, "NULL pointer");
+    if (ld_y < hidden || ld_out < hidden) return fail(FP8Q_ERR_STRIDE, "ld_y/ld_out < hidden");
+    if (!aligned16(y) || !aligned16(out) || ld_y % 8 || ld_out % 8 || !aligned4(row_of) || !aligned4(weights))
+      return fail(FP8Q_ERR_ALIGN, "y/out must be 16-byte aligned with ld_y, ld_out multiples of 8");
+  }
+  fp8q_status st = check_device();
+  if (st != FP8Q_OK) return st;
+  if (num_tokens == 0) return ok();
+  return launched(fp8q::launch_moe_combine(y, ld_y, row_of, weights, num_tokens, topk, hidden, out, ld_out,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                  "moe_combine");
+}
+
 }  // extern "C"

@@ -1,0 +1,307 @@
+// The MoE layer's data movement around the grouped GEMM, for gfx950: dispatch of
+// quantized tokens to their recorded experts, SwiGLU fused with fc2's 1x128
+// quantization, and the weighted combine of the expert outputs.
+//
+// MoE routing-replay page, "Rollout Routing Replay" (section 4) and its cost analysis
+// (section 5): the rollout records each token's top-k expert indices as int16 and the
+// tokens go to exactly those experts.  Rounding-location page, the SwiGLU fusion
+// region: SiLU's result is not rounded before it multiplies the up projection.
+// FP8-RL summary page, "Method step details" step 1: MoE fc1/fc2 inputs are quantized
+// per 1x128 group on every forward.
+//
+// All three are HBM streams.  Dispatch is deterministic without atomics: rows are
+// ordered by expert and, within an expert, by entry index f = t*topk + j (a stable
+// counting sort).
+#include "e4m3.hpp"
+#include "launch.hpp"
+
+namespace fp8q {
+
+// ----------------------------------------------------------------------------
+// Dispatch, routing step: one workgroup per expert e.  Each scans every recorded id
+// twice.  Pass 1 counts the valid ids below e (the first row of e) and equal to e.
+// Pass 2 hands the entries of e, in f order, consecutive rows: row_of[f] = row, and
+// copies the token's K/128 scales into the dispatched scale matrix.  Workgroup 0 also
+// marks invalid entries (id < 0 or id >= E) with row -1.
+// ----------------------------------------------------------------------------
+constexpr int kRouteThreads = 512;
+constexpr int kRoutePer = 64;  // ids per thread and pass chunk: eight 16-byte loads
+
+// ids [f0, f0 + 64) of this thread (entries at or past n read as -1)
+__device__ __forceinline__ void load_ids(const int16_t* __restrict__ ids, int64_t n, int64_t f0,
+                                         int (&v)[kRoutePer]) {
+  if (f0 + kRoutePer <= n) {
+    uint4 w[kRoutePer / 8];
+#pragma unroll
+    for (int i = 0; i < kRoutePer / 8; ++i) w[i] = load_plain(ids + f0 + 8 * i);
+#pragma unroll
+    for (int i = 0; i < kRoutePer / 8; ++i) {
+      const uint32_t d[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        v[8 * i + 2 * h] = (int)(int16_t)(d[h] & 0xffffu);
+        v[8 * i + 2 * h + 1] = (int)(int16_t)(d[h] >> 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kRoutePer; ++i) v[i] = (f0 + i < n) ? (int)ids[f0 + i] : -1;
+  }
+}
+
+// Exclusive prefix of v over the workgroup in thread order; `total` gets the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) sh[w] = incl;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < kRouteThreads / 64; ++i) {
+    const int s = sh[i];
+    base += (i < w) ? s : 0;
+    total += s;
+  }
+  __syncthreads();  // sh is reused by the next call
+  return base + incl - v;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
+    const int16_t* __restrict__ ids, int64_t n, int32_t topk, int32_t experts, const float* __restrict__ xs,
+    int64_t ld_xs, int64_t kgroups, float* __restrict__ as, int64_t ld_as, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_of) {
+  __shared__ int sh[kRouteThreads / 64];
+  const int e = blockIdx.x;
+  const int64_t chunk = (int64_t)kRouteThreads * kRoutePer;
+  int v[kRoutePer];
+
+  int below = 0, mine = 0;
+  for (int64_t c0 = 0; c0 < n; c0 += chunk) {
+    load_ids(ids, n, c0 + (int64_t)threadIdx.x * kRoutePer, v);
+#pragma unroll
+    for (int i = 0; i < kRoutePer; ++i) {
+      below += (v[i] >= 0 && v[i] < e) ? 1 : 0;
+      mine += (v[i] == e) ? 1 : 0;
+    }
+  }
+  int base, count;
+  (void)block_excl_scan(below, sh, base);
+  (void)block_excl_scan(mine, sh, count);
+  if (threadIdx.x == 0) {
+    offsets[e] = base;
+    if (e == experts - 1) offsets[experts] = base + count;
+  }
+
+  int running = base;
+  for (int64_t c0 = 0; c0 < n; c0 += chunk) {
+    const int64_t f0 = c0 + (int64_t)threadIdx.x * kRoutePer;
+    load_ids(ids, n, f0, v);
+    uint64_t match = 0, bad = 0;
+#pragma unroll
+    for (int i = 0; i < kRoutePer; ++i) {
+      match |= (uint64_t)(v[i] == e) << i;
+      bad |= (uint64_t)(f0 + i < n && (v[i] < 0 || v[i] >= experts)) << i;
+    }
+    int tot;
+    int r = running + block_excl_scan(__popcll(match), sh, tot);
+    while (match) {
+      const int64_t f = f0 + __builtin_ctzll(match);
+      match &= match - 1;
+      row_of[f] = r;
+      const int64_t t = f / topk;
+      for (int64_t g = 0; g < kgroups; ++g) as[g * ld_as + r] = xs[g * ld_xs + t];
+      ++r;
+    }
+    if (e == 0) {
+      while (bad) {
+        row_of[f0 + __builtin_ctzll(bad)] = -1;
+        bad &= bad - 1;
+      }
+    }
+    running += tot;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Dispatch, copy step: one wave per entry copies the token's K code bytes into its row.
+// ----------------------------------------------------------------------------
+constexpr int kGatherWaves = 4;
+
+__global__ __launch_bounds__(64 * kGatherWaves) void moe_gather_kernel(
+    const uint8_t* __restrict__ xq, int64_t ld_xq, const int32_t* __restrict__ row_of, int64_t n, int32_t topk,
+    int64_t k, uint8_t* __restrict__ aq, int64_t ld_aq) {
+  const int lane = threadIdx.x & 63;
+  const int64_t f = (int64_t)blockIdx.x * kGatherWaves + (threadIdx.x >> 6);
+  if (f >= n) return;
+  const int32_t r = row_of[f];
+  if (r < 0) return;
+  const uint8_t* src = xq + (f / topk) * ld_xq;
+  uint8_t* dst = aq + (int64_t)r * ld_aq;
+  for (int64_t c = (int64_t)lane * 16; c < k; c += 64 * 16) store_plain(dst + c, load_plain(src + c));
+}
+
+hipError_t launch_moe_dispatch(const void* xq, int64_t ld_xq, const float* xs, int64_t ld_xs, const int16_t* ids,
+                               int64_t tokens, int32_t topk, int32_t experts, int64_t k, void* aq, int64_t ld_aq,
+                               float* as, int64_t ld_as, int32_t* offsets, int32_t* row_of, hipStream_t stream) {
+  const int64_t n = tokens * topk;
+  hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)experts), dim3(kRouteThreads), 0, stream, ids, n, topk,
+                     experts, xs, ld_xs, k / 128, as, ld_as, offsets, row_of);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || n == 0) return err;
+  hipLaunchKernelGGL(moe_gather_kernel, dim3((unsigned)((n + kGatherWaves - 1) / kGatherWaves)),
+                     dim3(64 * kGatherWaves), 0, stream, reinterpret_cast<const uint8_t*>(xq), ld_xq, row_of, n,
+                     topk, k, reinterpret_cast<uint8_t*>(aq), ld_aq);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// SwiGLU + 1x128 quantization.  h = [gate | up], bf16 [m, 2n]; a = silu(gate) * up.
+// The value is formed in fp64, g / (1 + exp(-g)) * u, so that it sits far inside fp32
+// precision; the E4M3 encoding is its one rounding.  Per row and 128-column group:
+// amax = max |a| (exact), scale = fl32(fl64(amax / 448)) (1 for amax 0), code = the
+// E4M3 value nearest the fp64 quotient a / scale (ties to even, saturating).  The
+// quotient is rounded to fp32 with round-to-odd (truncate, then set the last bit if
+// anything was dropped), which keeps enough information for the hardware's
+// round-to-nearest-even conversion to give the nearest code of the fp64 value.
+// Same lane mapping as the activation quantizer: 8 lanes per group, 16 values each.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ double silu_times_up(double g, double u) {
+#pragma clang fp contract(off)
+  return g / (1.0 + exp(-g)) * u;
+}
+
+__device__ __forceinline__ float round_to_odd_f32(double u) {
+  const double au = fabs(u);
+  uint32_t b = __float_as_uint((float)au);
+  if ((double)__uint_as_float(b) > au) b -= 1u;           // toward zero
+  if ((double)__uint_as_float(b) != au) b |= 1u;          // sticky
+  return __builtin_copysignf(fminf(__uint_as_float(b), kE4M3Max), (float)u);
+}
+
+__device__ __forceinline__ double max_over_8_lanes_f64(double v) {
+  v = fmax(v, __shfl_xor(v, 1));
+  v = fmax(v, __shfl_xor(v, 2));
+  v = fmax(v, __shfl_xor(v, 4));
+  return v;
+}
+
+__global__ __launch_bounds__(256) void swiglu_quant_g128_kernel(const uint16_t* __restrict__ h, int64_t m,
+                                                                int64_t groups, int64_t n, int64_t ld_h,
+                                                                uint8_t* __restrict__ q, int64_t ld_q,
+                                                                float* __restrict__ s, int64_t ld_s,
+                                                                int64_t group_tiles) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t rb = blockIdx.x / group_tiles;
+  const int64_t g = (blockIdx.x - rb * group_tiles) * 4 + wave;
+  const int64_t row = rb * 8 + (lane >> 3);
+  const int col = (lane & 7) * 16;
+  const bool live = (g < groups) && (row < m);
+  uint4 ga = make_uint4(0, 0, 0, 0), gb = ga, ua = ga, ub = ga;
+  if (live) {
+    const uint16_t* p = h + row * ld_h + g * 128 + col;
+    ga = load_plain(p);
+    gb = load_plain(p + 8);
+    ua = load_plain(p + n);
+    ub = load_plain(p + n + 8);
+  }
+  const uint32_t gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+  const uint32_t uw[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+  double a[16];
+  double amax = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[2 * i] = silu_times_up((double)bf16_lo(gw[i]), (double)bf16_lo(uw[i]));
+    a[2 * i + 1] = silu_times_up((double)bf16_hi(gw[i]), (double)bf16_hi(uw[i]));
+    amax = fmax(amax, fmax(fabs(a[2 * i]), fabs(a[2 * i + 1])));
+  }
+  amax = max_over_8_lanes_f64(amax);
+  if (!live) return;
+  const float scale = (amax == 0.0) ? 1.0f : (float)(amax / (double)kE4M3Max);
+  if ((lane & 7) == 0) s[g * ld_s + row] = scale;
+  const double sd = (double)scale;
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = cvt4(round_to_odd_f32(a[4 * i] / sd), round_to_odd_f32(a[4 * i + 1] / sd),
+                round_to_odd_f32(a[4 * i + 2] / sd), round_to_odd_f32(a[4 * i + 3] / sd));
+  store_plain(q + row * ld_q + g * 128 + col, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+hipError_t launch_swiglu_quant(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q, int64_t ld_q, float* s,
+                               int64_t ld_s, hipStream_t stream) {
+  const int64_t groups = n / 128;
+  const int64_t group_tiles = (groups + 3) / 4;
+  const int64_t wgs = ((m + 7) / 8) * group_tiles;
+  hipLaunchKernelGGL(swiglu_quant_g128_kernel, dim3((unsigned)wgs), dim3(256), 0, stream,
+                     reinterpret_cast<const uint16_t*>(h), m, groups, n, ld_h, reinterpret_cast<uint8_t*>(q), ld_q,
+                     s, ld_s, group_tiles);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// Combine: out[t] = bf16( sum_j w[t, j] * y[row_of[t, j]] ), the sum in fp32 in the
+// order j = 0, 1, ... (one FMA per term), entries with row -1 skipped, one rounding to
+// bf16 at the store.  One wave per token; each lane takes 8 consecutive columns per
+// 512-column pass and has the up-to-8 expert rows of its columns in flight at once.
+// ----------------------------------------------------------------------------
+constexpr int kCombineWaves = 4;
+constexpr int kCombineBatch = 8;  // expert rows loaded together
+
+__device__ __forceinline__ uint32_t bf16_pack_rne(float lo, float hi) {
+  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+  a = (a + 0x7fffu + ((a >> 16) & 1u)) >> 16;
+  b = (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+  return a | (b << 16);
+}
+
+__global__ __launch_bounds__(64 * kCombineWaves) void moe_combine_kernel(
+    const uint16_t* __restrict__ y, int64_t ld_y, const int32_t* __restrict__ row_of, const float* __restrict__ w,
+    int64_t tokens, int32_t topk, int64_t hidden, uint16_t* __restrict__ out, int64_t ld_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+  if (t >= tokens) return;
+  const int32_t* rt = row_of + t * topk;
+  const float* wt = w + t * topk;
+  for (int64_t c = (int64_t)lane * 8; c < hidden; c += 64 * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < topk; j0 += kCombineBatch) {
+      uint4 v[kCombineBatch];
+      float wj[kCombineBatch];
+#pragma unroll
+      for (int j = 0; j < kCombineBatch; ++j) {
+        const int32_t r = (j0 + j < topk) ? rt[j0 + j] : -1;
+        wj[j] = (r >= 0) ? wt[j0 + j] : 0.0f;
+        v[j] = (r >= 0) ? load_plain(y + (int64_t)r * ld_y + c) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < kCombineBatch; ++j) {
+        if (j0 + j >= topk || rt[j0 + j] < 0) continue;
+        const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = __builtin_fmaf(wj[j], bf16_lo(d[i]), acc[2 * i]);
+          acc[2 * i + 1] = __builtin_fmaf(wj[j], bf16_hi(d[i]), acc[2 * i + 1]);
+        }
+      }
+    }
+    store_plain(out + t * ld_out + c, make_uint4(bf16_pack_rne(acc[0], acc[1]), bf16_pack_rne(acc[2], acc[3]),
+                                                 bf16_pack_rne(acc[4], acc[5]), bf16_pack_rne(acc[6], acc[7])));
+  }
+}
+
+hipError_t launch_moe_combine(const void* y, int64_t ld_y, const int32_t* row_of, const float* w, int64_t tokens,
+                              int32_t topk, int64_t hidden, void* out, int64_t ld_out, hipStream_t stream) {
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((tokens + kCombineWaves - 1) / kCombineWaves)),
+                     dim3(64 * kCombineWaves), 0, stream, reinterpret_cast<const uint16_t*>(y), ld_y, row_of, w,
+                     tokens, topk, hidden, reinterpret_cast<uint16_t*>(out), ld_out);
+  return hipGetLastError();
+}
+
+}  // namespace fp8q

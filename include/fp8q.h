@@ -5,7 +5,9 @@
  *   - 128x128 blockwise E4M3 weight quantization, run at every RL weight sync;
  *   - dynamic 1x128 per-token-group activation quantization, run on every forward;
  *   - the block-scaled W8A8 GEMM that consumes both, dense and MoE-grouped;
- *   - FP8 KV-cache quantize-on-write with per-step K/V scale recalibration.
+ *   - FP8 KV-cache quantize-on-write with per-step K/V scale recalibration;
+ *   - around the grouped GEMM: MoE dispatch by recorded expert ids, SwiGLU fused with
+ *     fc2's 1x128 quantization, and the weighted combine.
  *
  * Sources (page title, then section):
  *   [FP8-RL]   "FP8-RL: A Practical and Stable Low-Precision Stack for LLM Reinforcement
@@ -23,6 +25,10 @@
  *              to BF16 once, at the output.
  *   [1T-RL]    "1T-parameter RL on 100 GPUs", section 3.4: paged KV cache in fixed
  *              blocks; K and V each quantized to FP8 separately.
+ *   [R3]       MoE routing-replay page: "Rollout Routing Replay" (section 4: the rollout
+ *              records each token's expert indices and tokens are dispatched to the
+ *              recorded experts) and the cost analysis (section 5: 8 int16 indices per
+ *              token and layer).
  *
  * Number formats.  FP8 codes are OCP E4M3FN bytes (bias 7, max +-448 = 0x7E/0xFE,
  * subnormals m * 2^-9, NaN 0x7F/0xFF never produced).  BF16 inputs/outputs are
@@ -230,6 +236,56 @@ fp8q_status fp8q_kv_quant(const void* k, int64_t ld_k, const void* v, int64_t ld
                           const int64_t* slot_mapping, void* k_cache, void* v_cache,
                           int32_t page_size, int64_t num_pages, float* k_scale, float* v_scale,
                           float fp8_range, uint32_t flags, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * MoE layer around the grouped GEMM  [R3, "Rollout Routing Replay" and the cost
+ * analysis: each token's top-k expert indices are recorded as int16 and tokens are
+ * dispatched to exactly those experts; Rounding, SwiGLU fusion region; FP8-RL step 1]
+ *
+ * fp8q_moe_dispatch: gathers quantized token rows (and their 1x128 scales) into
+ * expert-sorted rows for fp8q_grouped_gemm_w8a8.
+ *   topk_ids: int16 [num_tokens][topk] (device, contiguous, 16-byte aligned).  Entry
+ *     f = t*topk + j is valid when 0 <= topk_ids[f] < num_experts; invalid entries are
+ *     dropped.  Valid entries are ordered by expert id and, within an expert, by f.
+ *   xq: e4m3fn [num_tokens][ld_xq], xs: fp32 [k/128][ld_xs] (the layout of
+ *     fp8q_quant_act_g128's output), ld_xq >= k, ld_xs >= num_tokens.
+ *   aq: e4m3fn [R][ld_aq], as: fp32 [k/128][ld_as], R = number of valid entries
+ *     <= num_tokens*topk, ld_as >= num_tokens*topk: row r of aq is token f/topk's codes
+ *     for the r-th entry in that order, as[g][r] its scale of group g.
+ *   offsets: int32 [num_experts + 1] (out): rows of expert e are [offsets[e],
+ *     offsets[e+1]); offsets[0] = 0, offsets[num_experts] = R.
+ *   row_of: int32 [num_tokens*topk] (out): the row of entry f, -1 if dropped.
+ * k a positive multiple of 128; topk >= 1; 1 <= num_experts <= 32767;
+ * num_tokens * topk < 2^31.  xq/aq 16-byte aligned with ld_xq, ld_aq multiples of 16.
+ * num_tokens == 0 writes offsets (all 0) only.
+ * ---------------------------------------------------------------------------- */
+fp8q_status fp8q_moe_dispatch(const void* xq, int64_t ld_xq, const float* xs, int64_t ld_xs,
+                              const int16_t* topk_ids, int64_t num_tokens, int32_t topk,
+                              int32_t num_experts, int64_t k, void* aq, int64_t ld_aq, float* as,
+                              int64_t ld_as, int32_t* offsets, int32_t* row_of, void* stream);
+
+/* fp8q_swiglu_quant_g128: h = [gate | up], bf16 [m][ld_h] with gate in columns [0, n)
+ * and up in [n, 2n) (fc1's output); a = silu(gate) * up = gate / (1 + exp(-gate)) * up,
+ * formed in fp64 and never rounded before the quantization; then the quantization rule
+ * above per row and 128-column group: amax = max |a|, scale = fl32(fl64(amax / 448))
+ * (1.0 if amax == 0), code = the E4M3FN value nearest the fp64 quotient a / scale.
+ * Output layout as fp8q_quant_act_g128: q e4m3fn [m][ld_q], s[g * ld_s + row].
+ * n a multiple of 128; ld_h >= 2n, ld_h % 8 == 0; ld_q >= n, ld_q % 16 == 0; ld_s >= m;
+ * h, q 16-byte aligned.  Precondition: amax / 448 fits binary32. */
+fp8q_status fp8q_swiglu_quant_g128(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q,
+                                   int64_t ld_q, float* s, int64_t ld_s, void* stream);
+
+/* fp8q_moe_combine: out[t][c] = bf16( sum_{j < topk, row_of[t*topk+j] >= 0}
+ *   weights[t*topk+j] * y[row_of[t*topk+j]][c] ), the sum in fp32 in the order of j
+ * (one fused multiply-add per term), rounded to bf16 (nearest even) once.
+ *   y: bf16 [rows][ld_y] (fc2's output in dispatch order); row_of: int32
+ *   [num_tokens*topk] (fp8q_moe_dispatch's); weights: fp32 [num_tokens*topk];
+ *   out: bf16 [num_tokens][ld_out].
+ * hidden a positive multiple of 8; ld_y, ld_out >= hidden and multiples of 8; y, out
+ * 16-byte aligned.  Precondition: every row_of entry is -1 or below the rows of y. */
+fp8q_status fp8q_moe_combine(const void* y, int64_t ld_y, const int32_t* row_of, const float* weights,
+                             int64_t num_tokens, int32_t topk, int64_t hidden, void* out,
+                             int64_t ld_out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -167,3 +167,50 @@ def test_ue8m0_entry_points_validate_like_the_fp32_ones():
     d[0] = fq.WeightDesc(A16, A16, A16, 100, 256, 256, 256)
     assert L.fp8q_quant_weight_blk128_ue8m0(d, 1, None) == fq.FP8Q_ERR_SHAPE
     assert L.fp8q_quant_weight_blk128_ue8m0(d, 0, None) == fq.FP8Q_ERR_SHAPE
+
+
+def test_moe_validation():
+    L = fq.lib()
+
+    def dispatch(**kw):
+        a = dict(xq=A16, ld_xq=256, xs=A16, ld_xs=8, ids=A16, t=8, topk=2, e=4, k=256, aq=A16, ld_aq=256,
+                 a_s=A16, ld_as=16, off=A16, row_of=A16)
+        a.update(kw)
+        return L.fp8q_moe_dispatch(a["xq"], a["ld_xq"], a["xs"], a["ld_xs"], a["ids"], a["t"], a["topk"], a["e"],
+                                   a["k"], a["aq"], a["ld_aq"], a["a_s"], a["ld_as"], a["off"], a["row_of"], None)
+
+    assert dispatch(topk=0) == fq.FP8Q_ERR_SHAPE
+    assert dispatch(e=0) == fq.FP8Q_ERR_SHAPE
+    assert dispatch(e=40000) == fq.FP8Q_ERR_SHAPE
+    assert dispatch(k=200, ld_xq=200, ld_aq=200) == fq.FP8Q_ERR_SHAPE
+    assert dispatch(t=1 << 30, topk=4) == fq.FP8Q_ERR_SHAPE
+    assert dispatch(off=None) == fq.FP8Q_ERR_NULL
+    assert dispatch(ids=None) == fq.FP8Q_ERR_NULL
+    assert dispatch(ld_as=15) == fq.FP8Q_ERR_STRIDE
+    assert dispatch(ld_xs=7) == fq.FP8Q_ERR_STRIDE
+    assert dispatch(ids=A16 + 2) == fq.FP8Q_ERR_ALIGN
+    assert dispatch(ld_aq=264) == fq.FP8Q_ERR_ALIGN
+
+    def swiglu(**kw):
+        a = dict(h=A16, m=4, n=256, ld_h=512, q=A16, ld_q=256, s=A16, ld_s=4)
+        a.update(kw)
+        return L.fp8q_swiglu_quant_g128(a["h"], a["m"], a["n"], a["ld_h"], a["q"], a["ld_q"], a["s"], a["ld_s"],
+                                        None)
+
+    assert swiglu(n=100) == fq.FP8Q_ERR_SHAPE
+    assert swiglu(q=None) == fq.FP8Q_ERR_NULL
+    assert swiglu(ld_h=256) == fq.FP8Q_ERR_STRIDE
+    assert swiglu(ld_s=3) == fq.FP8Q_ERR_STRIDE
+    assert swiglu(h=A16 + 8) == fq.FP8Q_ERR_ALIGN
+
+    def combine(**kw):
+        a = dict(y=A16, ld_y=256, row_of=A16, w=A16, t=4, topk=2, hidden=256, out=A16, ld_out=256)
+        a.update(kw)
+        return L.fp8q_moe_combine(a["y"], a["ld_y"], a["row_of"], a["w"], a["t"], a["topk"], a["hidden"],
+                                  a["out"], a["ld_out"], None)
+
+    assert combine(hidden=100) == fq.FP8Q_ERR_SHAPE
+    assert combine(topk=0) == fq.FP8Q_ERR_SHAPE
+    assert combine(w=None) == fq.FP8Q_ERR_NULL
+    assert combine(ld_out=128) == fq.FP8Q_ERR_STRIDE
+    assert combine(out=A16 + 4) == fq.FP8Q_ERR_ALIGN
