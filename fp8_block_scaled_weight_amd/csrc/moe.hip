@@ -20,9 +20,8 @@ namespace fp8q {
 // ----------------------------------------------------------------------------
 // Dispatch, routing step: one workgroup per expert e.  Each scans every recorded id
 // twice.  Pass 1 counts the valid ids below e (the first row of e) and equal to e.
-// Pass 2 hands the entries of e, in f order, consecutive rows: row_of[f] = row, and
-// copies the token's K/128 scales into the dispatched scale matrix.  Workgroup 0 also
-// marks invalid entries (id < 0 or id >= E) with row -1.
+// Pass 2 hands the entries of e, in f order, consecutive rows: row_of[f] = row.
+// Workgroup 0 also marks invalid entries (id < 0 or id >= E) with row -1.
 // ----------------------------------------------------------------------------
 constexpr int kRouteThreads = 512;
 constexpr int kRoutePer = 64;  // ids per thread and pass chunk: eight 16-byte loads
@@ -72,10 +71,9 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh, int& total) {
   return base + incl - v;
 }
 
-__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
-    const int16_t* __restrict__ ids, int64_t n, int32_t topk, int32_t experts, const float* __restrict__ xs,
-    int64_t ld_xs, int64_t kgroups, float* __restrict__ as, int64_t ld_as, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ row_of) {
+__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int16_t* __restrict__ ids, int64_t n,
+                                                                   int32_t experts, int32_t* __restrict__ offsets,
+                                                                   int32_t* __restrict__ row_of) {
   __shared__ int sh[kRouteThreads / 64];
   const int e = blockIdx.x;
   const int64_t chunk = (int64_t)kRouteThreads * kRoutePer;
@@ -111,12 +109,8 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     int tot;
     int r = running + block_excl_scan(__popcll(match), sh, tot);
     while (match) {
-      const int64_t f = f0 + __builtin_ctzll(match);
+      row_of[f0 + __builtin_ctzll(match)] = r++;
       match &= match - 1;
-      row_of[f] = r;
-      const int64_t t = f / topk;
-      for (int64_t g = 0; g < kgroups; ++g) as[g * ld_as + r] = xs[g * ld_xs + t];
-      ++r;
     }
     if (e == 0) {
       while (bad) {
@@ -129,51 +123,85 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
 }
 
 // ----------------------------------------------------------------------------
-// Dispatch, copy step: one wave per entry copies the token's K code bytes into its row.
+// Dispatch, copy step: one wave per entry copies the token's K code bytes into its row
+// and its K/128 scales into column `row` of the dispatched scale matrix.
 // ----------------------------------------------------------------------------
 constexpr int kGatherWaves = 4;
 
 __global__ __launch_bounds__(64 * kGatherWaves) void moe_gather_kernel(
-    const uint8_t* __restrict__ xq, int64_t ld_xq, const int32_t* __restrict__ row_of, int64_t n, int32_t topk,
-    int64_t k, uint8_t* __restrict__ aq, int64_t ld_aq) {
+    const uint8_t* __restrict__ xq, int64_t ld_xq, const float* __restrict__ xs, int64_t ld_xs,
+    const int32_t* __restrict__ row_of, int64_t n, int32_t topk, int64_t k, uint8_t* __restrict__ aq,
+    int64_t ld_aq, float* __restrict__ as, int64_t ld_as) {
   const int lane = threadIdx.x & 63;
   const int64_t f = (int64_t)blockIdx.x * kGatherWaves + (threadIdx.x >> 6);
   if (f >= n) return;
   const int32_t r = row_of[f];
   if (r < 0) return;
-  const uint8_t* src = xq + (f / topk) * ld_xq;
+  const int64_t t = f / topk;
+  const uint8_t* src = xq + t * ld_xq;
   uint8_t* dst = aq + (int64_t)r * ld_aq;
   for (int64_t c = (int64_t)lane * 16; c < k; c += 64 * 16) store_plain(dst + c, load_plain(src + c));
+  for (int64_t g = lane; g < k / 128; g += 64) as[g * ld_as + r] = xs[g * ld_xs + t];
 }
 
 hipError_t launch_moe_dispatch(const void* xq, int64_t ld_xq, const float* xs, int64_t ld_xs, const int16_t* ids,
                                int64_t tokens, int32_t topk, int32_t experts, int64_t k, void* aq, int64_t ld_aq,
                                float* as, int64_t ld_as, int32_t* offsets, int32_t* row_of, hipStream_t stream) {
   const int64_t n = tokens * topk;
-  hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)experts), dim3(kRouteThreads), 0, stream, ids, n, topk,
-                     experts, xs, ld_xs, k / 128, as, ld_as, offsets, row_of);
+  hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)experts), dim3(kRouteThreads), 0, stream, ids, n, experts,
+                     offsets, row_of);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || n == 0) return err;
   hipLaunchKernelGGL(moe_gather_kernel, dim3((unsigned)((n + kGatherWaves - 1) / kGatherWaves)),
-                     dim3(64 * kGatherWaves), 0, stream, reinterpret_cast<const uint8_t*>(xq), ld_xq, row_of, n,
-                     topk, k, reinterpret_cast<uint8_t*>(aq), ld_aq);
+                     dim3(64 * kGatherWaves), 0, stream, reinterpret_cast<const uint8_t*>(xq), ld_xq, xs, ld_xs,
+                     row_of, n, topk, k, reinterpret_cast<uint8_t*>(aq), ld_aq, as, ld_as);
   return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------
 // SwiGLU + 1x128 quantization.  h = [gate | up], bf16 [m, 2n]; a = silu(gate) * up.
-// The value is formed in fp64, g / (1 + exp(-g)) * u, so that it sits far inside fp32
-// precision; the E4M3 encoding is its one rounding.  Per row and 128-column group:
-// amax = max |a| (exact), scale = fl32(fl64(amax / 448)) (1 for amax 0), code = the
-// E4M3 value nearest the fp64 quotient a / scale (ties to even, saturating).  The
-// quotient is rounded to fp32 with round-to-odd (truncate, then set the last bit if
-// anything was dropped), which keeps enough information for the hardware's
+// The value is defined in fp64, g / (1 + exp(-g)) * u, far inside fp32 precision, so the
+// E4M3 encoding is its one rounding.  Per row and 128-column group: amax = max |a|
+// (exact), scale = fl32(fl64(amax / 448)) (1 for amax 0), code = the E4M3 value nearest
+// the fp64 quotient a / scale (ties to even, saturating).
+//
+// Fast path.  Each value is first formed in fp32 (relative error below 2^-20: exp(-g)
+// within about 2.5 ulps, one rounding each for 1 + e, the reciprocal and two products),
+// and the fp64 value is formed only where the fp32 one cannot decide:
+//   - inputs outside the range where that bound holds (gate <= -80, where expf
+//     overflows; |gate| or |up| >= 2^60; |a| below 2^-100 unless a is an exact zero);
+//   - the group maximum: every value within 2^-14 of the fp32 maximum is recomputed in
+//     fp64, so amax is the fp64 maximum;
+//   - codes: the fp32 quotient is moved by 2^-15 both ways; if both give one code, the
+//     fp64 quotient (within 2^-19 of it) gives that code too, since rounding is monotone;
+//     otherwise the code comes from the fp64 quotient.  Groups with a scale below
+//     2^-100 take the fp64 path throughout.
+// An fp64 quotient is rounded to fp32 with round-to-odd (truncate, then set the last bit
+// if anything was dropped), which keeps enough information for the hardware's
 // round-to-nearest-even conversion to give the nearest code of the fp64 value.
 // Same lane mapping as the activation quantizer: 8 lanes per group, 16 values each.
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ double silu_times_up(double g, double u) {
 #pragma clang fp contract(off)
   return g / (1.0 + exp(-g)) * u;
+}
+
+// exp(x) for x < 80: 2^(x log2 e) with the exponent carried as an fp32 head ph plus its
+// remainder pl (fma-exact product remainder and the low part of log2 e); the hardware
+// 2^ph (about 1 ulp) is corrected by the first-order factor 1 + pl ln 2 (|pl| <= 2^-17,
+// so the dropped second-order term is below 2^-35).  Very negative x gives 0.
+__device__ __forceinline__ float exp_lt80(float x) {
+  constexpr float kL2eHi = 0x1.715476p+0f;    // log2(e) rounded to fp32
+  constexpr float kL2eLo = 0x1.4ae0c0p-26f;   // log2(e) - kL2eHi, rounded
+  constexpr float kLn2 = 0x1.62e430p-1f;
+  const float ph = x * kL2eHi;
+  const float pl = __builtin_fmaf(x, kL2eHi, -ph) + x * kL2eLo;
+  return __builtin_amdgcn_exp2f(ph) * __builtin_fmaf(pl, kLn2, 1.0f);
+}
+
+__device__ __forceinline__ float silu_times_up_f32(float g, float u) {
+#pragma clang fp contract(off)
+  return g * __builtin_amdgcn_rcpf(1.0f + exp_lt80(-g)) * u;
 }
 
 __device__ __forceinline__ float round_to_odd_f32(double u) {
@@ -190,6 +218,22 @@ __device__ __forceinline__ double max_over_8_lanes_f64(double v) {
   v = fmax(v, __shfl_xor(v, 4));
   return v;
 }
+
+// gate and up of value i (0..15) of this lane, selected without dynamic register indexing
+__device__ __forceinline__ double swiglu_at(const uint32_t (&gw)[8], const uint32_t (&uw)[8], int i) {
+  uint32_t gword = gw[0], uword = uw[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) {
+    gword = ((i >> 1) == j) ? gw[j] : gword;
+    uword = ((i >> 1) == j) ? uw[j] : uword;
+  }
+  const float g = (i & 1) ? bf16_hi(gword) : bf16_lo(gword);
+  const float u = (i & 1) ? bf16_hi(uword) : bf16_lo(uword);
+  return silu_times_up((double)g, (double)u);
+}
+
+constexpr float kSwigluCodeSlack = 0x1p-15f;   // relative move of the fp32 quotient
+constexpr double kSwigluMaxSlack = 0x1p-14;     // values this close to the maximum are recomputed
 
 __global__ __launch_bounds__(256) void swiglu_quant_g128_kernel(const uint16_t* __restrict__ h, int64_t m,
                                                                 int64_t groups, int64_t n, int64_t ld_h,
@@ -213,24 +257,75 @@ __global__ __launch_bounds__(256) void swiglu_quant_g128_kernel(const uint16_t* 
   }
   const uint32_t gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
   const uint32_t uw[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
-  double a[16];
-  double amax = 0.0;
+
+  // fp32 values, and the values that need fp64 from the start
+  float a32[16];
+  uint32_t slow = 0;
+  float m32 = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[2 * i] = silu_times_up((double)bf16_lo(gw[i]), (double)bf16_lo(uw[i]));
-    a[2 * i + 1] = silu_times_up((double)bf16_hi(gw[i]), (double)bf16_hi(uw[i]));
-    amax = fmax(amax, fmax(fabs(a[2 * i]), fabs(a[2 * i + 1])));
+  for (int i = 0; i < 16; ++i) {
+    const float gv = (i & 1) ? bf16_hi(gw[i >> 1]) : bf16_lo(gw[i >> 1]);
+    const float uv = (i & 1) ? bf16_hi(uw[i >> 1]) : bf16_lo(uw[i >> 1]);
+    const float a = silu_times_up_f32(gv, uv);
+    const bool exact_zero = (gv == 0.0f) || (uv == 0.0f);
+    const bool ok = exact_zero || (gv > -80.0f && fabsf(gv) < 0x1p60f && fabsf(uv) < 0x1p60f && fabsf(a) >= 0x1p-100f);
+    slow |= ok ? 0u : (1u << i);
+    a32[i] = ok ? a : 0.0f;
+    m32 = fmaxf(m32, fabsf(a32[i]));
+  }
+
+  // amax in fp64: the fp64 values of the slow ones and of every value near the maximum
+  double approx = (double)m32, amax = 0.0;
+  for (uint32_t t = slow; t; t &= t - 1) {
+    const double a = fabs(swiglu_at(gw, uw, __builtin_ctz(t)));
+    approx = fmax(approx, a);
+    amax = fmax(amax, a);
+  }
+  approx = max_over_8_lanes_f64(approx);
+  if (approx > 0.0) {
+    const float thr = (float)(approx * (1.0 - kSwigluMaxSlack));
+    uint32_t cand = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cand |= (fabsf(a32[i]) >= thr) ? (1u << i) : 0u;
+    cand &= ~slow;
+    for (; cand; cand &= cand - 1) amax = fmax(amax, fabs(swiglu_at(gw, uw, __builtin_ctz(cand))));
   }
   amax = max_over_8_lanes_f64(amax);
   if (!live) return;
   const float scale = (amax == 0.0) ? 1.0f : (float)(amax / (double)kE4M3Max);
   if ((lane & 7) == 0) s[g * ld_s + row] = scale;
-  const double sd = (double)scale;
-  uint32_t o[4];
+
+  // codes: fp32 quotient moved both ways; the fp64 quotient where they disagree
+  uint32_t o[4] = {0u, 0u, 0u, 0u};
+  uint32_t need = 0xffffu;
+  if (scale >= 0x1p-100f) {
+    need = slow;
+    const float r32 = 1.0f / scale;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    o[i] = cvt4(round_to_odd_f32(a[4 * i] / sd), round_to_odd_f32(a[4 * i + 1] / sd),
-                round_to_odd_f32(a[4 * i + 2] / sd), round_to_odd_f32(a[4 * i + 3] / sd));
+    for (int w = 0; w < 4; ++w) {
+      float lo[4], hi[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = a32[4 * w + e] * r32;
+        const float av = fabsf(v);
+        lo[e] = __builtin_copysignf(fminf(av * (1.0f - kSwigluCodeSlack), kE4M3Max), v);
+        hi[e] = __builtin_copysignf(fminf(av * (1.0f + kSwigluCodeSlack), kE4M3Max), v);
+      }
+      const uint32_t cl = cvt4(lo[0], lo[1], lo[2], lo[3]);
+      const uint32_t diff = cl ^ cvt4(hi[0], hi[1], hi[2], hi[3]);
+      o[w] = cl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) need |= ((diff >> (8 * e)) & 0xffu) ? (1u << (4 * w + e)) : 0u;
+    }
+  }
+  const double sd = (double)scale;
+  for (; need; need &= need - 1) {
+    const int i = __builtin_ctz(need);
+    const uint32_t c = cvt4(round_to_odd_f32(swiglu_at(gw, uw, i) / sd), 0.0f, 0.0f, 0.0f) & 0xffu;
+    const int sh = 8 * (i & 3);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o[w] = ((i >> 2) == w) ? ((o[w] & ~(0xffu << sh)) | (c << sh)) : o[w];
+  }
   store_plain(q + row * ld_q + g * 128 + col, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
