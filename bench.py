@@ -712,6 +712,28 @@ def legs(torch, fq, synth, dev):
             tf = f / (ms * 1e-3) / 1e12
             res[f"a3_gemm_m{m}_n{n}"] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 2),
                                          "frac_roofline": round(tf / ceil, 4)}
+
+    # few tokens: activation quantization fused into the GEMM's operand load, against the
+    # activation quantizer followed by the GEMM (both as one graph of calls)
+    log("leg: fused activation quantization (few tokens)")
+    for m in (1, 4, 16, 64):
+        for n in (4096, 1024):
+            x = synth.device_activation(m, 4096, dev, 2, 9, m)
+            b = torch.randint(0, 0x77, (n, 4096), dtype=torch.uint8, device=dev)
+            bsc = torch.rand((n // 128, 32), device=dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            xq = torch.empty((m, 4096), dtype=torch.uint8, device=dev)
+            xs = torch.empty((32, m), dtype=torch.float32, device=dev)
+            ms_f = _time(torch, lambda: fq.fp8q_gemm_w8a8_bf16act(x, b, bsc, y), 20)
+
+            def two():
+                fq.fp8q_quant_act_g128(x, xq, xs)
+                fq.fp8q_gemm_w8a8_blkscaled(xq, xs, b, bsc, y)
+
+            ms_2 = _time(torch, two, 20)
+            by = 2 * m * 4096 + n * 4096 + 2 * m * n
+            res[f"f4_fused_m{m}_n{n}"] = {"us": round(ms_f * 1e3, 2), "quant_then_gemm_us": round(ms_2 * 1e3, 2),
+                                          "frac_hbm_roofline": round(by / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     return res
 
 

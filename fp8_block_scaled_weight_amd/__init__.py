@@ -34,6 +34,7 @@ EXPORTED = (
     "fp8q_quant_act_g128", "fp8q_gemm_w8a8_blkscaled", "fp8q_grouped_gemm_w8a8", "fp8q_kv_quant",
     "fp8q_quant_weight_blk128_ue8m0", "fp8q_quant_act_g128_ue8m0", "fp8q_gemm_w8a8_ue8m0",
     "fp8q_grouped_gemm_w8a8_ue8m0", "fp8q_moe_dispatch", "fp8q_swiglu_quant_g128", "fp8q_moe_combine",
+    "fp8q_gemm_w8a8_bf16act",
 )
 
 
@@ -75,6 +76,7 @@ def lib() -> ctypes.CDLL:
                                                                    i64, i64, vp]
         L.fp8q_gemm_w8a8_blkscaled.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp]
         L.fp8q_gemm_w8a8_ue8m0.argtypes = L.fp8q_gemm_w8a8_blkscaled.argtypes
+        L.fp8q_gemm_w8a8_bf16act.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp]
         L.fp8q_kv_quant.argtypes = [vp, i64, vp, i64, i64, i32, i32, vp, vp, vp, i32, i64, vp, vp, f32, u32, vp]
         L.fp8q_moe_dispatch.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i64, vp, i64, vp, i64, vp, vp, vp]
         L.fp8q_swiglu_quant_g128.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp]
@@ -194,6 +196,19 @@ def _gemm(fn, a, a_s, b, b_s, y, stream) -> None:
     _check(getattr(lib(), fn)(_dev(a, "a", FP8), _rows(a, "a"), _dev(a_s, "a_s", F32), a_s.stride(0),
                               _dev(b, "b", FP8), _rows(b, "b"), _dev(b_s, "b_s", F32),
                               _dev(y, "y", BF16), _rows(y, "y"), m, n, k, _stream(stream)), fn)
+
+
+def fp8q_gemm_w8a8_bf16act(x: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor, y: torch.Tensor,
+                           stream=None) -> None:
+    """y [m,n] bf16 = the block-scaled GEMM of x [m,k] bf16 (m <= 64), quantized per 1x128 group
+    inside the kernel, with b [n,k] fp8 (b_s [n/128,k/128])."""
+    m, k = x.shape
+    n = b.shape[0]
+    if b.shape[1] != k or tuple(y.shape) != (m, n) or not b_s.is_contiguous():
+        raise ValueError("shape mismatch between x, b and y")
+    _check(lib().fp8q_gemm_w8a8_bf16act(_dev(x, "x", BF16), _rows(x, "x"), _dev(b, "b", FP8), _rows(b, "b"),
+                                        _dev(b_s, "b_s", F32), _dev(y, "y", BF16), _rows(y, "y"), m, n, k,
+                                        _stream(stream)), "fp8q_gemm_w8a8_bf16act")
 
 
 def fp8q_grouped_gemm_w8a8(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,

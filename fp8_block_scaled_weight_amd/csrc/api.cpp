@@ -215,6 +215,28 @@ fp8q_status fp8q_gemm_w8a8_ue8m0(const void* a, int64_t ld_a, const float* a_s, 
   return gemm(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream, true);
 }
 
+fp8q_status fp8q_gemm_w8a8_bf16act(const void* x, int64_t ld_x, const void* b, int64_t ld_b, const float* b_s,
+                                   void* y, int64_t ld_y, int64_t m, int64_t n, int64_t k, void* stream) {
+  if (m < 0 || n < 0 || k < 0) return fail(FP8Q_ERR_SHAPE, "negative shape");
+  if (m > 64) return fail(FP8Q_ERR_SHAPE, "m=%lld: the fused activation quantization takes at most 64 tokens",
+                          (long long)m);
+  if (n % 128 || k % 128 || n == 0 || k == 0)
+    return fail(FP8Q_ERR_SHAPE, "n=%lld and k=%lld must be positive multiples of 128", (long long)n, (long long)k);
+  if (m > 0) {
+    if (!x || !b || !b_s || !y) return fail(FP8Q_ERR_NULL, "NULL pointer");
+    if (ld_x < k || ld_b < k || ld_y < n) return fail(FP8Q_ERR_STRIDE, "ld_x < k, ld_b < k or ld_y < n");
+    if (!aligned16(x) || !aligned16(b) || !aligned16(y) || ld_x % 8 || ld_b % 16 || ld_y % 8 || !aligned4(b_s))
+      return fail(FP8Q_ERR_ALIGN, "x/b/y must be 16-byte aligned with ld_x %% 8, ld_b %% 16, ld_y %% 8 == 0");
+    if (n * ld_b > kMaxOperandBytes) return fail(FP8Q_ERR_SHAPE, "b spans more than 2 GiB");
+  }
+  fp8q_status st = check_device();
+  if (st != FP8Q_OK) return st;
+  if (m == 0) return ok();
+  return launched(fp8q::launch_gemm_bf16act(x, ld_x, b, ld_b, b_s, y, ld_y, m, n, k,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                  "gemm_w8a8_bf16act");
+}
+
 static fp8q_status grouped_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                                 const float* b_s, const int32_t* group_offsets, int32_t num_groups, int64_t total_m,
                                 void* y, int64_t ld_y, int64_t n, int64_t k, void* stream, bool pow2) {

@@ -31,6 +31,7 @@
 // flight across the multiply.
 #include <utility>
 
+#include "e4m3.hpp"
 #include "launch.hpp"
 
 namespace fp8q {
@@ -471,15 +472,31 @@ static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, in
 // their fragments straight into registers (weights read once, with a non-temporal
 // hint; token rows come from L2).  The 8 partial sums are added through LDS in a fixed
 // order, so the result does not depend on timing.
+//
+// FUSED: the token rows arrive as bf16 and are quantized where they are loaded (FP8-RL
+// summary page, "Method step details" step 1: activations are quantized dynamically on
+// every forward).  Only the tile's live rows are quantized: 16 lanes per row take 8
+// values each of the K block's 128-wide group, the group amax is the maximum over those
+// 16 lanes, and the scale and codes follow the activation quantizer's rule with the same
+// encoder, so the MFMA sees exactly the codes and scales a separate quantization would
+// produce.  The wave stages the codes and scales in LDS (144-byte row pitch, so the 16
+// rows read at one offset fall in distinct banks) and reads them back in the MFMA
+// operand layout.
 // ----------------------------------------------------------------------------
 constexpr int kSmallWaves = 8;
 
-template <int WM>
+template <int WM, bool FUSED>
 __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
-    const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
+    const void* __restrict__ a_, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
     const uint8_t* __restrict__ b, int64_t ld_b, const float* __restrict__ bs, uint16_t* __restrict__ y,
     int64_t ld_y, int64_t m, int64_t n16, int kblocks) {
+  // K blocks in flight per wave (register budget permitting)
+  constexpr int U = FUSED ? (WM >= 4 ? 1 : (WM == 2 ? 2 : 4)) : (WM >= 4 ? 2 : 4);
+  constexpr int RT = 16 * WM;   // token rows of the tile
+  constexpr int kPitch = 144;   // staged code row pitch (bytes)
   __shared__ v4f part[kSmallWaves][WM][64];
+  __shared__ __align__(16) uint8_t qstage[FUSED ? kSmallWaves * U * RT * kPitch : 16];
+  __shared__ float sstage[FUSED ? kSmallWaves * U * RT : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t tn = blockIdx.x % n16;
@@ -487,6 +504,8 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
   const int64_t n0 = tn * 16;
   const int q = lane >> 4;
   const uint8_t* brow = b + (n0 + (lane & 15)) * ld_b + q * 32;
+  const uint8_t* a = reinterpret_cast<const uint8_t*>(a_);
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(a_);
   const uint8_t* arow[WM];
   int64_t srow[WM];  // token row of this lane (row 0 stands in for rows past m)
   bool live[WM];
@@ -497,15 +516,34 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
     srow[j] = live[j] ? r : 0;
     arow[j] = a + srow[j] * ld_a + q * 32;
   }
+  // FUSED: live rows of the tile and their 8-value chunks per K block
+  const int rows_live = (int)((m - m0) < RT ? (m - m0) : RT);
+  const int chunks = rows_live * 16;
   const float* bsrow = bs + (n0 / 128) * kblocks;
   v4f acc[WM];
 #pragma unroll
   for (int j = 0; j < WM; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int U = WM >= 4 ? 2 : 4;  // K blocks in flight per wave (register budget permitting)
   for (int kb0 = wave; kb0 < kblocks; kb0 += kSmallWaves * U) {
     v8i fw[U], ft[U][WM];
     float sa[U][WM], sb[U];
+    constexpr int P = 4 * WM;  // 64-lane passes over the chunks of a full tile
+    uint4 xc[FUSED ? U : 1][FUSED ? P : 1];
+    if constexpr (FUSED) {
+      // token rows first, so that their quantization overlaps the weight loads below;
+      // chunk c of a K block is values 8*(c%16) .. +7 of live row c/16
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kb = kb0 + u * kSmallWaves;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const int c = p * 64 + lane;
+          xc[u][p] = (kb < kblocks && c < chunks)
+                         ? load_plain(x + (m0 + c / 16) * ld_a + (int64_t)kb * 128 + (c % 16) * 8)
+                         : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kb = kb0 + u * kSmallWaves;
@@ -515,11 +553,55 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
         sb[u] = bsrow[kb];
 #pragma unroll
         for (int j = 0; j < WM; ++j) {
-          const u32x4* pt = reinterpret_cast<const u32x4*>(arow[j] + (int64_t)kb * 128);
-          ft[u][j] = live[j] ? join(pt[0], pt[1]) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-          const float sv = as[(int64_t)kb * ld_as + srow[j]];
-          sa[u][j] = live[j] ? sv : 0.0f;
+          if constexpr (!FUSED) {
+            const u32x4* pt = reinterpret_cast<const u32x4*>(arow[j] + (int64_t)kb * 128);
+            ft[u][j] = live[j] ? join(pt[0], pt[1]) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            const float sv = as[(int64_t)kb * ld_as + srow[j]];
+            sa[u][j] = live[j] ? sv : 0.0f;
+          }
         }
+      }
+    }
+    if constexpr (FUSED) {
+      // quantize the live chunks: group amax over the 16 lanes of a row, then the
+      // activation quantizer's scale and encoder; stage codes and scales, read them back
+      // in the MFMA operand layout (a wave reads only what it wrote itself)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (kb0 + u * kSmallWaves >= kblocks) continue;
+        uint8_t* qb = qstage + (wave * U + u) * RT * kPitch;
+        float* sbuf = sstage + (wave * U + u) * RT;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          if (p * 64 >= chunks) break;
+          const int c = p * 64 + lane;
+          const uint4 v = xc[u][p];
+          const u16x2 mm = __builtin_elementwise_max(__builtin_elementwise_max(mag2(v.x), mag2(v.y)),
+                                                     __builtin_elementwise_max(mag2(v.z), mag2(v.w)));
+          uint32_t mx = max_over_8_lanes(max((uint32_t)mm.x, (uint32_t)mm.y));
+          mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x140, 0xf, 0xf, false));  // row mirror
+          const float scale = scale_from_amax(bf16_bits_to_float(mx), kE4M3Max);
+          const Quantizer qz = make_quantizer(scale);
+          const uint2 code = (qz.xm == 1.0f) ? quant8<false>(v, qz, false) : quant8<false>(v, qz, true);
+          if (c < chunks) {
+            *reinterpret_cast<uint2*>(qb + (c / 16) * kPitch + (c % 16) * 8) = code;
+            if ((c & 15) == 0) sbuf[c / 16] = scale;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = 0; j < WM; ++j) {
+          const int r = 16 * j + (lane & 15);
+          if (r < rows_live) {
+            const uint8_t* src = qb + r * kPitch + q * 32;
+            ft[u][j] = join(*reinterpret_cast<const u32x4*>(src), *reinterpret_cast<const u32x4*>(src + 16));
+            sa[u][j] = sbuf[r];
+          } else {
+            ft[u][j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            sa[u][j] = 0.0f;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
       }
     }
 #pragma unroll
@@ -554,16 +636,35 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
   }
 }
 
-template <int WM>
+template <int WM, bool FUSED = false>
 static hipError_t launch_smallm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                                 int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                                 int64_t k, hipStream_t stream) {
   const int64_t n16 = n / 16;
   const int64_t groups = (m + 16 * WM - 1) / (16 * WM);
-  hipLaunchKernelGGL(gemm_smallm_kernel<WM>, dim3((unsigned)(n16 * groups)), dim3(64 * kSmallWaves), 0, stream,
-                     reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b), ld_b,
-                     b_s, reinterpret_cast<uint16_t*>(y), ld_y, m, n16, (int)(k / 128));
+  hipLaunchKernelGGL((gemm_smallm_kernel<WM, FUSED>), dim3((unsigned)(n16 * groups)), dim3(64 * kSmallWaves), 0,
+                     stream, a, ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b), ld_b, b_s,
+                     reinterpret_cast<uint16_t*>(y), ld_y, m, n16, (int)(k / 128));
   return hipGetLastError();
+}
+
+// Token groups per workgroup for few tokens: 16*WM tokens, WM shrinking (more
+// workgroups, each re-reading its weight rows from L2) until the grid covers every CU.
+template <bool FUSED>
+static hipError_t launch_few_tokens(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
+                                    int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
+                                    int64_t k, hipStream_t stream) {
+  const int64_t n16 = n / 16;
+  if (m > 32 && n16 >= 256)
+    return launch_smallm<4, FUSED>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  if (m > 16 && n16 * ((m + 31) / 32) >= 256)
+    return launch_smallm<2, FUSED>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  return launch_smallm<1, FUSED>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+}
+
+hipError_t launch_gemm_bf16act(const void* x, int64_t ld_x, const void* b, int64_t ld_b, const float* b_s, void* y,
+                               int64_t ld_y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  return launch_few_tokens<true>(x, ld_x, nullptr, 0, b, ld_b, b_s, y, ld_y, m, n, k, stream);
 }
 
 // Tile shape for M > 64 (POW2: the matrix core applies power-of-two block scales).
@@ -589,16 +690,8 @@ hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld
                        int64_t k, bool pow2, hipStream_t stream) {
   if (pow2 && m > 64) return launch_tiles<true>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   // (up to 64 tokens, power-of-two scales take the promotion path below: same result)
-  // few tokens: stream the weights over all CUs.  A workgroup takes 16*WM tokens; WM
-  // shrinks (more workgroups, each re-reading its weight rows from L2) until the grid
-  // covers every CU
-  if (m <= 64) {
-    const int64_t n16 = n / 16;
-    if (m > 32 && n16 >= 256) return launch_smallm<4>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-    if (m > 16 && n16 * ((m + 31) / 32) >= 256)
-      return launch_smallm<2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-    return launch_smallm<1>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-  }
+  // few tokens: stream the weights over all CUs
+  if (m <= 64) return launch_few_tokens<false>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   return launch_tiles<false>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
 }
 

@@ -199,6 +199,21 @@ fp8q_status fp8q_grouped_gemm_w8a8(const void* a, int64_t ld_a, const float* a_s
                                    int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k,
                                    void* stream);
 
+/* fp8q_gemm_w8a8_bf16act: the few-token GEMM with the activation quantization fused into
+ * its operand load [FP8-RL, "Method step details" step 1: activations quantized on every
+ * forward].  x is bf16 [m][ld_x]; each 1x128 group of each row is quantized inside the GEMM
+ * with the quantization rule above, exactly as fp8q_quant_act_g128 would, and y is what
+ * fp8q_gemm_w8a8_blkscaled computes from those codes and scales: the result is bit-identical
+ * to fp8q_quant_act_g128 followed by fp8q_gemm_w8a8_blkscaled.  The quantized activations
+ * are not written anywhere.
+ * 0 <= m <= 64 (decode and short prefill; for more tokens quantize once and call the GEMM:
+ * every workgroup of this kernel quantizes its token rows again); n, k positive multiples
+ * of 128; ld_x >= k with ld_x % 8 == 0; x and y 16-byte aligned; b, b_s, y and their
+ * strides as for fp8q_gemm_w8a8_blkscaled.  m == 0 is a no-op. */
+fp8q_status fp8q_gemm_w8a8_bf16act(const void* x, int64_t ld_x, const void* b, int64_t ld_b,
+                                   const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
+                                   int64_t k, void* stream);
+
 /* The grouped GEMM for power-of-two scales; arguments as fp8q_grouped_gemm_w8a8, scale
  * precondition as fp8q_gemm_w8a8_ue8m0. */
 fp8q_status fp8q_grouped_gemm_w8a8_ue8m0(const void* a, int64_t ld_a, const float* a_s,

@@ -214,3 +214,21 @@ def test_moe_validation():
     assert combine(w=None) == fq.FP8Q_ERR_NULL
     assert combine(ld_out=128) == fq.FP8Q_ERR_STRIDE
     assert combine(out=A16 + 4) == fq.FP8Q_ERR_ALIGN
+
+
+def test_bf16act_gemm_validation():
+    L = fq.lib()
+
+    def g(**kw):
+        a = dict(x=A16, ld_x=256, b=A16, ld_b=256, bs=A16, y=A16, ld_y=128, m=16, n=128, k=256)
+        a.update(kw)
+        return L.fp8q_gemm_w8a8_bf16act(a["x"], a["ld_x"], a["b"], a["ld_b"], a["bs"], a["y"], a["ld_y"], a["m"],
+                                        a["n"], a["k"], None)
+
+    assert g(m=65) == fq.FP8Q_ERR_SHAPE
+    assert g(m=-1) == fq.FP8Q_ERR_SHAPE
+    assert g(k=200, ld_x=200, ld_b=200) == fq.FP8Q_ERR_SHAPE
+    assert g(x=None) == fq.FP8Q_ERR_NULL
+    assert g(ld_x=128) == fq.FP8Q_ERR_STRIDE
+    assert g(ld_x=260) == fq.FP8Q_ERR_ALIGN
+    assert g(x=A16 + 2) == fq.FP8Q_ERR_ALIGN
