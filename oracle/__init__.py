@@ -73,11 +73,15 @@ def lib():
                                       ctypes.c_int32, _i64p, _u8p, _u8p, ctypes.c_int32, _i64,
                                       _f32p, _f32p, ctypes.c_float, ctypes.c_int]
         L.oracle_kv_scales.argtypes = [_u16p, _i64, _u16p, _i64, _i64, _i64, _i64p, ctypes.c_float, _f32p, _f32p]
+        L.oracle_q_scale.argtypes = [_u16p, _i64, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _f32p]
+        L.oracle_paged_decode_attention.argtypes = [_u16p, _i64, _u8p, _u8p, _i32p, _i64, _i32p, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                                    ctypes.c_float, ctypes.c_float, ctypes.c_double, _f64p]
         L.oracle_swiglu_quant_g128.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p, _i64, _f64p]
         L.oracle_silu_times_up.argtypes = [ctypes.c_double, ctypes.c_double]
         L.oracle_silu_times_up.restype = ctypes.c_double
         for f in ("oracle_kv_scales", "oracle_quant_weight_blk128", "oracle_quant_act_g128", "oracle_gemm_w8a8",
-                  "oracle_swiglu_quant_g128",
+                  "oracle_swiglu_quant_g128", "oracle_q_scale", "oracle_paged_decode_attention",
                   "oracle_quant_weight_blk128_ue8m0", "oracle_quant_act_g128_ue8m0",
                   "oracle_grouped_gemm_w8a8", "oracle_kv_quant", "oracle_num_threads"):
             getattr(L, f).restype = ctypes.c_int
@@ -280,4 +284,38 @@ def moe_combine(y_bits: np.ndarray, row_of: np.ndarray, weights: np.ndarray) -> 
     for j in range(topk):
         live = rows[:, j] >= 0
         out[live] += w[live, j][:, None] * yf[rows[live, j]]
+    return out
+
+
+# ---------------------------------------------------------------- FP8 paged decode attention
+# FP8-RL summary page, "Method step details" step 3 (Q/K/V scales recalibrated every RL
+# step) and "Experimental results" (full FP8: linear, KV cache and attention).
+
+def q_scale(q_bits: np.ndarray, rng: float = 448.0) -> np.float32:
+    """Recalibrated query scale fl32(amax / rng) over q bf16 [seqs, hq, 128] (1 if amax is 0)."""
+    q = _u16(q_bits)
+    seqs = q.shape[0]
+    row = int(np.prod(q.shape[1:]))
+    out = np.zeros(1, np.float32)
+    _check(lib().oracle_q_scale(q.reshape(seqs, row), row, seqs, row // 128, float(rng), out), "q_scale")
+    return out[0]
+
+
+def paged_decode_attention(q_bits, k_cache, v_cache, block_table, seq_lens, q_scale_: float, k_scale: float,
+                           v_scale: float, sm_scale: float) -> np.ndarray:
+    """fp64 decode attention of q bf16 [seqs, hq, 128] over FP8 paged caches
+    [pages, page_size, hkv, 128]; block_table int32 [seqs, ld_bt]; seq_lens int32 [seqs].
+    Returns fp64 [seqs, hq, 128]."""
+    q = _u16(q_bits)
+    seqs, hq, d = q.shape
+    kc = np.ascontiguousarray(k_cache, dtype=np.uint8)
+    vc = np.ascontiguousarray(v_cache, dtype=np.uint8)
+    pages, page_size, hkv, _ = kc.shape
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    out = np.zeros((seqs, hq, d), np.float64)
+    _check(lib().oracle_paged_decode_attention(q.reshape(seqs, hq * d), hq * d, kc.reshape(-1), vc.reshape(-1), bt,
+                                               bt.shape[1], sl, seqs, hq, hkv, page_size, float(q_scale_),
+                                               float(k_scale), float(v_scale), float(sm_scale), out),
+           "paged_decode_attention")
     return out

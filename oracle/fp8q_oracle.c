@@ -46,6 +46,8 @@
  *   - SwiGLU before MoE fc2 ([Rounding], SwiGLU fusion region): silu(gate)*up in
  *     fp64, quantized once per 1x128 group with the rule above (scale
  *     fl32(fl64(amax / 448))).
+ *   - FP8 decode attention: the query quantized with its own recalibrated scale,
+ *     FP8 x FP8 scores, softmax and the V sum in fp64 (see below).
  *   - MoE dispatch and combine ([R3]) are integer gathers and an fp64 sum;
  *     they are written in numpy in __init__.py.
  *
@@ -55,6 +57,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #ifdef _OPENMP
@@ -277,6 +280,80 @@ int oracle_swiglu_quant_g128(const uint16_t* h, int64_t m, int64_t n, int64_t ld
 
 /* SiLU(g) * u of one element, as above (exposed for the tests' pins). */
 double oracle_silu_times_up(double g, double u) { return silu_times_up(g, u); }
+
+/* ---- FP8 paged decode attention [FP8-RL, "Method step details" step 3 (per-step
+ * recalibration of the Q/K/V scales) and "Experimental results" (full FP8: linear,
+ * KV cache and attention); 1T-RL 3.4 (paged cache in fixed blocks)] ----
+ * Reading: the query is quantized to E4M3 with its own per-layer scale (the same rule
+ * as K and V: scale = fl32(amax / range) over the call's queries when recalibrating),
+ * scores are the FP8 x FP8 products s = sm_scale * q_scale * k_scale * sum_d
+ * dec(cq[d]) * dec(ck[t][d]), p = softmax over the sequence's L tokens, and
+ * out[d] = v_scale * sum_t p_t * dec(cv[t][d]).  Everything after the codes in fp64.
+ * Query head h reads KV head h / (hq / hkv).  Token t of sequence b sits in page
+ * block_table[b*ld_bt + t / page_size], slot t % page_size; caches are
+ * [page][slot][hkv][128] bytes.  q: bf16 [seqs][hq][128] rows with pitch ld_q per
+ * sequence; out: fp64 [seqs][hq][128]. */
+int oracle_q_scale(const uint16_t* q, int64_t ld_q, int32_t seqs, int32_t hq, float range, float* q_scale) {
+  float amax = 0.0f;
+  for (int32_t b = 0; b < seqs; ++b)
+    for (int64_t i = 0; i < (int64_t)hq * 128; ++i) {
+      float v = bf16_to_float(q[b * ld_q + i]);
+      if (!isfinite(v)) return -1;
+      if (fabsf(v) > amax) amax = fabsf(v);
+    }
+  *q_scale = oracle_scale(amax, range);
+  return 0;
+}
+
+int oracle_paged_decode_attention(const uint16_t* q, int64_t ld_q, const uint8_t* kc, const uint8_t* vc,
+                                  const int32_t* block_table, int64_t ld_bt, const int32_t* seq_lens, int32_t seqs,
+                                  int32_t hq, int32_t hkv, int32_t page_size, float q_scale, float k_scale,
+                                  float v_scale, double sm_scale, double* out) {
+  if (seqs < 0 || hq < 1 || hkv < 1 || hq % hkv || page_size < 1) return -2;
+  const int32_t group = hq / hkv;
+  int bad = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic) reduction(| : bad)
+  for (int32_t b = 0; b < seqs; ++b) {
+    for (int32_t h = 0; h < hq; ++h) {
+      const int32_t L = seq_lens[b];
+      const int32_t g = h / group;
+      double* o = out + ((int64_t)b * hq + h) * 128;
+      for (int d = 0; d < 128; ++d) o[d] = 0.0;
+      if (L <= 0) continue;
+      double cq[128];
+      for (int d = 0; d < 128; ++d) {
+        float x = bf16_to_float(q[b * ld_q + (int64_t)h * 128 + d]);
+        if (!isfinite(x)) bad = 1;
+        cq[d] = oracle_e4m3_decode(oracle_quantize_value(x, q_scale));
+      }
+      double* sc = (double*)malloc(sizeof(double) * (size_t)L);
+      const double f = sm_scale * (double)q_scale * (double)k_scale;
+      double mx = -INFINITY;
+      for (int32_t t = 0; t < L; ++t) {
+        const int64_t page = block_table[(int64_t)b * ld_bt + t / page_size];
+        const uint8_t* k = kc + ((page * page_size + t % page_size) * hkv + g) * 128;
+        double dot = 0.0;
+        for (int d = 0; d < 128; ++d) dot += cq[d] * oracle_e4m3_decode(k[d]);
+        sc[t] = f * dot;
+        if (sc[t] > mx) mx = sc[t];
+      }
+      double z = 0.0;
+      for (int32_t t = 0; t < L; ++t) {
+        sc[t] = exp(sc[t] - mx);
+        z += sc[t];
+      }
+      for (int32_t t = 0; t < L; ++t) {
+        const int64_t page = block_table[(int64_t)b * ld_bt + t / page_size];
+        const uint8_t* v = vc + ((page * page_size + t % page_size) * hkv + g) * 128;
+        const double p = sc[t] / z;
+        for (int d = 0; d < 128; ++d) o[d] += p * oracle_e4m3_decode(v[d]);
+      }
+      for (int d = 0; d < 128; ++d) o[d] *= (double)v_scale;
+      free(sc);
+    }
+  }
+  return bad ? -1 : 0;
+}
 
 /* ---- a3: block-scaled W8A8 GEMM [FP8-RL, step 1; Rounding] ----
  * y[i][j] = sum_kb (sa[kb][i] * sb[j/128][kb]) * sum_{t in kb} dec(a[i][t]) dec(b[j][t])
