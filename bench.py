@@ -530,6 +530,8 @@ def _time(torch, fn, iters, warm=2, reps=10):
 
 def legs(torch, fq, synth, dev):
     """Side measurements of the other hot-path workloads (not part of `value`)."""
+    import numpy as np
+
     res = {}
     # full weight sync: 36 layers x {q, k, v, o, gate, up, down}
     log("leg: 36-layer weight sync")
@@ -662,7 +664,28 @@ def legs(torch, fq, synth, dev):
     kd, vd, sd = k[dec_idx].contiguous(), v[dec_idx].contiguous(), sl[dec_idx].contiguous()
     ms = _time(torch, lambda: fq.fp8q_kv_quant(kd, vd, sd, kc, vc, ks, vs, 448.0, recalibrate=False), 20)
     res["a6_kv_decode_write_64_tokens"] = {"us": round(ms * 1e3, 2)}
-    del k, v, kc, vc
+
+    # FP8 decode attention over the layer's cache just written: 64 sequences x 20,000
+    # tokens, 32 query heads on 8 KV heads, one query per sequence; with and without the
+    # query-scale recalibration
+    log("leg: FP8 paged decode attention")
+    hq = 32
+    seqs = 64
+    bt = torch.from_numpy((slots_np.reshape(seqs, -1)[:, ::16] // 16).astype(np.int32)).to(dev)
+    lens = torch.full((seqs,), T // seqs, dtype=torch.int32, device=dev)
+    qd = synth.device_activation(seqs, hq * 128, dev, 5, 0, 50).view(seqs, hq, 128)
+    od = torch.empty((seqs, hq, 128), dtype=torch.bfloat16, device=dev)
+    qsc = torch.ones(1, device=dev)
+    att = lambda recal: fq.fp8q_paged_decode_attention(qd, kc, vc, bt, lens, qsc, ks, vs, 128 ** -0.5, od,
+                                                       recalibrate_q=recal)
+    ms_r = _time(torch, lambda: att(True), 10)
+    ms_s = _time(torch, lambda: att(False), 10)
+    by = 2 * T * 8 * 128 + 2 * 2 * seqs * hq * 128 + 4 * bt.numel() + 4 * seqs
+    res["f3_decode_attention_layer"] = {
+        "seqs": seqs, "context": T // seqs, "q_heads": hq, "kv_heads": 8,
+        "us": round(ms_s * 1e3, 1), "us_with_q_recalibration": round(ms_r * 1e3, 1),
+        "GBps": round(by / (ms_s * 1e-3) / 1e9, 1), "frac_hbm": round(by / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del k, v, kc, vc, qd, od
     torch.cuda.empty_cache()
 
     # power-of-two (UE8M0) scale variant of the attention block's calls: quantizers and

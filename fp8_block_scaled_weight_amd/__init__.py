@@ -28,13 +28,14 @@ FP8Q_ERR_ALIGN = 4
 FP8Q_ERR_LAUNCH = 5
 FP8Q_ERR_UNSUPPORTED = 6
 FP8Q_KV_RECALIBRATE = 1
+FP8Q_ATTN_RECALIBRATE_Q = 1
 
 EXPORTED = (
     "fp8q_status_string", "fp8q_last_error", "fp8q_abi_version", "fp8q_quant_weight_blk128",
     "fp8q_quant_act_g128", "fp8q_gemm_w8a8_blkscaled", "fp8q_grouped_gemm_w8a8", "fp8q_kv_quant",
     "fp8q_quant_weight_blk128_ue8m0", "fp8q_quant_act_g128_ue8m0", "fp8q_gemm_w8a8_ue8m0",
     "fp8q_grouped_gemm_w8a8_ue8m0", "fp8q_moe_dispatch", "fp8q_swiglu_quant_g128", "fp8q_moe_combine",
-    "fp8q_gemm_w8a8_bf16act",
+    "fp8q_gemm_w8a8_bf16act", "fp8q_paged_decode_attention",
 )
 
 
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
                                                                    i64, i64, vp]
         L.fp8q_gemm_w8a8_blkscaled.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp]
         L.fp8q_gemm_w8a8_ue8m0.argtypes = L.fp8q_gemm_w8a8_blkscaled.argtypes
+        L.fp8q_paged_decode_attention.argtypes = [vp, i64, vp, vp, vp, i64, vp, i32, i32, i32, i32, i32, i64, vp,
+                                                  vp, vp, f32, f32, u32, vp, i64, vp]
         L.fp8q_gemm_w8a8_bf16act.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp]
         L.fp8q_kv_quant.argtypes = [vp, i64, vp, i64, i64, i32, i32, vp, vp, vp, i32, i64, vp, vp, f32, u32, vp]
         L.fp8q_moe_dispatch.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i64, vp, i64, vp, i64, vp, vp, vp]
@@ -302,3 +305,29 @@ def fp8q_moe_combine(y: torch.Tensor, row_of: torch.Tensor, weights: torch.Tenso
     _check(lib().fp8q_moe_combine(_dev(y, "y", BF16), _rows(y, "y"), _dev(row_of, "row_of", (torch.int32,)),
                                   _dev(weights, "weights", F32), t, topk, hidden, _dev(out, "out", BF16),
                                   _rows(out, "out"), _stream(stream)), "fp8q_moe_combine")
+
+
+def fp8q_paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_table: torch.Tensor, seq_lens: torch.Tensor, q_scale: torch.Tensor,
+                                k_scale: torch.Tensor, v_scale: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                                recalibrate_q: bool = False, fp8_range: float = 448.0, stream=None) -> None:
+    """FP8 decode attention: q [S, H, 128] bf16 over caches [P, page, Hkv, 128] fp8 with block_table
+    [S, ld_bt] int32 and seq_lens [S] int32 -> out [S, H, 128] bf16.  recalibrate_q first sets
+    q_scale from the queries."""
+    seqs, hq, hd = q.shape
+    pages, page_size, hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or not k_cache.is_contiguous() or not v_cache.is_contiguous():
+        raise ValueError("caches must be contiguous [pages, page_size, heads, head_dim] of one shape")
+    if q.stride(2) != 1 or q.stride(1) != hd or out.stride(2) != 1 or out.stride(1) != hd:
+        raise ValueError("q/out rows must be contiguous over (heads, head_dim)")
+    if tuple(out.shape) != (seqs, hq, hd) or block_table.dim() != 2 or block_table.shape[0] != seqs:
+        raise ValueError("out must be [S, H, 128] and block_table [S, ld_bt]")
+    if block_table.stride(1) != 1 or not seq_lens.is_contiguous():
+        raise ValueError("block_table rows and seq_lens must be contiguous")
+    _check(lib().fp8q_paged_decode_attention(
+        _dev(q, "q", BF16), q.stride(0), _dev(k_cache, "k_cache", FP8), _dev(v_cache, "v_cache", FP8),
+        _dev(block_table, "block_table", (torch.int32,)), block_table.stride(0),
+        _dev(seq_lens, "seq_lens", (torch.int32,)), seqs, hq, hkv, hd, page_size, pages,
+        _dev(q_scale, "q_scale", F32), _dev(k_scale, "k_scale", F32), _dev(v_scale, "v_scale", F32),
+        float(sm_scale), float(fp8_range), FP8Q_ATTN_RECALIBRATE_Q if recalibrate_q else 0,
+        _dev(out, "out", BF16), out.stride(0), _stream(stream)), "fp8q_paged_decode_attention")

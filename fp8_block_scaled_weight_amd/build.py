@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfp8q.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quant.hip", "kv_quant.hip", "gemm.hip", "moe.hip"]
+SOURCES = ["api.cpp", "quant.hip", "kv_quant.hip", "gemm.hip", "moe.hip", "attention.hip"]
 
 # No fast-math: fp32 division and the residual FMA must be IEEE; denormals are kept.
 # Packed fp32 instructions are disabled for all device code.

@@ -365,4 +365,39 @@ fp8q_status fp8q_moe_combine(const void* y, int64_t ld_y, const int32_t* row_of,
                   "moe_combine");
 }
 
+fp8q_status fp8q_paged_decode_attention(const void* q, int64_t ld_q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_table, int64_t ld_bt, const int32_t* seq_lens,
+                                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t page_size, int64_t num_pages, float* q_scale,
+                                        const float* k_scale, const float* v_scale, float sm_scale,
+                                        float fp8_range, uint32_t flags, void* out, int64_t ld_out, void* stream) {
+  if (num_seqs < 0 || num_pages < 0) return fail(FP8Q_ERR_SHAPE, "negative shape");
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads || num_q_heads / num_kv_heads > 16)
+    return fail(FP8Q_ERR_SHAPE, "num_q_heads must be a multiple of num_kv_heads, at most 16 times it");
+  if (head_dim != 128) return fail(FP8Q_ERR_SHAPE, "head_dim must be 128 (got %d)", head_dim);
+  if (page_size < 1) return fail(FP8Q_ERR_SHAPE, "page_size must be >= 1");
+  if (flags & ~FP8Q_ATTN_RECALIBRATE_Q) return fail(FP8Q_ERR_SHAPE, "unknown flag bits 0x%x", flags);
+  if (!(fp8_range > 0.0f) || fp8_range > 3.4e38f) return fail(FP8Q_ERR_SHAPE, "fp8_range must be positive and finite");
+  if (!(sm_scale == sm_scale) || sm_scale > 3.4e38f || sm_scale < -3.4e38f)
+    return fail(FP8Q_ERR_SHAPE, "sm_scale must be finite");
+  if (!q_scale || !k_scale || !v_scale) return fail(FP8Q_ERR_NULL, "q_scale/k_scale/v_scale is NULL");
+  const int64_t row = (int64_t)num_q_heads * 128;
+  if (num_seqs > 0) {
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return fail(FP8Q_ERR_NULL, "NULL pointer");
+    if (ld_q < row || ld_out < row || ld_bt < 1) return fail(FP8Q_ERR_STRIDE, "ld_q/ld_out < heads*128 or ld_bt < 1");
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache) || ld_q % 8 || ld_out % 8 ||
+        !aligned4(block_table) || !aligned4(seq_lens) || !aligned4(q_scale) || !aligned4(k_scale) ||
+        !aligned4(v_scale))
+      return fail(FP8Q_ERR_ALIGN, "q/out/caches must be 16-byte aligned with ld_q, ld_out multiples of 8");
+  }
+  fp8q_status st = check_device();
+  if (st != FP8Q_OK) return st;
+  if (num_seqs == 0 && !(flags & FP8Q_ATTN_RECALIBRATE_Q)) return ok();
+  return launched(fp8q::launch_decode_attention(q, ld_q, k_cache, v_cache, block_table, ld_bt, seq_lens, num_seqs,
+                                                num_q_heads, num_kv_heads, page_size, q_scale, k_scale, v_scale,
+                                                sm_scale, fp8_range, (flags & FP8Q_ATTN_RECALIBRATE_Q) != 0, out,
+                                                ld_out, reinterpret_cast<hipStream_t>(stream)),
+                  "paged_decode_attention");
+}
+
 }  // extern "C"

@@ -176,6 +176,13 @@ __device__ __forceinline__ uint32_t absmax16(uint4 a, uint4 b) {
   return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
+// Largest |x| of 8 bf16 values as magnitude bits.
+__device__ __forceinline__ uint32_t absmax8(uint4 a) {
+  const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(mag2(a.x), mag2(a.y)),
+                                            __builtin_elementwise_max(mag2(a.z), mag2(a.w)));
+  return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
 // Max over groups of 8 consecutive lanes (DPP: quad swaps then half-row mirror).
 __device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));  // [1,0,3,2]

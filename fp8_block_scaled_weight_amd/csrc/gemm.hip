@@ -576,9 +576,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
           if (p * 64 >= chunks) break;
           const int c = p * 64 + lane;
           const uint4 v = xc[u][p];
-          const u16x2 mm = __builtin_elementwise_max(__builtin_elementwise_max(mag2(v.x), mag2(v.y)),
-                                                     __builtin_elementwise_max(mag2(v.z), mag2(v.w)));
-          uint32_t mx = max_over_8_lanes(max((uint32_t)mm.x, (uint32_t)mm.y));
+          uint32_t mx = max_over_8_lanes(absmax8(v));
           mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x140, 0xf, 0xf, false));  // row mirror
           const float scale = scale_from_amax(bf16_bits_to_float(mx), kE4M3Max);
           const Quantizer qz = make_quantizer(scale);

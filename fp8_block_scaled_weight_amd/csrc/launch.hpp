@@ -54,4 +54,9 @@ hipError_t launch_swiglu_quant(const void* h, int64_t m, int64_t n, int64_t ld_h
                                int64_t ld_s, hipStream_t stream);
 hipError_t launch_moe_combine(const void* y, int64_t ld_y, const int32_t* row_of, const float* w, int64_t tokens,
                               int32_t topk, int64_t hidden, void* out, int64_t ld_out, hipStream_t stream);
+hipError_t launch_decode_attention(const void* q, int64_t ld_q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, int64_t ld_bt, const int32_t* seq_lens, int32_t seqs,
+                                   int32_t hq, int32_t hkv, int32_t page_size, float* q_scale, const float* k_scale,
+                                   const float* v_scale, float sm_scale, float range, bool recalibrate, void* out,
+                                   int64_t ld_out, hipStream_t stream);
 }  // namespace fp8q

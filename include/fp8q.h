@@ -7,7 +7,9 @@
  *   - the block-scaled W8A8 GEMM that consumes both, dense and MoE-grouped;
  *   - FP8 KV-cache quantize-on-write with per-step K/V scale recalibration;
  *   - around the grouped GEMM: MoE dispatch by recorded expert ids, SwiGLU fused with
- *     fc2's 1x128 quantization, and the weighted combine.
+ *     fc2's 1x128 quantization, and the weighted combine;
+ *   - FP8 paged decode attention over that cache, with the query scale recalibrated
+ *     per step.
  *
  * Sources (page title, then section):
  *   [FP8-RL]   "FP8-RL: A Practical and Stable Low-Precision Stack for LLM Reinforcement
@@ -251,6 +253,42 @@ fp8q_status fp8q_kv_quant(const void* k, int64_t ld_k, const void* v, int64_t ld
                           const int64_t* slot_mapping, void* k_cache, void* v_cache,
                           int32_t page_size, int64_t num_pages, float* k_scale, float* v_scale,
                           float fp8_range, uint32_t flags, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * FP8 paged decode attention with per-step query-scale recalibration  [FP8-RL, "Method
+ * step details" step 3 (Q/K/V scales recalibrated before every RL step's rollout) and
+ * "Experimental results" (full FP8: linear layers, KV cache and attention); 1T-RL, 3.4]
+ *
+ * One decode query per sequence b and query head h; h reads KV head h / (H / Hkv).
+ * The context of sequence b is its tokens t < seq_lens[b], token t in page
+ * block_table[b * ld_bt + t / page_size], slot t % page_size, of caches laid out as
+ * fp8q_kv_quant writes them (e4m3fn [num_pages][page_size][Hkv][128]).
+ *   cq[d]  = E4M3 code of q[b][h][d] / *q_scale (the quantization rule above, saturating);
+ *   s_t    = sm_scale * q_scale * k_scale * sum_d dec(cq[d]) * dec(ck[t][d]);
+ *   out[d] = bf16( v_scale * sum_t softmax(s)_t * dec(cv[t][d]) ), softmax and sums in fp32.
+ * q: bf16 [num_seqs][ld_q], the H query heads of a sequence contiguous (ld_q >= H*128,
+ * ld_q % 8 == 0); out: bf16 [num_seqs][ld_out], same layout.  seq_lens: int32 [num_seqs];
+ * a sequence with length <= 0 gets a zero output.  block_table: int32 [num_seqs][ld_bt].
+ * q_scale, k_scale, v_scale: one fp32 each (device); k_scale and v_scale are the cache's
+ * (fp8q_kv_quant's), positive and finite.
+ * flags & FP8Q_ATTN_RECALIBRATE_Q: first set *q_scale = fl32(amax / fp8_range) over all
+ *   num_seqs * H * 128 query values (1.0 if amax == 0), then attend with it (the first
+ *   decode step of an RL step); flags == 0: use the stored *q_scale, which must be
+ *   positive and finite (query values beyond its range saturate to +-448 codes).
+ * head_dim == 128; 1 <= H / Hkv <= 16 with H a multiple of Hkv; page_size >= 1;
+ * q, out and the caches 16-byte aligned.  Preconditions not checked: every page id is
+ * below num_pages and every length at most ld_bt * page_size.
+ * ---------------------------------------------------------------------------- */
+#define FP8Q_ATTN_RECALIBRATE_Q 1u
+
+fp8q_status fp8q_paged_decode_attention(const void* q, int64_t ld_q, const void* k_cache,
+                                        const void* v_cache, const int32_t* block_table,
+                                        int64_t ld_bt, const int32_t* seq_lens, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t page_size, int64_t num_pages, float* q_scale,
+                                        const float* k_scale, const float* v_scale, float sm_scale,
+                                        float fp8_range, uint32_t flags, void* out, int64_t ld_out,
+                                        void* stream);
 
 /* ------------------------------------------------------------------------------
  * MoE layer around the grouped GEMM  [R3, "Rollout Routing Replay" and the cost

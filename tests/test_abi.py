@@ -232,3 +232,30 @@ def test_bf16act_gemm_validation():
     assert g(ld_x=128) == fq.FP8Q_ERR_STRIDE
     assert g(ld_x=260) == fq.FP8Q_ERR_ALIGN
     assert g(x=A16 + 2) == fq.FP8Q_ERR_ALIGN
+
+
+def test_decode_attention_validation():
+    L = fq.lib()
+
+    def att(**kw):
+        a = dict(q=A16, ld_q=1024, kc=A16, vc=A16, bt=A16, ld_bt=4, sl=A16, seqs=2, hq=8, hkv=2, d=128, ps=16,
+                 pages=8, qs=A16, ks=A16, vs=A16, sm=0.088, rng=448.0, flags=1, out=A16, ld_out=1024)
+        a.update(kw)
+        return L.fp8q_paged_decode_attention(a["q"], a["ld_q"], a["kc"], a["vc"], a["bt"], a["ld_bt"], a["sl"],
+                                             a["seqs"], a["hq"], a["hkv"], a["d"], a["ps"], a["pages"], a["qs"],
+                                             a["ks"], a["vs"], a["sm"], a["rng"], a["flags"], a["out"], a["ld_out"],
+                                             None)
+
+    assert att(hq=6, hkv=4) == fq.FP8Q_ERR_SHAPE          # not a multiple
+    assert att(hq=34, hkv=2) == fq.FP8Q_ERR_SHAPE         # group of 17
+    assert att(d=64) == fq.FP8Q_ERR_SHAPE
+    assert att(ps=0) == fq.FP8Q_ERR_SHAPE
+    assert att(flags=2) == fq.FP8Q_ERR_SHAPE
+    assert att(rng=0.0) == fq.FP8Q_ERR_SHAPE
+    assert att(sm=float("nan")) == fq.FP8Q_ERR_SHAPE
+    assert att(qs=None) == fq.FP8Q_ERR_NULL
+    assert att(bt=None) == fq.FP8Q_ERR_NULL
+    assert att(ld_q=512) == fq.FP8Q_ERR_STRIDE
+    assert att(ld_bt=0) == fq.FP8Q_ERR_STRIDE
+    assert att(kc=A16 + 8) == fq.FP8Q_ERR_ALIGN
+    assert att(ld_out=1028) == fq.FP8Q_ERR_ALIGN
