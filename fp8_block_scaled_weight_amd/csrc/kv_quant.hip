@@ -22,6 +22,7 @@ constexpr int kKvBlock = 256;                 // encode pass: 4 waves
 constexpr int kKvAmaxBlock = 1024;            // amax pass: 16 waves
 constexpr int kElemsPerWavePass = 64 * 16;    // 64 lanes x 16 bf16
 constexpr uint32_t kMarked = 0x80000000u;
+constexpr int kKvTokensInFlight = 2;          // encode pass: token rows loaded together per wave
 
 __global__ void kv_reset_kernel(float* k_scale, float* v_scale) {
   if (threadIdx.x == 0) {
@@ -49,8 +50,8 @@ __global__ __launch_bounds__(kKvAmaxBlock) void kv_amax_kernel(const uint16_t* _
     for (int64_t e = lane * 16; e < row; e += kElemsPerWavePass) {
       const uint4* pk = reinterpret_cast<const uint4*>(k + t * ld_k + e);
       const uint4* pv = reinterpret_cast<const uint4*>(v + t * ld_v + e);
-      mk = max(mk, absmax16(load_stream(pk), load_stream(pk + 1)));
-      mv = max(mv, absmax16(load_stream(pv), load_stream(pv + 1)));
+      mk = max(mk, absmax16(load_plain(pk), load_plain(pk + 1)));
+      mv = max(mv, absmax16(load_plain(pv), load_plain(pv + 1)));
     }
   };
   int64_t t = (int64_t)blockIdx.x * W + wave;
@@ -83,7 +84,8 @@ __device__ __forceinline__ float resolve_scale(uint32_t bits, float range) {
   return (bits & kMarked) ? scale_from_amax(__uint_as_float(bits & ~kMarked), range) : __uint_as_float(bits);
 }
 
-// One wave per token: K row then V row, 16 elements per lane per pass.
+// One wave per token: K row then V row, 16 elements per lane per pass.  Loads are
+// non-temporal here (measured faster for this pass), plain in the amax pass.
 __global__ __launch_bounds__(kKvBlock) void kv_write_kernel(const uint16_t* __restrict__ k, int64_t ld_k,
                                                             const uint16_t* __restrict__ v, int64_t ld_v,
                                                             int64_t tokens, int64_t row,
@@ -101,18 +103,32 @@ __global__ __launch_bounds__(kKvBlock) void kv_write_kernel(const uint16_t* __re
   }
   const Quantizer qk = make_quantizer(sk);
   const Quantizer qv = make_quantizer(sv);
-  for (int64_t t = (int64_t)blockIdx.x * (kKvBlock / 64) + wave; t < tokens; t += waves) {
-    const int64_t slot = slots[t];
-    if (slot < 0) continue;
+  // kKvTokensInFlight tokens per wave: every row's loads are issued before any is encoded
+  constexpr int NT = kKvTokensInFlight;
+  for (int64_t t0 = (int64_t)blockIdx.x * (kKvBlock / 64) + wave; t0 < tokens; t0 += NT * waves) {
+    int64_t sl[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) sl[u] = (t0 + u * waves < tokens) ? slots[t0 + u * waves] : -1;
     for (int64_t e = lane * 16; e < row; e += kElemsPerWavePass) {
-      const uint4* pk = reinterpret_cast<const uint4*>(k + t * ld_k + e);
-      const uint4* pv = reinterpret_cast<const uint4*>(v + t * ld_v + e);
-      uint4 ka = load_stream(pk), kb = load_stream(pk + 1);
-      uint4 va = load_stream(pv), vb = load_stream(pv + 1);
-      uint4 ok = quant16<true>(ka, kb, qk);
-      uint4 ov = quant16<true>(va, vb, qv);
-      store_stream(kc + slot * row + e, ok);
-      store_stream(vc + slot * row + e, ov);
+      uint4 x[NT][4];
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        if (sl[u] >= 0) {  // uniform per wave
+          const int64_t t = t0 + u * waves;
+          const uint4* pk = reinterpret_cast<const uint4*>(k + t * ld_k + e);
+          const uint4* pv = reinterpret_cast<const uint4*>(v + t * ld_v + e);
+          x[u][0] = load_stream(pk);
+          x[u][1] = load_stream(pk + 1);
+          x[u][2] = load_stream(pv);
+          x[u][3] = load_stream(pv + 1);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        if (sl[u] < 0) continue;
+        store_stream(kc + sl[u] * row + e, quant16<true>(x[u][0], x[u][1], qk));
+        store_stream(vc + sl[u] * row + e, quant16<true>(x[u][2], x[u][3], qv));
+      }
     }
   }
 }
