@@ -23,8 +23,8 @@ namespace fp8q {
 // Pass 2 hands the entries of e, in f order, consecutive rows: row_of[f] = row.
 // Workgroup 0 also marks invalid entries (id < 0 or id >= E) with row -1.
 // ----------------------------------------------------------------------------
-constexpr int kRouteThreads = 512;
-constexpr int kRoutePer = 64;  // ids per thread and pass chunk: eight 16-byte loads
+constexpr int kRouteThreads = 1024;
+constexpr int kRoutePer = 32;  // ids per thread and pass chunk: four 16-byte loads
 
 // ids [f0, f0 + 64) of this thread (entries at or past n read as -1)
 __device__ __forceinline__ void load_ids(const int16_t* __restrict__ ids, int64_t n, int64_t f0,
