@@ -55,6 +55,9 @@ def parse():
                    help="no GPU: matrix-core utilisation of the GEMM kernels from a rocprofv3 --pmc run of "
                         "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY SQ_INSTS_MFMA "
                         "SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS GRBM_GUI_ACTIVE")
+    p.add_argument("--vendor-reference", action="store_true",
+                   help="only time the vendor library's plain per-tensor-scaled FP8 GEMM (torch._scaled_mm) and "
+                        "the bf16 matmul at the dense GEMM shapes, as context for the block-scaled GEMM's rate")
     p.add_argument("--summarize-trace", nargs="+", metavar="TRACE_DIR [BENCH_JSON]",
                    help="no GPU: per-kernel table from a rocprofv3 --kernel-trace --stats output directory "
                         "(optionally with the JSON line of a bench.py run of the same source)")
@@ -289,6 +292,28 @@ def summarize_trace(d, bench_json=None):
     print("\n".join(md))
 
 
+def vendor_reference():
+    """Context only: the vendor library's plain FP8 GEMM (one scale per tensor, no blocks,
+    no promotion) and the bf16 matmul at the dense shapes, timed like the legs."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    res = {}
+    for m, n, k in ((4096, 4096, 4096), (4096, 1024, 4096), (4096, 12288, 4096), (4096, 4096, 16384)):
+        x = torch.randn(m, k, device=dev).to(torch.float8_e4m3fn)
+        w = torch.randn(n, k, device=dev).to(torch.float8_e4m3fn)
+        one = torch.tensor(1.0, device=dev)
+        ms8 = _time(torch, lambda: torch._scaled_mm(x, w.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16), 20)
+        xb = torch.randn(m, k, device=dev, dtype=torch.bfloat16)
+        wb = torch.randn(n, k, device=dev, dtype=torch.bfloat16)
+        msb = _time(torch, lambda: xb @ wb.t(), 20)
+        f = 2 * m * n * k
+        res[f"{m}x{n}x{k}"] = {"fp8_per_tensor_us": round(ms8 * 1e3, 1),
+                               "fp8_per_tensor_TFLOPs": round(f / (ms8 * 1e-3) / 1e12, 1),
+                               "bf16_us": round(msb * 1e3, 1), "bf16_TFLOPs": round(f / (msb * 1e-3) / 1e12, 1)}
+    print(json.dumps({"vendor_reference": res}))
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -299,6 +324,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)
+        return
+    if args.vendor_reference:
+        vendor_reference()
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
@@ -735,6 +763,24 @@ def legs(torch, fq, synth, dev):
             tf = f / (ms * 1e-3) / 1e12
             res[f"a3_gemm_m{m}_n{n}"] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 2),
                                          "frac_roofline": round(tf / ceil, 4)}
+
+    # dense MLP GEMMs: gate/up (4096 -> 12288) and down (12288 -> 4096) at 64 and 4096 tokens
+    log("leg: MLP GEMMs")
+    for name, n, k in (("gate_up", 12288, 4096), ("down", 4096, 12288)):
+        b = torch.randint(0, 0x77, (n, k), dtype=torch.uint8, device=dev)
+        bsc = torch.rand((n // 128, k // 128), device=dev)
+        for m in (64, 4096):
+            a = torch.randint(0, 0x77, (m, k), dtype=torch.uint8, device=dev)
+            asc = torch.rand((k // 128, m), device=dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            ms = _time(torch, lambda: fq.fp8q_gemm_w8a8_blkscaled(a, asc, b, bsc, y), 10)
+            f = 2 * m * n * k
+            by = m * k + n * k + 2 * m * n
+            ceil = min(FP8_PEAK_TFLOPS, f / by * HBM_PEAK_GBPS / 1e3)
+            tf = f / (ms * 1e-3) / 1e12
+            res[f"a3_mlp_{name}_m{m}"] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
+                                          "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+                                          "frac_roofline": round(tf / ceil, 4)}
 
     # few tokens: activation quantization fused into the GEMM's operand load, against the
     # activation quantizer followed by the GEMM (both as one graph of calls)
