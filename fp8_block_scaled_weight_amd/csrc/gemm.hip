@@ -490,8 +490,10 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
     const void* __restrict__ a_, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
     const uint8_t* __restrict__ b, int64_t ld_b, const float* __restrict__ bs, uint16_t* __restrict__ y,
     int64_t ld_y, int64_t m, int64_t n16, int kblocks) {
-  // K blocks in flight per wave (register budget permitting)
-  constexpr int U = FUSED ? (WM >= 4 ? 1 : (WM == 2 ? 2 : 4)) : (WM >= 4 ? 2 : 4);
+  // K blocks per wave per loop trip.  Measured at N = 4096 and 12288, K = 4096: one block
+  // per trip is fastest (the extra registers of a deeper unroll cost more in occupancy than
+  // the extra loads in flight gain), except for the 32-token tile of FP8 tokens, where two are.
+  constexpr int U = (!FUSED && WM == 2) ? 2 : 1;
   constexpr int RT = 16 * WM;   // token rows of the tile
   constexpr int kPitch = 144;   // staged code row pitch (bytes)
   __shared__ v4f part[kSmallWaves][WM][64];
