@@ -468,10 +468,15 @@ static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, in
 // ----------------------------------------------------------------------------
 // Few tokens (decode, short prefill): the GEMM streams the weight matrix once and is
 // HBM-bound, so it is spread over as many CUs as possible.  A workgroup owns 16 weight
-// rows and up to 16*WM token rows; its 8 waves take the K blocks round-robin and load
-// their fragments straight into registers (weights read once, with a non-temporal
-// hint; token rows come from L2).  The 8 partial sums are added through LDS in a fixed
-// order, so the result does not depend on timing.
+// rows and up to 16*WM token rows; its 8 waves take the K blocks round-robin.  For each
+// K block a wave loads the 16 weight rows (non-temporal) and its live token rows (from
+// L2) with 8 lanes per 128-byte line, writes them to its own LDS stage and reads them
+// back in the MFMA operand layout, while the loads of its next K block are in flight.
+// (Fragment loads straight from memory make every 16-lane quarter-wave touch 16 lines;
+// measured on these shapes they move the same bytes about 1.6x slower.)  A stage row is
+// 128 bytes with 16-byte chunk c of row r at c ^ (r & 7), so the row-wise writes and the
+// fragment reads are both free of bank conflicts.  The 8 partial sums are added through
+// LDS in a fixed order, so the result does not depend on timing.
 //
 // FUSED: the token rows arrive as bf16 and are quantized where they are loaded (FP8-RL
 // summary page, "Method step details" step 1: activations are quantized dynamically on
@@ -479,152 +484,153 @@ static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, in
 // values each of the K block's 128-wide group, the group amax is the maximum over those
 // 16 lanes, and the scale and codes follow the activation quantizer's rule with the same
 // encoder, so the MFMA sees exactly the codes and scales a separate quantization would
-// produce.  The wave stages the codes and scales in LDS (144-byte row pitch, so the 16
-// rows read at one offset fall in distinct banks) and reads them back in the MFMA
-// operand layout.
+// produce.  The codes go to the same stage rows, the scales beside them.
 // ----------------------------------------------------------------------------
 constexpr int kSmallWaves = 8;
 
-template <int WM, bool FUSED>
+// byte offset of 16-byte chunk c of row r in a stage
+__device__ __forceinline__ int stage_at(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+
+template <int WM, bool FUSED, int D>
 __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
     const void* __restrict__ a_, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
     const uint8_t* __restrict__ b, int64_t ld_b, const float* __restrict__ bs, uint16_t* __restrict__ y,
     int64_t ld_y, int64_t m, int64_t n16, int kblocks) {
-  // K blocks per wave per loop trip.  Measured at N = 4096 and 12288, K = 4096: one block
-  // per trip is fastest (the extra registers of a deeper unroll cost more in occupancy than
-  // the extra loads in flight gain), except for the 32-token tile of FP8 tokens, where two are.
-  constexpr int U = (!FUSED && WM == 2) ? 2 : 1;
-  constexpr int RT = 16 * WM;   // token rows of the tile
-  constexpr int kPitch = 144;   // staged code row pitch (bytes)
-  __shared__ v4f part[kSmallWaves][WM][64];
-  __shared__ __align__(16) uint8_t qstage[FUSED ? kSmallWaves * U * RT * kPitch : 16];
-  __shared__ float sstage[FUSED ? kSmallWaves * U * RT : 1];
+  constexpr int RT = 16 * WM;                                    // token rows of the tile
+  constexpr int kStage = (16 + RT) * 128 + (FUSED ? RT * 4 : 0);  // weight rows, token rows, scales
+  constexpr int TP = RT / 8;                                     // row-wise token loads per lane
+  constexpr int P = 4 * WM;                                      // FUSED: 64-lane passes over a tile's chunks
+  static_assert(kStage >= WM * 64 * 16, "the partial sums reuse the stage");
+  __shared__ __align__(16) uint8_t stages[kSmallWaves * kStage];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  uint8_t* wst = stages + wave * kStage;
+  uint8_t* tst = wst + 16 * 128;
+  float* sst = reinterpret_cast<float*>(wst + (16 + RT) * 128);
   const int64_t tn = blockIdx.x % n16;
-  const int64_t m0 = (blockIdx.x / n16) * (16 * WM);
+  const int64_t m0 = (blockIdx.x / n16) * RT;
   const int64_t n0 = tn * 16;
   const int q = lane >> 4;
-  const uint8_t* brow = b + (n0 + (lane & 15)) * ld_b + q * 32;
+  const int fr = lane & 15;  // fragment row
+  const int lr = lane >> 3, lc = lane & 7;  // row-wise lanes: row lr (+8i), chunk lc
+  const int rows_live = (int)((m - m0) < RT ? (m - m0) : RT);
+  const int chunks = rows_live * 16;  // FUSED: 8-value chunks of the live rows
   const uint8_t* a = reinterpret_cast<const uint8_t*>(a_);
   const uint16_t* x = reinterpret_cast<const uint16_t*>(a_);
-  const uint8_t* arow[WM];
-  int64_t srow[WM];  // token row of this lane (row 0 stands in for rows past m)
-  bool live[WM];
+  const uint8_t* w0 = b + (n0 + lr) * ld_b + lc * 16;
+  const uint8_t* w1 = w0 + 8 * ld_b;
+  const float* bsrow = bs + (n0 / 128) * kblocks;
+  int64_t srow[WM];  // token row of this lane's fragments (row 0 stands in for rows past m)
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
-    const int64_t r = m0 + 16 * j + (lane & 15);
-    live[j] = r < m;
-    srow[j] = live[j] ? r : 0;
-    arow[j] = a + srow[j] * ld_a + q * 32;
+    const int r = 16 * j + fr;
+    srow[j] = m0 + (r < rows_live ? r : 0);
   }
-  // FUSED: live rows of the tile and their 8-value chunks per K block
-  const int rows_live = (int)((m - m0) < RT ? (m - m0) : RT);
-  const int chunks = rows_live * 16;
-  const float* bsrow = bs + (n0 / 128) * kblocks;
+
+  // D K blocks in registers: slot d holds the wave's d-th, (d + D)-th, ... K block
+  u32x4 rw[D][2];
+  uint4 rt[D][FUSED ? P : TP];
+  float rsa[D][FUSED ? 1 : WM], rsb[D];
+  auto load = [&](int d, int kb) {
+    rw[d][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w0 + (int64_t)kb * 128));
+    rw[d][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w1 + (int64_t)kb * 128));
+    rsb[d] = bsrow[kb];
+    if constexpr (FUSED) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int c = p * 64 + lane;
+        rt[d][p] = c < chunks ? load_plain(x + (m0 + c / 16) * ld_a + (int64_t)kb * 128 + (c % 16) * 8)
+                              : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TP; ++i) {
+        const int r = 8 * i + lr;
+        rt[d][i] = r < rows_live
+                       ? *reinterpret_cast<const uint4*>(a + (m0 + r) * ld_a + (int64_t)kb * 128 + lc * 16)
+                       : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < WM; ++j) rsa[d][j] = as[(int64_t)kb * ld_as + srow[j]];
+    }
+  };
+
   v4f acc[WM];
 #pragma unroll
   for (int j = 0; j < WM; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int kb0 = wave; kb0 < kblocks; kb0 += kSmallWaves * U) {
-    v8i fw[U], ft[U][WM];
-    float sa[U][WM], sb[U];
-    constexpr int P = 4 * WM;  // 64-lane passes over the chunks of a full tile
-    uint4 xc[FUSED ? U : 1][FUSED ? P : 1];
-    if constexpr (FUSED) {
-      // token rows first, so that their quantization overlaps the weight loads below;
-      // chunk c of a K block is values 8*(c%16) .. +7 of live row c/16
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kb = kb0 + u * kSmallWaves;
+  for (int d = 0; d < D; ++d)
+    if (wave + d * kSmallWaves < kblocks) load(d, wave + d * kSmallWaves);
+  for (int kb0 = wave; kb0 < kblocks; kb0 += kSmallWaves * D) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-          const int c = p * 64 + lane;
-          xc[u][p] = (kb < kblocks && c < chunks)
-                         ? load_plain(x + (m0 + c / 16) * ld_a + (int64_t)kb * 128 + (c % 16) * 8)
-                         : make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kb = kb0 + u * kSmallWaves;
-      if (kb < kblocks) {
-        const u32x4* pw = reinterpret_cast<const u32x4*>(brow + (int64_t)kb * 128);
-        fw[u] = join(__builtin_nontemporal_load(pw), __builtin_nontemporal_load(pw + 1));
-        sb[u] = bsrow[kb];
-#pragma unroll
-        for (int j = 0; j < WM; ++j) {
-          if constexpr (!FUSED) {
-            const u32x4* pt = reinterpret_cast<const u32x4*>(arow[j] + (int64_t)kb * 128);
-            ft[u][j] = live[j] ? join(pt[0], pt[1]) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            const float sv = as[(int64_t)kb * ld_as + srow[j]];
-            sa[u][j] = live[j] ? sv : 0.0f;
-          }
-        }
-      }
-    }
-    if constexpr (FUSED) {
-      // quantize the live chunks: group amax over the 16 lanes of a row, then the
-      // activation quantizer's scale and encoder; stage codes and scales, read them back
-      // in the MFMA operand layout (a wave reads only what it wrote itself)
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (kb0 + u * kSmallWaves >= kblocks) continue;
-        uint8_t* qb = qstage + (wave * U + u) * RT * kPitch;
-        float* sbuf = sstage + (wave * U + u) * RT;
+    for (int d = 0; d < D; ++d) {
+      const int kb = kb0 + d * kSmallWaves;
+      if (kb >= kblocks) break;
+      // stage this K block
+      *reinterpret_cast<u32x4*>(wst + stage_at(lr, lc)) = rw[d][0];
+      *reinterpret_cast<u32x4*>(wst + stage_at(lr + 8, lc)) = rw[d][1];
+      float sa[WM];
+      const float sb = rsb[d];
+      if constexpr (FUSED) {
+        // group amax over the 16 lanes of a row, then the activation quantizer's scale and
+        // encoder; codes and scales into the stage
 #pragma unroll
         for (int p = 0; p < P; ++p) {
           if (p * 64 >= chunks) break;
           const int c = p * 64 + lane;
-          const uint4 v = xc[u][p];
+          const uint4 v = rt[d][p];
           uint32_t mx = max_over_8_lanes(absmax8(v));
           mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x140, 0xf, 0xf, false));  // row mirror
           const float scale = scale_from_amax(bf16_bits_to_float(mx), kE4M3Max);
           const Quantizer qz = make_quantizer(scale);
           const uint2 code = (qz.xm == 1.0f) ? quant8<false>(v, qz, false) : quant8<false>(v, qz, true);
           if (c < chunks) {
-            *reinterpret_cast<uint2*>(qb + (c / 16) * kPitch + (c % 16) * 8) = code;
-            if ((c & 15) == 0) sbuf[c / 16] = scale;
+            const int r = c / 16, h = c % 16;
+            *reinterpret_cast<uint2*>(tst + stage_at(r, h >> 1) + (h & 1) * 8) = code;
+            if (h == 0) sst[r] = scale;
           }
         }
-        __builtin_amdgcn_wave_barrier();
+      } else {
 #pragma unroll
-        for (int j = 0; j < WM; ++j) {
-          const int r = 16 * j + (lane & 15);
-          if (r < rows_live) {
-            const uint8_t* src = qb + r * kPitch + q * 32;
-            ft[u][j] = join(*reinterpret_cast<const u32x4*>(src), *reinterpret_cast<const u32x4*>(src + 16));
-            sa[u][j] = sbuf[r];
-          } else {
-            ft[u][j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            sa[u][j] = 0.0f;
-          }
+        for (int i = 0; i < TP; ++i) {
+          const int r = 8 * i + lr;
+          if (r < rows_live) *reinterpret_cast<uint4*>(tst + stage_at(r, lc)) = rt[d][i];
         }
-        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = 0; j < WM; ++j) sa[j] = rsa[d][j];
       }
-    }
+      // this slot's next K block flies while this one is multiplied
+      if (kb + kSmallWaves * D < kblocks) load(d, kb + kSmallWaves * D);
+      __builtin_amdgcn_wave_barrier();
+      const v8i fw = join(*reinterpret_cast<const u32x4*>(wst + stage_at(fr, 2 * q)),
+                          *reinterpret_cast<const u32x4*>(wst + stage_at(fr, 2 * q + 1)));
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kb = kb0 + u * kSmallWaves;
-      if (kb < kblocks) {
-#pragma unroll
-        for (int j = 0; j < WM; ++j) {
-          v4f p = mfma_fp8(fw[u], ft[u][j]);
-          acc[j] = p * (sa[u][j] * sb[u]) + acc[j];
+      for (int j = 0; j < WM; ++j) {
+        const int r = 16 * j + fr;
+        v8i ft = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        float s = 0.0f;
+        if (r < rows_live) {
+          ft = join(*reinterpret_cast<const u32x4*>(tst + stage_at(r, 2 * q)),
+                    *reinterpret_cast<const u32x4*>(tst + stage_at(r, 2 * q + 1)));
+          s = FUSED ? sst[r] : sa[j];
         }
+        const v4f p = mfma_fp8(fw, ft);
+        acc[j] = p * (s * sb) + acc[j];
       }
+      __builtin_amdgcn_wave_barrier();
     }
   }
+  // the partial sums go through the wave's own stage
+  v4f* part = reinterpret_cast<v4f*>(wst);
 #pragma unroll
-  for (int j = 0; j < WM; ++j) part[wave][j][lane] = acc[j];
+  for (int j = 0; j < WM; ++j) part[j * 64 + lane] = acc[j];
   __syncthreads();
   // wave j < WM adds the 8 partial sums of token tile j (fixed order) and stores it
   if (wave < WM) {
     const int j = wave;
-    v4f t = part[0][j][lane];
+    v4f t = reinterpret_cast<const v4f*>(stages)[j * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < kSmallWaves; ++w) t += part[w][j][lane];
+    for (int w = 1; w < kSmallWaves; ++w) t += reinterpret_cast<const v4f*>(stages + w * kStage)[j * 64 + lane];
     const int64_t row = m0 + 16 * j + (lane & 15);
     if (row < m) {
       const int64_t col = n0 + 4 * q;
@@ -642,9 +648,21 @@ static hipError_t launch_smallm(const void* a, int64_t ld_a, const float* a_s, i
                                 int64_t k, hipStream_t stream) {
   const int64_t n16 = n / 16;
   const int64_t groups = (m + 16 * WM - 1) / (16 * WM);
-  hipLaunchKernelGGL((gemm_smallm_kernel<WM, FUSED>), dim3((unsigned)(n16 * groups)), dim3(64 * kSmallWaves), 0,
-                     stream, a, ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b), ld_b, b_s,
-                     reinterpret_cast<uint16_t*>(y), ld_y, m, n16, (int)(k / 128));
+  const unsigned grid = (unsigned)(n16 * groups);
+  // K blocks in flight per wave: one, except two for a 16-token tile whose grid fits on the
+  // CUs at once (measured: 1-4 tokens, N = K = 4096, 5.7 -> 4.9 us; deeper rings cost more in
+  // occupancy than they gain wherever the grid is larger)
+  if constexpr (!FUSED && WM == 1) {
+    if (grid <= 256) {
+      hipLaunchKernelGGL((gemm_smallm_kernel<WM, FUSED, 2>), dim3(grid), dim3(64 * kSmallWaves), 0, stream, a, ld_a,
+                         a_s, ld_as, reinterpret_cast<const uint8_t*>(b), ld_b, b_s, reinterpret_cast<uint16_t*>(y),
+                         ld_y, m, n16, (int)(k / 128));
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_smallm_kernel<WM, FUSED, 1>), dim3(grid), dim3(64 * kSmallWaves), 0, stream, a, ld_a, a_s,
+                     ld_as, reinterpret_cast<const uint8_t*>(b), ld_b, b_s, reinterpret_cast<uint16_t*>(y), ld_y, m,
+                     n16, (int)(k / 128));
   return hipGetLastError();
 }
 
