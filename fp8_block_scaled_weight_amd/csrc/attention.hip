@@ -28,6 +28,10 @@
 // 8 head dimensions of all the group's heads for the chunk's tokens t = quarter (mod 4),
 // with the weights p read from LDS.  The waves' partial (max, sum, vector) triples are
 // combined through LDS in a fixed order, so the result does not depend on timing.
+// A chunk's key rows are loaded with 8 lanes per 128-byte row (a quarter-wave of MFMA
+// fragment loads would touch 16 rows, which measured slower) and pass through a per-wave
+// LDS stage (16-byte chunk c of row r at c ^ (r & 7), conflict-free both ways); value
+// rows already arrive as whole 128-byte lines per quarter-wave.
 #include "e4m3.hpp"
 #include "launch.hpp"
 
@@ -104,7 +108,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) void paged_decode_attn_kernel(
   __shared__ float pbuf[kAttnWaves][kAttnChunk][GMAX];  // a chunk's softmax weights
   __shared__ float abuf[kAttnWaves][GMAX];              // rescale factor of the running sums
   __shared__ float mred[kAttnWaves][GMAX], lred[kAttnWaves][GMAX];
-  __shared__ float ored[kAttnWaves][GMAX][128];
+  // per-wave key stages during the chunk loop, the waves' partial vectors after it
+  constexpr int kKeyStage = kAttnChunk * 128;
+  constexpr int kShared = kAttnWaves * (kKeyStage > GMAX * 128 * 4 ? kKeyStage : GMAX * 128 * 4);
+  __shared__ __align__(16) uint8_t kshare[kShared];
+  float(*ored)[GMAX][128] = reinterpret_cast<float(*)[GMAX][128]>(kshare);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hcol = lane & 15, quad = lane >> 4;
@@ -142,14 +150,15 @@ __global__ __launch_bounds__(64 * kAttnWaves) void paged_decode_attn_kernel(
 
   const int nchunks = (L + kAttnChunk - 1) / kAttnChunk;
   const int64_t page_bytes = (int64_t)pm.size * hkv * 128;
-  // PS16 lane offsets within a page: key rows (token hcol, dims 32*quad..), value rows
-  // (token quad + 4r, dims 8*hcol..)
-  const int koff = (hcol * hkv + g) * 128 + quad * 32;
+  // PS16 lane offsets within a page of value rows (token quad + 4r, dims 8*hcol..)
   int voff[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) voff[r] = ((quad + 4 * r) * hkv + g) * 128 + hcol * 8;
+  const int kr = lane >> 3, kcol = lane & 7;  // row-wise key lanes: token kr (+8u), 16-byte chunk kcol
+  const int kroff = (kr * hkv + g) * 128 + kcol * 16;  // PS16: offset within a page of token kr (+8)
+  uint8_t* kst = kshare + wave * kKeyStage;
   struct Chunk {
-    uint4 fk[4][2];  // keys: tile i, lane row = token t0 + 16i + hcol, 32 code bytes
+    uint4 kr[8];     // keys: token t0 + 8u + kr, bytes 16 * kcol .. +15
     uint2 vr[16];    // values: tokens t0 + quad + 4j, dimensions 8 * hcol .. +7
   };
   auto load_chunk = [&](int c, Chunk& R) {
@@ -161,20 +170,19 @@ __global__ __launch_bounds__(64 * kAttnWaves) void paged_decode_attn_kernel(
         if (t0 + 16 * i < L) pbase[i] = (int64_t)btb[c * 4 + i] * page_bytes;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 16 * i + hcol;
-      R.fk[i][0] = R.fk[i][1] = make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < 8; ++u) {
+      const int t = t0 + 8 * u + kr;
+      R.kr[u] = make_uint4(0, 0, 0, 0);
       if (t < L) {
         const uint8_t* kp;
         if constexpr (PS16) {
-          kp = kc + pbase[i] + koff;
+          kp = kc + pbase[u / 2] + (u & 1) * 8 * hkv * 128 + kroff;
         } else {
           int pi, slot;
           pm.split(t, pi, slot);
-          kp = kc + (((int64_t)btb[pi] * pm.size + slot) * hkv + g) * 128 + quad * 32;
+          kp = kc + (((int64_t)btb[pi] * pm.size + slot) * hkv + g) * 128 + kcol * 16;
         }
-        R.fk[i][0] = load_plain(kp);
-        R.fk[i][1] = load_plain(kp + 16);
+        R.kr[u] = load_plain(kp);
       }
     }
 #pragma unroll
@@ -196,16 +204,26 @@ __global__ __launch_bounds__(64 * kAttnWaves) void paged_decode_attn_kernel(
   };
   auto compute_chunk = [&](int c, const Chunk& R) {
     const int t0 = c * kAttnChunk;
+    // key rows into the wave's stage, then back in the MFMA layout: tile i, lane row =
+    // token t0 + 16i + hcol, code bytes 32 * quad .. +31
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      *reinterpret_cast<uint4*>(kst + (8 * u + kr) * 128 + ((kcol ^ ((8 * u + kr) & 7)) << 4)) = R.kr[u];
+    __builtin_amdgcn_wave_barrier();
     // scores: lane holds head hcol, tokens t0 + 16i + 4 * quad + e
     float sc[4][4];
     float mc = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int row = 16 * i + hcol;
+      const uint8_t* kb = kst + row * 128;
+      const uint4 k0 = *reinterpret_cast<const uint4*>(kb + (((2 * quad) ^ (row & 7)) << 4));
+      const uint4 k1 = *reinterpret_cast<const uint4*>(kb + (((2 * quad + 1) ^ (row & 7)) << 4));
       att_v4f r = {0.f, 0.f, 0.f, 0.f};
-      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(R.fk[i][0].x, R.fk[i][0].y), fq[0], r, 0, 0, 0);
-      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(R.fk[i][0].z, R.fk[i][0].w), fq[1], r, 0, 0, 0);
-      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(R.fk[i][1].x, R.fk[i][1].y), fq[2], r, 0, 0, 0);
-      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(R.fk[i][1].z, R.fk[i][1].w), fq[3], r, 0, 0, 0);
+      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k0.x, k0.y), fq[0], r, 0, 0, 0);
+      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k0.z, k0.w), fq[1], r, 0, 0, 0);
+      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k1.x, k1.y), fq[2], r, 0, 0, 0);
+      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k1.z, k1.w), fq[3], r, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         sc[i][e] = (t0 + 16 * i + 4 * quad + e < L) ? r[e] * f : -INFINITY;
@@ -271,7 +289,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void paged_decode_attn_kernel(
     load_chunk(c, R);
     compute_chunk(c, R);
   }
-  // the four quarters of the chunk's tokens, then the waves
+  // the four quarters of the chunk's tokens, then the waves (whose partial vectors reuse
+  // the key stages: every wave has left its chunk loop before any is overwritten)
+  __syncthreads();
 #pragma unroll
   for (int h = 0; h < GMAX; ++h)
 #pragma unroll

@@ -167,6 +167,12 @@ def test_grouped_small_with_empty_groups():
     check_grouped(grouped_case([3, 0, 130, 1, 0, 257, 64], 256, 384, 5))
 
 
+def test_grouped_long_k_large_tiles():
+    """K = 2048 with n % 256 == 0 takes the 256x256 tile: empty groups, groups smaller than
+    a tile and groups spanning several tiles with ragged ends."""
+    check_grouped(grouped_case([3, 0, 300, 1, 0, 513, 64, 256], 512, 2048, 8))
+
+
 def test_grouped_all_empty_but_one():
     check_grouped(grouped_case([0, 0, 200, 0], 128, 256, 6))
 
