@@ -97,189 +97,221 @@ struct PageMap {
   }
 };
 
-// PS16: 16-token pages, so a 64-token chunk is four whole pages: the page ids are
-// wave-uniform (scalar loads) and every lane's offset within a page is fixed.
-template <int GMAX, bool PS16>
+// PS16: 16-token pages, so a chunk is whole pages: the page ids are wave-uniform (scalar
+// loads) and every lane's offset within a page is fixed.
+// HG: KV heads per workgroup.  The cache keeps a token's KV heads side by side, so with
+// HG = 2 every token contributes 256 contiguous bytes (a read of this cache with one head
+// per workgroup measured 5.4 TB/s, with two 6.1 TB/s).  A chunk holds 64 / HG tokens, so a
+// wave's loads per chunk stay at 16 KB.
+template <int GMAX, bool PS16, int HG>
 __global__ __launch_bounds__(64 * kAttnWaves) void paged_decode_attn_kernel(
     const uint16_t* __restrict__ q, int64_t ld_q, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const int32_t* __restrict__ bt, int64_t ld_bt, const int32_t* __restrict__ seq_lens, int32_t hkv,
     int32_t group, PageMap pm, const float* __restrict__ q_scale, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, float sm_scale, uint16_t* __restrict__ out, int64_t ld_out) {
-  __shared__ float pbuf[kAttnWaves][kAttnChunk][GMAX];  // a chunk's softmax weights
-  __shared__ float abuf[kAttnWaves][GMAX];              // rescale factor of the running sums
-  __shared__ float mred[kAttnWaves][GMAX], lred[kAttnWaves][GMAX];
+  constexpr int CT = kAttnChunk / HG;  // tokens per chunk
+  constexpr int NT = CT / 16;          // 16-token score tiles per chunk
+  constexpr int NV = CT / 4;           // value rows per lane, chunk and head
+  constexpr int NP = (CT + 15) / 16;   // PS16: pages per chunk
+  constexpr int TPI = 8 / HG;          // tokens per row-wise key load
+  constexpr int GH = HG * GMAX;        // head slots of the workgroup
+  __shared__ float pbuf[kAttnWaves][HG][CT][GMAX];  // a chunk's softmax weights
+  __shared__ float abuf[kAttnWaves][GH];             // rescale factor of the running sums
+  __shared__ float mred[kAttnWaves][GH], lred[kAttnWaves][GH];
   // per-wave key stages during the chunk loop, the waves' partial vectors after it
-  constexpr int kKeyStage = kAttnChunk * 128;
-  constexpr int kShared = kAttnWaves * (kKeyStage > GMAX * 128 * 4 ? kKeyStage : GMAX * 128 * 4);
+  constexpr int kKeyStage = CT * HG * 128;
+  constexpr int kShared = kAttnWaves * (kKeyStage > GH * 128 * 4 ? kKeyStage : GH * 128 * 4);
   __shared__ __align__(16) uint8_t kshare[kShared];
-  float(*ored)[GMAX][128] = reinterpret_cast<float(*)[GMAX][128]>(kshare);
+  float(*ored)[GH][128] = reinterpret_cast<float(*)[GH][128]>(kshare);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hcol = lane & 15, quad = lane >> 4;
-  const int b = blockIdx.x / hkv, g = blockIdx.x - (blockIdx.x / hkv) * hkv;
+  const int hkg = hkv / HG;  // workgroups per sequence
+  const int b = blockIdx.x / hkg, g0 = (blockIdx.x - (blockIdx.x / hkg) * hkg) * HG;
   const int L = seq_lens[b];
-  const uint16_t* qb = q + (int64_t)b * ld_q + (int64_t)g * group * 128;
-  uint16_t* ob = out + (int64_t)b * ld_out + (int64_t)g * group * 128;
+  const uint16_t* qb = q + (int64_t)b * ld_q + (int64_t)g0 * group * 128;
+  uint16_t* ob = out + (int64_t)b * ld_out + (int64_t)g0 * group * 128;
   if (L <= 0) {
-    for (int t = threadIdx.x; t < group * 128; t += 64 * kAttnWaves) ob[t] = 0;
+    for (int t = threadIdx.x; t < HG * group * 128; t += 64 * kAttnWaves) ob[t] = 0;
     return;
   }
   const int32_t* btb = bt + (int64_t)b * ld_bt;
   const float qs = q_scale[0], ks = k_scale[0], vs = v_scale[0];
 
-  // query codes in the MFMA B layout: lane l holds head l % 16 (zero past the group),
-  // dimensions 32 * (l / 16) + 8c .. +7 for MFMA c; codes saturate (a stored scale may
-  // be exceeded)
-  uint4 c0 = make_uint4(0, 0, 0, 0), c1 = c0;
-  if (hcol < group) {
-    const uint16_t* p = qb + hcol * 128 + quad * 32;
-    const Quantizer qz = make_quantizer(qs);
-    c0 = quant16<true>(load_plain(p), load_plain(p + 8), qz);
-    c1 = quant16<true>(load_plain(p + 16), load_plain(p + 24), qz);
+  // query codes of KV head g0 + hh in the MFMA B layout: lane l holds head l % 16 of the
+  // group (zero past it), dimensions 32 * (l / 16) + 8c .. +7 for MFMA c; codes saturate
+  // (a stored scale may be exceeded)
+  att_v8bf fq[HG][4];
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh) {
+    uint4 c0 = make_uint4(0, 0, 0, 0), c1 = c0;
+    if (hcol < group) {
+      const uint16_t* p = qb + (hh * group + hcol) * 128 + quad * 32;
+      const Quantizer qz = make_quantizer(qs);
+      c0 = quant16<true>(load_plain(p), load_plain(p + 8), qz);
+      c1 = quant16<true>(load_plain(p + 16), load_plain(p + 24), qz);
+    }
+    fq[hh][0] = fp8x8_to_bf16(c0.x, c0.y);
+    fq[hh][1] = fp8x8_to_bf16(c0.z, c0.w);
+    fq[hh][2] = fp8x8_to_bf16(c1.x, c1.y);
+    fq[hh][3] = fp8x8_to_bf16(c1.z, c1.w);
   }
-  const att_v8bf fq[4] = {fp8x8_to_bf16(c0.x, c0.y), fp8x8_to_bf16(c0.z, c0.w), fp8x8_to_bf16(c1.x, c1.y),
-                          fp8x8_to_bf16(c1.z, c1.w)};
   const float f = sm_scale * qs * ks * kLog2e;  // scores in log2 units
 
-  float m_run = -INFINITY, l_run = 0.0f;  // head hcol
-  float acc[GMAX][8];
+  float m_run[HG], l_run[HG];  // head hcol of each KV head's group
+  float acc[HG][GMAX][8];
 #pragma unroll
-  for (int h = 0; h < GMAX; ++h)
+  for (int hh = 0; hh < HG; ++hh) {
+    m_run[hh] = -INFINITY;
+    l_run[hh] = 0.0f;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) acc[h][d] = 0.0f;
+    for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[hh][h][d] = 0.0f;
+  }
 
-  const int nchunks = (L + kAttnChunk - 1) / kAttnChunk;
+  const int nchunks = (L + CT - 1) / CT;
   const int64_t page_bytes = (int64_t)pm.size * hkv * 128;
   // PS16 lane offsets within a page of value rows (token quad + 4r, dims 8*hcol..)
   int voff[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) voff[r] = ((quad + 4 * r) * hkv + g) * 128 + hcol * 8;
-  const int kr = lane >> 3, kcol = lane & 7;  // row-wise key lanes: token kr (+8u), 16-byte chunk kcol
-  const int kroff = (kr * hkv + g) * 128 + kcol * 16;  // PS16: offset within a page of token kr (+8)
+  for (int r = 0; r < 4; ++r) voff[r] = ((quad + 4 * r) * hkv + g0) * 128 + hcol * 8;
+  // row-wise key lanes: token kt (+TPI*u), 16-byte chunk kcol of the token's HG heads
+  const int kt = lane / (8 * HG), kcol = lane % (8 * HG);
+  const int kroff = (kt * hkv + g0) * 128 + kcol * 16;  // PS16: within a page
   uint8_t* kst = kshare + wave * kKeyStage;
   struct Chunk {
-    uint4 kr[8];     // keys: token t0 + 8u + kr, bytes 16 * kcol .. +15
-    uint2 vr[16];    // values: tokens t0 + quad + 4j, dimensions 8 * hcol .. +7
+    uint4 kr[8];        // keys: token t0 + TPI*u + kt, bytes 16 * kcol .. +15 of its HG heads
+    uint2 vr[HG][NV];   // values of head g0 + hh: tokens t0 + quad + 4j, dimensions 8 * hcol .. +7
   };
   auto load_chunk = [&](int c, Chunk& R) {
-    const int t0 = c * kAttnChunk;
-    int64_t pbase[4] = {0, 0, 0, 0};
+    const int t0 = c * CT;
+    int64_t pbase[NP];
     if constexpr (PS16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (t0 + 16 * i < L) pbase[i] = (int64_t)btb[c * 4 + i] * page_bytes;
+      for (int i = 0; i < NP; ++i) pbase[i] = (t0 + 16 * i < L) ? (int64_t)btb[c * NP + i] * page_bytes : 0;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int t = t0 + 8 * u + kr;
+      const int t = t0 + TPI * u + kt;
       R.kr[u] = make_uint4(0, 0, 0, 0);
       if (t < L) {
         const uint8_t* kp;
         if constexpr (PS16) {
-          kp = kc + pbase[u / 2] + (u & 1) * 8 * hkv * 128 + kroff;
+          kp = kc + pbase[(TPI * u) / 16] + ((TPI * u) % 16) * hkv * 128 + kroff;
         } else {
           int pi, slot;
           pm.split(t, pi, slot);
-          kp = kc + (((int64_t)btb[pi] * pm.size + slot) * hkv + g) * 128 + kcol * 16;
+          kp = kc + (((int64_t)btb[pi] * pm.size + slot) * hkv + g0) * 128 + kcol * 16;
         }
         R.kr[u] = load_plain(kp);
       }
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int t = t0 + quad + 4 * j;
-      R.vr[j] = make_uint2(0, 0);
-      if (t < L) {
-        const uint8_t* vp;
-        if constexpr (PS16) {
-          vp = vc + pbase[j / 4] + voff[j % 4];
-        } else {
-          int pi, slot;
-          pm.split(t, pi, slot);
-          vp = vc + (((int64_t)btb[pi] * pm.size + slot) * hkv + g) * 128 + hcol * 8;
+    for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int t = t0 + quad + 4 * j;
+        R.vr[hh][j] = make_uint2(0, 0);
+        if (t < L) {
+          const uint8_t* vp;
+          if constexpr (PS16) {
+            vp = vc + pbase[j / 4] + voff[j % 4] + hh * 128;
+          } else {
+            int pi, slot;
+            pm.split(t, pi, slot);
+            vp = vc + (((int64_t)btb[pi] * pm.size + slot) * hkv + g0 + hh) * 128 + hcol * 8;
+          }
+          R.vr[hh][j] = *reinterpret_cast<const uint2*>(vp);
         }
-        R.vr[j] = *reinterpret_cast<const uint2*>(vp);
       }
-    }
   };
   auto compute_chunk = [&](int c, const Chunk& R) {
-    const int t0 = c * kAttnChunk;
-    // key rows into the wave's stage, then back in the MFMA layout: tile i, lane row =
-    // token t0 + 16i + hcol, code bytes 32 * quad .. +31
+    const int t0 = c * CT;
+    // key rows into the wave's stage (row = token * HG + head), then back in the MFMA
+    // layout: tile i, lane row = token t0 + 16i + hcol, code bytes 32 * quad .. +31
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      *reinterpret_cast<uint4*>(kst + (8 * u + kr) * 128 + ((kcol ^ ((8 * u + kr) & 7)) << 4)) = R.kr[u];
-    __builtin_amdgcn_wave_barrier();
-    // scores: lane holds head hcol, tokens t0 + 16i + 4 * quad + e
-    float sc[4][4];
-    float mc = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * i + hcol;
-      const uint8_t* kb = kst + row * 128;
-      const uint4 k0 = *reinterpret_cast<const uint4*>(kb + (((2 * quad) ^ (row & 7)) << 4));
-      const uint4 k1 = *reinterpret_cast<const uint4*>(kb + (((2 * quad + 1) ^ (row & 7)) << 4));
-      att_v4f r = {0.f, 0.f, 0.f, 0.f};
-      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k0.x, k0.y), fq[0], r, 0, 0, 0);
-      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k0.z, k0.w), fq[1], r, 0, 0, 0);
-      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k1.x, k1.y), fq[2], r, 0, 0, 0);
-      r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k1.z, k1.w), fq[3], r, 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sc[i][e] = (t0 + 16 * i + 4 * quad + e < L) ? r[e] * f : -INFINITY;
-        mc = fmaxf(mc, sc[i][e]);
-      }
-    }
-    mc = fmaxf(mc, __shfl_xor(mc, 16));
-    mc = fmaxf(mc, __shfl_xor(mc, 32));
-    const float m_new = fmaxf(m_run, mc);  // finite: the chunk holds a token below L
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float ls = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sc[i][e] = __builtin_amdgcn_exp2f(sc[i][e] - m_new);
-        ls += sc[i][e];
-      }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-    // weights and rescale factors to LDS; the wave reads only what it wrote
-    if (hcol < GMAX) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pbuf[wave][16 * i + 4 * quad + e][hcol] = sc[i][e];
-      if (quad == 0) abuf[wave][hcol] = alpha;
+    for (int u = 0; u < 8; ++u) {
+      const int row = (TPI * u + kt) * HG + (kcol >> 3);
+      *reinterpret_cast<uint4*>(kst + row * 128 + (((kcol & 7) ^ (row & 7)) << 4)) = R.kr[u];
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int h = 0; h < GMAX; ++h) {
-      const float a = abuf[wave][h];
+    for (int hh = 0; hh < HG; ++hh) {
+      // scores: lane holds head hcol, tokens t0 + 16i + 4 * quad + e
+      float sc[NT][4];
+      float mc = -INFINITY;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) acc[h][d] *= a;
-    }
+      for (int i = 0; i < NT; ++i) {
+        const int row = (16 * i + hcol) * HG + hh;
+        const uint8_t* kb = kst + row * 128;
+        const uint4 k0 = *reinterpret_cast<const uint4*>(kb + (((2 * quad) ^ (row & 7)) << 4));
+        const uint4 k1 = *reinterpret_cast<const uint4*>(kb + (((2 * quad + 1) ^ (row & 7)) << 4));
+        att_v4f r = {0.f, 0.f, 0.f, 0.f};
+        r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k0.x, k0.y), fq[hh][0], r, 0, 0, 0);
+        r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k0.z, k0.w), fq[hh][1], r, 0, 0, 0);
+        r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k1.x, k1.y), fq[hh][2], r, 0, 0, 0);
+        r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k1.z, k1.w), fq[hh][3], r, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int tl = quad + 4 * j;
-      float v[8];
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const uint32_t word = w ? R.vr[j].y : R.vr[j].x;
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
-        v[4 * w + 0] = lo[0];
-        v[4 * w + 1] = lo[1];
-        v[4 * w + 2] = hi[0];
-        v[4 * w + 3] = hi[1];
+        for (int e = 0; e < 4; ++e) {
+          sc[i][e] = (t0 + 16 * i + 4 * quad + e < L) ? r[e] * f : -INFINITY;
+          mc = fmaxf(mc, sc[i][e]);
+        }
       }
+      mc = fmaxf(mc, __shfl_xor(mc, 16));
+      mc = fmaxf(mc, __shfl_xor(mc, 32));
+      const float m_new = fmaxf(m_run[hh], mc);  // finite: the chunk holds a token below L
+      const float alpha = __builtin_amdgcn_exp2f(m_run[hh] - m_new);
+      float ls = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sc[i][e] = __builtin_amdgcn_exp2f(sc[i][e] - m_new);
+          ls += sc[i][e];
+        }
+      ls += __shfl_xor(ls, 16);
+      ls += __shfl_xor(ls, 32);
+      l_run[hh] = l_run[hh] * alpha + ls;
+      m_run[hh] = m_new;
+      // weights and rescale factors to LDS; the wave reads only what it wrote
+      if (hcol < GMAX) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pbuf[wave][hh][16 * i + 4 * quad + e][hcol] = sc[i][e];
+        if (quad == 0) abuf[wave][hh * GMAX + hcol] = alpha;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
 #pragma unroll
       for (int h = 0; h < GMAX; ++h) {
-        const float p = pbuf[wave][tl][h];
+        const float a = abuf[wave][hh * GMAX + h];
 #pragma unroll
-        for (int d = 0; d < 8; ++d) acc[h][d] = __builtin_fmaf(p, v[d], acc[h][d]);
+        for (int d = 0; d < 8; ++d) acc[hh][h][d] *= a;
+      }
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int tl = quad + 4 * j;
+        float v[8];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const uint32_t word = w ? R.vr[hh][j].y : R.vr[hh][j].x;
+          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+          v[4 * w + 0] = lo[0];
+          v[4 * w + 1] = lo[1];
+          v[4 * w + 2] = hi[0];
+          v[4 * w + 3] = hi[1];
+        }
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+          const float p = pbuf[wave][hh][tl][h];
+#pragma unroll
+          for (int d = 0; d < 8; ++d) acc[hh][h][d] = __builtin_fmaf(p, v[d], acc[hh][h][d]);
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -293,34 +325,41 @@ __global__ __launch_bounds__(64 * kAttnWaves) void paged_decode_attn_kernel(
   // the key stages: every wave has left its chunk loop before any is overwritten)
   __syncthreads();
 #pragma unroll
-  for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      acc[h][d] += __shfl_xor(acc[h][d], 16);
-      acc[h][d] += __shfl_xor(acc[h][d], 32);
-    }
-  if (quad == 0) {
+  for (int hh = 0; hh < HG; ++hh)
 #pragma unroll
     for (int h = 0; h < GMAX; ++h)
 #pragma unroll
-      for (int d = 0; d < 8; ++d) ored[wave][h][8 * hcol + d] = acc[h][d];
-    if (hcol < GMAX) {
-      mred[wave][hcol] = m_run;
-      lred[wave][hcol] = l_run;
+      for (int d = 0; d < 8; ++d) {
+        acc[hh][h][d] += __shfl_xor(acc[hh][h][d], 16);
+        acc[hh][h][d] += __shfl_xor(acc[hh][h][d], 32);
+      }
+  if (quad == 0) {
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) ored[wave][hh * GMAX + h][8 * hcol + d] = acc[hh][h][d];
+      if (hcol < GMAX) {
+        mred[wave][hh * GMAX + hcol] = m_run[hh];
+        lred[wave][hh * GMAX + hcol] = l_run[hh];
+      }
     }
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < group * 128; t += 64 * kAttnWaves) {
-    const int h = t >> 7, d = t & 127;
+  for (int t = threadIdx.x; t < HG * group * 128; t += 64 * kAttnWaves) {
+    const int hh = t / (group * 128);
+    const int rem = t - hh * group * 128;
+    const int slot = hh * GMAX + (rem >> 7), d = rem & 127;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, mred[w][h]);
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, mred[w][slot]);
     float num = 0.0f, den = 0.0f;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
-      const float e = __builtin_amdgcn_exp2f(mred[w][h] - M);  // 0 for a wave without tokens
-      num = __builtin_fmaf(e, ored[w][h][d], num);
-      den = __builtin_fmaf(e, lred[w][h], den);
+      const float e = __builtin_amdgcn_exp2f(mred[w][slot] - M);  // 0 for a wave without tokens
+      num = __builtin_fmaf(e, ored[w][slot][d], num);
+      den = __builtin_fmaf(e, lred[w][slot], den);
     }
     const uint32_t u = __float_as_uint(vs * (num / den));
     ob[t] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
@@ -343,7 +382,12 @@ hipError_t launch_decode_attention(const void* q, int64_t ld_q, const void* k_ca
   pm.size = page_size;
   pm.shift = ((page_size & (page_size - 1)) == 0) ? __builtin_ctz((unsigned)page_size) : -1;
   const int32_t group = hq / hkv;
-  const dim3 grid((unsigned)((int64_t)seqs * hkv)), block(64 * kAttnWaves);
+  // two KV heads per workgroup: 256 contiguous bytes per token, while half as many
+  // workgroups still cover the 256 CUs (measured, 64 sequences x 8 KV heads x 20,000 tokens:
+  // 538 -> 521 us; 16 sequences: 38 -> 68 us, hence the grid condition); the pair's
+  // registers fit for groups of up to 4 query heads
+  const bool pair_heads = group <= 4 && hkv % 2 == 0 && (int64_t)seqs * hkv >= 512;
+  const dim3 grid((unsigned)((int64_t)seqs * (pair_heads ? hkv / 2 : hkv))), block(64 * kAttnWaves);
   const auto* qp = reinterpret_cast<const uint16_t*>(q);
   const auto* kp = reinterpret_cast<const uint8_t*>(k_cache);
   const auto* vp = reinterpret_cast<const uint8_t*>(v_cache);
@@ -353,12 +397,14 @@ hipError_t launch_decode_attention(const void* q, int64_t ld_q, const void* k_ca
                        pm, q_scale, k_scale, v_scale, sm_scale, op, ld_out);
   };
   const bool ps16 = page_size == 16;
-  if (group <= 4)
-    ps16 ? launch(paged_decode_attn_kernel<4, true>) : launch(paged_decode_attn_kernel<4, false>);
+  if (pair_heads)
+    ps16 ? launch(paged_decode_attn_kernel<4, true, 2>) : launch(paged_decode_attn_kernel<4, false, 2>);
+  else if (group <= 4)
+    ps16 ? launch(paged_decode_attn_kernel<4, true, 1>) : launch(paged_decode_attn_kernel<4, false, 1>);
   else if (group <= 8)
-    ps16 ? launch(paged_decode_attn_kernel<8, true>) : launch(paged_decode_attn_kernel<8, false>);
+    ps16 ? launch(paged_decode_attn_kernel<8, true, 1>) : launch(paged_decode_attn_kernel<8, false, 1>);
   else
-    ps16 ? launch(paged_decode_attn_kernel<16, true>) : launch(paged_decode_attn_kernel<16, false>);
+    ps16 ? launch(paged_decode_attn_kernel<16, true, 1>) : launch(paged_decode_attn_kernel<16, false, 1>);
   return hipGetLastError();
 }
 

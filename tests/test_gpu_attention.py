@@ -69,6 +69,30 @@ def test_small_contexts(hq, hkv, ps):
         assert ok, f"recal={recal}: worst err/bound {ratio:.3f}"
 
 
+@pytest.mark.parametrize("ps", [16, 5])
+def test_many_sequences_pair_kv_heads(ps):
+    """64 sequences x 8 KV heads with groups of 4 query heads: the kernel reads two KV heads
+    per workgroup (32-token chunks).  Lengths span empty, single-token, sub-chunk,
+    chunk-boundary and multi-chunk contexts."""
+    seqs, hq, hkv = 64, 32, 8
+    g = np.random.default_rng(40 + ps)
+    lens = g.integers(0, 200, size=seqs).astype(np.int32)
+    lens[:8] = [0, 1, 31, 32, 33, 64, 65, 199]
+    per = -(-int(lens.max()) // ps)
+    pages = seqs * per + 5
+    bt = g.permutation(pages)[:seqs * per].reshape(seqs, per).astype(np.int32)
+    kc, vc = _codes(50 + ps, (pages, ps, hkv, 128)), _codes(51 + ps, (pages, ps, hkv, 128))
+    q = synth.activation(5, 1, 60 + ps, seqs, hq * 128).reshape(seqs, hq, 128)
+    ks, vs, sm = 0.02, 0.015, 128 ** -0.5
+    qs = float(oracle.q_scale(q))
+    got, qs_dev = _run(q, kc, vc, bt, lens, 0.01, ks, vs, sm, True)
+    assert np.float32(qs_dev) == np.float32(qs)
+    ref = oracle.paged_decode_attention(q, kc, vc, bt, lens, qs, ks, vs, sm)
+    assert np.all(got[0] == 0), "a sequence of length 0 gives zeros"
+    ok, ratio = _gate(got, ref)
+    assert ok, f"worst err/bound {ratio:.3f}"
+
+
 def test_saturating_stored_query_scale_and_peaked_scores():
     """A stored q_scale smaller than the queries need (codes saturate) and large scores."""
     seqs, hq, hkv, ps, L = 2, 4, 1, 16, 300
