@@ -67,11 +67,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 __global__ __launch_bounds__(1024) void q_scale_kernel(const uint16_t* __restrict__ q, int64_t ld_q, int64_t seqs,
                                                        int64_t row, float range, float* __restrict__ q_scale) {
   __shared__ uint32_t red[16];
+  constexpr int U = 16;  // loads in flight per thread (one per trip serialises on latency)
   uint32_t mx = 0;
   const int64_t total = seqs * row;
-  for (int64_t i = (int64_t)threadIdx.x * 8; i < total; i += 1024 * 8) {
-    const int64_t b = i / row;
-    mx = max(mx, absmax8(load_plain(q + b * ld_q + (i - b * row))));
+  for (int64_t i0 = (int64_t)threadIdx.x * 8; i0 < total; i0 += 1024 * 8 * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + (int64_t)u * 1024 * 8;
+      const int64_t b = i / row;
+      v[u] = i < total ? load_plain(q + b * ld_q + (i - b * row)) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = max(mx, absmax8(v[u]));
   }
   mx = max_over_wave(mx);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;

@@ -124,7 +124,8 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const int16_t*
 
 // ----------------------------------------------------------------------------
 // Dispatch, copy step: one wave per entry copies the token's K code bytes into its row
-// and its K/128 scales into column `row` of the dispatched scale matrix.
+// (up to 4 KB in flight before the first store) and its K/128 scales into column `row` of
+// the dispatched scale matrix.
 // ----------------------------------------------------------------------------
 constexpr int kGatherWaves = 4;
 
@@ -140,7 +141,20 @@ __global__ __launch_bounds__(64 * kGatherWaves) void moe_gather_kernel(
   const int64_t t = f / topk;
   const uint8_t* src = xq + t * ld_xq;
   uint8_t* dst = aq + (int64_t)r * ld_aq;
-  for (int64_t c = (int64_t)lane * 16; c < k; c += 64 * 16) store_plain(dst + c, load_plain(src + c));
+  // up to 4 KB of the row in flight before the first store
+  for (int64_t c0 = (int64_t)lane * 16; c0 < k; c0 += 4 * 64 * 16) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t c = c0 + u * 64 * 16;
+      v[u] = c < k ? load_plain(src + c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t c = c0 + u * 64 * 16;
+      if (c < k) store_plain(dst + c, v[u]);
+    }
+  }
   for (int64_t g = lane; g < k / 128; g += 64) as[g * ld_as + r] = xs[g * ld_xs + t];
 }
 
@@ -343,8 +357,10 @@ hipError_t launch_swiglu_quant(const void* h, int64_t m, int64_t n, int64_t ld_h
 // ----------------------------------------------------------------------------
 // Combine: out[t] = bf16( sum_j w[t, j] * y[row_of[t, j]] ), the sum in fp32 in the
 // order j = 0, 1, ... (one FMA per term), entries with row -1 skipped, one rounding to
-// bf16 at the store.  One wave per token; each lane takes 8 consecutive columns per
-// 512-column pass and has the up-to-8 expert rows of its columns in flight at once.
+// bf16 at the store.  One wave per (token, 512-column block); each lane takes 8
+// consecutive columns and has the up-to-8 expert rows of its columns in flight at once,
+// so a wave makes a single round trip (a wave per token walking its columns in passes
+// waits on each pass in turn).
 // ----------------------------------------------------------------------------
 constexpr int kCombineWaves = 4;
 constexpr int kCombineBatch = 8;  // expert rows loaded together
@@ -360,11 +376,16 @@ __global__ __launch_bounds__(64 * kCombineWaves) void moe_combine_kernel(
     const uint16_t* __restrict__ y, int64_t ld_y, const int32_t* __restrict__ row_of, const float* __restrict__ w,
     int64_t tokens, int32_t topk, int64_t hidden, uint16_t* __restrict__ out, int64_t ld_out) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
-  if (t >= tokens) return;
+  // one wave per (token, 512-column block): a single round trip of loads per wave
+  const int64_t cblocks = (hidden + 64 * 8 - 1) / (64 * 8);
+  const int64_t f = (int64_t)blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+  if (f >= tokens * cblocks) return;
+  const int64_t t = f / cblocks;
   const int32_t* rt = row_of + t * topk;
   const float* wt = w + t * topk;
-  for (int64_t c = (int64_t)lane * 8; c < hidden; c += 64 * 8) {
+  {
+    const int64_t c = (f - t * cblocks) * 64 * 8 + (int64_t)lane * 8;
+    if (c >= hidden) return;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < topk; j0 += kCombineBatch) {
       uint4 v[kCombineBatch];
@@ -393,7 +414,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void moe_combine_kernel(
 
 hipError_t launch_moe_combine(const void* y, int64_t ld_y, const int32_t* row_of, const float* w, int64_t tokens,
                               int32_t topk, int64_t hidden, void* out, int64_t ld_out, hipStream_t stream) {
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((tokens + kCombineWaves - 1) / kCombineWaves)),
+  const int64_t waves = tokens * ((hidden + 64 * 8 - 1) / (64 * 8));
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((waves + kCombineWaves - 1) / kCombineWaves)),
                      dim3(64 * kCombineWaves), 0, stream, reinterpret_cast<const uint16_t*>(y), ld_y, row_of, w,
                      tokens, topk, hidden, reinterpret_cast<uint16_t*>(out), ld_out);
   return hipGetLastError();
