@@ -538,6 +538,24 @@ def _time_graph(torch, g, iters):
     return a.elapsed_time(b) / iters
 
 
+def _time_cold(torch, fn, iters=10):
+    """Median time of one call of `fn` after a 512 MB fill has evicted the last-level cache
+    (HIP events around the call alone)."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    fn()
+    ts = []
+    for _ in range(iters):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del flush
+    return sorted(ts)[len(ts) // 2]
+
+
 def _time(torch, fn, iters, warm=2, reps=10):
     """Average time of one call of `fn`: `reps` calls captured into one graph, the graph
     replayed `iters` times back to back."""
@@ -646,9 +664,13 @@ def legs(torch, fq, synth, dev):
     q2 = torch.empty((n, I), dtype=torch.uint8, device=dev)
     s2 = torch.empty((I // 128, n), dtype=torch.float32, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    ms_d = _time(torch, lambda: fq.fp8q_moe_dispatch(xq, xsc, ids, E, dq, dsc, doff, row_of), 10)
-    ms_sw = _time(torch, lambda: fq.fp8q_swiglu_quant_g128(y1, q2, s2), 10)
-    ms_c = _time(torch, lambda: fq.fp8q_moe_combine(y2, row_of, rw, out), 10)
+    f_d = lambda: fq.fp8q_moe_dispatch(xq, xsc, ids, E, dq, dsc, doff, row_of)
+    f_sw = lambda: fq.fp8q_swiglu_quant_g128(y1, q2, s2)
+    f_c = lambda: fq.fp8q_moe_combine(y2, row_of, rw, out)
+    ms_d, ms_sw, ms_c = _time(torch, f_d, 10), _time(torch, f_sw, 10), _time(torch, f_c, 10)
+    # their inputs (75-150 MB) fit the 256 MB last-level cache, so back-to-back calls run
+    # partly from it; the cold figure evicts it (a 512 MB fill) before each single call
+    cold = {k: _time_cold(torch, f_) for k, f_ in (("d", f_d), ("sw", f_sw), ("c", f_c))}
 
     def layer():
         fq.fp8q_moe_dispatch(xq, xsc, ids, E, dq, dsc, doff, row_of)
@@ -661,10 +683,12 @@ def legs(torch, fq, synth, dev):
     by_d = T * H + 4 * T * H / 128 + 2 * n + n * H + 4 * n * H / 128 + 4 * n + 4 * (E + 1)
     by_sw = n * 2 * I * 2 + n * I + 4 * n * I / 128
     by_c = n * H * 2 + 8 * n + T * H * 2
-    for name, by, ms_ in (("f1_moe_dispatch", by_d, ms_d), ("f1_swiglu_quant", by_sw, ms_sw),
-                          ("f1_moe_combine", by_c, ms_c)):
+    for name, by, ms_, key in (("f1_moe_dispatch", by_d, ms_d, "d"), ("f1_swiglu_quant", by_sw, ms_sw, "sw"),
+                               ("f1_moe_combine", by_c, ms_c, "c")):
         res[name] = {"us": round(ms_ * 1e3, 1), "GBps": round(by / (ms_ * 1e-3) / 1e9, 1),
-                     "frac_hbm": round(by / (ms_ * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+                     "frac_hbm": round(by / (ms_ * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "cold_us": round(cold[key] * 1e3, 1),
+                     "cold_GBps": round(by / (cold[key] * 1e-3) / 1e9, 1)}
     res["f1_moe_layer"] = {"tokens": T, "rows": n, "us": round(ms_l * 1e3, 1),
                            "TFLOPs": round((f1 + f2) / (ms_l * 1e-3) / 1e12, 1),
                            "steps": "dispatch, fc1, swiglu-quant, fc2, combine"}

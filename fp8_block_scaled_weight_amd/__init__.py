@@ -27,6 +27,7 @@ FP8Q_ERR_STRIDE = 3
 FP8Q_ERR_ALIGN = 4
 FP8Q_ERR_LAUNCH = 5
 FP8Q_ERR_UNSUPPORTED = 6
+FP8Q_ERR_PRECONDITION = 7  # FP8Q_DEBUG=1: a documented precondition is violated
 FP8Q_KV_RECALIBRATE = 1
 FP8Q_ATTN_RECALIBRATE_Q = 1
 

@@ -3,9 +3,13 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <initializer_list>
+#include <vector>
 
 #include "../../include/fp8q.h"
 #include "launch.hpp"
@@ -63,6 +67,127 @@ fp8q_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+// ---------------------------------------------------------------- debug mode (FP8Q_DEBUG=1)
+// Checks of the preconditions the kernels trust, before anything is enqueued; device data
+// is read after synchronizing the call's stream.  After the launch the stream is
+// synchronized again, so a device fault is reported by the call that caused it.
+
+bool debug_on() {
+  const char* e = std::getenv("FP8Q_DEBUG");
+  return e && e[0] == '1' && e[1] == '\0';
+}
+
+// [lo, hi) byte extent of `rows` rows of `row_bytes` bytes, `pitch` bytes apart
+struct Extent {
+  uintptr_t lo = 0, hi = 0;
+  const char* name = "";
+};
+Extent extent(const void* p, int64_t rows, int64_t row_bytes, int64_t pitch, const char* name) {
+  Extent e;
+  e.name = name;
+  if (p && rows > 0 && row_bytes > 0) {
+    e.lo = reinterpret_cast<uintptr_t>(p);
+    e.hi = e.lo + static_cast<uintptr_t>((rows - 1) * pitch + row_bytes);
+  }
+  return e;
+}
+bool overlap(const Extent& a, const Extent& b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+fp8q_status check_disjoint(const std::vector<Extent>& outs, const std::vector<Extent>& ins) {
+  for (size_t o = 0; o < outs.size(); ++o) {
+    for (const Extent& i : ins)
+      if (overlap(outs[o], i))
+        return fail(FP8Q_ERR_PRECONDITION, "output %s overlaps input %s", outs[o].name, i.name);
+    for (size_t o2 = o + 1; o2 < outs.size(); ++o2)
+      if (overlap(outs[o], outs[o2]))
+        return fail(FP8Q_ERR_PRECONDITION, "output %s overlaps output %s", outs[o].name, outs[o2].name);
+  }
+  return FP8Q_OK;
+}
+
+// settle the stream before reading device data; a capturing stream cannot be read
+fp8q_status debug_sync(void* stream) {
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(FP8Q_ERR_LAUNCH, "FP8Q_DEBUG: cannot query the stream");
+  }
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(FP8Q_ERR_UNSUPPORTED, "FP8Q_DEBUG=1 reads device data and cannot run on a capturing stream");
+  const hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(FP8Q_ERR_LAUNCH, "FP8Q_DEBUG: earlier work on the stream failed: %s", hipGetErrorString(e));
+  }
+  return FP8Q_OK;
+}
+
+// rows x cols elements of T, `ld` elements apart, copied to the host
+template <class T>
+fp8q_status fetch(std::vector<T>& out, const void* p, int64_t rows, int64_t cols, int64_t ld) {
+  out.assign(static_cast<size_t>(rows > 0 && cols > 0 ? rows * cols : 0), T{});
+  if (out.empty()) return FP8Q_OK;
+  const hipError_t e = hipMemcpy2D(out.data(), cols * sizeof(T), p, ld * sizeof(T), cols * sizeof(T), rows,
+                                   hipMemcpyDeviceToHost);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(FP8Q_ERR_LAUNCH, "FP8Q_DEBUG: reading device data failed: %s", hipGetErrorString(e));
+  }
+  return FP8Q_OK;
+}
+
+fp8q_status finite_bf16(const void* p, int64_t rows, int64_t cols, int64_t ld, const char* name) {
+  std::vector<uint16_t> v;
+  fp8q_status st = fetch(v, p, rows, cols, ld);
+  for (size_t i = 0; st == FP8Q_OK && i < v.size(); ++i)
+    if ((v[i] & 0x7f80u) == 0x7f80u)
+      return fail(FP8Q_ERR_PRECONDITION, "%s[%lld][%lld] is not finite (bf16 0x%04x)", name,
+                  (long long)(i / cols), (long long)(i % cols), v[i]);
+  return st;
+}
+
+// finite fp32 values; pow2: positive powers of two (normal or subnormal)
+fp8q_status check_f32(const void* p, int64_t rows, int64_t cols, int64_t ld, const char* name, bool pow2,
+                      bool positive) {
+  std::vector<float> v;
+  fp8q_status st = fetch(v, p, rows, cols, ld);
+  for (size_t i = 0; st == FP8Q_OK && i < v.size(); ++i) {
+    const float x = v[i];
+    uint32_t b;
+    std::memcpy(&b, &x, 4);
+    const uint32_t man = b & 0x7fffffu, ex = (b >> 23) & 0xffu;
+    const bool bad = !std::isfinite(x) || (positive && !(x > 0.0f)) ||
+                     (pow2 && (!(x > 0.0f) || (ex != 0 ? man != 0 : (man & (man - 1)) != 0)));
+    if (bad)
+      return fail(FP8Q_ERR_PRECONDITION, "%s[%lld][%lld] = %g is not %s", name, (long long)(i / cols),
+                  (long long)(i % cols), (double)x,
+                  pow2 ? "a positive power of two" : (positive ? "positive and finite" : "finite"));
+  }
+  return st;
+}
+
+fp8q_status no_nan_codes(const void* p, int64_t rows, int64_t cols, int64_t ld, const char* name) {
+  std::vector<uint8_t> v;
+  fp8q_status st = fetch(v, p, rows, cols, ld);
+  for (size_t i = 0; st == FP8Q_OK && i < v.size(); ++i)
+    if ((v[i] & 0x7fu) == 0x7fu)
+      return fail(FP8Q_ERR_PRECONDITION, "%s[%lld][%lld] is an E4M3 NaN code (0x%02x)", name,
+                  (long long)(i / cols), (long long)(i % cols), v[i]);
+  return st;
+}
+
+// after the launch: report a device fault of this call
+fp8q_status finish(fp8q_status st, void* stream, const char* what) {
+  if (st != FP8Q_OK || !debug_on()) return st;
+  const hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(FP8Q_ERR_LAUNCH, "%s: device error: %s", what, hipGetErrorString(e));
+  }
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -76,6 +201,7 @@ const char* fp8q_status_string(fp8q_status s) {
     case FP8Q_ERR_ALIGN: return "FP8Q_ERR_ALIGN";
     case FP8Q_ERR_LAUNCH: return "FP8Q_ERR_LAUNCH";
     case FP8Q_ERR_UNSUPPORTED: return "FP8Q_ERR_UNSUPPORTED";
+    case FP8Q_ERR_PRECONDITION: return "FP8Q_ERR_PRECONDITION";
   }
   return "FP8Q_(unknown status)";
 }
@@ -104,6 +230,21 @@ static fp8q_status quant_weight(const fp8q_weight_desc* descs, int32_t count, vo
   fp8q_status st = check_device();
   if (st != FP8Q_OK) return st;
   if (total == 0) return ok();
+  if (debug_on()) {
+    std::vector<Extent> outs, ins;
+    for (int32_t i = 0; i < count; ++i) {
+      const fp8q_weight_desc& d = descs[i];
+      if (d.n == 0 || d.k == 0) continue;
+      outs.push_back(extent(d.q, d.n, d.k, d.ld_q, "q"));
+      outs.push_back(extent(d.s, 1, (d.n / 128) * (d.k / 128) * 4, 0, "s"));
+      ins.push_back(extent(d.w, d.n, 2 * d.k, 2 * d.ld_w, "w"));
+    }
+    st = check_disjoint(outs, ins);
+    if (st == FP8Q_OK) st = debug_sync(stream);
+    for (int32_t i = 0; st == FP8Q_OK && i < count; ++i)
+      if (descs[i].n > 0 && descs[i].k > 0) st = finite_bf16(descs[i].w, descs[i].n, descs[i].k, descs[i].ld_w, "w");
+    if (st != FP8Q_OK) return st;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   fp8q::WeightChunk chunk;
   chunk.count = 0;
@@ -128,7 +269,8 @@ static fp8q_status quant_weight(const fp8q_weight_desc* descs, int32_t count, vo
     e.kblocks = (int32_t)(d.k / 128);
     blocks += nblk;
   }
-  return launched(fp8q::launch_quant_weight_chunk(chunk, blocks, pow2, s), "quant_weight_blk128");
+  return finish(launched(fp8q::launch_quant_weight_chunk(chunk, blocks, pow2, s), "quant_weight_blk128"), stream,
+                "quant_weight_blk128");
 }
 
 fp8q_status fp8q_quant_weight_blk128(const fp8q_weight_desc* descs, int32_t count, void* stream) {
@@ -153,8 +295,17 @@ static fp8q_status quant_act(const void* x, int64_t m, int64_t k, int64_t ld_x, 
     return fail(FP8Q_ERR_ALIGN, "x/q must be 16-byte aligned with ld_x %% 8 == 0 and ld_q %% 16 == 0");
   fp8q_status st = check_device();
   if (st != FP8Q_OK) return st;
-  return launched(fp8q::launch_quant_act(x, m, k, ld_x, q, ld_q, s, ld_s, pow2, reinterpret_cast<hipStream_t>(stream)),
-                  "quant_act_g128");
+  if (debug_on()) {
+    st = check_disjoint({extent(q, m, k, ld_q, "q"), extent(s, k / 128, 4 * m, 4 * ld_s, "s")},
+                        {extent(x, m, 2 * k, 2 * ld_x, "x")});
+    if (st == FP8Q_OK) st = debug_sync(stream);
+    if (st == FP8Q_OK) st = finite_bf16(x, m, k, ld_x, "x");
+    if (st != FP8Q_OK) return st;
+  }
+  return finish(launched(fp8q::launch_quant_act(x, m, k, ld_x, q, ld_q, s, ld_s, pow2,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                         "quant_act_g128"),
+                stream, "quant_act_g128");
 }
 
 fp8q_status fp8q_quant_act_g128(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q, int64_t ld_q,
@@ -198,9 +349,21 @@ static fp8q_status gemm(const void* a, int64_t ld_a, const float* a_s, int64_t l
   st = check_device();
   if (st != FP8Q_OK) return st;
   if (m == 0) return ok();
-  return launched(fp8q::launch_gemm(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, pow2,
-                                    reinterpret_cast<hipStream_t>(stream)),
-                  "gemm_w8a8_blkscaled");
+  if (debug_on()) {
+    st = check_disjoint({extent(y, m, 2 * n, 2 * ld_y, "y")},
+                        {extent(a, m, k, ld_a, "a"), extent(a_s, k / 128, 4 * m, 4 * ld_as, "a_s"),
+                         extent(b, n, k, ld_b, "b"), extent(b_s, 1, (n / 128) * (k / 128) * 4, 0, "b_s")});
+    if (st == FP8Q_OK) st = debug_sync(stream);
+    if (st == FP8Q_OK) st = no_nan_codes(a, m, k, ld_a, "a");
+    if (st == FP8Q_OK) st = no_nan_codes(b, n, k, ld_b, "b");
+    if (st == FP8Q_OK) st = check_f32(a_s, k / 128, m, ld_as, "a_s", pow2, false);
+    if (st == FP8Q_OK) st = check_f32(b_s, n / 128, k / 128, k / 128, "b_s", pow2, false);
+    if (st != FP8Q_OK) return st;
+  }
+  return finish(launched(fp8q::launch_gemm(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, pow2,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                         "gemm_w8a8_blkscaled"),
+                stream, "gemm_w8a8_blkscaled");
 }
 
 fp8q_status fp8q_gemm_w8a8_blkscaled(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
@@ -232,9 +395,20 @@ fp8q_status fp8q_gemm_w8a8_bf16act(const void* x, int64_t ld_x, const void* b, i
   fp8q_status st = check_device();
   if (st != FP8Q_OK) return st;
   if (m == 0) return ok();
-  return launched(fp8q::launch_gemm_bf16act(x, ld_x, b, ld_b, b_s, y, ld_y, m, n, k,
-                                            reinterpret_cast<hipStream_t>(stream)),
-                  "gemm_w8a8_bf16act");
+  if (debug_on()) {
+    st = check_disjoint({extent(y, m, 2 * n, 2 * ld_y, "y")},
+                        {extent(x, m, 2 * k, 2 * ld_x, "x"), extent(b, n, k, ld_b, "b"),
+                         extent(b_s, 1, (n / 128) * (k / 128) * 4, 0, "b_s")});
+    if (st == FP8Q_OK) st = debug_sync(stream);
+    if (st == FP8Q_OK) st = finite_bf16(x, m, k, ld_x, "x");
+    if (st == FP8Q_OK) st = no_nan_codes(b, n, k, ld_b, "b");
+    if (st == FP8Q_OK) st = check_f32(b_s, n / 128, k / 128, k / 128, "b_s", false, false);
+    if (st != FP8Q_OK) return st;
+  }
+  return finish(launched(fp8q::launch_gemm_bf16act(x, ld_x, b, ld_b, b_s, y, ld_y, m, n, k,
+                                                   reinterpret_cast<hipStream_t>(stream)),
+                         "gemm_w8a8_bf16act"),
+                stream, "gemm_w8a8_bf16act");
 }
 
 static fp8q_status grouped_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
@@ -252,9 +426,34 @@ static fp8q_status grouped_gemm(const void* a, int64_t ld_a, const float* a_s, i
   st = check_device();
   if (st != FP8Q_OK) return st;
   if (total_m == 0) return ok();
-  return launched(fp8q::launch_grouped_gemm(a, ld_a, a_s, ld_as, b, b_s, group_offsets, num_groups, total_m, y,
-                                            ld_y, n, k, pow2, reinterpret_cast<hipStream_t>(stream)),
-                  "grouped_gemm_w8a8");
+  if (debug_on()) {
+    st = check_disjoint({extent(y, total_m, 2 * n, 2 * ld_y, "y")},
+                        {extent(a, total_m, k, ld_a, "a"), extent(a_s, k / 128, 4 * total_m, 4 * ld_as, "a_s"),
+                         extent(b, num_groups, n * k, n * k, "b"),
+                         extent(b_s, num_groups, (n / 128) * (k / 128) * 4, (n / 128) * (k / 128) * 4, "b_s"),
+                         extent(group_offsets, 1, 4 * ((int64_t)num_groups + 1), 0, "group_offsets")});
+    if (st == FP8Q_OK) st = debug_sync(stream);
+    std::vector<int32_t> off;
+    if (st == FP8Q_OK) st = fetch(off, group_offsets, 1, (int64_t)num_groups + 1, (int64_t)num_groups + 1);
+    if (st == FP8Q_OK) {
+      if (off[0] != 0) st = fail(FP8Q_ERR_PRECONDITION, "group_offsets[0] = %d, not 0", off[0]);
+      for (int32_t g = 0; st == FP8Q_OK && g < num_groups; ++g)
+        if (off[g + 1] < off[g])
+          st = fail(FP8Q_ERR_PRECONDITION, "group_offsets decrease at %d (%d -> %d)", g, off[g], off[g + 1]);
+      if (st == FP8Q_OK && off[num_groups] != total_m)
+        st = fail(FP8Q_ERR_PRECONDITION, "group_offsets[%d] = %d, not total_m = %lld", num_groups, off[num_groups],
+                  (long long)total_m);
+    }
+    if (st == FP8Q_OK) st = no_nan_codes(a, total_m, k, ld_a, "a");
+    if (st == FP8Q_OK) st = no_nan_codes(b, num_groups * n, k, k, "b");
+    if (st == FP8Q_OK) st = check_f32(a_s, k / 128, total_m, ld_as, "a_s", pow2, false);
+    if (st == FP8Q_OK) st = check_f32(b_s, num_groups * (n / 128), k / 128, k / 128, "b_s", pow2, false);
+    if (st != FP8Q_OK) return st;
+  }
+  return finish(launched(fp8q::launch_grouped_gemm(a, ld_a, a_s, ld_as, b, b_s, group_offsets, num_groups, total_m,
+                                                   y, ld_y, n, k, pow2, reinterpret_cast<hipStream_t>(stream)),
+                         "grouped_gemm_w8a8"),
+                stream, "grouped_gemm_w8a8");
 }
 
 fp8q_status fp8q_grouped_gemm_w8a8(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
@@ -292,10 +491,35 @@ fp8q_status fp8q_kv_quant(const void* k, int64_t ld_k, const void* v, int64_t ld
   fp8q_status st = check_device();
   if (st != FP8Q_OK) return st;
   if (num_tokens == 0 && !(flags & FP8Q_KV_RECALIBRATE)) return ok();
-  return launched(fp8q::launch_kv_quant(k, ld_k, v, ld_v, num_tokens, num_kv_heads, slot_mapping, k_cache, v_cache,
-                                        k_scale, v_scale, fp8_range, (flags & FP8Q_KV_RECALIBRATE) != 0,
-                                        reinterpret_cast<hipStream_t>(stream)),
-                  "kv_quant");
+  if (debug_on()) {
+    const bool recal = (flags & FP8Q_KV_RECALIBRATE) != 0;
+    const int64_t cache_bytes = num_pages * page_size * row;
+    std::vector<Extent> outs = {extent(k_cache, 1, cache_bytes, 0, "k_cache"),
+                                extent(v_cache, 1, cache_bytes, 0, "v_cache")};
+    std::vector<Extent> ins = {extent(k, num_tokens, 2 * row, 2 * ld_k, "k"), extent(v, num_tokens, 2 * row, 2 * ld_v, "v"),
+                               extent(slot_mapping, 1, 8 * num_tokens, 0, "slot_mapping")};
+    (recal ? outs : ins).push_back(extent(k_scale, 1, 4, 0, "k_scale"));
+    (recal ? outs : ins).push_back(extent(v_scale, 1, 4, 0, "v_scale"));
+    st = check_disjoint(outs, ins);
+    if (st == FP8Q_OK) st = debug_sync(stream);
+    std::vector<int64_t> slots;
+    if (st == FP8Q_OK) st = fetch(slots, slot_mapping, 1, num_tokens, num_tokens);
+    for (int64_t t = 0; st == FP8Q_OK && t < num_tokens; ++t)
+      if (slots[t] >= num_pages * page_size)
+        st = fail(FP8Q_ERR_PRECONDITION, "slot_mapping[%lld] = %lld is not below num_pages * page_size = %lld",
+                  (long long)t, (long long)slots[t], (long long)(num_pages * page_size));
+    if (st == FP8Q_OK) st = finite_bf16(k, num_tokens, row, ld_k, "k");
+    if (st == FP8Q_OK) st = finite_bf16(v, num_tokens, row, ld_v, "v");
+    if (st == FP8Q_OK && !recal) st = check_f32(k_scale, 1, 1, 1, "k_scale", false, true);
+    if (st == FP8Q_OK && !recal) st = check_f32(v_scale, 1, 1, 1, "v_scale", false, true);
+    if (st != FP8Q_OK) return st;
+  }
+  return finish(launched(fp8q::launch_kv_quant(k, ld_k, v, ld_v, num_tokens, num_kv_heads, slot_mapping, k_cache,
+                                               v_cache, k_scale, v_scale, fp8_range,
+                                               (flags & FP8Q_KV_RECALIBRATE) != 0,
+                                               reinterpret_cast<hipStream_t>(stream)),
+                         "kv_quant"),
+                stream, "kv_quant");
 }
 
 fp8q_status fp8q_moe_dispatch(const void* xq, int64_t ld_xq, const float* xs, int64_t ld_xs, const int16_t* topk_ids,
@@ -321,9 +545,22 @@ fp8q_status fp8q_moe_dispatch(const void* xq, int64_t ld_xq, const float* xs, in
   }
   fp8q_status st = check_device();
   if (st != FP8Q_OK) return st;
-  return launched(fp8q::launch_moe_dispatch(xq, ld_xq, xs, ld_xs, topk_ids, num_tokens, topk, num_experts, k, aq,
-                                            ld_aq, as, ld_as, offsets, row_of, reinterpret_cast<hipStream_t>(stream)),
-                  "moe_dispatch");
+  if (debug_on()) {
+    st = check_disjoint({extent(aq, n, k, ld_aq, "aq"), extent(as, k / 128, 4 * n, 4 * ld_as, "as"),
+                         extent(offsets, 1, 4 * ((int64_t)num_experts + 1), 0, "offsets"),
+                         extent(row_of, 1, 4 * n, 0, "row_of")},
+                        {extent(xq, num_tokens, k, ld_xq, "xq"), extent(xs, k / 128, 4 * num_tokens, 4 * ld_xs, "xs"),
+                         extent(topk_ids, 1, 2 * n, 0, "topk_ids")});
+    if (st == FP8Q_OK) st = debug_sync(stream);
+    if (st == FP8Q_OK && n > 0) st = no_nan_codes(xq, num_tokens, k, ld_xq, "xq");
+    if (st == FP8Q_OK && n > 0) st = check_f32(xs, k / 128, num_tokens, ld_xs, "xs", false, false);
+    if (st != FP8Q_OK) return st;
+  }
+  return finish(launched(fp8q::launch_moe_dispatch(xq, ld_xq, xs, ld_xs, topk_ids, num_tokens, topk, num_experts, k,
+                                                   aq, ld_aq, as, ld_as, offsets, row_of,
+                                                   reinterpret_cast<hipStream_t>(stream)),
+                         "moe_dispatch"),
+                stream, "moe_dispatch");
 }
 
 fp8q_status fp8q_swiglu_quant_g128(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q, int64_t ld_q,
@@ -340,8 +577,36 @@ fp8q_status fp8q_swiglu_quant_g128(const void* h, int64_t m, int64_t n, int64_t 
     return fail(FP8Q_ERR_ALIGN, "h/q must be 16-byte aligned with ld_h %% 8 == 0 and ld_q %% 16 == 0");
   fp8q_status st = check_device();
   if (st != FP8Q_OK) return st;
-  return launched(fp8q::launch_swiglu_quant(h, m, n, ld_h, q, ld_q, s, ld_s, reinterpret_cast<hipStream_t>(stream)),
-                  "swiglu_quant_g128");
+  if (debug_on()) {
+    st = check_disjoint({extent(q, m, n, ld_q, "q"), extent(s, n / 128, 4 * m, 4 * ld_s, "s")},
+                        {extent(h, m, 4 * n, 2 * ld_h, "h")});
+    if (st == FP8Q_OK) st = debug_sync(stream);
+    std::vector<uint16_t> hv;
+    if (st == FP8Q_OK) st = fetch(hv, h, m, 2 * n, ld_h);
+    auto dec = [](uint16_t b) {
+      const uint32_t u = (uint32_t)b << 16;
+      float f;
+      std::memcpy(&f, &u, 4);
+      return (double)f;
+    };
+    for (int64_t r = 0; st == FP8Q_OK && r < m; ++r)
+      for (int64_t c = 0; st == FP8Q_OK && c < n; ++c) {
+        const uint16_t gb = hv[r * 2 * n + c], ub = hv[r * 2 * n + n + c];
+        if ((gb & 0x7f80u) == 0x7f80u || (ub & 0x7f80u) == 0x7f80u) {
+          st = fail(FP8Q_ERR_PRECONDITION, "h[%lld][%lld] or its up value is not finite", (long long)r, (long long)c);
+          break;
+        }
+        const double g = dec(gb), a = g / (1.0 + std::exp(-g)) * dec(ub);
+        if (std::fabs(a) / 448.0 > 3.4028234663852886e38)
+          st = fail(FP8Q_ERR_PRECONDITION, "silu(h[%lld][%lld]) * up = %g: its group's amax / 448 exceeds binary32",
+                    (long long)r, (long long)c, a);
+      }
+    if (st != FP8Q_OK) return st;
+  }
+  return finish(launched(fp8q::launch_swiglu_quant(h, m, n, ld_h, q, ld_q, s, ld_s,
+                                                   reinterpret_cast<hipStream_t>(stream)),
+                         "swiglu_quant_g128"),
+                stream, "swiglu_quant_g128");
 }
 
 fp8q_status fp8q_moe_combine(const void* y, int64_t ld_y, const int32_t* row_of, const float* weights,
@@ -360,9 +625,29 @@ fp8q_status fp8q_moe_combine(const void* y, int64_t ld_y, const int32_t* row_of,
   fp8q_status st = check_device();
   if (st != FP8Q_OK) return st;
   if (num_tokens == 0) return ok();
-  return launched(fp8q::launch_moe_combine(y, ld_y, row_of, weights, num_tokens, topk, hidden, out, ld_out,
-                                           reinterpret_cast<hipStream_t>(stream)),
-                  "moe_combine");
+  if (debug_on()) {
+    // y's rows are not passed: its extent is taken up to the largest row the call reads
+    const int64_t entries = num_tokens * topk;
+    st = debug_sync(stream);
+    std::vector<int32_t> rows;
+    if (st == FP8Q_OK) st = fetch(rows, row_of, 1, entries, entries);
+    int64_t last = -1;
+    for (int64_t i = 0; st == FP8Q_OK && i < entries; ++i) {
+      if (rows[i] < -1)
+        st = fail(FP8Q_ERR_PRECONDITION, "row_of[%lld] = %d is neither -1 nor a row", (long long)i, rows[i]);
+      last = rows[i] > last ? rows[i] : last;
+    }
+    if (st == FP8Q_OK)
+      st = check_disjoint({extent(out, num_tokens, 2 * hidden, 2 * ld_out, "out")},
+                          {extent(y, last + 1, 2 * hidden, 2 * ld_y, "y"), extent(row_of, 1, 4 * entries, 0, "row_of"),
+                           extent(weights, 1, 4 * entries, 0, "weights")});
+    if (st == FP8Q_OK) st = check_f32(weights, 1, entries, entries, "weights", false, false);
+    if (st != FP8Q_OK) return st;
+  }
+  return finish(launched(fp8q::launch_moe_combine(y, ld_y, row_of, weights, num_tokens, topk, hidden, out, ld_out,
+                                                  reinterpret_cast<hipStream_t>(stream)),
+                         "moe_combine"),
+                stream, "moe_combine");
 }
 
 fp8q_status fp8q_paged_decode_attention(const void* q, int64_t ld_q, const void* k_cache, const void* v_cache,
@@ -393,11 +678,50 @@ fp8q_status fp8q_paged_decode_attention(const void* q, int64_t ld_q, const void*
   fp8q_status st = check_device();
   if (st != FP8Q_OK) return st;
   if (num_seqs == 0 && !(flags & FP8Q_ATTN_RECALIBRATE_Q)) return ok();
-  return launched(fp8q::launch_decode_attention(q, ld_q, k_cache, v_cache, block_table, ld_bt, seq_lens, num_seqs,
-                                                num_q_heads, num_kv_heads, page_size, q_scale, k_scale, v_scale,
-                                                sm_scale, fp8_range, (flags & FP8Q_ATTN_RECALIBRATE_Q) != 0, out,
-                                                ld_out, reinterpret_cast<hipStream_t>(stream)),
-                  "paged_decode_attention");
+  if (debug_on()) {
+    const bool recal = (flags & FP8Q_ATTN_RECALIBRATE_Q) != 0;
+    const int64_t cache_bytes = num_pages * page_size * (int64_t)num_kv_heads * 128;
+    std::vector<Extent> outs = {extent(out, num_seqs, 2 * row, 2 * ld_out, "out")};
+    std::vector<Extent> ins = {extent(q, num_seqs, 2 * row, 2 * ld_q, "q"),
+                               extent(k_cache, 1, cache_bytes, 0, "k_cache"),
+                               extent(v_cache, 1, cache_bytes, 0, "v_cache"),
+                               extent(block_table, num_seqs, 4 * ld_bt, 4 * ld_bt, "block_table"),
+                               extent(seq_lens, 1, 4 * (int64_t)num_seqs, 0, "seq_lens"),
+                               extent(k_scale, 1, 4, 0, "k_scale"), extent(v_scale, 1, 4, 0, "v_scale")};
+    (recal ? outs : ins).push_back(extent(q_scale, 1, 4, 0, "q_scale"));
+    st = check_disjoint(outs, ins);
+    if (st == FP8Q_OK) st = debug_sync(stream);
+    std::vector<int32_t> lens, table;
+    if (st == FP8Q_OK) st = fetch(lens, seq_lens, 1, num_seqs, num_seqs);
+    if (st == FP8Q_OK) st = fetch(table, block_table, num_seqs, ld_bt, ld_bt);
+    for (int32_t b = 0; st == FP8Q_OK && b < num_seqs; ++b) {
+      if (lens[b] < 0 || (int64_t)lens[b] > ld_bt * page_size) {
+        st = fail(FP8Q_ERR_PRECONDITION, "seq_lens[%d] = %d is outside [0, ld_bt * page_size]", b, lens[b]);
+        break;
+      }
+      const int64_t used = ((int64_t)lens[b] + page_size - 1) / page_size;
+      for (int64_t i = 0; i < used; ++i) {
+        const int32_t id = table[(size_t)b * ld_bt + i];
+        if (id < 0 || id >= num_pages) {
+          st = fail(FP8Q_ERR_PRECONDITION, "block_table[%d][%lld] = %d is not a page below num_pages = %lld", b,
+                    (long long)i, id, (long long)num_pages);
+          break;
+        }
+      }
+    }
+    if (st == FP8Q_OK) st = finite_bf16(q, num_seqs, row, ld_q, "q");
+    if (st == FP8Q_OK) st = check_f32(k_scale, 1, 1, 1, "k_scale", false, true);
+    if (st == FP8Q_OK) st = check_f32(v_scale, 1, 1, 1, "v_scale", false, true);
+    if (st == FP8Q_OK && !recal) st = check_f32(q_scale, 1, 1, 1, "q_scale", false, true);
+    if (st != FP8Q_OK) return st;
+  }
+  return finish(launched(fp8q::launch_decode_attention(q, ld_q, k_cache, v_cache, block_table, ld_bt, seq_lens,
+                                                       num_seqs, num_q_heads, num_kv_heads, page_size, q_scale,
+                                                       k_scale, v_scale, sm_scale, fp8_range,
+                                                       (flags & FP8Q_ATTN_RECALIBRATE_Q) != 0, out, ld_out,
+                                                       reinterpret_cast<hipStream_t>(stream)),
+                         "paged_decode_attention"),
+                stream, "paged_decode_attention");
 }
 
 }  // extern "C"

@@ -66,7 +66,20 @@
  *   - Preconditions not checked (undefined behaviour if violated): inputs are finite;
  *     outputs do not overlap inputs or each other; group offsets are nondecreasing
  *     with offsets[0] = 0 and offsets[G] = total_m; every KV slot is below
- *     num_pages * page_size.
+ *     num_pages * page_size; and the per-call preconditions stated below.
+ *   - Debug mode: with the environment variable FP8Q_DEBUG=1 (read at every call) a call
+ *     also checks those preconditions before it enqueues anything, and returns
+ *     FP8Q_ERR_PRECONDITION, with the offending element in fp8q_last_error(), if one
+ *     fails.  It checks that outputs overlap no input or other output (byte extents);
+ *     and, after synchronizing `stream` and copying the data to the host: bf16 and fp32
+ *     inputs are finite, FP8 operands of the GEMMs hold no NaN code (0x7F/0xFF), GEMM
+ *     scales are finite (powers of two for *_ue8m0), group offsets and KV slots are in
+ *     range, and the attention call's lengths, page ids and stored scales are valid.
+ *     Not checked even then: the FP8 codes of the KV caches, whose size makes a host
+ *     copy impractical, and the combine's row indices against the rows of y, which the
+ *     call is not told.  After the launch a debug-mode call synchronizes `stream`, so a
+ *     device fault is reported (FP8Q_ERR_LAUNCH) by the call that caused it.  Debug
+ *     mode cannot run on a stream under graph capture (FP8Q_ERR_UNSUPPORTED).
  *   - Calls are thread-safe.
  */
 #ifndef FP8Q_H
@@ -87,8 +100,11 @@ typedef enum fp8q_status {
                                count/num_groups < 1, head_dim != 128, page_size < 1 */
   FP8Q_ERR_STRIDE = 3,      /* a leading dimension is smaller than the row length */
   FP8Q_ERR_ALIGN = 4,       /* a data pointer or row pitch is not 16-byte aligned */
-  FP8Q_ERR_LAUNCH = 5,      /* the HIP runtime refused a launch */
-  FP8Q_ERR_UNSUPPORTED = 6  /* no gfx950 device is current */
+  FP8Q_ERR_LAUNCH = 5,      /* the HIP runtime refused a launch (with FP8Q_DEBUG=1 also:
+                               the kernel faulted, or a debug read of device data failed) */
+  FP8Q_ERR_UNSUPPORTED = 6, /* no gfx950 device is current; with FP8Q_DEBUG=1 also: the
+                               stream is being captured */
+  FP8Q_ERR_PRECONDITION = 7 /* FP8Q_DEBUG=1 only: a precondition listed above is violated */
 } fp8q_status;
 
 /* Static string naming a status code. */

@@ -43,7 +43,8 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_status_strings():
     assert fq.abi_version() == 1
     for code, name in ((0, "FP8Q_OK"), (1, "FP8Q_ERR_NULL"), (2, "FP8Q_ERR_SHAPE"), (3, "FP8Q_ERR_STRIDE"),
-                       (4, "FP8Q_ERR_ALIGN"), (5, "FP8Q_ERR_LAUNCH"), (6, "FP8Q_ERR_UNSUPPORTED")):
+                       (4, "FP8Q_ERR_ALIGN"), (5, "FP8Q_ERR_LAUNCH"), (6, "FP8Q_ERR_UNSUPPORTED"),
+                       (7, "FP8Q_ERR_PRECONDITION")):
         assert fq.status_string(code) == name
 
 
