@@ -680,6 +680,20 @@ def legs(torch, fq, synth, dev):
         fq.fp8q_moe_combine(y2, row_of, rw, out)
 
     ms_l = _time(torch, layer, 5, reps=2)
+
+    # fc1 with SwiGLU and fc2's input quantization fused into its epilogue (no bf16 fc1
+    # output): alone, and in the layer in place of fc1 + SwiGLU-quant
+    q2f = torch.empty((n, I), dtype=torch.uint8, device=dev)
+    s2f = torch.empty((I // 128, n), dtype=torch.float32, device=dev)
+    ms_f1f = _time(torch, lambda: fq.fp8q_grouped_gemm_swiglu_quant(dq, dsc, b1, b1s, doff, q2f, s2f), 10)
+
+    def layer_fused():
+        fq.fp8q_moe_dispatch(xq, xsc, ids, E, dq, dsc, doff, row_of)
+        fq.fp8q_grouped_gemm_swiglu_quant(dq, dsc, b1, b1s, doff, q2f, s2f)
+        fq.fp8q_grouped_gemm_w8a8(q2f, s2f, b2, b2s, doff, y2)
+        fq.fp8q_moe_combine(y2, row_of, rw, out)
+
+    ms_lf = _time(torch, layer_fused, 5, reps=2)
     by_d = T * H + 4 * T * H / 128 + 2 * n + n * H + 4 * n * H / 128 + 4 * n + 4 * (E + 1)
     by_sw = n * 2 * I * 2 + n * I + 4 * n * I / 128
     by_c = n * H * 2 + 8 * n + T * H * 2
@@ -692,7 +706,13 @@ def legs(torch, fq, synth, dev):
     res["f1_moe_layer"] = {"tokens": T, "rows": n, "us": round(ms_l * 1e3, 1),
                            "TFLOPs": round((f1 + f2) / (ms_l * 1e-3) / 1e12, 1),
                            "steps": "dispatch, fc1, swiglu-quant, fc2, combine"}
-    del xq, dq, q2, out
+    res["a4_moe_fc1_swiglu_fused"] = {"rows": n, "us": round(ms_f1f * 1e3, 1),
+                                      "TFLOPs": round(f1 / (ms_f1f * 1e-3) / 1e12, 1),
+                                      "unfused_fc1_plus_swiglu_us": round((ms1 + ms_sw) * 1e3, 1)}
+    res["f1_moe_layer_fused"] = {"tokens": T, "rows": n, "us": round(ms_lf * 1e3, 1),
+                                 "TFLOPs": round((f1 + f2) / (ms_lf * 1e-3) / 1e12, 1),
+                                 "steps": "dispatch, fc1 + swiglu-quant fused, fc2, combine"}
+    del xq, dq, q2, out, q2f, s2f
     del fc1, fc2, fc1q, fc2q, x, xs_rows, a1q, a2, a2q, y1, y2
     torch.cuda.empty_cache()
 

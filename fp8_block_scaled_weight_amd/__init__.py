@@ -36,7 +36,7 @@ EXPORTED = (
     "fp8q_quant_act_g128", "fp8q_gemm_w8a8_blkscaled", "fp8q_grouped_gemm_w8a8", "fp8q_kv_quant",
     "fp8q_quant_weight_blk128_ue8m0", "fp8q_quant_act_g128_ue8m0", "fp8q_gemm_w8a8_ue8m0",
     "fp8q_grouped_gemm_w8a8_ue8m0", "fp8q_moe_dispatch", "fp8q_swiglu_quant_g128", "fp8q_moe_combine",
-    "fp8q_gemm_w8a8_bf16act", "fp8q_paged_decode_attention",
+    "fp8q_gemm_w8a8_bf16act", "fp8q_paged_decode_attention", "fp8q_grouped_gemm_swiglu_quant",
 )
 
 
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.fp8q_kv_quant.argtypes = [vp, i64, vp, i64, i64, i32, i32, vp, vp, vp, i32, i64, vp, vp, f32, u32, vp]
         L.fp8q_moe_dispatch.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i64, vp, i64, vp, i64, vp, vp, vp]
         L.fp8q_swiglu_quant_g128.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp]
+        L.fp8q_grouped_gemm_swiglu_quant.argtypes = [vp, i64, vp, i64, vp, vp, vp, i32, i64, vp, i64, vp, i64,
+                                                     i64, i64, vp]
         L.fp8q_moe_combine.argtypes = [vp, i64, vp, vp, i64, i32, i64, vp, i64, vp]
         for name in EXPORTED[3:]:
             getattr(L, name).restype = ctypes.c_int
@@ -292,6 +294,29 @@ def fp8q_swiglu_quant_g128(h: torch.Tensor, q: torch.Tensor, s: torch.Tensor, st
         raise ValueError("q must be [m, n] and s [n/128, ld_s] with unit column stride")
     _check(lib().fp8q_swiglu_quant_g128(_dev(h, "h", BF16), m, n, _rows(h, "h"), _dev(q, "q", FP8), _rows(q, "q"),
                                         _dev(s, "s", F32), s.stride(0), _stream(stream)), "fp8q_swiglu_quant_g128")
+
+
+def fp8q_grouped_gemm_swiglu_quant(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
+                                   group_offsets: torch.Tensor, q: torch.Tensor, s: torch.Tensor,
+                                   stream=None) -> None:
+    """MoE fc1 with SwiGLU and fc2's 1x128 input quantization fused: b [G, 2*n_half, k] holds each
+    expert's gate rows, then its up rows.  Equal, bit for bit, to fp8q_grouped_gemm_w8a8 into a
+    bf16 [total_m, 2*n_half] buffer followed by fp8q_swiglu_quant_g128 on it: q [total_m, n_half]
+    fp8, s [n_half/128, ld_s] fp32."""
+    total_m, k = a.shape
+    g, n2, kb = b.shape
+    n_half = n2 // 2
+    if kb != k or n2 % 2 or tuple(q.shape) != (total_m, n_half) or not b.is_contiguous() or not b_s.is_contiguous():
+        raise ValueError("shape mismatch between a, b and q")
+    if s.dim() != 2 or s.shape[0] != n_half // 128 or s.stride(1) != 1:
+        raise ValueError("s must be [n_half/128, ld_s] with unit column stride")
+    if group_offsets.numel() != g + 1:
+        raise ValueError("group_offsets must have G+1 entries")
+    _check(lib().fp8q_grouped_gemm_swiglu_quant(
+        _dev(a, "a", FP8), _rows(a, "a"), _dev(a_s, "a_s", F32), a_s.stride(0), _dev(b, "b", FP8),
+        _dev(b_s, "b_s", F32), _dev(group_offsets, "group_offsets", (torch.int32,)), g, total_m,
+        _dev(q, "q", FP8), _rows(q, "q"), _dev(s, "s", F32), s.stride(0), n_half, k, _stream(stream)),
+        "fp8q_grouped_gemm_swiglu_quant")
 
 
 def fp8q_moe_combine(y: torch.Tensor, row_of: torch.Tensor, weights: torch.Tensor, out: torch.Tensor,

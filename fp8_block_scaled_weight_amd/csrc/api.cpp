@@ -469,6 +469,60 @@ fp8q_status fp8q_grouped_gemm_w8a8_ue8m0(const void* a, int64_t ld_a, const floa
   return grouped_gemm(a, ld_a, a_s, ld_as, b, b_s, group_offsets, num_groups, total_m, y, ld_y, n, k, stream, true);
 }
 
+fp8q_status fp8q_grouped_gemm_swiglu_quant(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
+                                           const void* b, const float* b_s, const int32_t* group_offsets,
+                                           int32_t num_groups, int64_t total_m, void* q, int64_t ld_q, float* s,
+                                           int64_t ld_s, int64_t n_half, int64_t k, void* stream) {
+  if (num_groups < 1) return fail(FP8Q_ERR_SHAPE, "num_groups must be >= 1 (got %d)", num_groups);
+  if (total_m < 0 || n_half < 0 || k < 0) return fail(FP8Q_ERR_SHAPE, "negative shape");
+  if (n_half == 0 || n_half % 128 || k == 0 || k % 128)
+    return fail(FP8Q_ERR_SHAPE, "n_half=%lld and k=%lld must be positive multiples of 128", (long long)n_half,
+                (long long)k);
+  if (total_m > 0) {
+    if (!a || !a_s || !b || !b_s || !group_offsets || !q || !s) return fail(FP8Q_ERR_NULL, "NULL pointer");
+    if (ld_a < k || ld_as < total_m || ld_q < n_half || ld_s < total_m)
+      return fail(FP8Q_ERR_STRIDE, "ld_a < k, ld_as < total_m, ld_q < n_half or ld_s < total_m");
+    if (!aligned16(a) || !aligned16(b) || !aligned16(q) || ld_a % 16 || ld_q % 16 || !aligned4(a_s) ||
+        !aligned4(b_s) || !aligned4(s) || !aligned4(group_offsets))
+      return fail(FP8Q_ERR_ALIGN, "a/b/q must be 16-byte aligned with ld_a, ld_q multiples of 16");
+    if (total_m * ld_a > kMaxOperandBytes || ld_as * 4 > kMaxOperandBytes || 2 * n_half * k > kMaxOperandBytes)
+      return fail(FP8Q_ERR_SHAPE, "an operand spans more than 2 GiB");
+  }
+  fp8q_status st = check_device();
+  if (st != FP8Q_OK) return st;
+  if (total_m == 0) return ok();
+  if (debug_on()) {
+    const int64_t bs_bytes = (2 * n_half / 128) * (k / 128) * 4;
+    st = check_disjoint({extent(q, total_m, n_half, ld_q, "q"), extent(s, n_half / 128, 4 * total_m, 4 * ld_s, "s")},
+                        {extent(a, total_m, k, ld_a, "a"), extent(a_s, k / 128, 4 * total_m, 4 * ld_as, "a_s"),
+                         extent(b, num_groups, 2 * n_half * k, 2 * n_half * k, "b"),
+                         extent(b_s, num_groups, bs_bytes, bs_bytes, "b_s"),
+                         extent(group_offsets, 1, 4 * ((int64_t)num_groups + 1), 0, "group_offsets")});
+    if (st == FP8Q_OK) st = debug_sync(stream);
+    std::vector<int32_t> off;
+    if (st == FP8Q_OK) st = fetch(off, group_offsets, 1, (int64_t)num_groups + 1, (int64_t)num_groups + 1);
+    if (st == FP8Q_OK) {
+      if (off[0] != 0) st = fail(FP8Q_ERR_PRECONDITION, "group_offsets[0] = %d, not 0", off[0]);
+      for (int32_t g = 0; st == FP8Q_OK && g < num_groups; ++g)
+        if (off[g + 1] < off[g])
+          st = fail(FP8Q_ERR_PRECONDITION, "group_offsets decrease at %d (%d -> %d)", g, off[g], off[g + 1]);
+      if (st == FP8Q_OK && off[num_groups] != total_m)
+        st = fail(FP8Q_ERR_PRECONDITION, "group_offsets[%d] = %d, not total_m = %lld", num_groups, off[num_groups],
+                  (long long)total_m);
+    }
+    if (st == FP8Q_OK) st = no_nan_codes(a, total_m, k, ld_a, "a");
+    if (st == FP8Q_OK) st = no_nan_codes(b, num_groups * 2 * n_half, k, k, "b");
+    if (st == FP8Q_OK) st = check_f32(a_s, k / 128, total_m, ld_as, "a_s", false, false);
+    if (st == FP8Q_OK) st = check_f32(b_s, num_groups * (2 * n_half / 128), k / 128, k / 128, "b_s", false, false);
+    if (st != FP8Q_OK) return st;
+  }
+  return finish(launched(fp8q::launch_grouped_swiglu(a, ld_a, a_s, ld_as, b, b_s, group_offsets, num_groups, total_m,
+                                                     n_half, k, q, ld_q, s, ld_s,
+                                                     reinterpret_cast<hipStream_t>(stream)),
+                         "grouped_gemm_swiglu_quant"),
+                stream, "grouped_gemm_swiglu_quant");
+}
+
 fp8q_status fp8q_kv_quant(const void* k, int64_t ld_k, const void* v, int64_t ld_v, int64_t num_tokens,
                           int32_t num_kv_heads, int32_t head_dim, const int64_t* slot_mapping, void* k_cache,
                           void* v_cache, int32_t page_size, int64_t num_pages, float* k_scale, float* v_scale,

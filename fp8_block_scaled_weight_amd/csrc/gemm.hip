@@ -33,6 +33,7 @@
 
 #include "e4m3.hpp"
 #include "launch.hpp"
+#include "swiglu.hpp"
 
 namespace fp8q {
 
@@ -136,13 +137,29 @@ __device__ __forceinline__ T lds_ld(const uint8_t FP8Q_LDS* base, uint32_t off) 
   return *reinterpret_cast<const T FP8Q_LDS*>(base + off);
 }
 
-template <class C, bool POW2>
+// SW (MoE fc1 with SwiGLU fused): B holds [gate; up] rows, `half` each.  A 256-wide tile
+// jt = n0 / 256 multiplies gate rows 128jt .. +127 (tile columns 0..127) and up rows
+// half + 128jt .. +127 (columns 128..255), and its epilogue writes, instead of y, the
+// SwiGLU of the bf16-rounded outputs quantized per 1x128 group: codes q[m][128jt + c],
+// scale s[jt * ld_s + m].
+struct SwigluOut {
+  uint8_t* q = nullptr;
+  int64_t ld_q = 0;
+  float* s = nullptr;
+  int64_t ld_s = 0;
+  int64_t half = 0;
+};
+
+template <class C, bool POW2, bool SW = false>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t ld_a, int64_t a_rows,
                                           const float* __restrict__ as, int64_t ld_as,
                                           const uint8_t* __restrict__ b, int64_t ld_b,
                                           const float* __restrict__ bs, int kblocks,
                                           uint16_t* __restrict__ y, int64_t ld_y, int64_t m0, int64_t m_end,
-                                          int64_t n0, uint8_t FP8Q_LDS* lds) {
+                                          int64_t n0, uint8_t FP8Q_LDS* lds, const SwigluOut sw = SwigluOut{}) {
+  static_assert(!SW || (C::BN == 256 && C::TN == 64 && C::WAVES_N == 4 && C::THREADS == 512 && C::BM % 64 == 0),
+                "the fused SwiGLU epilogue assumes the 256x256 tile");
+  const int64_t jt = n0 / 256;  // SW: the tile's 128-row gate and up blocks
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -157,7 +174,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
     const int r = (i * C::WAVES + wave) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ swz(r);
     if (i < C::LOADS_W) {
-      src[i] = (uint32_t)((n0 + r) * ld_b) + chunk * 16;
+      const int64_t wr = SW ? (r < 128 ? 128 * jt + r : sw.half + 128 * jt + (r - 128)) : n0 + r;
+      src[i] = (uint32_t)(wr * ld_b) + chunk * 16;
     } else {
       int64_t m = m0 + (r - C::BN);
       m = m < m_end ? m : m_end - 1;
@@ -175,12 +193,13 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
   // weight scales: every wave copies the tile's NWS weight scales (lanes SPW ..
   // SPW+NWS-1) into its own slots, so that each wave issues the same number of copies
   const bool wsc_lane = lane >= C::SPW && lane < C::SPW + C::NWS;
-  const uint32_t wsrc = (uint32_t)(((n0 / 128) + (lane - C::SPW)) * kblocks * 4);
+  const int64_t wsrow = SW ? ((lane - C::SPW) == 0 ? jt : sw.half / 128 + jt) : (n0 / 128) + (lane - C::SPW);
+  const uint32_t wsrc = (uint32_t)(wsrow * kblocks * 4);
 
   const v4i ra = make_rsrc(a, (uint32_t)(a_rows * ld_a));
-  const v4i rb = make_rsrc(b, (uint32_t)((n0 + C::BN) * ld_b));
+  const v4i rb = make_rsrc(b, (uint32_t)((SW ? 2 * sw.half : n0 + C::BN) * ld_b));
   const v4i rsa = make_rsrc(as, (uint32_t)(ld_as * kblocks * 4));
-  const v4i rsb = make_rsrc(bs, (uint32_t)((n0 / 128 + C::NWS) * kblocks * 4));
+  const v4i rsb = make_rsrc(bs, (uint32_t)((SW ? 2 * sw.half / 128 : n0 / 128 + C::NWS) * kblocks * 4));
 
   auto issue = [&](int kb, int stage) {
     const uint32_t dst = lds_base + (uint32_t)(stage * C::STAGE_BYTES);
@@ -387,6 +406,34 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
         o.y = bf16_rne(acc[i][j][4 * q4 + 2]) | (bf16_rne(acc[i][j][4 * q4 + 3]) << 16);
         *reinterpret_cast<u32x2 FP8Q_LDS*>(ep + row * (C::TN * 2) + chunk * 16 + 8 * g) = o;
       }
+  if constexpr (SW) {
+    // every wave's block is staged; 8 lanes per tile row take its 128 outputs, 16 each:
+    // gate values from the wave block of columns 16cc.., up values from the block 128
+    // columns further, both at the row's swizzled chunks 2(cc % 4) and 2(cc % 4) + 1
+    __syncthreads();
+    const int cc = lane & 7;
+#pragma unroll 1
+    for (int p = 0; p < C::BM / 64; ++p) {
+      const int r = p * 64 + (tid >> 3);
+      const int lr = r % C::TM, x = (lr / RPW) & (CPR - 1), c0 = 2 * (cc % 4);
+      const uint8_t FP8Q_LDS* gb = lds + ((r / C::TM) * 4 + cc / 4) * (C::TM * C::TN * 2) + lr * (C::TN * 2);
+      const uint8_t FP8Q_LDS* ub = gb + 2 * (C::TM * C::TN * 2);
+      const u32x4 g0 = *reinterpret_cast<const u32x4 FP8Q_LDS*>(gb + ((c0 ^ x) << 4));
+      const u32x4 g1 = *reinterpret_cast<const u32x4 FP8Q_LDS*>(gb + (((c0 + 1) ^ x) << 4));
+      const u32x4 u0 = *reinterpret_cast<const u32x4 FP8Q_LDS*>(ub + ((c0 ^ x) << 4));
+      const u32x4 u1 = *reinterpret_cast<const u32x4 FP8Q_LDS*>(ub + (((c0 + 1) ^ x) << 4));
+      const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      const int64_t m = m0 + r;
+      uint32_t o[4];
+      float scale;
+      if (swiglu_quant16(gw, uw, m < m_end, o, scale)) {
+        if (cc == 0) sw.s[jt * sw.ld_s + m] = scale;
+        store_plain(sw.q + m * sw.ld_q + jt * 128 + cc * 16, make_uint4(o[0], o[1], o[2], o[3]));
+      }
+    }
+    return;
+  }
   const int c_in = lane % CPR;
 #pragma unroll
   for (int t = 0; t < C::TM / RPI; ++t) {
@@ -724,17 +771,13 @@ hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld
 // workgroups per CU (measured faster than the four-stage ring here).
 using CfgGrouped = CfgMid2;
 
-template <class C, bool POW2>
-__global__ __launch_bounds__(C::THREADS) void grouped_gemm_w8a8_kernel(
-    const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
-    const uint8_t* __restrict__ b, const float* __restrict__ bs, const int32_t* __restrict__ off,
-    int32_t groups, uint16_t* __restrict__ y, int64_t ld_y, int64_t n, int64_t k, int64_t n_tiles) {
-  __shared__ __align__(1024) uint8_t lds[C::LDS_BYTES];
-  __shared__ int32_t sel[2];
-  const int64_t tile_n = blockIdx.x % n_tiles;
-  const int64_t tile_m = blockIdx.x / n_tiles;  // global m-tile index
+// The (group, m-tile) of global m-tile `tile_m`: the groups' tiles, ceil(rows / BM) each,
+// are numbered in group order; a 64-lane prefix sum per pass of 64 groups finds it.
+// Wave 0 writes sel[0] = group (-1: none) and sel[1] = the tile within the group.
+template <int BM>
+__device__ __forceinline__ void find_group_tile(const int32_t* __restrict__ off, int32_t groups, int64_t tile_m,
+                                                int32_t* sel) {
   if (threadIdx.x < 64) {
-    // prefix over groups of ceil(rows / BM), 64 groups per pass
     const int lane = threadIdx.x;
     int64_t base = 0;
     int found_g = -1;
@@ -742,7 +785,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_w8a8_kernel(
     for (int g0 = 0; g0 < groups && found_g < 0; g0 += 64) {
       const int g = g0 + lane;
       int64_t tiles = 0;
-      if (g < groups) tiles = (off[g + 1] - off[g] + C::BM - 1) / C::BM;
+      if (g < groups) tiles = (off[g + 1] - off[g] + BM - 1) / BM;
       int64_t incl = tiles;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -765,6 +808,17 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_w8a8_kernel(
     }
   }
   __syncthreads();
+}
+
+template <class C, bool POW2>
+__global__ __launch_bounds__(C::THREADS) void grouped_gemm_w8a8_kernel(
+    const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
+    const uint8_t* __restrict__ b, const float* __restrict__ bs, const int32_t* __restrict__ off,
+    int32_t groups, uint16_t* __restrict__ y, int64_t ld_y, int64_t n, int64_t k, int64_t n_tiles) {
+  __shared__ __align__(1024) uint8_t lds[C::LDS_BYTES];
+  __shared__ int32_t sel[2];
+  const int64_t tile_n = blockIdx.x % n_tiles;
+  find_group_tile<C::BM>(off, groups, blockIdx.x / n_tiles, sel);
   const int g = sel[0];
   if (g < 0) return;
   const int kblocks = (int)(k / 128);
@@ -774,7 +828,38 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_w8a8_kernel(
   const uint8_t* bg = b + (int64_t)g * n * k;
   const float* bsg = bs + (int64_t)g * (n / 128) * kblocks;
   gemm_tile<C, POW2>(a, ld_a, a_rows, as, ld_as, bg, k, bsg, kblocks, y, ld_y, row0, row_end, tile_n * C::BN,
-               (uint8_t FP8Q_LDS*)lds);
+                     (uint8_t FP8Q_LDS*)lds);
+}
+
+// MoE fc1 with SwiGLU and fc2's 1x128 quantization fused into the epilogue: B is
+// [G][2 half][k] (gate rows, then up rows); tile column tn covers outputs 128tn .. +127.
+template <bool POW2>
+__global__ __launch_bounds__(CfgLarge::THREADS) void grouped_swiglu_kernel(
+    const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
+    const uint8_t* __restrict__ b, const float* __restrict__ bs, const int32_t* __restrict__ off,
+    int32_t groups, int64_t half, int64_t k, int64_t n_tiles, uint8_t* __restrict__ q, int64_t ld_q,
+    float* __restrict__ s, int64_t ld_s) {
+  using C = CfgLarge;
+  __shared__ __align__(1024) uint8_t lds[C::LDS_BYTES];
+  __shared__ int32_t sel[2];
+  const int64_t tile_n = blockIdx.x % n_tiles;
+  find_group_tile<C::BM>(off, groups, blockIdx.x / n_tiles, sel);
+  const int g = sel[0];
+  if (g < 0) return;
+  const int kblocks = (int)(k / 128);
+  const int64_t row0 = off[g] + (int64_t)sel[1] * C::BM;
+  const int64_t row_end = (row0 + C::BM) < off[g + 1] ? (row0 + C::BM) : off[g + 1];
+  const int64_t a_rows = off[groups];
+  const uint8_t* bg = b + (int64_t)g * 2 * half * k;
+  const float* bsg = bs + (int64_t)g * (2 * half / 128) * kblocks;
+  SwigluOut so;
+  so.q = q;
+  so.ld_q = ld_q;
+  so.s = s;
+  so.ld_s = ld_s;
+  so.half = half;
+  gemm_tile<C, POW2, true>(a, ld_a, a_rows, as, ld_as, bg, k, bsg, kblocks, nullptr, 0, row0, row_end,
+                           tile_n * C::BN, (uint8_t FP8Q_LDS*)lds, so);
 }
 
 template <class C>
@@ -794,6 +879,19 @@ static hipError_t launch_grouped(const void* a, int64_t ld_a, const float* a_s, 
 // traffic per FLOP wins despite more padding in small experts (MoE fc1, 128 experts,
 // K = 2048, median 94 rows per expert: 240 -> 213 us); with few K steps two co-resident
 // 128x128 workgroups hide each other's prologue and epilogue (fc2, K = 768: 129 us vs 134).
+hipError_t launch_grouped_swiglu(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
+                                 const float* b_s, const int32_t* offsets, int32_t groups, int64_t total_m,
+                                 int64_t half, int64_t k, void* q, int64_t ld_q, float* s, int64_t ld_s,
+                                 hipStream_t stream) {
+  using C = CfgLarge;
+  const int64_t n_tiles = half / 128;
+  const int64_t m_tiles = (total_m + C::BM - 1) / C::BM + groups;
+  hipLaunchKernelGGL(grouped_swiglu_kernel<false>, dim3((unsigned)(n_tiles * m_tiles)), dim3(C::THREADS), 0, stream,
+                     reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b), b_s,
+                     offsets, groups, half, k, n_tiles, reinterpret_cast<uint8_t*>(q), ld_q, s, ld_s);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
                                const void* b, const float* b_s, const int32_t* offsets, int32_t groups,
                                int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k, bool pow2,

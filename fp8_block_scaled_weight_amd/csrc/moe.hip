@@ -14,6 +14,7 @@
 // counting sort).
 #include "e4m3.hpp"
 #include "launch.hpp"
+#include "swiglu.hpp"
 
 namespace fp8q {
 
@@ -173,82 +174,10 @@ hipError_t launch_moe_dispatch(const void* xq, int64_t ld_xq, const float* xs, i
 }
 
 // ----------------------------------------------------------------------------
-// SwiGLU + 1x128 quantization.  h = [gate | up], bf16 [m, 2n]; a = silu(gate) * up.
-// The value is defined in fp64, g / (1 + exp(-g)) * u, far inside fp32 precision, so the
-// E4M3 encoding is its one rounding.  Per row and 128-column group: amax = max |a|
-// (exact), scale = fl32(fl64(amax / 448)) (1 for amax 0), code = the E4M3 value nearest
-// the fp64 quotient a / scale (ties to even, saturating).
-//
-// Fast path.  Each value is first formed in fp32 (relative error below 2^-20: exp(-g)
-// within about 2.5 ulps, one rounding each for 1 + e, the reciprocal and two products),
-// and the fp64 value is formed only where the fp32 one cannot decide:
-//   - inputs outside the range where that bound holds (gate <= -80, where expf
-//     overflows; |gate| or |up| >= 2^60; |a| below 2^-100 unless a is an exact zero);
-//   - the group maximum: every value within 2^-14 of the fp32 maximum is recomputed in
-//     fp64, so amax is the fp64 maximum;
-//   - codes: the fp32 quotient is moved by 2^-15 both ways; if both give one code, the
-//     fp64 quotient (within 2^-19 of it) gives that code too, since rounding is monotone;
-//     otherwise the code comes from the fp64 quotient.  Groups with a scale below
-//     2^-100 take the fp64 path throughout.
-// An fp64 quotient is rounded to fp32 with round-to-odd (truncate, then set the last bit
-// if anything was dropped), which keeps enough information for the hardware's
-// round-to-nearest-even conversion to give the nearest code of the fp64 value.
-// Same lane mapping as the activation quantizer: 8 lanes per group, 16 values each.
+// SwiGLU + 1x128 quantization, standalone: h = [gate | up], bf16 [m, 2n].  8 lanes per
+// (row, 128-column group), 16 values each (the activation quantizer's lane mapping); the
+// arithmetic is swiglu_quant16 (swiglu.hpp), which the fc1 GEMM's fused epilogue shares.
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ double silu_times_up(double g, double u) {
-#pragma clang fp contract(off)
-  return g / (1.0 + exp(-g)) * u;
-}
-
-// exp(x) for x < 80: 2^(x log2 e) with the exponent carried as an fp32 head ph plus its
-// remainder pl (fma-exact product remainder and the low part of log2 e); the hardware
-// 2^ph (about 1 ulp) is corrected by the first-order factor 1 + pl ln 2 (|pl| <= 2^-17,
-// so the dropped second-order term is below 2^-35).  Very negative x gives 0.
-__device__ __forceinline__ float exp_lt80(float x) {
-  constexpr float kL2eHi = 0x1.715476p+0f;    // log2(e) rounded to fp32
-  constexpr float kL2eLo = 0x1.4ae0c0p-26f;   // log2(e) - kL2eHi, rounded
-  constexpr float kLn2 = 0x1.62e430p-1f;
-  const float ph = x * kL2eHi;
-  const float pl = __builtin_fmaf(x, kL2eHi, -ph) + x * kL2eLo;
-  return __builtin_amdgcn_exp2f(ph) * __builtin_fmaf(pl, kLn2, 1.0f);
-}
-
-__device__ __forceinline__ float silu_times_up_f32(float g, float u) {
-#pragma clang fp contract(off)
-  return g * __builtin_amdgcn_rcpf(1.0f + exp_lt80(-g)) * u;
-}
-
-__device__ __forceinline__ float round_to_odd_f32(double u) {
-  const double au = fabs(u);
-  uint32_t b = __float_as_uint((float)au);
-  if ((double)__uint_as_float(b) > au) b -= 1u;           // toward zero
-  if ((double)__uint_as_float(b) != au) b |= 1u;          // sticky
-  return __builtin_copysignf(fminf(__uint_as_float(b), kE4M3Max), (float)u);
-}
-
-__device__ __forceinline__ double max_over_8_lanes_f64(double v) {
-  v = fmax(v, __shfl_xor(v, 1));
-  v = fmax(v, __shfl_xor(v, 2));
-  v = fmax(v, __shfl_xor(v, 4));
-  return v;
-}
-
-// gate and up of value i (0..15) of this lane, selected without dynamic register indexing
-__device__ __forceinline__ double swiglu_at(const uint32_t (&gw)[8], const uint32_t (&uw)[8], int i) {
-  uint32_t gword = gw[0], uword = uw[0];
-#pragma unroll
-  for (int j = 1; j < 8; ++j) {
-    gword = ((i >> 1) == j) ? gw[j] : gword;
-    uword = ((i >> 1) == j) ? uw[j] : uword;
-  }
-  const float g = (i & 1) ? bf16_hi(gword) : bf16_lo(gword);
-  const float u = (i & 1) ? bf16_hi(uword) : bf16_lo(uword);
-  return silu_times_up((double)g, (double)u);
-}
-
-constexpr float kSwigluCodeSlack = 0x1p-15f;   // relative move of the fp32 quotient
-constexpr double kSwigluMaxSlack = 0x1p-14;     // values this close to the maximum are recomputed
-
 __global__ __launch_bounds__(256) void swiglu_quant_g128_kernel(const uint16_t* __restrict__ h, int64_t m,
                                                                 int64_t groups, int64_t n, int64_t ld_h,
                                                                 uint8_t* __restrict__ q, int64_t ld_q,
@@ -272,74 +201,10 @@ __global__ __launch_bounds__(256) void swiglu_quant_g128_kernel(const uint16_t* 
   const uint32_t gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
   const uint32_t uw[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
 
-  // fp32 values, and the values that need fp64 from the start
-  float a32[16];
-  uint32_t slow = 0;
-  float m32 = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float gv = (i & 1) ? bf16_hi(gw[i >> 1]) : bf16_lo(gw[i >> 1]);
-    const float uv = (i & 1) ? bf16_hi(uw[i >> 1]) : bf16_lo(uw[i >> 1]);
-    const float a = silu_times_up_f32(gv, uv);
-    const bool exact_zero = (gv == 0.0f) || (uv == 0.0f);
-    const bool ok = exact_zero || (gv > -80.0f && fabsf(gv) < 0x1p60f && fabsf(uv) < 0x1p60f && fabsf(a) >= 0x1p-100f);
-    slow |= ok ? 0u : (1u << i);
-    a32[i] = ok ? a : 0.0f;
-    m32 = fmaxf(m32, fabsf(a32[i]));
-  }
-
-  // amax in fp64: the fp64 values of the slow ones and of every value near the maximum
-  double approx = (double)m32, amax = 0.0;
-  for (uint32_t t = slow; t; t &= t - 1) {
-    const double a = fabs(swiglu_at(gw, uw, __builtin_ctz(t)));
-    approx = fmax(approx, a);
-    amax = fmax(amax, a);
-  }
-  approx = max_over_8_lanes_f64(approx);
-  if (approx > 0.0) {
-    const float thr = (float)(approx * (1.0 - kSwigluMaxSlack));
-    uint32_t cand = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) cand |= (fabsf(a32[i]) >= thr) ? (1u << i) : 0u;
-    cand &= ~slow;
-    for (; cand; cand &= cand - 1) amax = fmax(amax, fabs(swiglu_at(gw, uw, __builtin_ctz(cand))));
-  }
-  amax = max_over_8_lanes_f64(amax);
-  if (!live) return;
-  const float scale = (amax == 0.0) ? 1.0f : (float)(amax / (double)kE4M3Max);
+  uint32_t o[4];
+  float scale;
+  if (!swiglu_quant16(gw, uw, live, o, scale)) return;
   if ((lane & 7) == 0) s[g * ld_s + row] = scale;
-
-  // codes: fp32 quotient moved both ways; the fp64 quotient where they disagree
-  uint32_t o[4] = {0u, 0u, 0u, 0u};
-  uint32_t need = 0xffffu;
-  if (scale >= 0x1p-100f) {
-    need = slow;
-    const float r32 = 1.0f / scale;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      float lo[4], hi[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = a32[4 * w + e] * r32;
-        const float av = fabsf(v);
-        lo[e] = __builtin_copysignf(fminf(av * (1.0f - kSwigluCodeSlack), kE4M3Max), v);
-        hi[e] = __builtin_copysignf(fminf(av * (1.0f + kSwigluCodeSlack), kE4M3Max), v);
-      }
-      const uint32_t cl = cvt4(lo[0], lo[1], lo[2], lo[3]);
-      const uint32_t diff = cl ^ cvt4(hi[0], hi[1], hi[2], hi[3]);
-      o[w] = cl;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) need |= ((diff >> (8 * e)) & 0xffu) ? (1u << (4 * w + e)) : 0u;
-    }
-  }
-  const double sd = (double)scale;
-  for (; need; need &= need - 1) {
-    const int i = __builtin_ctz(need);
-    const uint32_t c = cvt4(round_to_odd_f32(swiglu_at(gw, uw, i) / sd), 0.0f, 0.0f, 0.0f) & 0xffu;
-    const int sh = 8 * (i & 3);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) o[w] = ((i >> 2) == w) ? ((o[w] & ~(0xffu << sh)) | (c << sh)) : o[w];
-  }
   store_plain(q + row * ld_q + g * 128 + col, make_uint4(o[0], o[1], o[2], o[3]));
 }
 

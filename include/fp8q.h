@@ -232,6 +232,30 @@ fp8q_status fp8q_gemm_w8a8_bf16act(const void* x, int64_t ld_x, const void* b, i
                                    const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                                    int64_t k, void* stream);
 
+/* fp8q_grouped_gemm_swiglu_quant: MoE fc1 with the SwiGLU activation and fc2's 1x128
+ * input quantization fused into the GEMM's epilogue [R3, section 4: the grouped expert
+ * GEMM over the recorded routing; Rounding, the SwiGLU fusion region: silu(gate) is
+ * multiplied by up before any rounding; FP8-RL, "Method step details" step 1: fc2's
+ * input is quantized per 1x128 group on every forward].
+ * b is e4m3 [G][2*n_half][k]: per expert the gate rows 0..n_half-1, then the up rows;
+ * b_s fp32 [G][2*n_half/128][k/128].  The results equal, bit for bit, the two calls
+ *   fp8q_grouped_gemm_w8a8(a, ..., b, b_s, ..., y, ld_y = 2*n_half, n = 2*n_half, k)
+ *   fp8q_swiglu_quant_g128(y, total_m, n_half, 2*n_half, q, ld_q, s, ld_s)
+ * (the GEMM's outputs rounded to bf16 once, then SwiGLU and the quantization exactly as
+ * fp8q_swiglu_quant_g128 defines them), without the bf16 buffer y: q receives e4m3 codes
+ * [total_m][ld_q], n_half per row; s receives the scale of group g of row m at
+ * s[g * ld_s + m].  The 256x256 tiles each take 128 gate and the matching 128 up rows.
+ * n_half and k positive multiples of 128, 2*n_half*k <= 2^31; ld_q >= n_half and
+ * ld_s >= total_m; a, b, q 16-byte aligned with ld_a and ld_q multiples of 16; the other
+ * arguments and preconditions as fp8q_grouped_gemm_w8a8 and fp8q_swiglu_quant_g128 (the
+ * amax / 448 of every group fits binary32; debug mode cannot check this one, which needs
+ * the GEMM's outputs).  total_m == 0 is a no-op. */
+fp8q_status fp8q_grouped_gemm_swiglu_quant(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
+                                           const void* b, const float* b_s, const int32_t* group_offsets,
+                                           int32_t num_groups, int64_t total_m, void* q, int64_t ld_q,
+                                           float* s, int64_t ld_s, int64_t n_half, int64_t k,
+                                           void* stream);
+
 /* The grouped GEMM for power-of-two scales; arguments as fp8q_grouped_gemm_w8a8, scale
  * precondition as fp8q_gemm_w8a8_ue8m0. */
 fp8q_status fp8q_grouped_gemm_w8a8_ue8m0(const void* a, int64_t ld_a, const float* a_s,

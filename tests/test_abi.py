@@ -217,6 +217,34 @@ def test_moe_validation():
     assert combine(out=A16 + 4) == fq.FP8Q_ERR_ALIGN
 
 
+def test_fused_swiglu_grouped_gemm_validation():
+    L = fq.lib()
+
+    def g(**kw):
+        a = dict(a=A16, ld_a=256, a_s=A16, ld_as=64, b=A16, b_s=A16, off=A16, groups=4, m=64, q=A16, ld_q=256,
+                 s=A16, ld_s=64, half=256, k=256)
+        a.update(kw)
+        return L.fp8q_grouped_gemm_swiglu_quant(a["a"], a["ld_a"], a["a_s"], a["ld_as"], a["b"], a["b_s"], a["off"],
+                                                a["groups"], a["m"], a["q"], a["ld_q"], a["s"], a["ld_s"],
+                                                a["half"], a["k"], None)
+
+    assert g(groups=0) == fq.FP8Q_ERR_SHAPE
+    assert g(half=100) == fq.FP8Q_ERR_SHAPE
+    assert g(half=0) == fq.FP8Q_ERR_SHAPE
+    assert g(k=200) == fq.FP8Q_ERR_SHAPE
+    assert g(m=-1) == fq.FP8Q_ERR_SHAPE
+    assert g(q=None) == fq.FP8Q_ERR_NULL
+    assert g(off=None) == fq.FP8Q_ERR_NULL
+    assert g(ld_q=128) == fq.FP8Q_ERR_STRIDE
+    assert g(ld_s=63) == fq.FP8Q_ERR_STRIDE
+    assert g(ld_as=32) == fq.FP8Q_ERR_STRIDE
+    assert g(q=A16 + 8) == fq.FP8Q_ERR_ALIGN
+    assert g(ld_q=264) == fq.FP8Q_ERR_ALIGN
+    assert g(half=1 << 20, k=1 << 11, ld_q=1 << 20, ld_a=1 << 11) == fq.FP8Q_ERR_SHAPE  # weights beyond 2 GiB
+    # a valid call reaches the device check (none here)
+    assert g() == fq.FP8Q_ERR_UNSUPPORTED
+
+
 def test_bf16act_gemm_validation():
     L = fq.lib()
 

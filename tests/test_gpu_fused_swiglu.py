@@ -1,0 +1,93 @@
+"""GPU parity of MoE fc1 with SwiGLU and fc2's 1x128 quantization fused into the GEMM epilogue.
+
+The fused call is defined as fp8q_grouped_gemm_w8a8 (bf16 output) followed by
+fp8q_swiglu_quant_g128, so it must reproduce those two calls bit for bit: codes byte for
+byte and scales bit for bit.  Rounding-location page, the SwiGLU fusion region (SiLU's
+result is multiplied by up before any rounding); FP8-RL summary page, "Method step
+details" step 1 (fc2's input is quantized per 1x128 group).  The small cases are also
+checked against the oracle's SwiGLU quantization applied to the GEMM's own bf16 output
+(the GEMM itself is pinned to the oracle by its own tests, within the GEMM tolerance).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_block_scaled_weight_amd as fq
+from fp8_block_scaled_weight_amd import synth
+from tests._helpers import bf16_bits
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _operands(sizes, n_half, k, seed):
+    """Quantized fc1 inputs: tokens ~N(0,1) with outlier channels, expert weights ~N(0,0.02)."""
+    g = len(sizes)
+    off = np.zeros(g + 1, np.int32)
+    off[1:] = np.cumsum(sizes)
+    m = int(off[-1])
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    x = torch.randn((max(m, 1), k), device=DEV, generator=gen)
+    x[:, 7] *= 40.0
+    x = x.to(torch.bfloat16)[:m]
+    w = (torch.randn((g * 2 * n_half, k), device=DEV, generator=gen) * 0.02).to(torch.bfloat16)
+    aq = torch.empty((m, k), dtype=torch.uint8, device=DEV)
+    a_s = torch.empty((k // 128, max(m, 1)), dtype=torch.float32, device=DEV)
+    if m:
+        fq.fp8q_quant_act_g128(x, aq, a_s)
+    bq = torch.empty((g * 2 * n_half, k), dtype=torch.uint8, device=DEV)
+    b_s = torch.empty((g * 2 * n_half // 128, k // 128), dtype=torch.float32, device=DEV)
+    fq.fp8q_quant_weight_blk128([(w, bq, b_s)])
+    return (aq, a_s, bq.view(g, 2 * n_half, k), b_s.view(g, 2 * n_half // 128, k // 128),
+            torch.from_numpy(off).to(DEV), m)
+
+
+def _both(aq, a_s, bq, b_s, off, m, n_half):
+    y = torch.empty((m, 2 * n_half), dtype=torch.bfloat16, device=DEV)
+    fq.fp8q_grouped_gemm_w8a8(aq, a_s, bq, b_s, off, y)
+    q1 = torch.full((m, n_half), 0x5A, dtype=torch.uint8, device=DEV)
+    s1 = torch.full((n_half // 128, m + 3), -1.0, device=DEV)
+    fq.fp8q_swiglu_quant_g128(y, q1, s1)
+    q2 = torch.full((m, n_half), 0xA5, dtype=torch.uint8, device=DEV)
+    s2 = torch.full((n_half // 128, m + 3), -2.0, device=DEV)
+    fq.fp8q_grouped_gemm_swiglu_quant(aq, a_s, bq, b_s, off, q2, s2)
+    torch.cuda.synchronize()
+    return y, q1, s1, q2, s2
+
+
+@pytest.mark.parametrize("sizes,n_half,k", [
+    ([3, 0, 300, 1, 0, 513, 64, 256], 256, 2048),   # empty, sub-tile, ragged multi-tile groups
+    ([5, 130, 0, 77], 128, 256),                    # short K, one 128-output tile column
+    ([260], 384, 1024),                             # one group, three tile columns
+])
+def test_fused_equals_gemm_then_swiglu_and_the_oracle(sizes, n_half, k):
+    aq, a_s, bq, b_s, off, m = _operands(sizes, n_half, k, seed=len(sizes) * 7 + k)
+    y, q1, s1, q2, s2 = _both(aq, a_s, bq, b_s, off, m, n_half)
+    assert torch.equal(q1, q2), f"codes differ at {int((q1 != q2).sum())} places"
+    assert torch.equal(s1[:, :m].view(torch.int32), s2[:, :m].view(torch.int32)), "scales differ"
+    assert torch.all(s2[:, m:] == -2.0), "scale columns past total_m are not written"
+    # the oracle's SwiGLU quantization of the GEMM's own bf16 output
+    q_ref, s_ref = oracle.swiglu_quant_g128(bf16_bits(y))
+    assert np.array_equal(q2.cpu().numpy(), q_ref)
+    assert np.array_equal(s2[:, :m].cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_fused_equals_gemm_then_swiglu_at_the_moe_layer_shape():
+    """128 experts, 4096 tokens routed top-8 (Zipf-skewed), hidden 2048, expert intermediate
+    768: the full fused output against the two calls, every byte."""
+    _, off_np, _ = synth.moe_routing(0)
+    sizes = list(np.diff(off_np))
+    aq, a_s, bq, b_s, off, m = _operands(sizes, 768, 2048, seed=11)
+    _, q1, s1, q2, s2 = _both(aq, a_s, bq, b_s, off, m, 768)
+    assert torch.equal(q1, q2), f"codes differ at {int((q1 != q2).sum())} places"
+    assert torch.equal(s1[:, :m].view(torch.int32), s2[:, :m].view(torch.int32)), "scales differ"
+
+
+def test_fused_with_no_rows_is_a_no_op():
+    aq, a_s, bq, b_s, off, m = _operands([0, 0], 128, 256, seed=3)
+    q = torch.empty((0, 128), dtype=torch.uint8, device=DEV)
+    s = torch.empty((1, 1), dtype=torch.float32, device=DEV)
+    fq.fp8q_grouped_gemm_swiglu_quant(aq, a_s, bq, b_s, off, q, s)
+    torch.cuda.synchronize()
