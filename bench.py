@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--vendor-reference", action="store_true",
                    help="only time the vendor library's plain per-tensor-scaled FP8 GEMM (torch._scaled_mm) and "
                         "the bf16 matmul at the dense GEMM shapes, as context for the block-scaled GEMM's rate")
+    p.add_argument("--summarize-legs-trace", metavar="TRACE_DIR",
+                   help="write profiles/bench_legs_kernel_trace.md from a rocprofv3 --stats run of the full bench")
     p.add_argument("--summarize-trace", nargs="+", metavar="TRACE_DIR [BENCH_JSON]",
                    help="no GPU: per-kernel table from a rocprofv3 --kernel-trace --stats output directory "
                         "(optionally with the JSON line of a bench.py run of the same source)")
@@ -292,6 +294,45 @@ def summarize_trace(d, bench_json=None):
     print("\n".join(md))
 
 
+def summarize_legs_trace(d):
+    """Markdown table of every libfp8q kernel in a rocprofv3 --stats run of the full bench
+    (step and side legs), written to profiles/bench_legs_kernel_trace.md."""
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = [r for r in csv.DictReader(open(files[0])) if "fp8q" in r["Name"]]
+    md = [
+        "# Kernel trace of the full benchmark (step and side legs)",
+        "",
+        "Command (on one MI355X, from the repository root, TMPDIR=/tmp):",
+        "",
+        "    rocprofv3 --kernel-trace --stats --output-format csv -d <out>/legs -o legs -- "
+        "python3 bench.py --steps 5 --warmup 2 --no-cpu",
+        "",
+        "Table written by `python3 bench.py --summarize-legs-trace <out>/legs` from `legs_kernel_stats.csv`.",
+        "Every launch of the run is counted: warm-ups, graph replays and the per-call timing graphs.  A kernel",
+        "that several legs run at different shapes (the few-token GEMM, the quantizers, the KV passes) mixes",
+        "those shapes in its average; min and max bound them.  Kernels run by one leg at one shape: the",
+        "attention kernels (64 sequences x 20,000 tokens; q_scale_kernel with recalibration), the MoE kernels",
+        "(4096 tokens top-8 of 128 experts: route, gather, SwiGLU-quant, combine, fc1 and fc2 grouped GEMMs,",
+        "the fused fc1 + SwiGLU-quant kernel).",
+        "",
+        "| kernel | calls | average (us) | min (us) | max (us) |",
+        "|---|---|---|---|---|",
+    ]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].split("(")[0].replace("void ", "").replace("fp8q::", "")
+        md.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    md += ["", "Source digests: " + ", ".join(f"{f} {source_digest(f)}" for f in
+                                             ("gemm.hip", "moe.hip", "attention.hip", "kv_quant.hip", "quant.hip"))]
+    with open(os.path.join(ROOT, "profiles", "bench_legs_kernel_trace.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def vendor_reference():
     """Context only: the vendor library's plain FP8 GEMM (one scale per tensor, no blocks,
     no promotion) and the bf16 matmul at the dense shapes, timed like the legs."""
@@ -321,6 +362,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_legs_trace:
+        summarize_legs_trace(args.summarize_legs_trace)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)

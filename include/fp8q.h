@@ -7,7 +7,8 @@
  *   - the block-scaled W8A8 GEMM that consumes both, dense and MoE-grouped;
  *   - FP8 KV-cache quantize-on-write with per-step K/V scale recalibration;
  *   - around the grouped GEMM: MoE dispatch by recorded expert ids, SwiGLU fused with
- *     fc2's 1x128 quantization, and the weighted combine;
+ *     fc2's 1x128 quantization (standalone, or in fc1's epilogue), and the weighted
+ *     combine;
  *   - FP8 paged decode attention over that cache, with the query scale recalibrated
  *     per step.
  *
