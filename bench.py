@@ -730,10 +730,16 @@ def legs(torch, fq, synth, dev):
     q2f = torch.empty((n, I), dtype=torch.uint8, device=dev)
     s2f = torch.empty((I // 128, n), dtype=torch.float32, device=dev)
     ms_f1f = _time(torch, lambda: fq.fp8q_grouped_gemm_swiglu_quant(dq, dsc, b1, b1s, doff, q2f, s2f), 10)
+    # and reading the token rows through the routing's row -> token map (no dispatch copy)
+    rtok = torch.empty(n, dtype=torch.int32, device=dev)
+    fq.fp8q_moe_route(ids, E, doff, row_of, rtok)
+    ms_f1t = _time(torch, lambda: fq.fp8q_grouped_gemm_swiglu_quant(xq, xsc, b1, b1s, doff, q2f, s2f,
+                                                                    row_token=rtok), 10)
+    ms_rt = _time(torch, lambda: fq.fp8q_moe_route(ids, E, doff, row_of, rtok), 10)
 
     def layer_fused():
-        fq.fp8q_moe_dispatch(xq, xsc, ids, E, dq, dsc, doff, row_of)
-        fq.fp8q_grouped_gemm_swiglu_quant(dq, dsc, b1, b1s, doff, q2f, s2f)
+        fq.fp8q_moe_route(ids, E, doff, row_of, rtok)
+        fq.fp8q_grouped_gemm_swiglu_quant(xq, xsc, b1, b1s, doff, q2f, s2f, row_token=rtok)
         fq.fp8q_grouped_gemm_w8a8(q2f, s2f, b2, b2s, doff, y2)
         fq.fp8q_moe_combine(y2, row_of, rw, out)
 
@@ -752,11 +758,13 @@ def legs(torch, fq, synth, dev):
                            "steps": "dispatch, fc1, swiglu-quant, fc2, combine"}
     res["a4_moe_fc1_swiglu_fused"] = {"rows": n, "us": round(ms_f1f * 1e3, 1),
                                       "TFLOPs": round(f1 / (ms_f1f * 1e-3) / 1e12, 1),
+                                      "token_rows_us": round(ms_f1t * 1e3, 1),
                                       "unfused_fc1_plus_swiglu_us": round((ms1 + ms_sw) * 1e3, 1)}
+    res["f1_moe_route"] = {"us": round(ms_rt * 1e3, 1)}
     res["f1_moe_layer_fused"] = {"tokens": T, "rows": n, "us": round(ms_lf * 1e3, 1),
                                  "TFLOPs": round((f1 + f2) / (ms_lf * 1e-3) / 1e12, 1),
-                                 "steps": "dispatch, fc1 + swiglu-quant fused, fc2, combine"}
-    del xq, dq, q2, out, q2f, s2f
+                                 "steps": "route, fc1 + swiglu-quant fused reading the token rows, fc2, combine"}
+    del xq, dq, q2, out, q2f, s2f, rtok
     del fc1, fc2, fc1q, fc2q, x, xs_rows, a1q, a2, a2q, y1, y2
     torch.cuda.empty_cache()
 

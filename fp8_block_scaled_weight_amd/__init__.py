@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Iterable, Sequence
+from typing import Iterable, Optional, Sequence
 
 import torch
 
@@ -37,6 +37,7 @@ EXPORTED = (
     "fp8q_quant_weight_blk128_ue8m0", "fp8q_quant_act_g128_ue8m0", "fp8q_gemm_w8a8_ue8m0",
     "fp8q_grouped_gemm_w8a8_ue8m0", "fp8q_moe_dispatch", "fp8q_swiglu_quant_g128", "fp8q_moe_combine",
     "fp8q_gemm_w8a8_bf16act", "fp8q_paged_decode_attention", "fp8q_grouped_gemm_swiglu_quant",
+    "fp8q_moe_route",
 )
 
 
@@ -84,8 +85,9 @@ def lib() -> ctypes.CDLL:
         L.fp8q_kv_quant.argtypes = [vp, i64, vp, i64, i64, i32, i32, vp, vp, vp, i32, i64, vp, vp, f32, u32, vp]
         L.fp8q_moe_dispatch.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i64, vp, i64, vp, i64, vp, vp, vp]
         L.fp8q_swiglu_quant_g128.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp]
-        L.fp8q_grouped_gemm_swiglu_quant.argtypes = [vp, i64, vp, i64, vp, vp, vp, i32, i64, vp, i64, vp, i64,
-                                                     i64, i64, vp]
+        L.fp8q_grouped_gemm_swiglu_quant.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, vp, i32, i64, vp, i64,
+                                                     vp, i64, i64, i64, vp]
+        L.fp8q_moe_route.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
         L.fp8q_moe_combine.argtypes = [vp, i64, vp, vp, i64, i32, i64, vp, i64, vp]
         for name in EXPORTED[3:]:
             getattr(L, name).restype = ctypes.c_int
@@ -285,6 +287,18 @@ def fp8q_moe_dispatch(xq: torch.Tensor, xs: torch.Tensor, topk_ids: torch.Tensor
                                    _stream(stream)), "fp8q_moe_dispatch")
 
 
+def fp8q_moe_route(topk_ids: torch.Tensor, num_experts: int, offsets: torch.Tensor, row_of: torch.Tensor,
+                   row_token: torch.Tensor, stream=None) -> None:
+    """The routing of fp8q_moe_dispatch without its copies: offsets [E+1], row_of [T, topk], and
+    row_token [T*topk] (row -> token) for a fc1 that reads the token rows directly."""
+    t, topk = topk_ids.shape
+    if offsets.numel() != num_experts + 1 or row_of.numel() != t * topk or row_token.numel() < t * topk:
+        raise ValueError("offsets must have E+1 entries, row_of and row_token T*topk")
+    _check(lib().fp8q_moe_route(_dev(topk_ids, "topk_ids", (torch.int16,)), t, topk, int(num_experts),
+                                _dev(offsets, "offsets", (torch.int32,)), _dev(row_of, "row_of", (torch.int32,)),
+                                _dev(row_token, "row_token", (torch.int32,)), _stream(stream)), "fp8q_moe_route")
+
+
 def fp8q_swiglu_quant_g128(h: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
     """silu(gate) * up of h = [gate | up] ([m, 2n] bf16), quantized per 1x128 group:
     q [m, n] fp8, s [n/128, ld_s] fp32."""
@@ -298,22 +312,27 @@ def fp8q_swiglu_quant_g128(h: torch.Tensor, q: torch.Tensor, s: torch.Tensor, st
 
 def fp8q_grouped_gemm_swiglu_quant(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
                                    group_offsets: torch.Tensor, q: torch.Tensor, s: torch.Tensor,
-                                   stream=None) -> None:
+                                   row_token: Optional[torch.Tensor] = None, stream=None) -> None:
     """MoE fc1 with SwiGLU and fc2's 1x128 input quantization fused: b [G, 2*n_half, k] holds each
     expert's gate rows, then its up rows.  Equal, bit for bit, to fp8q_grouped_gemm_w8a8 into a
     bf16 [total_m, 2*n_half] buffer followed by fp8q_swiglu_quant_g128 on it: q [total_m, n_half]
-    fp8, s [n_half/128, ld_s] fp32."""
-    total_m, k = a.shape
+    fp8, s [n_half/128, ld_s] fp32.  With row_token (fp8q_moe_route's), a [T, k] and a_s are the
+    token rows and dispatched row r reads token row_token[r]."""
+    a_rows, k = a.shape
+    total_m = q.shape[0]
     g, n2, kb = b.shape
     n_half = n2 // 2
-    if kb != k or n2 % 2 or tuple(q.shape) != (total_m, n_half) or not b.is_contiguous() or not b_s.is_contiguous():
+    if row_token is None and a_rows != total_m:
+        raise ValueError("without row_token, a holds the total_m dispatched rows")
+    if kb != k or n2 % 2 or q.shape[1] != n_half or not b.is_contiguous() or not b_s.is_contiguous():
         raise ValueError("shape mismatch between a, b and q")
     if s.dim() != 2 or s.shape[0] != n_half // 128 or s.stride(1) != 1:
         raise ValueError("s must be [n_half/128, ld_s] with unit column stride")
     if group_offsets.numel() != g + 1:
         raise ValueError("group_offsets must have G+1 entries")
+    tok = 0 if row_token is None else _dev(row_token, "row_token", (torch.int32,))
     _check(lib().fp8q_grouped_gemm_swiglu_quant(
-        _dev(a, "a", FP8), _rows(a, "a"), _dev(a_s, "a_s", F32), a_s.stride(0), _dev(b, "b", FP8),
+        _dev(a, "a", FP8), _rows(a, "a"), _dev(a_s, "a_s", F32), a_s.stride(0), tok, a_rows, _dev(b, "b", FP8),
         _dev(b_s, "b_s", F32), _dev(group_offsets, "group_offsets", (torch.int32,)), g, total_m,
         _dev(q, "q", FP8), _rows(q, "q"), _dev(s, "s", F32), s.stride(0), n_half, k, _stream(stream)),
         "fp8q_grouped_gemm_swiglu_quant")

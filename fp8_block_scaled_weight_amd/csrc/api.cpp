@@ -470,22 +470,25 @@ fp8q_status fp8q_grouped_gemm_w8a8_ue8m0(const void* a, int64_t ld_a, const floa
 }
 
 fp8q_status fp8q_grouped_gemm_swiglu_quant(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
-                                           const void* b, const float* b_s, const int32_t* group_offsets,
-                                           int32_t num_groups, int64_t total_m, void* q, int64_t ld_q, float* s,
-                                           int64_t ld_s, int64_t n_half, int64_t k, void* stream) {
+                                           const int32_t* row_token, int64_t token_rows, const void* b,
+                                           const float* b_s, const int32_t* group_offsets, int32_t num_groups,
+                                           int64_t total_m, void* q, int64_t ld_q, float* s, int64_t ld_s,
+                                           int64_t n_half, int64_t k, void* stream) {
   if (num_groups < 1) return fail(FP8Q_ERR_SHAPE, "num_groups must be >= 1 (got %d)", num_groups);
-  if (total_m < 0 || n_half < 0 || k < 0) return fail(FP8Q_ERR_SHAPE, "negative shape");
+  if (total_m < 0 || n_half < 0 || k < 0 || token_rows < 0) return fail(FP8Q_ERR_SHAPE, "negative shape");
+  const int64_t a_rows = row_token ? token_rows : total_m;  // rows of a (and columns of a_s)
   if (n_half == 0 || n_half % 128 || k == 0 || k % 128)
     return fail(FP8Q_ERR_SHAPE, "n_half=%lld and k=%lld must be positive multiples of 128", (long long)n_half,
                 (long long)k);
   if (total_m > 0) {
     if (!a || !a_s || !b || !b_s || !group_offsets || !q || !s) return fail(FP8Q_ERR_NULL, "NULL pointer");
-    if (ld_a < k || ld_as < total_m || ld_q < n_half || ld_s < total_m)
-      return fail(FP8Q_ERR_STRIDE, "ld_a < k, ld_as < total_m, ld_q < n_half or ld_s < total_m");
+    if (row_token && token_rows < 1) return fail(FP8Q_ERR_SHAPE, "token_rows must be >= 1 with row_token");
+    if (ld_a < k || ld_as < a_rows || ld_q < n_half || ld_s < total_m)
+      return fail(FP8Q_ERR_STRIDE, "ld_a < k, ld_as < rows of a, ld_q < n_half or ld_s < total_m");
     if (!aligned16(a) || !aligned16(b) || !aligned16(q) || ld_a % 16 || ld_q % 16 || !aligned4(a_s) ||
-        !aligned4(b_s) || !aligned4(s) || !aligned4(group_offsets))
+        !aligned4(b_s) || !aligned4(s) || !aligned4(group_offsets) || !aligned4(row_token))
       return fail(FP8Q_ERR_ALIGN, "a/b/q must be 16-byte aligned with ld_a, ld_q multiples of 16");
-    if (total_m * ld_a > kMaxOperandBytes || ld_as * 4 > kMaxOperandBytes || 2 * n_half * k > kMaxOperandBytes)
+    if (a_rows * ld_a > kMaxOperandBytes || ld_as * 4 > kMaxOperandBytes || 2 * n_half * k > kMaxOperandBytes)
       return fail(FP8Q_ERR_SHAPE, "an operand spans more than 2 GiB");
   }
   fp8q_status st = check_device();
@@ -494,7 +497,8 @@ fp8q_status fp8q_grouped_gemm_swiglu_quant(const void* a, int64_t ld_a, const fl
   if (debug_on()) {
     const int64_t bs_bytes = (2 * n_half / 128) * (k / 128) * 4;
     st = check_disjoint({extent(q, total_m, n_half, ld_q, "q"), extent(s, n_half / 128, 4 * total_m, 4 * ld_s, "s")},
-                        {extent(a, total_m, k, ld_a, "a"), extent(a_s, k / 128, 4 * total_m, 4 * ld_as, "a_s"),
+                        {extent(a, a_rows, k, ld_a, "a"), extent(a_s, k / 128, 4 * a_rows, 4 * ld_as, "a_s"),
+                         extent(row_token, 1, 4 * total_m, 0, "row_token"),
                          extent(b, num_groups, 2 * n_half * k, 2 * n_half * k, "b"),
                          extent(b_s, num_groups, bs_bytes, bs_bytes, "b_s"),
                          extent(group_offsets, 1, 4 * ((int64_t)num_groups + 1), 0, "group_offsets")});
@@ -510,14 +514,22 @@ fp8q_status fp8q_grouped_gemm_swiglu_quant(const void* a, int64_t ld_a, const fl
         st = fail(FP8Q_ERR_PRECONDITION, "group_offsets[%d] = %d, not total_m = %lld", num_groups, off[num_groups],
                   (long long)total_m);
     }
-    if (st == FP8Q_OK) st = no_nan_codes(a, total_m, k, ld_a, "a");
+    if (st == FP8Q_OK && row_token) {
+      std::vector<int32_t> tokens;
+      st = fetch(tokens, row_token, 1, total_m, total_m);
+      for (int64_t r = 0; st == FP8Q_OK && r < total_m; ++r)
+        if (tokens[r] < 0 || tokens[r] >= token_rows)
+          st = fail(FP8Q_ERR_PRECONDITION, "row_token[%lld] = %d is not a row below token_rows = %lld",
+                    (long long)r, tokens[r], (long long)token_rows);
+    }
+    if (st == FP8Q_OK) st = no_nan_codes(a, a_rows, k, ld_a, "a");
     if (st == FP8Q_OK) st = no_nan_codes(b, num_groups * 2 * n_half, k, k, "b");
-    if (st == FP8Q_OK) st = check_f32(a_s, k / 128, total_m, ld_as, "a_s", false, false);
+    if (st == FP8Q_OK) st = check_f32(a_s, k / 128, a_rows, ld_as, "a_s", false, false);
     if (st == FP8Q_OK) st = check_f32(b_s, num_groups * (2 * n_half / 128), k / 128, k / 128, "b_s", false, false);
     if (st != FP8Q_OK) return st;
   }
   return finish(launched(fp8q::launch_grouped_swiglu(a, ld_a, a_s, ld_as, b, b_s, group_offsets, num_groups, total_m,
-                                                     n_half, k, q, ld_q, s, ld_s,
+                                                     n_half, k, q, ld_q, s, ld_s, row_token, token_rows,
                                                      reinterpret_cast<hipStream_t>(stream)),
                          "grouped_gemm_swiglu_quant"),
                 stream, "grouped_gemm_swiglu_quant");
@@ -615,6 +627,36 @@ fp8q_status fp8q_moe_dispatch(const void* xq, int64_t ld_xq, const float* xs, in
                                                    reinterpret_cast<hipStream_t>(stream)),
                          "moe_dispatch"),
                 stream, "moe_dispatch");
+}
+
+fp8q_status fp8q_moe_route(const int16_t* topk_ids, int64_t num_tokens, int32_t topk, int32_t num_experts,
+                           int32_t* offsets, int32_t* row_of, int32_t* row_token, void* stream) {
+  if (num_tokens < 0) return fail(FP8Q_ERR_SHAPE, "negative shape");
+  if (topk < 1) return fail(FP8Q_ERR_SHAPE, "topk must be >= 1 (got %d)", topk);
+  if (num_experts < 1 || num_experts > 32767)
+    return fail(FP8Q_ERR_SHAPE, "num_experts must be in [1, 32767] (got %d)", num_experts);
+  const int64_t n = num_tokens * (int64_t)topk;
+  if (n > 0x7fffffffLL) return fail(FP8Q_ERR_SHAPE, "num_tokens * topk must be below 2^31");
+  if (!offsets) return fail(FP8Q_ERR_NULL, "offsets is NULL");
+  if (!aligned4(offsets)) return fail(FP8Q_ERR_ALIGN, "offsets must be 4-byte aligned");
+  if (n > 0) {
+    if (!topk_ids || !row_of || !row_token) return fail(FP8Q_ERR_NULL, "NULL pointer");
+    if (!aligned16(topk_ids) || !aligned4(row_of) || !aligned4(row_token))
+      return fail(FP8Q_ERR_ALIGN, "topk_ids must be 16-byte aligned, row_of and row_token 4-byte aligned");
+  }
+  fp8q_status st = check_device();
+  if (st != FP8Q_OK) return st;
+  if (debug_on()) {
+    st = check_disjoint({extent(offsets, 1, 4 * ((int64_t)num_experts + 1), 0, "offsets"),
+                         extent(row_of, 1, 4 * n, 0, "row_of"), extent(row_token, 1, 4 * n, 0, "row_token")},
+                        {extent(topk_ids, 1, 2 * n, 0, "topk_ids")});
+    if (st == FP8Q_OK) st = debug_sync(stream);
+    if (st != FP8Q_OK) return st;
+  }
+  return finish(launched(fp8q::launch_moe_route(topk_ids, num_tokens, topk, num_experts, offsets, row_of, row_token,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                         "moe_route"),
+                stream, "moe_route");
 }
 
 fp8q_status fp8q_swiglu_quant_g128(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q, int64_t ld_q,

@@ -156,7 +156,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
                                           const uint8_t* __restrict__ b, int64_t ld_b,
                                           const float* __restrict__ bs, int kblocks,
                                           uint16_t* __restrict__ y, int64_t ld_y, int64_t m0, int64_t m_end,
-                                          int64_t n0, uint8_t FP8Q_LDS* lds, const SwigluOut sw = SwigluOut{}) {
+                                          int64_t n0, uint8_t FP8Q_LDS* lds, const SwigluOut sw = SwigluOut{},
+                                          const int32_t* __restrict__ tok = nullptr) {
   static_assert(!SW || (C::BN == 256 && C::TN == 64 && C::WAVES_N == 4 && C::THREADS == 512 && C::BM % 64 == 0),
                 "the fused SwiGLU epilogue assumes the 256x256 tile");
   const int64_t jt = n0 / 256;  // SW: the tile's 128-row gate and up blocks
@@ -179,6 +180,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
     } else {
       int64_t m = m0 + (r - C::BN);
       m = m < m_end ? m : m_end - 1;
+      if (tok) m = tok[m];  // the row's token (a holds the token rows)
       src[i] = (uint32_t)(m * ld_a) + chunk * 16;
     }
   }
@@ -188,6 +190,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
   const int seg = slot / C::TM, q = slot % C::TM;
   int64_t srow = m0 + seg * C::TM + 32 * (q % C::JM) + q / C::JM;
   srow = srow < m_end ? srow : m_end - 1;
+  if (tok) srow = tok[srow];
   const uint32_t ssrc = (uint32_t)(srow * 4);
   const bool tok_lane = lane < C::SPW;
   // weight scales: every wave copies the tile's NWS weight scales (lanes SPW ..
@@ -838,7 +841,7 @@ __global__ __launch_bounds__(CfgLarge::THREADS) void grouped_swiglu_kernel(
     const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
     const uint8_t* __restrict__ b, const float* __restrict__ bs, const int32_t* __restrict__ off,
     int32_t groups, int64_t half, int64_t k, int64_t n_tiles, uint8_t* __restrict__ q, int64_t ld_q,
-    float* __restrict__ s, int64_t ld_s) {
+    float* __restrict__ s, int64_t ld_s, const int32_t* __restrict__ row_token, int64_t token_rows) {
   using C = CfgLarge;
   __shared__ __align__(1024) uint8_t lds[C::LDS_BYTES];
   __shared__ int32_t sel[2];
@@ -849,7 +852,7 @@ __global__ __launch_bounds__(CfgLarge::THREADS) void grouped_swiglu_kernel(
   const int kblocks = (int)(k / 128);
   const int64_t row0 = off[g] + (int64_t)sel[1] * C::BM;
   const int64_t row_end = (row0 + C::BM) < off[g + 1] ? (row0 + C::BM) : off[g + 1];
-  const int64_t a_rows = off[groups];
+  const int64_t a_rows = row_token ? token_rows : off[groups];
   const uint8_t* bg = b + (int64_t)g * 2 * half * k;
   const float* bsg = bs + (int64_t)g * (2 * half / 128) * kblocks;
   SwigluOut so;
@@ -859,7 +862,7 @@ __global__ __launch_bounds__(CfgLarge::THREADS) void grouped_swiglu_kernel(
   so.ld_s = ld_s;
   so.half = half;
   gemm_tile<C, POW2, true>(a, ld_a, a_rows, as, ld_as, bg, k, bsg, kblocks, nullptr, 0, row0, row_end,
-                           tile_n * C::BN, (uint8_t FP8Q_LDS*)lds, so);
+                           tile_n * C::BN, (uint8_t FP8Q_LDS*)lds, so, row_token);
 }
 
 template <class C>
@@ -882,13 +885,14 @@ static hipError_t launch_grouped(const void* a, int64_t ld_a, const float* a_s, 
 hipError_t launch_grouped_swiglu(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                                  const float* b_s, const int32_t* offsets, int32_t groups, int64_t total_m,
                                  int64_t half, int64_t k, void* q, int64_t ld_q, float* s, int64_t ld_s,
-                                 hipStream_t stream) {
+                                 const int32_t* row_token, int64_t token_rows, hipStream_t stream) {
   using C = CfgLarge;
   const int64_t n_tiles = half / 128;
   const int64_t m_tiles = (total_m + C::BM - 1) / C::BM + groups;
   hipLaunchKernelGGL(grouped_swiglu_kernel<false>, dim3((unsigned)(n_tiles * m_tiles)), dim3(C::THREADS), 0, stream,
                      reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b), b_s,
-                     offsets, groups, half, k, n_tiles, reinterpret_cast<uint8_t*>(q), ld_q, s, ld_s);
+                     offsets, groups, half, k, n_tiles, reinterpret_cast<uint8_t*>(q), ld_q, s, ld_s, row_token,
+                     token_rows);
   return hipGetLastError();
 }
 

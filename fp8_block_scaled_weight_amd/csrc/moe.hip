@@ -208,6 +208,28 @@ __global__ __launch_bounds__(256) void swiglu_quant_g128_kernel(const uint16_t* 
   store_plain(q + row * ld_q + g * 128 + col, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
+// The inverse of row_of, for GEMMs that read each dispatched row straight from the token
+// matrix: row_token[row_of[f]] = f / topk (f < 2^31), one thread per entry.
+__global__ __launch_bounds__(256) void moe_row_token_kernel(const int32_t* __restrict__ row_of, int32_t n,
+                                                            int32_t topk, int32_t* __restrict__ row_token) {
+  const int32_t f = (int32_t)(blockIdx.x * 256 + threadIdx.x);
+  if (f >= n) return;
+  const int32_t r = row_of[f];
+  if (r >= 0) row_token[r] = (int32_t)((uint32_t)f / (uint32_t)topk);
+}
+
+hipError_t launch_moe_route(const int16_t* ids, int64_t tokens, int32_t topk, int32_t experts, int32_t* offsets,
+                            int32_t* row_of, int32_t* row_token, hipStream_t stream) {
+  const int64_t n = tokens * topk;
+  hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)experts), dim3(kRouteThreads), 0, stream, ids, n, experts,
+                     offsets, row_of);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || n == 0) return err;
+  hipLaunchKernelGGL(moe_row_token_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, row_of,
+                     (int32_t)n, topk, row_token);
+  return hipGetLastError();
+}
+
 hipError_t launch_swiglu_quant(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q, int64_t ld_q, float* s,
                                int64_t ld_s, hipStream_t stream) {
   const int64_t groups = n / 128;

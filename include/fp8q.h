@@ -246,13 +246,20 @@ fp8q_status fp8q_gemm_w8a8_bf16act(const void* x, int64_t ld_x, const void* b, i
  * fp8q_swiglu_quant_g128 defines them), without the bf16 buffer y: q receives e4m3 codes
  * [total_m][ld_q], n_half per row; s receives the scale of group g of row m at
  * s[g * ld_s + m].  The 256x256 tiles each take 128 gate and the matching 128 up rows.
- * n_half and k positive multiples of 128, 2*n_half*k <= 2^31; ld_q >= n_half and
- * ld_s >= total_m; a, b, q 16-byte aligned with ld_a and ld_q multiples of 16; the other
- * arguments and preconditions as fp8q_grouped_gemm_w8a8 and fp8q_swiglu_quant_g128 (the
- * amax / 448 of every group fits binary32; debug mode cannot check this one, which needs
- * the GEMM's outputs).  total_m == 0 is a no-op. */
+ * Rows of a: with row_token NULL, a and a_s hold the total_m dispatched rows
+ * (fp8q_moe_dispatch's aq and as; token_rows is ignored).  Otherwise a and a_s hold
+ * token_rows token rows (fp8q_quant_act_g128's output, not copied), and dispatched row r
+ * reads a[row_token[r]] and a_s[g][row_token[r]] (fp8q_moe_route's row_token): the
+ * results are those of the dispatched-row call.  Precondition: 0 <= row_token[r] <
+ * token_rows for r < total_m.
+ * n_half and k positive multiples of 128, 2*n_half*k <= 2^31; ld_q >= n_half,
+ * ld_s >= total_m, ld_as >= the rows of a; a, b, q 16-byte aligned with ld_a and ld_q
+ * multiples of 16; the other arguments and preconditions as fp8q_grouped_gemm_w8a8 and
+ * fp8q_swiglu_quant_g128 (the amax / 448 of every group fits binary32; debug mode cannot
+ * check this one, which needs the GEMM's outputs).  total_m == 0 is a no-op. */
 fp8q_status fp8q_grouped_gemm_swiglu_quant(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
-                                           const void* b, const float* b_s, const int32_t* group_offsets,
+                                           const int32_t* row_token, int64_t token_rows, const void* b,
+                                           const float* b_s, const int32_t* group_offsets,
                                            int32_t num_groups, int64_t total_m, void* q, int64_t ld_q,
                                            float* s, int64_t ld_s, int64_t n_half, int64_t k,
                                            void* stream);
@@ -357,6 +364,15 @@ fp8q_status fp8q_moe_dispatch(const void* xq, int64_t ld_xq, const float* xs, in
                               const int16_t* topk_ids, int64_t num_tokens, int32_t topk,
                               int32_t num_experts, int64_t k, void* aq, int64_t ld_aq, float* as,
                               int64_t ld_as, int32_t* offsets, int32_t* row_of, void* stream);
+
+/* fp8q_moe_route: the routing step of fp8q_moe_dispatch without the copies, for a fc1
+ * that reads each dispatched row straight from the token matrix
+ * (fp8q_grouped_gemm_swiglu_quant with row_token).  offsets and row_of are exactly
+ * those fp8q_moe_dispatch writes; row_token: int32 [num_tokens*topk] (out), its first
+ * R entries set: row_token[r] = the token of row r (row_token[row_of[f]] = f / topk).
+ * Arguments and limits as fp8q_moe_dispatch; row_token 4-byte aligned. */
+fp8q_status fp8q_moe_route(const int16_t* topk_ids, int64_t num_tokens, int32_t topk, int32_t num_experts,
+                           int32_t* offsets, int32_t* row_of, int32_t* row_token, void* stream);
 
 /* fp8q_swiglu_quant_g128: h = [gate | up], bf16 [m][ld_h] with gate in columns [0, n)
  * and up in [n, 2n) (fc1's output); a = silu(gate) * up = gate / (1 + exp(-gate)) * up,

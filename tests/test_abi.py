@@ -221,12 +221,12 @@ def test_fused_swiglu_grouped_gemm_validation():
     L = fq.lib()
 
     def g(**kw):
-        a = dict(a=A16, ld_a=256, a_s=A16, ld_as=64, b=A16, b_s=A16, off=A16, groups=4, m=64, q=A16, ld_q=256,
-                 s=A16, ld_s=64, half=256, k=256)
+        a = dict(a=A16, ld_a=256, a_s=A16, ld_as=64, tok=None, rows=0, b=A16, b_s=A16, off=A16, groups=4, m=64,
+                 q=A16, ld_q=256, s=A16, ld_s=64, half=256, k=256)
         a.update(kw)
-        return L.fp8q_grouped_gemm_swiglu_quant(a["a"], a["ld_a"], a["a_s"], a["ld_as"], a["b"], a["b_s"], a["off"],
-                                                a["groups"], a["m"], a["q"], a["ld_q"], a["s"], a["ld_s"],
-                                                a["half"], a["k"], None)
+        return L.fp8q_grouped_gemm_swiglu_quant(a["a"], a["ld_a"], a["a_s"], a["ld_as"], a["tok"], a["rows"], a["b"],
+                                                a["b_s"], a["off"], a["groups"], a["m"], a["q"], a["ld_q"], a["s"],
+                                                a["ld_s"], a["half"], a["k"], None)
 
     assert g(groups=0) == fq.FP8Q_ERR_SHAPE
     assert g(half=100) == fq.FP8Q_ERR_SHAPE
@@ -241,8 +241,30 @@ def test_fused_swiglu_grouped_gemm_validation():
     assert g(q=A16 + 8) == fq.FP8Q_ERR_ALIGN
     assert g(ld_q=264) == fq.FP8Q_ERR_ALIGN
     assert g(half=1 << 20, k=1 << 11, ld_q=1 << 20, ld_a=1 << 11) == fq.FP8Q_ERR_SHAPE  # weights beyond 2 GiB
+    # rows read through row_token: token_rows bounds ld_as, and must be positive
+    assert g(tok=A16, rows=0) == fq.FP8Q_ERR_SHAPE
+    assert g(tok=A16, rows=100) == fq.FP8Q_ERR_STRIDE     # ld_as = 64 < 100 token rows
+    assert g(tok=A16 + 2, rows=32) == fq.FP8Q_ERR_ALIGN
     # a valid call reaches the device check (none here)
     assert g() == fq.FP8Q_ERR_UNSUPPORTED
+    assert g(tok=A16, rows=32) == fq.FP8Q_ERR_UNSUPPORTED
+
+
+def test_moe_route_validation():
+    L = fq.lib()
+
+    def r(**kw):
+        a = dict(ids=A16, t=16, topk=8, e=128, off=A16, row_of=A16, tok=A16)
+        a.update(kw)
+        return L.fp8q_moe_route(a["ids"], a["t"], a["topk"], a["e"], a["off"], a["row_of"], a["tok"], None)
+
+    assert r(topk=0) == fq.FP8Q_ERR_SHAPE
+    assert r(e=0) == fq.FP8Q_ERR_SHAPE
+    assert r(t=-1) == fq.FP8Q_ERR_SHAPE
+    assert r(off=None) == fq.FP8Q_ERR_NULL
+    assert r(tok=None) == fq.FP8Q_ERR_NULL
+    assert r(ids=A16 + 2) == fq.FP8Q_ERR_ALIGN
+    assert r() == fq.FP8Q_ERR_UNSUPPORTED
 
 
 def test_bf16act_gemm_validation():

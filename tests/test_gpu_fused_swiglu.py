@@ -91,3 +91,56 @@ def test_fused_with_no_rows_is_a_no_op():
     s = torch.empty((1, 1), dtype=torch.float32, device=DEV)
     fq.fp8q_grouped_gemm_swiglu_quant(aq, a_s, bq, b_s, off, q, s)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("tokens,experts,topk,invalid", [(4096, 128, 8, 0), (300, 16, 4, 25)])
+def test_route_and_token_rows_equal_the_dispatched_rows(tokens, experts, topk, invalid):
+    """fp8q_moe_route writes dispatch's offsets and row_of plus row_token; fc1 reading the token
+    rows through row_token gives the dispatched-row call's codes and scales, every byte.  The
+    second case drops some entries (ids -1 and >= experts)."""
+    ids_np, _ = synth.moe_topk(0, tokens=tokens, experts=experts, topk=topk)
+    if invalid:
+        g = np.random.default_rng(5)
+        flat = ids_np.reshape(-1)
+        pick = g.choice(flat.size, invalid, replace=False)
+        flat[pick[: invalid // 2]] = -1
+        flat[pick[invalid // 2:]] = experts + 3
+    ids = torch.from_numpy(ids_np).to(DEV)
+    n_half, k = 256, 512
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(tokens)
+    x = torch.randn((tokens, k), device=DEV, generator=gen).to(torch.bfloat16)
+    xq = torch.empty((tokens, k), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((k // 128, tokens), dtype=torch.float32, device=DEV)
+    fq.fp8q_quant_act_g128(x, xq, xs)
+    n = tokens * topk
+    dq = torch.empty((n, k), dtype=torch.uint8, device=DEV)
+    ds = torch.empty((k // 128, n), dtype=torch.float32, device=DEV)
+    off1 = torch.empty(experts + 1, dtype=torch.int32, device=DEV)
+    row1 = torch.empty((tokens, topk), dtype=torch.int32, device=DEV)
+    fq.fp8q_moe_dispatch(xq, xs, ids, experts, dq, ds, off1, row1)
+    off2 = torch.full((experts + 1,), -7, dtype=torch.int32, device=DEV)
+    row2 = torch.full((tokens, topk), -7, dtype=torch.int32, device=DEV)
+    tok = torch.full((n,), -7, dtype=torch.int32, device=DEV)
+    fq.fp8q_moe_route(ids, experts, off2, row2, tok)
+    torch.cuda.synchronize()
+    assert torch.equal(off1, off2) and torch.equal(row1, row2)
+    rows = int(off2[-1].item())
+    r = row2.reshape(-1)
+    valid = r >= 0
+    f = torch.arange(n, device=DEV)
+    assert torch.equal(tok[r[valid].long()], (f[valid] // topk).to(torch.int32))
+    w = (torch.randn((experts * 2 * n_half, k), device=DEV, generator=gen) * 0.02).to(torch.bfloat16)
+    bq = torch.empty((experts * 2 * n_half, k), dtype=torch.uint8, device=DEV)
+    bs = torch.empty((experts * 2 * n_half // 128, k // 128), dtype=torch.float32, device=DEV)
+    fq.fp8q_quant_weight_blk128([(w, bq, bs)])
+    bq, bs = bq.view(experts, 2 * n_half, k), bs.view(experts, 2 * n_half // 128, k // 128)
+    q1 = torch.empty((rows, n_half), dtype=torch.uint8, device=DEV)
+    s1 = torch.empty((n_half // 128, rows), dtype=torch.float32, device=DEV)
+    fq.fp8q_grouped_gemm_swiglu_quant(dq[:rows], ds[:, :rows], bq, bs, off1, q1, s1)
+    q2 = torch.full((rows, n_half), 0x5A, dtype=torch.uint8, device=DEV)
+    s2 = torch.full((n_half // 128, rows), -1.0, device=DEV)
+    fq.fp8q_grouped_gemm_swiglu_quant(xq, xs, bq, bs, off2, q2, s2, row_token=tok)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2), f"codes differ at {int((q1 != q2).sum())} places"
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
