@@ -144,3 +144,19 @@ def test_route_and_token_rows_equal_the_dispatched_rows(tokens, experts, topk, i
     torch.cuda.synchronize()
     assert torch.equal(q1, q2), f"codes differ at {int((q1 != q2).sum())} places"
     assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
+def test_fused_with_padded_output_strides():
+    """q and s with leading dimensions beyond n_half and total_m: the padding is left alone."""
+    aq, a_s, bq, b_s, off, m = _operands([70, 0, 190], 256, 512, seed=21)
+    y = torch.empty((m, 512), dtype=torch.bfloat16, device=DEV)
+    fq.fp8q_grouped_gemm_w8a8(aq, a_s, bq, b_s, off, y)
+    q1 = torch.empty((m, 256), dtype=torch.uint8, device=DEV)
+    s1 = torch.empty((2, m), dtype=torch.float32, device=DEV)
+    fq.fp8q_swiglu_quant_g128(y, q1, s1)
+    qbuf = torch.full((m, 256 + 48), 0x33, dtype=torch.uint8, device=DEV)
+    sbuf = torch.full((2, m + 40), -5.0, device=DEV)
+    fq.fp8q_grouped_gemm_swiglu_quant(aq, a_s, bq, b_s, off, qbuf[:, :256], sbuf[:, :m])
+    torch.cuda.synchronize()
+    assert torch.equal(qbuf[:, :256], q1) and torch.all(qbuf[:, 256:] == 0x33)
+    assert torch.equal(sbuf[:, :m].view(torch.int32), s1.view(torch.int32)) and torch.all(sbuf[:, m:] == -5.0)
