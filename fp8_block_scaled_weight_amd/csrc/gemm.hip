@@ -204,15 +204,33 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
   const v4i rsa = make_rsrc(as, (uint32_t)(ld_as * kblocks * 4));
   const v4i rsb = make_rsrc(bs, (uint32_t)((SW ? 2 * sw.half / 128 : n0 / 128 + C::NWS) * kblocks * 4));
 
-  auto issue = [&](int kb, int stage) {
+  // copies [i0, i1) of this thread's 16-byte row copies for step kb into stage `stage`
+  auto issue_rows = [&](int kb, int stage, int i0, int i1) {
     const uint32_t dst = lds_base + (uint32_t)(stage * C::STAGE_BYTES);
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i)
-      dma16(i < C::LOADS_W ? rb : ra, src[i], (uint32_t)kb * 128u, dst + (uint32_t)((i * C::WAVES + wave) * 1024));
+      if (i >= i0 && i < i1)
+        dma16(i < C::LOADS_W ? rb : ra, src[i], (uint32_t)kb * 128u, dst + (uint32_t)((i * C::WAVES + wave) * 1024));
+  };
+  auto issue_scales = [&](int kb, int stage) {
+    const uint32_t dst = lds_base + (uint32_t)(stage * C::STAGE_BYTES);
     const uint32_t sdst = dst + C::SCALE_OFF + (uint32_t)(wave * C::SPW * 4);
     if (tok_lane) dma4(rsa, ssrc, (uint32_t)(kb * ld_as * 4), sdst);
     if (wsc_lane) dma4(rsb, wsrc, (uint32_t)kb * 4u, dst + C::WSC_OFF + (uint32_t)((wave * C::NWS - C::SPW) * 4));
   };
+  auto issue = [&](int kb, int stage) {
+    issue_rows(kb, stage, 0, C::LOADS);
+    issue_scales(kb, stage);
+  };
+  // With two stages the next step's row copies are spread over the step, PER of them
+  // behind each of the first MFMA chains: issued all at once, they hold a wave at the
+  // copy queue before its first MFMA (4096^3: 79 -> 68 us).  In the last step the rows
+  // copied are the last block again, in range and into the stage no later step reads,
+  // so that no branch separates the chains (one spills the accumulators); the final
+  // waits cover these copies.  Deeper rings keep issuing a step's copies at once,
+  // where such tail copies would be several steps' worth.
+  constexpr bool SPREAD = C::STAGES == 2;
+  constexpr int PER = 2;
 
   // ---- fragment offsets: lane l reads row l%32 of a 32-row tile, 16-byte chunks
   // 4h + 2(l/32) + e (e = 0, 1) for the MFMA of K half h
@@ -249,7 +267,14 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
       } else {
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
-      if (kb + S - 1 < kblocks) issue(kb + S - 1, cur == 0 ? S - 1 : cur - 1);
+      const bool more = kb + S - 1 < kblocks;
+      const int nst = cur == 0 ? S - 1 : cur - 1;
+      const int kn = more ? kb + S - 1 : kblocks - 1;
+      if constexpr (SPREAD) {
+        if (more) issue_scales(kn, nst);
+      } else {
+        if (more) issue(kn, nst);
+      }
       const uint8_t FP8Q_LDS* st = lds + cur * C::STAGE_BYTES;
       const uint8_t FP8Q_LDS* stw = st + wn * 128;
       const uint8_t FP8Q_LDS* stt = st + (C::BN + wm) * 128;
@@ -278,6 +303,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
         for (int i = 0; i < C::IN; ++i) {
           acc[i][j] = mfma32_scaled(fa[i][0], fb[0], acc[i][j], ea, eb[j]);
           acc[i][j] = mfma32_scaled(fa[i][1], fb[1], acc[i][j], ea, eb[j]);
+          const int ch = j * C::IN + i;
+          if (SPREAD && ch * PER < C::LOADS) issue_rows(kn, nst, ch * PER, ch + 1 == C::IN * C::JM ? C::LOADS : (ch + 1) * PER);
         }
       }
       cur = (cur + 1 == S) ? 0 : cur + 1;
@@ -335,7 +362,14 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
     __builtin_amdgcn_sched_barrier(0);
     read_a(C::IN - 1);
     __builtin_amdgcn_sched_barrier(0);
-    if (kb + S - 1 < kblocks) issue(kb + S - 1, cur == 0 ? S - 1 : cur - 1);
+    const bool more = kb + S - 1 < kblocks;
+    const int nst = cur == 0 ? S - 1 : cur - 1;  // the stage step kb+S-1 fills
+    const int kn = more ? kb + S - 1 : kblocks - 1;
+    if constexpr (SPREAD) {
+      if (more) issue_scales(kn, nst);
+    } else {
+      if (more) issue(kn, nst);
+    }
     __builtin_amdgcn_sched_barrier(0);
     float sa[C::JM];
     if constexpr (C::JM == 4) {
@@ -360,6 +394,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
         const int ch = j * C::IN + i;
         if (ch == CH - 1) break;  // deferred to the next step
         chain(ch & 1, i, j & 1);
+        if (SPREAD && ch * PER < C::LOADS) issue_rows(kn, nst, ch * PER, (ch + 1) * PER);
         if (i == 0 && j + 1 < C::JM) read_b(j + 1);
         if (ch > 0) {
           const int pi = (i == 0) ? C::IN - 1 : i - 1;
@@ -372,6 +407,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
       }
       c_prev = c;
     }
+    if (SPREAD && (CH - 1) * PER < C::LOADS) issue_rows(kn, nst, (CH - 1) * PER, C::LOADS);
     // the deferred chain's operands fa[IN-1], fb[(JM-1)&1] are already in flight
     pc = sa[C::JM - 1] * sb;
     if (CH >= 2) promote((CH - 2) & 1, (CH - 2) % C::IN, (CH - 2) / C::IN, (C::IN == 1) ? sa[C::JM - 2] * sb : pc);
