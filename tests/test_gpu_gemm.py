@@ -121,6 +121,24 @@ def test_deterministic():
     assert np.array_equal(a, b)
 
 
+def test_stacked_weights_equal_separate_gemms():
+    """k and v stored as one weight (rows stacked, 128-row scale blocks kept apart): the one
+    GEMM's column slices equal the two separate GEMMs byte for byte, although the two layouts
+    run different tile configurations (4096 x 2048: 512 128x128 tiles on a 2-stage ring;
+    4096 x 1024: 256 tiles on a 4-stage ring).  Sampled rows are also checked against the
+    oracle."""
+    m, kd, h = 4096, 1024, 4096
+    xq, xs, wk, sk = quantized_operands(m, kd, h, tensor=13)
+    _, _, wv, sv = quantized_operands(8, kd, h, tensor=14)
+    wkv, skv = np.concatenate([wk, wv]), np.concatenate([sk, sv])
+    yk, _ = gpu_gemm(xq, xs, wk, sk)
+    yv, _ = gpu_gemm(xq, xs, wv, sv)
+    ykv, _ = gpu_gemm(xq, xs, wkv, skv)
+    assert np.array_equal(ykv[:, :kd], yk) and np.array_equal(ykv[:, kd:], yv)
+    rows = np.array([0, 1, 127, 128, 2047, 4095])
+    check(xq, xs, wkv, skv, rows=rows)
+
+
 # ------------------------------------------------------------------------- grouped
 def grouped_case(sizes, n, k, seed):
     g = np.random.Generator(np.random.PCG64(seed))
