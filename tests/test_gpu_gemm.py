@@ -92,6 +92,8 @@ def test_mlp_shapes_sampled():
     (1000, 1024, 512),    # 128x128 tiles, four-stage copy ring, ragged
     (700, 1024, 640),     # 128x64 tiles, ragged
     (65536, 384, 256),    # n not a multiple of 256 with enough rows for 256x256 tiles
+    (4000, 4096, 128),    # 256x256 tiles, one K step: the only step is also the last
+    (4000, 4096, 256),    # 256x256 tiles, two K steps
 ])
 def test_tile_configs_ragged(m, n, k):
     g = np.random.Generator(np.random.PCG64(m + n))

@@ -98,6 +98,8 @@ def _gpu_gemm(fn, xq, xs, wq, ws):
     (1000, 1024, 1024),  # 128x128 tiles, four-stage ring, ragged
     (2000, 4096, 512),   # 128x128 tiles, two workgroups per CU, ragged
     (4000, 4096, 1024),  # 256x256 tiles, ragged
+    (4000, 4096, 128),   # 256x256 tiles, one K step
+    (4000, 4096, 256),   # 256x256 tiles, two K steps
 ])
 def test_gemm_matches_oracle(m, n, k):
     xq, xs, wq, ws = _operands(m, n, k, tensor=n // 128 + m % 7)
