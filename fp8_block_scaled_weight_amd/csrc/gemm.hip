@@ -393,7 +393,12 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
       for (int i = 0; i < C::IN; ++i) {
         const int ch = j * C::IN + i;
         if (ch == CH - 1) break;  // deferred to the next step
+        // a wave issuing MFMAs goes ahead of one issuing copies or promotion FMAs on the
+        // same SIMD (4096^3: 74 -> 70 us; the power-of-two loop, which has no promotion
+        // FMAs, measured no gain from it)
+        __builtin_amdgcn_s_setprio(1);
         chain(ch & 1, i, j & 1);
+        __builtin_amdgcn_s_setprio(0);
         if (SPREAD && ch * PER < C::LOADS) issue_rows(kn, nst, ch * PER, (ch + 1) * PER);
         if (i == 0 && j + 1 < C::JM) read_b(j + 1);
         if (ch > 0) {
