@@ -413,8 +413,8 @@ def main():
     # The k and v projections are one 2048x4096 weight, as serving engines store them: k's
     # and v's quantized rows and scale rows are row blocks of one buffer (their 128-row
     # scale blocks never straddle the two), and one GEMM writes both outputs as column
-    # slices of one [tokens, 2048] result: 256 tiles of 128 tokens x 256 weights, one per
-    # CU, where two 1024-column GEMMs run 256 128x128 tiles each.
+    # slices of one [tokens, 2048] result: 512 128x128 tiles, two workgroups per CU, where
+    # two 1024-column GEMMs run 256 tiles each.
     WQ["kv"] = torch.empty((2 * KV_DIM, HIDDEN), dtype=torch.uint8, device=dev)
     WS["kv"] = torch.empty((2 * KV_DIM // 128, HIDDEN // 128), dtype=torch.float32, device=dev)
     WQ["k"], WQ["v"] = WQ["kv"][:KV_DIM], WQ["kv"][KV_DIM:]

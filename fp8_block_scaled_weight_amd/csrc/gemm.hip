@@ -521,7 +521,6 @@ __device__ __forceinline__ void tile_coords(int64_t t, int64_t m_tiles, int64_t 
 using CfgLarge = GemmCfg<256, 256, 2, 4, 2>;   // 128 x 64 per wave, 132 KB LDS
 using CfgMid = GemmCfg<128, 128, 2, 4, 4>;     // 64 x 32 per wave, 132 KB LDS
 using CfgMid2 = GemmCfg<128, 128, 2, 4, 2>;    // two workgroups per CU when tiles are plenty
-using CfgTall = GemmCfg<128, 256, 2, 4, 2>;    // 64 x 64 per wave, 98 KB LDS: 256 weight rows, 128 tokens
 using CfgSmall = GemmCfg<128, 64, 2, 2, 4>;    // 64 x 32 per wave, 100 KB LDS
 
 template <class C, bool POW2>
@@ -787,11 +786,6 @@ static hipError_t launch_tiles(const void* a, int64_t ld_a, const float* a_s, in
   const int64_t large_tiles = ((m + CfgLarge::BM - 1) / CfgLarge::BM) * (n / CfgLarge::BN);
   if (n % CfgLarge::BN == 0 && large_tiles >= 256)
     return launch_dense<CfgLarge, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-  // otherwise 128-token x 256-weight tiles, one per CU, when they are enough to fill the
-  // chip (4096 x 2048 x 4096: 42 us against 50 us with 128x128 tiles, same bytes)
-  const int64_t tall_tiles = ((m + CfgTall::BM - 1) / CfgTall::BM) * (n / CfgTall::BN);
-  if (n % CfgTall::BN == 0 && tall_tiles >= 256)
-    return launch_dense<CfgTall, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   // with at least two tiles per CU, two co-resident workgroups hide each other's waits
   // better than deeper copy rings
   const int64_t mid_tiles = ((m + CfgMid::BM - 1) / CfgMid::BM) * (n / CfgMid::BN);

@@ -88,8 +88,8 @@ def test_mlp_shapes_sampled():
 
 @pytest.mark.parametrize("m,n,k", [
     (4000, 4096, 1024),   # 256x256 tiles, ragged last token tile
-    (2000, 4096, 512),    # 128x256 tiles, ragged
-    (1100, 2048, 384),    # 128x128 tiles, four-stage copy ring, ragged (too few 128x256 tiles)
+    (2000, 4096, 512),    # 128x128 tiles, two workgroups per CU, ragged
+    (1100, 2048, 384),    # 128x128 tiles, four-stage copy ring, ragged
     (1000, 1024, 512),    # 128x64 tiles (m < 1024), ragged
     (700, 1024, 640),     # 128x64 tiles, ragged
     (65536, 384, 256),    # n not a multiple of 256 with enough rows for 256x256 tiles
@@ -127,8 +127,8 @@ def test_deterministic():
 def test_stacked_weights_equal_separate_gemms():
     """k and v stored as one weight (rows stacked, 128-row scale blocks kept apart): the one
     GEMM's column slices equal the two separate GEMMs byte for byte, although the two layouts
-    run different tile configurations (4096 x 2048: 256 tiles of 128 tokens x 256 weights on a
-    2-stage ring; 4096 x 1024: 256 tiles of 128x128 on a 4-stage ring).  Sampled rows are also
+    run different tile configurations (4096 x 2048: 512 128x128 tiles on a 2-stage ring, two
+    workgroups per CU; 4096 x 1024: 256 tiles on a 4-stage ring).  Sampled rows are also
     checked against the oracle."""
     m, kd, h = 4096, 1024, 4096
     xq, xs, wk, sk = quantized_operands(m, kd, h, tensor=13)

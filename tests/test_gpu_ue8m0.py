@@ -96,8 +96,8 @@ def _gpu_gemm(fn, xq, xs, wq, ws):
     (16, 256, 256),      # few tokens: promotion path
     (130, 1024, 512),    # 128x64 tiles, ragged
     (1100, 1024, 1024),  # 128x128 tiles, four-stage ring, ragged
-    (2000, 4096, 512),   # 128x256 tiles, ragged
-    (65536, 384, 256),   # 128x128 tiles, two workgroups per CU
+    (2000, 4096, 512),   # 128x128 tiles, two workgroups per CU, ragged
+    (65536, 384, 256),   # 128x128 tiles, two workgroups per CU, n not a multiple of 256
     (4000, 4096, 1024),  # 256x256 tiles, ragged
     (4000, 4096, 128),   # 256x256 tiles, one K step
     (4000, 4096, 256),   # 256x256 tiles, two K steps
