@@ -34,6 +34,7 @@ FP8_PEAK_TFLOPS = 5000.0
 TOKENS = 4096
 HIDDEN = 4096
 KV_DIM = 1024
+DOM_LAUNCHES = 100      # back-to-back launches that time the dominant GEMM
 
 
 def log(*a):
@@ -47,6 +48,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-legs", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-full", action="store_true",
+                   help="time the oracle on the whole step (about 150 s) instead of the 512-token sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only copy 1 GiB device-to-device 3 times (reference for HBM byte counters)")
     p.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
@@ -263,7 +266,7 @@ def summarize_trace(d, bench_json=None):
         "Command (on one MI355X, from the repository root, TMPDIR=/tmp):",
         "",
         "    rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace -o bench -- "
-        "python3 bench.py --steps 30 --no-legs --no-cpu",
+        "python3 bench.py --steps 20 --no-legs --no-cpu",
         "",
         "Table written by `python3 bench.py --summarize-trace <out>/trace [<bench json line>]` from "
         "`bench_kernel_stats.csv` (all",
@@ -283,16 +286,62 @@ def summarize_trace(d, bench_json=None):
     if bench_json:
         line = [l for l in open(bench_json) if l.startswith("{")][-1]
         live = f" ({json.loads(line)['roofline']['avg_us']} us in the run of the same source)"
+    dom = _dominant_loop_from_trace(d)
     md += [
         "",
         "The 256x256-tile GEMM instantiation runs only the two M=N=K=4096 projections (q, o) in this command,",
         "so its average is the dominant kernel's duration under the tracer; bench.py measures the same kernel",
         f"live with HIP events on its launch stream (`roofline.avg_us`{live}).",
-        f"gemm.hip source_digest: {source_digest('gemm.hip')}",
     ]
+    if dom:
+        md += [
+            "",
+            f"The launches bench.py times live are the run of {DOM_LAUNCHES + 3} consecutive launches of that kernel",
+            f"(3 untimed, then {DOM_LAUNCHES} between the two events), found in `bench_kernel_trace.csv`: "
+            f"average {dom['loop_avg_us']:.2f} us",
+            f"over those {dom['loop_n']} launches (min {dom['loop_min_us']:.2f}, max {dom['loop_max_us']:.2f}); "
+            f"all {dom['all_n']} launches average {dom['all_avg_us']:.2f} us.",
+            f"roofline.frac from the traced loop: 2*4096^3 FLOP / {dom['loop_avg_us']:.2f} us / 5.0 PF = "
+            f"{2 * 4096 ** 3 / (dom['loop_avg_us'] * 1e-6) / 5e15:.4f}.",
+        ]
+    md += [f"gemm.hip source_digest: {source_digest('gemm.hip')}"]
     with open(os.path.join(ROOT, "profiles", "bench_step_kernel_trace.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     print("\n".join(md))
+
+
+def _dominant_loop_from_trace(d):
+    """From a rocprofv3 kernel trace: the launches of the 256x256 FP32-scale GEMM that
+    bench.py times live (the run of DOM_LAUNCHES + 3 consecutive dispatches of that kernel,
+    whose last DOM_LAUNCHES are timed), and the average over all its launches."""
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        return None
+    rows = list(csv.DictReader(open(files[0])))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    tag = "GemmCfg<256, 256, 2, 4, 2>, false>"
+    is_dom = [tag in r["Kernel_Name"] for r in rows]
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    alld = [x for x, f in zip(dur, is_dom) if f]
+    runs, i = [], 0
+    while i < len(rows):
+        if is_dom[i]:
+            j = i
+            while j < len(rows) and is_dom[j]:
+                j += 1
+            runs.append((i, j))
+            i = j
+        else:
+            i += 1
+    loop = [(a, b) for a, b in runs if b - a == DOM_LAUNCHES + 3]
+    if not loop or not alld:
+        return None
+    a, b = loop[-1]
+    ld = dur[a + 3:b]
+    return {"loop_n": len(ld), "loop_avg_us": sum(ld) / len(ld), "loop_min_us": min(ld), "loop_max_us": max(ld),
+            "all_n": len(alld), "all_avg_us": sum(alld) / len(alld)}
 
 
 def summarize_legs_trace(d):
@@ -499,14 +548,44 @@ def main():
     per_call_ms = {}
     for name, fn in calls:
         per_call_ms[name] = _time(torch, fn, 5, reps=20)
+    # The quantizer calls again with their operands outside the caches (the step's working
+    # set, about 130 MB, is otherwise served by the 256 MB last-level cache on back-to-back
+    # calls): each call on its own buffer set, rotated over >= 1 GB.  These cold times are
+    # the calls' HBM rates.
+    log("cold quantizer timing (buffer rotation over >= 1 GB)")
+    cold_ms = {}
+    per_set = 3 * sum(w.numel() for w in W.values())
+    fns = []
+    for _ in range(_rotation_sets(per_set)):
+        d = [(W[n].clone(), torch.empty_like(WQ[n]), torch.empty_like(WS[n])) for n in ("q", "k", "v", "o")]
+        fns.append(lambda d=d: fq.fp8q_quant_weight_blk128(d))
+    cold_ms["a1_weight_sync_qkvo"] = _time_rotated(torch, fns)
+    for name, src in (("a2_act_quant_x", X), ("a2_act_quant_o", O_in)):
+        fns = []
+        for _ in range(_rotation_sets(3 * src.numel())):
+            xc, qc, sc = src.clone(), torch.empty_like(Xq), torch.empty_like(Xs)
+            fns.append(lambda xc=xc, qc=qc, sc=sc: fq.fp8q_quant_act_g128(xc, qc, sc))
+        cold_ms[name] = _time_rotated(torch, fns)
+    fns = []
+    for _ in range(_rotation_sets(2 * Y["kv"].numel() + 2 * Kc.numel())):
+        ykv, kc_, vc_ = Y["kv"].clone(), torch.empty_like(Kc), torch.empty_like(Vc)
+        ks_, vs_ = torch.ones_like(ks), torch.ones_like(vs)
+        fns.append(lambda ykv=ykv, kc_=kc_, vc_=vc_, ks_=ks_, vs_=vs_: fq.fp8q_kv_quant(
+            ykv[:, :KV_DIM].view(TOKENS, 8, 128), ykv[:, KV_DIM:].view(TOKENS, 8, 128), slots, kc_, vc_, ks_, vs_,
+            448.0, recalibrate=True))
+    cold_ms["a5a6_kv_recal_write"] = _time_rotated(torch, fns)
+    del fns, d, xc, qc, sc, ykv, kc_, vc_, ks_, vs_
+    torch.cuda.empty_cache()
+
     # The dominant kernel, launched directly (no graph), back to back on the current
-    # stream between two HIP events: its average duration.
+    # stream between two HIP events: its average duration.  These are the kernel's only
+    # back-to-back launches in the run, so a kernel trace of the same command isolates them.
     dom_fn = calls[2][1]
     for _ in range(3):
         dom_fn()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    n_dom = max(20, args.steps)
+    n_dom = DOM_LAUNCHES
     torch.cuda.synchronize()
     e0.record()
     for _ in range(n_dom):
@@ -529,14 +608,16 @@ def main():
     for name, ms in per_call_ms.items():
         d = {"avg_us": round(ms * 1e3, 2)}
         if name in bytes_of:
-            gbs = bytes_of[name] / (ms * 1e-3) / 1e9
+            # quantizers: the cold (rotated-buffer) time is the rate; the warm time is context
+            d = {"avg_us": round(cold_ms[name] * 1e3, 2), "warm_us": round(ms * 1e3, 2)}
+            gbs = bytes_of[name] / (cold_ms[name] * 1e-3) / 1e9
             d.update(GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBPS, 4))
         if name in flops_of:
             tf = flops_of[name] / (ms * 1e-3) / 1e12
             d.update(TFLOPs=round(tf, 1), frac_fp8_peak=round(tf / FP8_PEAK_TFLOPS, 4))
         call_info[name] = d
     q_bytes = sum(bytes_of.values())
-    q_ms = sum(per_call_ms[n] for n in bytes_of)
+    q_ms = sum(cold_ms[n] for n in bytes_of)
     g_ms = sum(per_call_ms[n] for n in flops_of)
 
     dom_flops = 2 * TOKENS * HIDDEN * HIDDEN
@@ -567,6 +648,7 @@ def main():
                    "tokens": TOKENS, "hidden": HIDDEN, "kv_heads": 8, "head_dim": 128, "parallelism": "none"},
         "gemm_TFLOPs": round(gemm_flops / (g_ms * 1e-3) / 1e12, 1),
         "gemm_frac_fp8_peak": round(gemm_flops / (g_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "quantizer_timing": "cold: each call on its own buffers, rotated over >= 1 GB (4x the last-level cache)",
         "quantizer_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
         "quantizer_frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "calls": call_info,
@@ -577,7 +659,8 @@ def main():
         out["legs"] = legs(torch, fq, synth, dev)
 
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(torch, np, X, O_in, W, slots_np, value, gemm_flops)
+        out["cpu_baseline"] = cpu_baseline(torch, np, X, O_in, W, slots_np, value, gemm_flops,
+                                           rows=TOKENS if args.cpu_full else 512)
 
     print(json.dumps(out), flush=True)
 
@@ -612,6 +695,34 @@ def _time_cold(torch, fn, iters=10):
         ts.append(e0.elapsed_time(e1))
     del flush
     return sorted(ts)[len(ts) // 2]
+
+
+ROTATE_BYTES = 1 << 30   # buffer rotation footprint: 4x the 256 MB last-level cache
+
+
+def _time_rotated(torch, fns, iters=5):
+    """Average time of one call when every call finds its operands outside the caches:
+    `fns` are the same call on distinct buffer sets whose total footprint is at least
+    ROTATE_BYTES, captured in order into one graph and replayed `iters` times, so each
+    call's buffers were last touched a whole rotation (>= 1 GB of traffic) earlier."""
+    for f in fns[:2]:
+        f()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for f in fns:
+                f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return _time_graph(torch, g, iters) / len(fns)
+
+
+def _rotation_sets(set_bytes):
+    """Buffer sets needed for a ROTATE_BYTES rotation of sets of `set_bytes` each."""
+    return max(2, -(-ROTATE_BYTES // int(set_bytes)))
 
 
 def _time(torch, fn, iters, warm=2, reps=10):
@@ -680,7 +791,12 @@ def legs(torch, fq, synth, dev):
     a2 = synth.device_activation(mrows, I, dev, 4, 0, 6, outlier_channels=0)
     a2q = torch.empty((mrows, I), dtype=torch.uint8, device=dev)
     a2s = torch.empty((I // 128, mrows), dtype=torch.float32, device=dev)
-    ms_aq = _time(torch, lambda: fq.fp8q_quant_act_g128(a2, a2q, a2s), 10)
+    fns = []
+    for _ in range(_rotation_sets(3 * a2.numel())):
+        xc, qc, sc = a2.clone(), torch.empty_like(a2q), torch.empty_like(a2s)
+        fns.append(lambda xc=xc, qc=qc, sc=sc: fq.fp8q_quant_act_g128(xc, qc, sc))
+    ms_aq = _time_rotated(torch, fns)
+    del fns, xc, qc, sc
     offs = torch.from_numpy(off).to(dev)
     y1 = torch.empty((mrows, 2 * I), dtype=torch.bfloat16, device=dev)
     y2 = torch.empty((mrows, H), dtype=torch.bfloat16, device=dev)
@@ -700,8 +816,9 @@ def legs(torch, fq, synth, dev):
         res[name] = {"rows": mrows, "us": round(ms_ * 1e3, 1), "TFLOPs": round(tf, 1),
                      "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4), "frac_roofline": round(tf / ceil, 4),
                      "roofline_TFLOPs": round(ceil, 1)}
-    res["a2_moe_fc2_act_quant"] = {"us": round(ms_aq * 1e3, 1),
-                                   "GBps": round((3 * a2.numel() + 4 * a2.numel() / 128) / (ms_aq * 1e-3) / 1e9, 1)}
+    gbs = (3 * a2.numel() + 4 * a2.numel() / 128) / (ms_aq * 1e-3) / 1e9
+    res["a2_moe_fc2_act_quant"] = {"us": round(ms_aq * 1e3, 1), "GBps": round(gbs, 1),
+                                   "frac_hbm": round(gbs / HBM_PEAK_GBPS, 4), "timing": "cold (1 GB rotation)"}
 
     # the layer's data movement around the grouped GEMMs: dispatch of the quantized tokens
     # by their recorded top-8 expert ids, SwiGLU + 1x128 quantization of fc1's output,
@@ -874,6 +991,24 @@ def legs(torch, fq, synth, dev):
             res[f"a3_gemm_m{m}_n{n}"] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 2),
                                          "frac_roofline": round(tf / ceil, 4)}
 
+    # 1x128 activation quantization at the dense model's other shapes: 4096 tokens of the
+    # MLP's down-projection input (K = 12288) and 64 tokens at K = 4096 and 12288, cold
+    log("leg: activation quantization shapes")
+    for m, k in ((4096, 12288), (64, 4096), (64, 12288)):
+        x = synth.device_activation(m, k, dev, 3, 0, 20 + k // 4096)
+        fns = []
+        for _ in range(_rotation_sets(3 * x.numel())):
+            xc = x.clone()
+            qc = torch.empty((m, k), dtype=torch.uint8, device=dev)
+            sc = torch.empty((k // 128, m), dtype=torch.float32, device=dev)
+            fns.append(lambda xc=xc, qc=qc, sc=sc: fq.fp8q_quant_act_g128(xc, qc, sc))
+        ms = _time_rotated(torch, fns, iters=5 if m > 64 else 2)
+        gbs = (3 * m * k + 4 * m * k / 128) / (ms * 1e-3) / 1e9
+        res[f"a2_act_quant_m{m}_k{k}"] = {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1),
+                                          "frac_hbm": round(gbs / HBM_PEAK_GBPS, 4), "timing": "cold (1 GB rotation)"}
+        del fns, xc, qc, sc, x
+    torch.cuda.empty_cache()
+
     # dense MLP GEMMs: gate/up (4096 -> 12288) and down (12288 -> 4096) at 64 and 4096 tokens
     log("leg: MLP GEMMs")
     for name, n, k in (("gate_up", 12288, 4096), ("down", 4096, 12288)):
@@ -916,55 +1051,55 @@ def legs(torch, fq, synth, dev):
     return res
 
 
-def cpu_baseline(torch, np, X, O_in, W, slots_np, gpu_value, gemm_flops):
-    """The oracle, as it stands, on a bounded sample of the step: 128 of the 4096 tokens
-    through act-quant, the q/k/v/o GEMMs (fp64) and the KV write, plus one 128-row block
-    row of each weight through blockwise quantization.  Each part is scaled to the full
-    step (x32 for the token parts, x20 for the weight sync) and the step's GEMM FLOPs are
-    divided by the estimated step time (TFLOP/s, like `value`)."""
+def cpu_baseline(torch, np, X, O_in, W, slots_np, gpu_value, gemm_flops, rows=512):
+    """The oracle, as it stands, on a bounded sample of the step: every weight of q/k/v/o
+    through blockwise quantization (the whole sync of the step), and `rows` of the 4096
+    tokens through act-quant, the q/k/v/o GEMMs (fp64), the KV write and the o input's
+    act-quant; the token part is scaled by 4096/rows to a full step, and the step's GEMM
+    FLOPs are divided by the estimated step time (TFLOP/s, like `value`).  rows = 4096 runs
+    the whole step unsampled (about 150 s of 16 host threads)."""
     import oracle
 
-    rows = 128
     tok_scale = TOKENS / rows
     h = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     xb, ob = h(X[:rows]), h(O_in[:rows])
     wfull = {n: h(W[n]) for n in W}
-    wrow = {n: wfull[n][:128] for n in W}
-    w_scale = sum(w.shape[0] for w in wfull.values()) / (128 * len(W))
-    log(f"cpu baseline: oracle on {rows} tokens and {len(W)} weight block-rows "
-        f"({oracle.num_threads()} threads)")
-    wq = {n: oracle.quant_weight_blk128(wfull[n]) for n in wfull}  # operands of the sampled GEMMs (setup)
+    log(f"cpu baseline: oracle on the q/k/v/o weights and {rows} of {TOKENS} tokens "
+        f"({oracle.num_threads()} threads, {os.cpu_count()} logical CPUs on the host)")
 
     t0 = time.perf_counter()
-    for n in wrow:
-        oracle.quant_weight_blk128(wrow[n])
+    wq = {n: oracle.quant_weight_blk128(wfull[n]) for n in wfull}
     t_w = time.perf_counter() - t0
 
     t1 = time.perf_counter()
     xq, xs = oracle.quant_act_g128(xb)
-    yq = oracle.gemm_w8a8(xq, xs, *wq["q"])
+    oracle.gemm_w8a8(xq, xs, *wq["q"])
     yk = oracle.gemm_w8a8(xq, xs, *wq["k"])
     yv = oracle.gemm_w8a8(xq, xs, *wq["v"])
     t_gemm_kv_in = time.perf_counter() - t1
     bf = lambda y: torch.from_numpy(y.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy() \
         .view(np.uint16).reshape(rows, 8, 128)
     kb, vb = bf(yk), bf(yv)
-    cache = np.zeros((int(slots_np[:rows].max()) // 16 + 1, 16, 8, 128), np.uint8)
+    kcache = np.zeros((int(slots_np[:rows].max()) // 16 + 1, 16, 8, 128), np.uint8)
+    vcache = kcache.copy()
     t2 = time.perf_counter()
-    oracle.kv_quant(kb, vb, slots_np[:rows], cache, cache, 16)
+    oracle.kv_quant(kb, vb, slots_np[:rows], kcache, vcache, 16)
     oq, os_ = oracle.quant_act_g128(ob)
     oracle.gemm_w8a8(oq, os_, *wq["o"])
     t_rest = time.perf_counter() - t2
 
     t_tok = t_gemm_kv_in + t_rest
     sample_s = t_w + t_tok
-    est_step_s = t_w * w_scale + t_tok * tok_scale
+    est_step_s = t_w + t_tok * tok_scale
     value = gemm_flops / est_step_s / 1e12
+    what = ("the whole step (unsampled)" if rows == TOKENS else
+            f"all q/k/v/o weights (blockwise quantization, unscaled) and {rows} of {TOKENS} tokens "
+            f"(act quant, q/k/v/o GEMMs in fp64, KV write; scaled x{tok_scale:g})")
     return {"value": value, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{rows} of {TOKENS} tokens (act quant, q/k/v/o GEMMs in fp64, KV write; x{tok_scale:g}) "
-                      f"and one 128-row block row of each of q/k/v/o (blockwise quantization; x{w_scale:g}); "
-                      f"{sample_s:.1f} s measured, {est_step_s:.0f} s estimated per step",
+            "sample": f"{what}; {sample_s:.1f} s measured, {est_step_s:.1f} s per step",
+            "host_logical_cpus": os.cpu_count(), "threads": oracle.num_threads(),
             "sample_seconds": round(sample_s, 2), "est_step_seconds": round(est_step_s, 1),
+            "weight_sync_seconds": round(t_w, 2), "token_part_seconds": round(t_tok, 2),
             "gpu_over_cpu": round(gpu_value / value, 1)}
 
 

@@ -147,7 +147,8 @@ fp8q_status finite_bf16(const void* p, int64_t rows, int64_t cols, int64_t ld, c
   return st;
 }
 
-// finite fp32 values; pow2: positive powers of two (normal or subnormal)
+// finite fp32 values; pow2: 2^e with -127 <= e <= 127 (normal, or the one subnormal
+// 2^-127, whose E8M0 code is 0: smaller subnormals have no E8M0 code)
 fp8q_status check_f32(const void* p, int64_t rows, int64_t cols, int64_t ld, const char* name, bool pow2,
                       bool positive) {
   std::vector<float> v;
@@ -158,11 +159,11 @@ fp8q_status check_f32(const void* p, int64_t rows, int64_t cols, int64_t ld, con
     std::memcpy(&b, &x, 4);
     const uint32_t man = b & 0x7fffffu, ex = (b >> 23) & 0xffu;
     const bool bad = !std::isfinite(x) || (positive && !(x > 0.0f)) ||
-                     (pow2 && (!(x > 0.0f) || (ex != 0 ? man != 0 : (man & (man - 1)) != 0)));
+                     (pow2 && (!(x > 0.0f) || (ex != 0 ? man != 0 : man != 0x400000u)));
     if (bad)
       return fail(FP8Q_ERR_PRECONDITION, "%s[%lld][%lld] = %g is not %s", name, (long long)(i / cols),
                   (long long)(i % cols), (double)x,
-                  pow2 ? "a positive power of two" : (positive ? "positive and finite" : "finite"));
+                  pow2 ? "a positive power of two 2^e, -127 <= e <= 127" : (positive ? "positive and finite" : "finite"));
   }
   return st;
 }
@@ -329,8 +330,9 @@ static fp8q_status check_gemm_common(const void* a, int64_t ld_a, const float* a
   if (ld_a < k || ld_as < m || ld_y < n) return fail(FP8Q_ERR_STRIDE, "ld_a < k, ld_as < m or ld_y < n");
   if (!aligned16(a) || !aligned16(y) || ld_a % 16 || ld_y % 8 || !aligned4(a_s))
     return fail(FP8Q_ERR_ALIGN, "a/y must be 16-byte aligned with ld_a %% 16 == 0 and ld_y %% 8 == 0");
-  if (m * ld_a > kMaxOperandBytes || ld_as * 4 > kMaxOperandBytes)
-    return fail(FP8Q_ERR_SHAPE, "an operand spans more than 2 GiB");
+  // the token scales are addressed as one [k/128][ld_as] fp32 range
+  if (m * ld_a > kMaxOperandBytes || ld_as * 4 * (k / 128) > kMaxOperandBytes)
+    return fail(FP8Q_ERR_SHAPE, "an operand spans more than 2 GiB (a, or a_s: 4 * ld_as * k/128 bytes)");
   return FP8Q_OK;
 }
 
@@ -488,8 +490,9 @@ fp8q_status fp8q_grouped_gemm_swiglu_quant(const void* a, int64_t ld_a, const fl
     if (!aligned16(a) || !aligned16(b) || !aligned16(q) || ld_a % 16 || ld_q % 16 || !aligned4(a_s) ||
         !aligned4(b_s) || !aligned4(s) || !aligned4(group_offsets) || !aligned4(row_token))
       return fail(FP8Q_ERR_ALIGN, "a/b/q must be 16-byte aligned with ld_a, ld_q multiples of 16");
-    if (a_rows * ld_a > kMaxOperandBytes || ld_as * 4 > kMaxOperandBytes || 2 * n_half * k > kMaxOperandBytes)
-      return fail(FP8Q_ERR_SHAPE, "an operand spans more than 2 GiB");
+    if (a_rows * ld_a > kMaxOperandBytes || ld_as * 4 * (k / 128) > kMaxOperandBytes ||
+        2 * n_half * k > kMaxOperandBytes)
+      return fail(FP8Q_ERR_SHAPE, "an operand spans more than 2 GiB (a, a_s: 4 * ld_as * k/128 bytes, or b)");
   }
   fp8q_status st = check_device();
   if (st != FP8Q_OK) return st;

@@ -178,8 +178,8 @@ fp8q_status fp8q_quant_act_g128_ue8m0(const void* x, int64_t m, int64_t k, int64
  *   b_s: fp32 [n/128][k/128] contiguous (as written by fp8q_quant_weight_blk128);
  *   y:   bf16 [m, n] row-major, ld_y elements >= n, ld_y % 8 == 0.
  *   n % 128 == 0, k % 128 == 0, k >= 128.  m == 0 is a no-op.  No bias.
- *   Each operand (m * ld_a, n * ld_b, 4 * ld_as bytes) spans at most 2 GiB (else
- *   FP8Q_ERR_SHAPE).
+ *   Each operand spans at most 2 GiB (else FP8Q_ERR_SHAPE): a (m * ld_a bytes), b
+ *   (n * ld_b bytes) and a_s, addressed whole as 4 * ld_as * (k/128) bytes.
  * Accuracy: every element within half a bf16 ulp of the exact value plus 2e-3 of the
  * largest |y| (fp32 accumulation order differs from exact arithmetic).
  * ---------------------------------------------------------------------------- */
@@ -210,7 +210,8 @@ fp8q_status fp8q_gemm_w8a8_ue8m0(const void* a, int64_t ld_a, const float* a_s, 
  *   y:   bf16 [total_m, n], ld_y elements.
  * Empty groups are allowed.  num_groups >= 1; n, k multiples of 128; total_m == 0 is a
  * no-op.  Rows outside [offsets[0], offsets[G]) are not written.  As for the dense call,
- * total_m * ld_a, n * k (one expert) and 4 * ld_as bytes are each at most 2 GiB.
+ * total_m * ld_a, n * k (one expert) and 4 * ld_as * (k/128) bytes (the whole a_s) are
+ * each at most 2 GiB.
  * ---------------------------------------------------------------------------- */
 fp8q_status fp8q_grouped_gemm_w8a8(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
                                    const void* b, const float* b_s,

@@ -20,9 +20,20 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fp8q_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libfp8q_oracle.so")
 
 CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC"]
+
+# FP8Q_ORACLE_SANITIZE=1 builds and loads a separate AddressSanitizer + UndefinedBehavior-
+# Sanitizer build of the oracle (host code only; the interpreter must run with gcc's
+# libasan preloaded, e.g. LD_PRELOAD=$(gcc -print-file-name=libasan.so)
+# ASAN_OPTIONS=detect_leaks=0), so the CPU test suite can run against it.
+SANITIZE = os.environ.get("FP8Q_ORACLE_SANITIZE", "0") == "1"
+if SANITIZE:
+    _LIB_PATH = os.path.join(_HERE, "libfp8q_oracle_asan.so")
+    CFLAGS = CFLAGS + ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                       "-fno-sanitize-recover=undefined"]
+else:
+    _LIB_PATH = os.path.join(_HERE, "libfp8q_oracle.so")
 
 
 def build(force: bool = True) -> str:
@@ -165,6 +176,34 @@ def gemm_w8a8(a: np.ndarray, a_s: np.ndarray, b: np.ndarray, b_s: np.ndarray) ->
     n = b.shape[0]
     y = np.empty((m, n), dtype=np.float64)
     _check(lib().oracle_gemm_w8a8(a, k, a_s, a_s.shape[1], b, k, b_s, y, n, m, n, k), "gemm_w8a8")
+    return y
+
+
+def e4m3_table() -> np.ndarray:
+    """The oracle's decoded value of each of the 256 E4M3FN codes (NaN codes as NaN)."""
+    return np.array([lib().oracle_e4m3_decode(c) for c in range(256)], dtype=np.float64)
+
+
+def gemm_w8a8_blockwise(a: np.ndarray, a_s: np.ndarray, b: np.ndarray, b_s: np.ndarray) -> np.ndarray:
+    """The same fp64 block-scaled GEMM as ``gemm_w8a8``, for full-size shapes: each K block's
+    product sum_{t in kb} dec(a[i,t]) dec(b[j,t]) is one float64 matrix product of the
+    decoded codes (a library step; every partial sum is an integer multiple of 2^-18 below
+    2^43, so it is exact in any summation order), then y += (sa * sb) * P_kb with kb
+    ascending, the definition's outer sum in the C oracle's order and operations."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    a_s = np.asarray(a_s, dtype=np.float32)
+    b_s = np.asarray(b_s, dtype=np.float32)
+    m, k = a.shape
+    n = b.shape[0]
+    dec = e4m3_table()
+    y = np.zeros((m, n), dtype=np.float64)
+    for kb in range(k // 128):
+        da = dec[a[:, kb * 128:(kb + 1) * 128]]
+        db = dec[b[:, kb * 128:(kb + 1) * 128]]
+        p = da @ db.T
+        s = a_s[kb, :m].astype(np.float64)[:, None] * np.repeat(b_s[:, kb].astype(np.float64), 128)[None, :]
+        y += s * p
     return y
 
 

@@ -90,6 +90,29 @@ def test_gemm_validation():
     assert _gemm(n=big_n, ld_y=big_n) == fq.FP8Q_ERR_SHAPE
 
 
+# The token scales a_s are addressed as one [k/128][ld_as] fp32 range: a padded ld_as
+# whose whole span 4 * ld_as * k/128 passes 2 GiB is rejected, though one row of it fits.
+_LD_AS_WRAP = (1 << 31) // (4 * 64) + 16   # k = 8192: 64 scale rows of 4 * ld_as bytes
+
+
+def test_gemm_rejects_a_token_scale_span_beyond_2gib():
+    assert 4 * _LD_AS_WRAP < (1 << 31) < 4 * _LD_AS_WRAP * 64
+    for f in (fq.lib().fp8q_gemm_w8a8_blkscaled, fq.lib().fp8q_gemm_w8a8_ue8m0):
+        assert f(A16, 8192, A16, _LD_AS_WRAP, A16, 8192, A16, A16, 128, 8, 128, 8192, None) == fq.FP8Q_ERR_SHAPE
+        assert "a_s" in fq.last_error()
+        # the same call with a compact ld_as passes validation (no device here)
+        assert f(A16, 8192, A16, 8, A16, 8192, A16, A16, 128, 8, 128, 8192, None) == fq.FP8Q_ERR_UNSUPPORTED
+    for f in (fq.lib().fp8q_grouped_gemm_w8a8, fq.lib().fp8q_grouped_gemm_w8a8_ue8m0):
+        assert f(A16, 8192, A16, _LD_AS_WRAP, A16, A16, A16, 4, 64, A16, 128, 128, 8192,
+                 None) == fq.FP8Q_ERR_SHAPE
+        assert f(A16, 8192, A16, 64, A16, A16, A16, 4, 64, A16, 128, 128, 8192, None) == fq.FP8Q_ERR_UNSUPPORTED
+    L = fq.lib()
+    assert L.fp8q_grouped_gemm_swiglu_quant(A16, 8192, A16, _LD_AS_WRAP, None, 0, A16, A16, A16, 4, 64, A16, 256,
+                                            A16, 64, 256, 8192, None) == fq.FP8Q_ERR_SHAPE
+    assert L.fp8q_grouped_gemm_swiglu_quant(A16, 8192, A16, 64, None, 0, A16, A16, A16, 4, 64, A16, 256,
+                                            A16, 64, 256, 8192, None) == fq.FP8Q_ERR_UNSUPPORTED
+
+
 def test_grouped_validation():
     L = fq.lib()
     f = L.fp8q_grouped_gemm_w8a8

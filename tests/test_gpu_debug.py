@@ -93,6 +93,14 @@ def test_gemm_nan_code_and_bad_ue8m0_scale_are_rejected(debug):
     a_s[1, 3] = 0.3
     msg = _expect(fq.FP8Q_ERR_PRECONDITION, fq.fp8q_gemm_w8a8_ue8m0, a, a_s, b, b_s, y)
     assert "power of two" in msg
+    # 2^-127 (the smallest E8M0 scale, a binary32 subnormal) is accepted; 2^-130 has no
+    # E8M0 code and is rejected
+    a_s[1, 3] = 2.0 ** -127
+    fq.fp8q_gemm_w8a8_ue8m0(a, a_s, b, b_s, y)
+    a_s[1, 3] = 2.0 ** -130
+    assert a_s[1, 3].item() == 2.0 ** -130
+    msg = _expect(fq.FP8Q_ERR_PRECONDITION, fq.fp8q_gemm_w8a8_ue8m0, a, a_s, b, b_s, y)
+    assert "a_s[1][3]" in msg
     a_s[1, 3] = 0.5
     b[5, 9] = 0xFF
     msg = _expect(fq.FP8Q_ERR_PRECONDITION, fq.fp8q_gemm_w8a8_blkscaled, a, a_s, b, b_s, y)

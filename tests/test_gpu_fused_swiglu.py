@@ -15,7 +15,7 @@ import torch
 import oracle
 import fp8_block_scaled_weight_amd as fq
 from fp8_block_scaled_weight_amd import synth
-from tests._helpers import bf16_bits
+from tests._helpers import swiglu_near_decisions, bf16_bits
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -71,6 +71,7 @@ def test_fused_equals_gemm_then_swiglu_and_the_oracle(sizes, n_half, k):
     assert torch.all(s2[:, m:] == -2.0), "scale columns past total_m are not written"
     # the oracle's SwiGLU quantization of the GEMM's own bf16 output
     q_ref, s_ref = oracle.swiglu_quant_g128(bf16_bits(y))
+    assert swiglu_near_decisions(bf16_bits(y), s_ref) == (0, 0)
     assert np.array_equal(q2.cpu().numpy(), q_ref)
     assert np.array_equal(s2[:, :m].cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
 

@@ -43,9 +43,14 @@ def gpu_gemm(xq, xs, wq, ws, ld_y=None):
     return bf16_bits(y), bf16_bits(yfull)
 
 
-def check(xq, xs, wq, ws, rows=None, ld_y=None):
+def check(xq, xs, wq, ws, rows=None, ld_y=None, blockwise=False):
+    """blockwise: the oracle's full-size form (one float64 product per K block), which
+    gives the scalar oracle's numbers bit for bit in seconds at 4096-token shapes."""
     y, yfull = gpu_gemm(xq, xs, wq, ws, ld_y)
-    if rows is None:
+    if blockwise:
+        ref = oracle.gemm_w8a8_blockwise(xq, xs, wq, ws)
+        got = y
+    elif rows is None:
         ref = oracle.gemm_w8a8(xq, xs, wq, ws)
         got = y
     else:
@@ -70,12 +75,17 @@ def test_attention_shapes(m, n):
     check(*quantized_operands(m, n, 4096, tensor=n))
 
 
-def test_m4096_sampled_rows():
-    g = np.random.Generator(np.random.PCG64(1))
-    rows = np.sort(g.choice(4096, size=96, replace=False))
-    rows[:2] = [0, 4095]
-    for n in (4096, 1024):
-        check(*quantized_operands(4096, n, 4096, tensor=n + 1), rows=rows)
+@pytest.mark.parametrize("n", [4096, 2048, 1024])
+def test_m4096_all_rows(n):
+    """4096 tokens, every output: q/o (4096x4096), k and v stacked (2048x4096), k (1024x4096)."""
+    check(*quantized_operands(4096, n, 4096, tensor=n + 1), blockwise=True)
+
+
+@pytest.mark.parametrize("n,k", [(12288, 4096), (4096, 12288)])
+def test_mlp_m4096_all_rows(n, k):
+    """The dense MLP at 4096 tokens, every output: gate/up (12288x4096, 256x256 tiles over
+    32 K steps) and down (4096x12288, 96 K steps)."""
+    check(*quantized_operands(4096, n, k, cfg=3, tensor=3 + n // 4096), blockwise=True)
 
 
 def test_mlp_shapes_sampled():

@@ -17,7 +17,7 @@ import torch
 import oracle
 import fp8_block_scaled_weight_amd as fq
 from fp8_block_scaled_weight_amd import synth
-from tests._helpers import bf16_bits, bf16_to_f64, f32, to_dev_bf16, u8, ulp_bf16
+from tests._helpers import swiglu_near_decisions, bf16_bits, bf16_to_f64, f32, to_dev_bf16, u8, ulp_bf16
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -115,6 +115,9 @@ def _check_swiglu(h, ld_s=None):
     rq, rs, amax = oracle.swiglu_quant_g128(h, ld_s=ld_s, with_amax=True)
     assert np.all(gs[:, m:] == -5.0)
     assert not np.any(_near_boundary(amax)), "an input sits on an fp32 rounding boundary"
+    # the device's and glibc's fp64 exp are different implementations: no decision may sit
+    # close enough to a boundary for a few ulps of exp to move it
+    assert swiglu_near_decisions(h, rs) == (0, 0)
     assert np.array_equal(gs[:, :m].view(np.uint32), rs[:, :m].view(np.uint32)), "scales differ"
     bad = gq != rq
     assert not np.any(bad), f"{int(bad.sum())} codes differ"

@@ -10,7 +10,10 @@ decoded codes.
 Pins: one token (softmax of one score is 1), identical keys (uniform weights: the mean of
 V), one dominant key (the softmax saturates onto its V row), invariance under a permutation
 of the pages, the grouped-query head mapping, masking of cache bytes past the sequence
-length, query saturation under a stored scale, and the recalibrated query scale.
+length, query saturation under a stored scale, and the recalibrated query scale.  The
+softmax temperature sm_scale * q_scale * k_scale is pinned by closed forms: with two keys
+the weights are the logistic function of the score difference, and hand-picked codes make
+every dot product a small integer multiple of a power of two, written out by hand below.
 """
 import numpy as np
 import pytest
@@ -130,3 +133,68 @@ def test_recalibrated_query_scale():
     q[0, 0, 0] = synth.to_bf16_bits(np.array([1.5], np.float32))[0]
     assert oracle.q_scale(q) == np.float32(2.75) / np.float32(448)
     assert oracle.q_scale(np.zeros((1, 1, 128), np.uint16)) == 1.0
+
+
+# Hand-chosen codes for the closed-form pins: E4M3FN 0x7E = 448, 0x76 = 224, 0x38 = 1,
+# 0x30 = 0.5, 0x40 = 2, 0xB8 = -1, 0xF6 = -224 (format definition: bias 7, 3 mantissa bits).
+# the scales are binary32 at the boundary (sm_scale is fp64), so take binary32 values
+SM, QS, KS, VS = 0.08838834764831845, 0.5, float(np.float32(0.05)), 0.375
+
+
+def _two_key_cache():
+    """One KV head, one 16-token page; token 0 keys (1, 0.5), token 1 keys (0.5, -1) in
+    dims 0 and 1, zeros elsewhere; value rows seeded."""
+    kc = np.zeros((1, PS, 1, 128), np.uint8)
+    kc[0, 0, 0, :2] = (0x38, 0x30)
+    kc[0, 1, 0, :2] = (0x30, 0xB8)
+    return kc, _cache(21, 1, 1)
+
+
+def test_two_keys_give_logistic_weights():
+    """Query head 0 = (224, 0, ...) and head 1 = (0, -112, ...) with q_scale 0.5 encode to
+    codes 448 and -224 exactly.  Dots: head 0 -> (448, 224), head 1 -> (-112, 224).  With
+    f = sm_scale * q_scale * k_scale the weight of key 0 is 1 / (1 + exp(-f * (d0 - d1)))."""
+    q = np.zeros((1, 2, 128), np.float32)
+    q[0, 0, 0], q[0, 1, 1] = 224.0, -112.0
+    q = synth.to_bf16_bits(q)
+    kc, vc = _two_key_cache()
+    out = oracle.paged_decode_attention(q, kc, vc, np.array([[0]], np.int32), np.array([2], np.int32),
+                                        QS, KS, VS, SM)
+    f = SM * QS * KS
+    v0, v1 = _dec(vc[0, 0, 0]), _dec(vc[0, 1, 0])
+    for h, diff in ((0, 448.0 - 224.0), (1, -112.0 - 224.0)):
+        p0 = 1.0 / (1.0 + np.exp(-f * diff))
+        ref = VS * (p0 * v0 + (1.0 - p0) * v1)
+        assert np.allclose(out[0, h], ref, rtol=1e-13, atol=1e-15), h
+    # the weights are far from 0, 1 and 1/2, so each scale factor moves them
+    assert 0.55 < 1.0 / (1.0 + np.exp(-f * 224.0)) < 0.65
+
+
+def test_three_keys_over_two_pages_closed_form():
+    """Three tokens over pages of 2 (the second page holds one live token), two query heads
+    sharing one KV head, hand dot products; softmax written out with exp."""
+    ps = 2
+    q = np.zeros((1, 2, 128), np.float32)
+    q[0, 0, :3] = (224.0, 112.0, -0.5)     # / 0.5 -> codes 448, 224, -1
+    q[0, 1, :3] = (-112.0, 0.5, 1.0)       # / 0.5 -> codes -224, 1, 2
+    q = synth.to_bf16_bits(q)
+    kc = np.zeros((3, ps, 1, 128), np.uint8)
+    keys = {0: (0x38, 0x30, 0x40), 1: (0xB8, 0x38, 0x00), 2: (0x30, 0xB8, 0x38)}  # token -> dims 0..2
+    bt = np.array([[2, 0]], np.int32)      # tokens 0, 1 in page 2; token 2 in page 0
+    for t, codes in keys.items():
+        kc[bt[0, t // ps], t % ps, 0, :3] = codes
+    vc = np.zeros((3, ps, 1, 128), np.uint8)
+    vals = _cache(22, 3, 1)
+    for t in range(3):
+        vc[bt[0, t // ps], t % ps] = vals[t, 0]
+    out = oracle.paged_decode_attention(q, kc, vc, bt, np.array([3], np.int32), QS, KS, VS, SM)
+    # dots by hand: key values (1, .5, 2), (-1, 1, 0), (.5, -1, 1)
+    dots = {0: (448 * 1 + 224 * 0.5 + -1 * 2, 448 * -1 + 224 * 1 + 0, 448 * 0.5 + 224 * -1 + -1 * 1),
+            1: (-224 * 1 + 1 * 0.5 + 2 * 2, -224 * -1 + 1 * 1 + 0, -224 * 0.5 + 1 * -1 + 2 * 1)}
+    assert dots[0] == (558.0, -224.0, -1.0) and dots[1] == (-219.5, 225.0, -111.0)
+    f = SM * QS * KS
+    for h in (0, 1):
+        e = np.exp(f * np.array(dots[h]))
+        p = e / e.sum()
+        ref = VS * sum(p[t] * _dec(vals[t, 0, 0]) for t in range(3))
+        assert np.allclose(out[0, h], ref, rtol=1e-13, atol=1e-15), h

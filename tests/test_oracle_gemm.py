@@ -137,3 +137,34 @@ def test_grouped_equals_dense_per_group():
             continue
         ye = oracle.gemm_w8a8(aq[r0:r1], as_[:, r0:r1], bq[e], bs[e])
         assert np.array_equal(y[r0:r1], ye)
+
+
+def test_blockwise_matmul_form_equals_the_scalar_oracle():
+    """The full-size form (one float64 matrix product per K block, then the scaled outer
+    sum in K-block order) gives the scalar oracle's numbers bit for bit: every block sum is
+    exact in fp64, and the outer sum takes the same operations in the same order.  Codes
+    span the whole finite range, with the largest magnitudes forced into one row and one
+    column so block sums reach their largest values."""
+    g = np.random.Generator(np.random.PCG64(31))
+    m, n, k = 70, 256, 640
+    codes = np.concatenate([np.arange(0, 0x7F), np.arange(0x80, 0xFF)]).astype(np.uint8)
+    a = g.choice(codes, size=(m, k))
+    b = g.choice(codes, size=(n, k))
+    a[5], b[7] = 0x7E, 0x7E          # 128 * 448 * 448 block sums
+    b[9] = 0xFE
+    a_s = np.zeros((k // 128, m + 6), np.float32)   # padded ld_as
+    a_s[:, :m] = g.uniform(1e-4, 3.0, size=(k // 128, m)).astype(np.float32)
+    b_s = g.uniform(1e-5, 1e-2, size=(n // 128, k // 128)).astype(np.float32)
+    y_ref = oracle.gemm_w8a8(a, a_s, b, b_s)
+    y = oracle.gemm_w8a8_blockwise(a, a_s, b, b_s)
+    assert np.array_equal(y, y_ref)
+    assert np.abs(y).max() > 1e3
+
+
+def test_e4m3_table_matches_the_format_definition():
+    t = oracle.e4m3_table()
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            assert np.isnan(t[c])
+        else:
+            assert t[c] == float(_e4m3_fraction(c))
