@@ -34,7 +34,9 @@ FP8_PEAK_TFLOPS = 5000.0
 TOKENS = 4096
 HIDDEN = 4096
 KV_DIM = 1024
-DOM_LAUNCHES = 100      # back-to-back launches that time the dominant GEMM
+DOM_STEPS = 20          # eager steps whose q and o GEMMs time the dominant kernel
+DOM_BURST = 20          # back-to-back launches of it: a short burst ...
+DOM_SUSTAINED = 100     # ... and sustained load
 
 
 def log(*a):
@@ -282,28 +284,38 @@ def summarize_trace(d, bench_json=None):
         md.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                   f"{100 * float(r['TotalDurationNs']) / total:.1f} % |")
-    live = ""
+    dom = _dominant_loop_from_trace(d)
+    live = {}
     if bench_json:
         line = [l for l in open(bench_json) if l.startswith("{")][-1]
-        live = f" ({json.loads(line)['roofline']['avg_us']} us in the run of the same source)"
-    dom = _dominant_loop_from_trace(d)
+        live = json.loads(line)["roofline"]
     md += [
         "",
-        "The 256x256-tile GEMM instantiation runs only the two M=N=K=4096 projections (q, o) in this command,",
-        "so its average is the dominant kernel's duration under the tracer; bench.py measures the same kernel",
-        f"live with HIP events on its launch stream (`roofline.avg_us`{live}).",
+        "The 256x256-tile GEMM instantiation runs only the two M=N=K=4096 projections (q, o) in this command.",
+        "Its launches, grouped by pattern from `bench_kernel_trace.csv`, against bench.py's live HIP-event",
+        "figures in the same run:",
+        "",
+        "| launches | traced | traced average (us) | live (us) |",
+        "|---|---|---|---|",
     ]
     if dom:
-        md += [
-            "",
-            f"The launches bench.py times live are the run of {DOM_LAUNCHES + 3} consecutive launches of that kernel",
-            f"(3 untimed, then {DOM_LAUNCHES} between the two events), found in `bench_kernel_trace.csv`: "
-            f"average {dom['loop_avg_us']:.2f} us",
-            f"over those {dom['loop_n']} launches (min {dom['loop_min_us']:.2f}, max {dom['loop_max_us']:.2f}); "
-            f"all {dom['all_n']} launches average {dom['all_avg_us']:.2f} us.",
-            f"roofline.frac from the traced loop: 2*4096^3 FLOP / {dom['loop_avg_us']:.2f} us / 5.0 PF = "
-            f"{2 * 4096 ** 3 / (dom['loop_avg_us'] * 1e-6) / 5e15:.4f}.",
-        ]
+        for key, what, lkey in (("step", "single launches between other kernels: the q and o GEMMs inside steps "
+                                 "(eager and graph-replayed)", "avg_us"),
+                                ("burst", f"a burst of {DOM_BURST} back to back (the last {DOM_BURST} of a run "
+                                 f"of {DOM_BURST + 3})", "burst_avg_us"),
+                                ("sustained", f"{DOM_SUSTAINED} back to back (the last {DOM_SUSTAINED} of a run "
+                                 f"of {DOM_SUSTAINED + 3})", "sustained_avg_us"),
+                                ("other", "other runs (per-call timing graphs)", None),
+                                ("all", "all launches", None)):
+            g = dom.get(key)
+            if not g:
+                continue
+            lv = live.get(lkey, "") if lkey else ""
+            md.append(f"| {what} | {g['n']} | {g['avg']:.2f} (min {g['min']:.2f}, max {g['max']:.2f}) | {lv} |")
+        st = dom.get("step")
+        if st:
+            md += ["", f"`roofline.avg_us` is the in-step figure; from the trace: 2*4096^3 FLOP / {st['avg']:.2f} us "
+                       f"/ 5.0 PF = {2 * 4096 ** 3 / (st['avg'] * 1e-6) / 5e15:.4f} of the FP8 peak."]
     md += [f"gemm.hip source_digest: {source_digest('gemm.hip')}"]
     with open(os.path.join(ROOT, "profiles", "bench_step_kernel_trace.md"), "w") as f:
         f.write("\n".join(md) + "\n")
@@ -311,9 +323,9 @@ def summarize_trace(d, bench_json=None):
 
 
 def _dominant_loop_from_trace(d):
-    """From a rocprofv3 kernel trace: the launches of the 256x256 FP32-scale GEMM that
-    bench.py times live (the run of DOM_LAUNCHES + 3 consecutive dispatches of that kernel,
-    whose last DOM_LAUNCHES are timed), and the average over all its launches."""
+    """Durations of the 256x256 FP32-scale GEMM's launches in a rocprofv3 kernel trace,
+    grouped by launch pattern: single launches between other kernels (inside steps), the
+    timed part of the burst and sustained runs of consecutive launches, other runs, all."""
     import csv
     import glob
     files = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
@@ -324,24 +336,27 @@ def _dominant_loop_from_trace(d):
     tag = "GemmCfg<256, 256, 2, 4, 2>, false>"
     is_dom = [tag in r["Kernel_Name"] for r in rows]
     dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
-    alld = [x for x, f in zip(dur, is_dom) if f]
-    runs, i = [], 0
+    groups = {"step": [], "burst": [], "sustained": [], "other": [], "all": []}
+    i = 0
     while i < len(rows):
-        if is_dom[i]:
-            j = i
-            while j < len(rows) and is_dom[j]:
-                j += 1
-            runs.append((i, j))
-            i = j
-        else:
+        if not is_dom[i]:
             i += 1
-    loop = [(a, b) for a, b in runs if b - a == DOM_LAUNCHES + 3]
-    if not loop or not alld:
-        return None
-    a, b = loop[-1]
-    ld = dur[a + 3:b]
-    return {"loop_n": len(ld), "loop_avg_us": sum(ld) / len(ld), "loop_min_us": min(ld), "loop_max_us": max(ld),
-            "all_n": len(alld), "all_avg_us": sum(alld) / len(alld)}
+            continue
+        j = i
+        while j < len(rows) and is_dom[j]:
+            j += 1
+        run = dur[i:j]
+        groups["all"] += run
+        if j - i == 1:
+            groups["step"] += run
+        elif j - i == DOM_BURST + 3:
+            groups["burst"] += run[3:]
+        elif j - i == DOM_SUSTAINED + 3:
+            groups["sustained"] += run[3:]
+        else:
+            groups["other"] += run
+        i = j
+    return {k: {"n": len(v), "avg": sum(v) / len(v), "min": min(v), "max": max(v)} for k, v in groups.items() if v}
 
 
 def summarize_legs_trace(d):
@@ -577,22 +592,48 @@ def main():
     del fns, d, xc, qc, sc, ykv, kc_, vc_, ks_, vs_
     torch.cuda.empty_cache()
 
-    # The dominant kernel, launched directly (no graph), back to back on the current
-    # stream between two HIP events: its average duration.  These are the kernel's only
-    # back-to-back launches in the run, so a kernel trace of the same command isolates them.
+    # The dominant kernel (the q and o GEMMs) inside steps: DOM_STEPS eager steps, each GEMM
+    # launch between two HIP events on its launch stream.  Its average duration there is
+    # `roofline.avg_us`.  For context, the same kernel in a short burst (20 launches back to
+    # back) and sustained (100 back to back), where the chip lowers its clock under the
+    # continuous matrix-core load.  Each group is a distinct launch pattern in a kernel
+    # trace of the same command (single launches between other kernels, and runs of 23 and
+    # 103 consecutive launches of which the last 20 / 100 are timed).
+    dom_names = ("a3_gemm_q", "a3_gemm_o")
+    pairs = []
+    torch.cuda.synchronize()
+    for _ in range(DOM_STEPS):
+        for name, fn in calls:
+            if name in dom_names:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                pairs.append((e0, e1))
+            else:
+                fn()
+    torch.cuda.synchronize()
+    dom_avg_ms = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+    n_dom = len(pairs)
     dom_fn = calls[2][1]
-    for _ in range(3):
-        dom_fn()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    n_dom = DOM_LAUNCHES
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(n_dom):
-        dom_fn()
-    e1.record()
-    torch.cuda.synchronize()
-    dom_avg_ms = e0.elapsed_time(e1) / n_dom
+
+    def back_to_back(n):
+        for _ in range(3):
+            dom_fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            dom_fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    burst_ms = back_to_back(DOM_BURST)
+    fill = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    fill.fill_(0)  # a different kernel between the two runs
+    sustained_ms = back_to_back(DOM_SUSTAINED)
+    del fill
 
     # algorithmic bytes / flops per call
     w_elems = sum(w.numel() for w in W.values())
@@ -626,7 +667,10 @@ def main():
                 "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
                 "traffic": traffic_from_profile("gemm_w8a8_4096", source_digest("gemm.hip")),
                 "kernel": "gemm_w8a8_kernel<GemmCfg<256,256,2,4,2>> M=N=K=4096 (q/o projection)",
-                "avg_us": round(dom_avg_ms * 1e3, 2), "launches_timed": n_dom}
+                "avg_us": round(dom_avg_ms * 1e3, 2), "launches_timed": n_dom,
+                "timed_as": f"q and o GEMM launches inside {DOM_STEPS} steps, each between two HIP events",
+                "burst_avg_us": round(burst_ms * 1e3, 2), "burst_launches": DOM_BURST,
+                "sustained_avg_us": round(sustained_ms * 1e3, 2), "sustained_launches": DOM_SUSTAINED}
 
     out = {
         "metric": "W8A8 block-scaled GEMM TFLOP/s (% FP8 peak) + quantizer GB/s (% HBM) at 1 GPU",
