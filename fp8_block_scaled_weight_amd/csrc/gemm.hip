@@ -519,6 +519,7 @@ __device__ __forceinline__ void tile_coords(int64_t t, int64_t m_tiles, int64_t 
 // halves operand traffic per FLOP but leaves room in LDS for only two stages; the
 // smaller tiles keep three steps of copies in flight, which their shorter steps need.
 using CfgLarge = GemmCfg<256, 256, 2, 4, 2>;   // 128 x 64 per wave, 132 KB LDS
+using CfgLargeHalf = GemmCfg<128, 256, 2, 4, 2>;  // 64 x 64 per wave: a group's last <= 128 rows
 using CfgMid = GemmCfg<128, 128, 2, 4, 4>;     // 64 x 32 per wave, 132 KB LDS
 using CfgMid2 = GemmCfg<128, 128, 2, 4, 2>;    // two workgroups per CU when tiles are plenty
 using CfgSmall = GemmCfg<128, 64, 2, 2, 4>;    // 64 x 32 per wave, 100 KB LDS
@@ -875,6 +876,82 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_w8a8_kernel(
                      (uint8_t FP8Q_LDS*)lds);
 }
 
+// Two tile heights for the 256-wide tiles.  A group's rows are covered by 256-row tiles
+// while more than 128 rows are left, and a remainder of at most 128 rows by one 128-row
+// tile (a 94-row expert then runs 128 rows of MFMAs, not 256).  The global m-tile list
+// holds every group's 256-row tiles in group order, then the 128-row tiles: the longer
+// tiles are dispatched first.  Wave 0 writes sel[0] = group (-1: none), sel[1] = the
+// tile's first row within the group, sel[2] = 1 for a 128-row tile.
+__device__ __forceinline__ void find_group_tile_mixed(const int32_t* __restrict__ off, int32_t groups,
+                                                      int64_t tile_m, int32_t* sel) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int found_g = -1, found_row = 0, small = 0;
+    for (int pass = 0; pass < 2 && found_g < 0; ++pass) {
+      int64_t base = 0;
+      for (int g0 = 0; g0 < groups; g0 += 64) {
+        const int g = g0 + lane;
+        int64_t rows = g < groups ? (int64_t)(off[g + 1] - off[g]) : 0;
+        const int64_t rem = rows & 255;
+        const int64_t tiles = pass == 0 ? (rows >> 8) + (rem > 128) : (rem > 0 && rem <= 128);
+        int64_t incl = tiles;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int64_t o = __shfl_up(incl, d);
+          if (lane >= d) incl += o;
+        }
+        const int64_t excl = incl - tiles;
+        const bool mine = tiles > 0 && tile_m >= base + excl && tile_m < base + incl;
+        const unsigned long long hit = __ballot(mine);
+        if (hit && found_g < 0) {
+          const int src = __ffsll(hit) - 1;
+          found_g = g0 + src;
+          const int64_t t = tile_m - base - __shfl(excl, src);
+          found_row = pass == 0 ? (int)(256 * t) : (int)(__shfl(rows, src) & ~(int64_t)255);
+          small = pass;
+        }
+        base += __shfl(incl, 63);
+      }
+      tile_m -= base;  // the 128-row tiles are numbered after all 256-row tiles
+    }
+    if (lane == 0) {
+      sel[0] = found_g;
+      sel[1] = found_row;
+      sel[2] = small;
+    }
+  }
+  __syncthreads();
+}
+
+// 256-wide tiles of both heights in one grid (for K >= 2048; see launch_grouped_gemm)
+template <bool POW2>
+__global__ __launch_bounds__(CfgLarge::THREADS) void grouped_gemm_mixed_kernel(
+    const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
+    const uint8_t* __restrict__ b, const float* __restrict__ bs, const int32_t* __restrict__ off,
+    int32_t groups, uint16_t* __restrict__ y, int64_t ld_y, int64_t n, int64_t k, int64_t n_tiles) {
+  static_assert(CfgLargeHalf::LDS_BYTES <= CfgLarge::LDS_BYTES && CfgLargeHalf::THREADS == CfgLarge::THREADS,
+                "both tile heights share the launch");
+  __shared__ __align__(1024) uint8_t lds[CfgLarge::LDS_BYTES];
+  __shared__ int32_t sel[3];
+  const int64_t tile_n = blockIdx.x % n_tiles;
+  find_group_tile_mixed(off, groups, blockIdx.x / n_tiles, sel);
+  const int g = sel[0];
+  if (g < 0) return;
+  const int kblocks = (int)(k / 128);
+  const int64_t row0 = off[g] + sel[1];
+  const int64_t a_rows = off[groups];
+  const uint8_t* bg = b + (int64_t)g * n * k;
+  const float* bsg = bs + (int64_t)g * (n / 128) * kblocks;
+  if (sel[2] == 0) {
+    const int64_t row_end = (row0 + 256) < off[g + 1] ? (row0 + 256) : off[g + 1];
+    gemm_tile<CfgLarge, POW2>(a, ld_a, a_rows, as, ld_as, bg, k, bsg, kblocks, y, ld_y, row0, row_end,
+                              tile_n * 256, (uint8_t FP8Q_LDS*)lds);
+  } else {
+    gemm_tile<CfgLargeHalf, POW2>(a, ld_a, a_rows, as, ld_as, bg, k, bsg, kblocks, y, ld_y, row0, off[g + 1],
+                                  tile_n * 256, (uint8_t FP8Q_LDS*)lds);
+  }
+}
+
 // MoE fc1 with SwiGLU and fc2's 1x128 quantization fused into the epilogue: B is
 // [G][2 half][k] (gate rows, then up rows); tile column tn covers outputs 128tn .. +127.
 template <bool POW2>
@@ -883,16 +960,14 @@ __global__ __launch_bounds__(CfgLarge::THREADS) void grouped_swiglu_kernel(
     const uint8_t* __restrict__ b, const float* __restrict__ bs, const int32_t* __restrict__ off,
     int32_t groups, int64_t half, int64_t k, int64_t n_tiles, uint8_t* __restrict__ q, int64_t ld_q,
     float* __restrict__ s, int64_t ld_s, const int32_t* __restrict__ row_token, int64_t token_rows) {
-  using C = CfgLarge;
-  __shared__ __align__(1024) uint8_t lds[C::LDS_BYTES];
-  __shared__ int32_t sel[2];
+  __shared__ __align__(1024) uint8_t lds[CfgLarge::LDS_BYTES];
+  __shared__ int32_t sel[3];
   const int64_t tile_n = blockIdx.x % n_tiles;
-  find_group_tile<C::BM>(off, groups, blockIdx.x / n_tiles, sel);
+  find_group_tile_mixed(off, groups, blockIdx.x / n_tiles, sel);
   const int g = sel[0];
   if (g < 0) return;
   const int kblocks = (int)(k / 128);
-  const int64_t row0 = off[g] + (int64_t)sel[1] * C::BM;
-  const int64_t row_end = (row0 + C::BM) < off[g + 1] ? (row0 + C::BM) : off[g + 1];
+  const int64_t row0 = off[g] + sel[1];
   const int64_t a_rows = row_token ? token_rows : off[groups];
   const uint8_t* bg = b + (int64_t)g * 2 * half * k;
   const float* bsg = bs + (int64_t)g * (2 * half / 128) * kblocks;
@@ -902,8 +977,14 @@ __global__ __launch_bounds__(CfgLarge::THREADS) void grouped_swiglu_kernel(
   so.s = s;
   so.ld_s = ld_s;
   so.half = half;
-  gemm_tile<C, POW2, true>(a, ld_a, a_rows, as, ld_as, bg, k, bsg, kblocks, nullptr, 0, row0, row_end,
-                           tile_n * C::BN, (uint8_t FP8Q_LDS*)lds, so, row_token);
+  if (sel[2] == 0) {
+    const int64_t row_end = (row0 + 256) < off[g + 1] ? (row0 + 256) : off[g + 1];
+    gemm_tile<CfgLarge, POW2, true>(a, ld_a, a_rows, as, ld_as, bg, k, bsg, kblocks, nullptr, 0, row0, row_end,
+                                    tile_n * 256, (uint8_t FP8Q_LDS*)lds, so, row_token);
+  } else {
+    gemm_tile<CfgLargeHalf, POW2, true>(a, ld_a, a_rows, as, ld_as, bg, k, bsg, kblocks, nullptr, 0, row0,
+                                        off[g + 1], tile_n * 256, (uint8_t FP8Q_LDS*)lds, so, row_token);
+  }
 }
 
 template <class C>
@@ -929,7 +1010,8 @@ hipError_t launch_grouped_swiglu(const void* a, int64_t ld_a, const float* a_s, 
                                  const int32_t* row_token, int64_t token_rows, hipStream_t stream) {
   using C = CfgLarge;
   const int64_t n_tiles = half / 128;
-  const int64_t m_tiles = (total_m + C::BM - 1) / C::BM + groups;
+  // 256-row tiles: at most total_m / 256 + one per group; 128-row tiles: at most one per group
+  const int64_t m_tiles = (total_m + 255) / 256 + 2 * (int64_t)groups;
   hipLaunchKernelGGL(grouped_swiglu_kernel<false>, dim3((unsigned)(n_tiles * m_tiles)), dim3(C::THREADS), 0, stream,
                      reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b), b_s,
                      offsets, groups, half, k, n_tiles, reinterpret_cast<uint8_t*>(q), ld_q, s, ld_s, row_token,
@@ -941,9 +1023,15 @@ hipError_t launch_grouped_gemm(const void* a, int64_t ld_a, const float* a_s, in
                                const void* b, const float* b_s, const int32_t* offsets, int32_t groups,
                                int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k, bool pow2,
                                hipStream_t stream) {
-  if (k >= 16 * 128 && n % CfgLarge::BN == 0)
-    return launch_grouped<CfgLarge>(a, ld_a, a_s, ld_as, b, b_s, offsets, groups, total_m, y, ld_y, n, k, pow2,
-                                    stream);
+  if (k >= 16 * 128 && n % CfgLarge::BN == 0) {
+    const int64_t n_tiles = n / 256;
+    const int64_t m_tiles = (total_m + 255) / 256 + 2 * (int64_t)groups;  // as for the fused fc1
+    auto kernel = pow2 ? grouped_gemm_mixed_kernel<true> : grouped_gemm_mixed_kernel<false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(n_tiles * m_tiles)), dim3(CfgLarge::THREADS), 0, stream,
+                       reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b),
+                       b_s, offsets, groups, reinterpret_cast<uint16_t*>(y), ld_y, n, k, n_tiles);
+    return hipGetLastError();
+  }
   return launch_grouped<CfgGrouped>(a, ld_a, a_s, ld_as, b, b_s, offsets, groups, total_m, y, ld_y, n, k, pow2,
                                     stream);
 }

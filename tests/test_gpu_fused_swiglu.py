@@ -62,6 +62,7 @@ def _both(aq, a_s, bq, b_s, off, m, n_half):
     ([5, 130, 0, 77], 128, 256),                    # short K, one 128-output tile column
     ([260], 384, 1024),                             # one group, three tile columns
     ([40, 300], 256, 128),                          # one K step: the only step is also the last
+    ([200, 128, 129, 0, 384, 255, 1], 256, 2048),   # 256- and 128-row tiles: remainders 200, 128, 129, 127, 1
 ])
 def test_fused_equals_gemm_then_swiglu_and_the_oracle(sizes, n_half, k):
     aq, a_s, bq, b_s, off, m = _operands(sizes, n_half, k, seed=len(sizes) * 7 + k)

@@ -204,6 +204,13 @@ def test_grouped_long_k_large_tiles():
     check_grouped(grouped_case([3, 0, 300, 1, 0, 513, 64, 256], 512, 2048, 8))
 
 
+def test_grouped_mixed_tile_heights():
+    """K >= 2048 covers a group with 256-row tiles while more than 128 rows are left and a
+    remainder of at most 128 rows with one 128-row tile: remainders of 128 (a full short
+    tile), 129 and 200 (one 256-row tile), 127, 255 and 1, exact multiples of 256, empty."""
+    check_grouped(grouped_case([200, 128, 129, 0, 384, 255, 257, 127, 512, 1], 256, 2048, 11))
+
+
 def test_grouped_all_empty_but_one():
     check_grouped(grouped_case([0, 0, 200, 0], 128, 256, 6))
 
