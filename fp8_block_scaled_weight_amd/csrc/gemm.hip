@@ -79,30 +79,39 @@ __device__ __forceinline__ v16f mfma32_scaled(v8i a, v8i b, v16f c, int ea, int 
 }
 __device__ __forceinline__ int e8m0_of(float pow2_scale) { return (int)(__float_as_uint(pow2_scale) >> 23); }
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+// KSPLIT > 1: the workgroup holds KSPLIT groups of WAVES_M x WAVES_N waves.  Group g takes
+// the K blocks g, g + KSPLIT, ... through its own copy ring, in lockstep with the others
+// (one barrier per step for all), and at the end the groups' partial sums are added in
+// group order through LDS.  It doubles the waves per SIMD of a small tile without a
+// workspace.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int KSPLIT_ = 1>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
-  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int KSPLIT = KSPLIT_;
+  static constexpr int GW = WAVES_M * WAVES_N;                // waves per K group
+  static constexpr int WAVES = GW * KSPLIT;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;  // wave tile: tokens x weights
   static constexpr int JM = TM / 32, IN = TN / 32;            // 32x32 sub-tiles per wave
   static constexpr int ROWS = BN + BM;                        // staged rows: weights, then tokens
   static constexpr int SCALE_OFF = ROWS * 128;
-  static constexpr int SPW = BM / WAVES;                      // token scales copied per wave
+  static constexpr int SPW = BM / GW;                         // token scales copied per wave
   static constexpr int NWS = BN >= 128 ? BN / 128 : 1;        // weight scales per step
   static constexpr int WSC_OFF = SCALE_OFF + BM * 4;            // per-wave weight scales
-  static constexpr int STAGE_BYTES = ((WSC_OFF + WAVES * NWS * 4) + 1023) / 1024 * 1024;
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int LOADS = ROWS / (8 * WAVES);
-  static constexpr int LOADS_W = BN / (8 * WAVES);
+  static constexpr int STAGE_BYTES = ((WSC_OFF + GW * NWS * 4) + 1023) / 1024 * 1024;
+  static constexpr int LDS_BYTES = KSPLIT * STAGES * STAGE_BYTES;
+  static constexpr int LOADS = ROWS / (8 * GW);
+  static constexpr int LOADS_W = BN / (8 * GW);
   static constexpr int VM_PER_STEP = LOADS + 2;  // copies per thread and step
+  static constexpr int RED_OFF = BM * BN * 2;    // KSPLIT > 1: partial sums, after the epilogue stage
   static_assert(TM % 32 == 0 && TN % 32 == 0, "32x32 sub-tiles");
-  static_assert(ROWS % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "whole 1 KB copies per wave");
+  static_assert(ROWS % (8 * GW) == 0 && BN % (8 * GW) == 0, "whole 1 KB copies per wave");
   static_assert(TN <= 128 && 128 % TN == 0, "a wave's weight rows lie in one scale block");
-  static_assert(SPW >= 1 && SPW + NWS <= 64 && BM % WAVES == 0, "scale copies");
+  static_assert(SPW >= 1 && SPW + NWS <= 64 && BM % GW == 0, "scale copies");
   static_assert(JM == 2 || JM == 4, "token scales per lane; the deferred chain's token "
                 "fragment must not be the one the next step reads first");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(KSPLIT == 1 || RED_OFF + (KSPLIT - 1) * BM * BN * 4 <= LDS_BYTES, "partial sums fit in LDS");
   static_assert(STAGES >= 2 && (STAGES - 2) * VM_PER_STEP <= 63, "vmcnt range");
 };
 
@@ -160,19 +169,31 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
                                           const int32_t* __restrict__ tok = nullptr) {
   static_assert(!SW || (C::BN == 256 && C::TN == 64 && C::WAVES_N == 4 && C::THREADS == 512 && C::BM % 64 == 0),
                 "the fused SwiGLU epilogue assumes the 256x256 tile");
+  static_assert(C::KSPLIT == 1 || (!SW && !POW2), "K groups: fp32-scale GEMM only");
   const int64_t jt = n0 / 256;  // SW: the tile's 128-row gate and up blocks
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave_all / C::GW;   // K group
+  const int wave = wave_all % C::GW;  // wave within its K group
   const int wm = (wave / C::WAVES_N) * C::TM;
   const int wn = (wave % C::WAVES_N) * C::TN;
-  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  uint8_t FP8Q_LDS* const lds0 = lds;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds + (uint32_t)(grp * C::STAGES * C::STAGE_BYTES);
+  lds += grp * C::STAGES * C::STAGE_BYTES;  // this group's copy ring
+  // step s of this group multiplies K block s * KSPLIT + grp (the last block again, with
+  // a zero scale product, where that passes the end)
+  const int nsteps = (kblocks + C::KSPLIT - 1) / C::KSPLIT;
+  auto kblock = [&](int step) {
+    const int kb = step * C::KSPLIT + grp;
+    return kb < kblocks ? kb : kblocks - 1;
+  };
 
   // ---- copy sources (fixed while K advances; K enters through the scalar offset)
   uint32_t src[C::LOADS];
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
-    const int r = (i * C::WAVES + wave) * 8 + (lane >> 3);
+    const int r = (i * C::GW + wave) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ swz(r);
     if (i < C::LOADS_W) {
       const int64_t wr = SW ? (r < 128 ? 128 * jt + r : sw.half + 128 * jt + (r - 128)) : n0 + r;
@@ -210,7 +231,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i)
       if (i >= i0 && i < i1)
-        dma16(i < C::LOADS_W ? rb : ra, src[i], (uint32_t)kb * 128u, dst + (uint32_t)((i * C::WAVES + wave) * 1024));
+        dma16(i < C::LOADS_W ? rb : ra, src[i], (uint32_t)kb * 128u, dst + (uint32_t)((i * C::GW + wave) * 1024));
   };
   auto issue_scales = [&](int kb, int stage) {
     const uint32_t dst = lds_base + (uint32_t)(stage * C::STAGE_BYTES);
@@ -330,13 +351,15 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
   constexpr int S = C::STAGES;
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
-    if (p < kblocks) issue(p, p);
-  int cur = 0;  // stage of step kb
-  for (int kb = 0; kb < kblocks; ++kb) {
-    // this thread's copies for step kb have landed (those of up to S-2 later steps may
+    if (p < nsteps) issue(kblock(p), p);
+  int cur = 0;  // stage of step ks
+  for (int ks = 0; ks < nsteps; ++ks) {
+    // K groups: a step past this group's last K block adds nothing (zero scale product)
+    const float live = (C::KSPLIT == 1 || ks * C::KSPLIT + grp < kblocks) ? 1.0f : 0.0f;
+    // this thread's copies for step ks have landed (those of up to S-2 later steps may
     // still be in flight); after the barrier every thread's have, and no wave still
     // reads the stage the copies issued next overwrite
-    if (kb + S - 2 < kblocks) {
+    if (ks + S - 2 < nsteps) {
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((S - 2) * C::VM_PER_STEP) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -358,13 +381,13 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
 #pragma unroll
     for (int i = 0; i + 1 < C::IN; ++i) read_a(i);
     __builtin_amdgcn_sched_barrier(0);
-    if (kb > 0) chain(1, C::IN - 1, (C::JM - 1) & 1);
+    if (ks > 0) chain(1, C::IN - 1, (C::JM - 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
     read_a(C::IN - 1);
     __builtin_amdgcn_sched_barrier(0);
-    const bool more = kb + S - 1 < kblocks;
-    const int nst = cur == 0 ? S - 1 : cur - 1;  // the stage step kb+S-1 fills
-    const int kn = more ? kb + S - 1 : kblocks - 1;
+    const bool more = ks + S - 1 < nsteps;
+    const int nst = cur == 0 ? S - 1 : cur - 1;  // the stage step ks+S-1 fills
+    const int kn = kblock(more ? ks + S - 1 : nsteps - 1);
     if constexpr (SPREAD) {
       if (more) issue_scales(kn, nst);
     } else {
@@ -382,7 +405,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
     } else {
       sa[0] = lds_ld<float>(st, so);
     }
-    const float sb = lds_ld<float>(st, wso);
+    const float sb = C::KSPLIT == 1 ? lds_ld<float>(st, wso) : lds_ld<float>(st, wso) * live;
     __builtin_amdgcn_sched_barrier(0);
 
     float c_prev = pc;
@@ -405,7 +428,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
           const int pi = (i == 0) ? C::IN - 1 : i - 1;
           const int pj = (i == 0) ? j - 1 : j;
           promote((ch - 1) & 1, pi, pj, (i == 0) ? c_prev : c);
-        } else if (kb > 0) {
+        } else if (ks > 0) {
           promote(1, C::IN - 1, C::JM - 1, pc);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -419,9 +442,38 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
     __builtin_amdgcn_sched_barrier(0);
     cur = (cur + 1 == S) ? 0 : cur + 1;
   }
-  if (kblocks > 0) {
+  if (nsteps > 0) {
     chain(1, C::IN - 1, (C::JM - 1) & 1);
     promote(1, C::IN - 1, C::JM - 1, pc);
+  }
+  if constexpr (C::KSPLIT > 1) {
+    // the groups' partial sums, added in group order: group g > 0 writes its sums (lane-
+    // contiguous, so every write and read covers whole bank rows), group 0 adds them
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    float FP8Q_LDS* red = reinterpret_cast<float FP8Q_LDS*>(lds0 + C::RED_OFF);
+    constexpr int PER_WAVE = C::IN * C::JM * 16 * 64;
+    if (grp > 0) {
+      float FP8Q_LDS* dst = red + ((grp - 1) * C::GW + wave) * PER_WAVE + lane;
+#pragma unroll
+      for (int i = 0; i < C::IN; ++i)
+#pragma unroll
+        for (int j = 0; j < C::JM; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) dst[((i * C::JM + j) * 16 + e) * 64] = acc[i][j][e];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (grp == 0) {
+#pragma unroll 1
+      for (int g = 1; g < C::KSPLIT; ++g) {
+        const float FP8Q_LDS* srcp = red + ((g - 1) * C::GW + wave) * PER_WAVE + lane;
+#pragma unroll
+        for (int i = 0; i < C::IN; ++i)
+#pragma unroll
+          for (int j = 0; j < C::JM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] += srcp[((i * C::JM + j) * 16 + e) * 64];
+      }
+    }
   }
 
   }
@@ -434,9 +486,10 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
   constexpr int CPR = C::TN / 8;          // 16-byte chunks per row
   constexpr int RPW = 16 / CPR;           // rows per 256-byte bank window
   constexpr int RPI = 64 / CPR;           // rows per wave store instruction
-  static_assert(C::WAVES * C::TM * C::TN * 2 <= C::LDS_BYTES, "epilogue staging fits in LDS");
+  static_assert(C::GW * C::TM * C::TN * 2 <= C::LDS_BYTES, "epilogue staging fits in LDS");
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  uint8_t FP8Q_LDS* ep = lds + wave * (C::TM * C::TN * 2);
+  if (grp > 0) return;  // K groups: group 0 holds the sums
+  uint8_t FP8Q_LDS* ep = lds0 + wave * (C::TM * C::TN * 2);
 #pragma unroll
   for (int j = 0; j < C::JM; ++j)
 #pragma unroll
@@ -523,6 +576,7 @@ using CfgLargeHalf = GemmCfg<128, 256, 2, 4, 2>;  // 64 x 64 per wave: a group's
 using CfgMid = GemmCfg<128, 128, 2, 4, 4>;     // 64 x 32 per wave, 132 KB LDS
 using CfgMid2 = GemmCfg<128, 128, 2, 4, 2>;    // two workgroups per CU when tiles are plenty
 using CfgSmall = GemmCfg<128, 64, 2, 2, 4>;    // 64 x 32 per wave, 100 KB LDS
+using CfgSmallK2 = GemmCfg<128, 64, 2, 2, 3, 2>;  // two K groups of 4 waves, 3-stage rings, 150 KB LDS
 
 template <class C, bool POW2>
 __global__ __launch_bounds__(C::THREADS) void gemm_w8a8_kernel(const uint8_t* __restrict__ a, int64_t ld_a,
@@ -782,7 +836,14 @@ template <bool POW2>
 static hipError_t launch_tiles(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                                int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                                int64_t k, hipStream_t stream) {
-  if (m < 1024) return launch_dense<CfgSmall, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  if (m < 1024) {
+    // two K groups per tile where each gets at least 4 steps (measured, interleaved medians:
+    // 512x4096x4096 19.5 -> 17.1 us, 300x4096x12288 48.6 -> 39.3 us, 130x1024x4096 17.6 ->
+    // 14.2 us; with 4-5 K steps in all the single group is faster: 700x1024x640 5.7 vs 6.1 us)
+    if (!POW2 && k >= 1024)
+      return launch_dense<CfgSmallK2, false>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+    return launch_dense<CfgSmall, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  }
   // large tiles when they cover n exactly and still give every CU a tile
   const int64_t large_tiles = ((m + CfgLarge::BM - 1) / CfgLarge::BM) * (n / CfgLarge::BN);
   if (n % CfgLarge::BN == 0 && large_tiles >= 256)
