@@ -34,7 +34,7 @@ FP8_PEAK_TFLOPS = 5000.0
 TOKENS = 4096
 HIDDEN = 4096
 KV_DIM = 1024
-DOM_STEPS = 20          # eager steps whose q and o GEMMs time the dominant kernel
+DOM_ROUNDS = 5          # alternating rounds of step graphs with and without the q and o GEMMs
 DOM_BURST = 20          # back-to-back launches of it: a short burst ...
 DOM_SUSTAINED = 100     # ... and sustained load
 
@@ -64,6 +64,11 @@ def parse():
     p.add_argument("--vendor-reference", action="store_true",
                    help="only time the vendor library's plain per-tensor-scaled FP8 GEMM (torch._scaled_mm) and "
                         "the bf16 matmul at the dense GEMM shapes, as context for the block-scaled GEMM's rate")
+    p.add_argument("--profile-gemms", action="store_true",
+                   help="only launch each GEMM workload of the side legs 8 times (a target for counter passes)")
+    p.add_argument("--summarize-gemm-counters", nargs=5,
+                   metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE", "MFMA"),
+                   help="write profiles/gemm_workloads_counters.md from counter passes over --profile-gemms")
     p.add_argument("--summarize-legs-trace", metavar="TRACE_DIR",
                    help="write profiles/bench_legs_kernel_trace.md from a rocprofv3 --stats run of the full bench")
     p.add_argument("--summarize-trace", nargs="+", metavar="TRACE_DIR [BENCH_JSON]",
@@ -186,6 +191,113 @@ def summarize_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
     with open(os.path.join(ROOT, "profiles", "quantizers_traffic.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     print("\n".join(lines))
+
+
+# GEMM workloads of the side legs, as targets for counter passes: (label, kind, m, n, k);
+# grouped workloads run the MoE layer's routing (128 experts, 4096 tokens top-8 = 32768 rows).
+_GEMM_WORKLOADS = [
+    ("dense 4096x4096x4096 (q, o)", "dense", 4096, 4096, 4096),
+    ("dense 4096x2048x4096 (k and v stacked)", "dense", 4096, 2048, 4096),
+    ("dense 512x4096x4096", "dense", 512, 4096, 4096),
+    ("dense 512x1024x4096", "dense", 512, 1024, 4096),
+    ("dense 4096x12288x4096 (gate/up)", "dense", 4096, 12288, 4096),
+    ("grouped MoE fc1 (128 experts, 32768 rows, 1536x2048)", "grouped", 32768, 1536, 2048),
+    ("grouped MoE fc2 (128 experts, 32768 rows, 2048x768)", "grouped", 32768, 2048, 768),
+]
+_MOE_EXPERTS = 128
+
+
+def _gemm_work(kind, m, n, k):
+    """FLOPs and algorithmic bytes (operands, bf16 output, scales) of one workload."""
+    g = _MOE_EXPERTS if kind == "grouped" else 1
+    flops = 2 * m * n * k
+    by = m * k + g * n * k + 2 * m * n + 4 * (k // 128) * m + 4 * g * (n // 128) * (k // 128)
+    return flops, by
+
+
+def profile_gemms():
+    """Launch each GEMM workload 8 times, eagerly (a target for counter passes)."""
+    import torch
+    import fp8_block_scaled_weight_amd as fq
+    from fp8_block_scaled_weight_amd import synth
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    _, off, _ = synth.moe_routing(0)
+    offs = torch.from_numpy(off).to(dev)
+    for label, kind, m, n, k in _GEMM_WORKLOADS:
+        e = _MOE_EXPERTS if kind == "grouped" else 1
+        a = torch.randint(0, 0x77, (m, k), dtype=torch.uint8, device=dev, generator=gen)
+        asc = torch.rand((k // 128, m), device=dev, generator=gen)
+        b = torch.randint(0, 0x77, (e * n, k), dtype=torch.uint8, device=dev, generator=gen)
+        bsc = torch.rand((e * n // 128, k // 128), device=dev, generator=gen)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        for _ in range(8):
+            if kind == "grouped":
+                fq.fp8q_grouped_gemm_w8a8(a, asc, b.view(e, n, k), bsc.view(e, n // 128, k // 128), offs, y)
+            else:
+                fq.fp8q_gemm_w8a8_blkscaled(a, asc, b, bsc, y)
+        torch.cuda.synchronize()
+        log(f"profiled: {label}")
+
+
+def summarize_gemm_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, mfma_dir):
+    """Per GEMM workload of --profile-gemms (matched by launch order, 8 dispatches each):
+    average duration, HBM bytes fetched and written (FETCH_SIZE / WRITE_SIZE scaled by the
+    1 GiB copy calibration) against the algorithmic bytes, and the matrix-core busy share.
+    Writes profiles/gemm_workloads_counters.md."""
+    import csv
+    import glob
+
+    def dispatches(d):
+        per = {}
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            for r in csv.DictReader(open(f)):
+                if "fp8q" not in r["Kernel_Name"] or "gemm" not in r["Kernel_Name"]:
+                    continue
+                e = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"].split("(")[0],
+                                                           "ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+                e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return [per[k] for k in sorted(per)]
+
+    cf, cw = _counter_rows(cal_fetch_dir), _counter_rows(cal_write_dir)
+    kib = (1 << 30) / 1024
+    fs = kib / max(x for _, c, x in cf if c.startswith("FETCH_SIZE"))
+    ws = kib / max(x for _, c, x in cw if c.startswith("WRITE_SIZE"))
+    fd, wd, md_ = dispatches(fetch_dir), dispatches(write_dir), dispatches(mfma_dir)
+    md = ["# HBM traffic and matrix-core use of the GEMM workloads", "",
+          "Counter passes over `python3 bench.py --profile-gemms` (each workload launched 8 times, eagerly),",
+          "one MI355X, repository root, TMPDIR=/tmp:", "",
+          "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/g_fetch -o g -- python3 bench.py --profile-gemms",
+          "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/g_write -o g -- python3 bench.py --profile-gemms",
+          "    rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d <out>/g_mfma -o g -- "
+          "python3 bench.py --profile-gemms",
+          "    python3 bench.py --summarize-gemm-counters <out>/g_fetch <out>/g_write <out>/cal_FETCH_SIZE "
+          "<out>/cal_WRITE_SIZE <out>/g_mfma", "",
+          f"FETCH_SIZE x{fs:.4f} and WRITE_SIZE x{ws:.4f} (the 1 GiB copy calibration of "
+          "`gemm_w8a8_4096_traffic.txt`).  Averages over dispatches 3-8 of each workload.  Matrix core busy:",
+          "SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x the kernel duration x 2.4 GHz (the clock of the 5.0 PF peak).", "",
+          "| workload | kernel | us | TFLOP/s | fetched MB | written MB | algorithmic MB | HBM / algorithmic | "
+          "matrix core busy |",
+          "|---|---|---|---|---|---|---|---|---|"]
+    for i, (label, kind, m, n, k) in enumerate(_GEMM_WORKLOADS):
+        flops, alg = _gemm_work(kind, m, n, k)
+        sl = lambda lst: lst[8 * i + 2: 8 * i + 8]
+        f_, w_, m_ = sl(fd), sl(wd), sl(md_)
+        if not f_ or not w_ or not m_:
+            continue
+        avg = lambda lst, c: sum(x.get(c, 0.0) for x in lst) / len(lst)
+        ns = avg(m_, "ns")
+        fb = avg(f_, "FETCH_SIZE") * 1024 * fs
+        wb = avg(w_, "WRITE_SIZE") * 1024 * ws
+        busy = avg(m_, "SQ_VALU_MFMA_BUSY_CYCLES") / (1024 * ns * 2.4)
+        md.append(f"| {label} | `{m_[0]['name'].replace('void fp8q::', '')}` | {ns / 1e3:.1f} | "
+                  f"{flops / ns / 1e3:.0f} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {alg / 1e6:.1f} | "
+                  f"{(fb + wb) / alg:.2f} | {busy:.3f} |")
+    md += ["", f"gemm.hip source_digest: {source_digest('gemm.hip')}"]
+    with open(os.path.join(ROOT, "profiles", "gemm_workloads_counters.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
 
 
 def summarize_mfma(d):
@@ -333,7 +445,7 @@ def _dominant_loop_from_trace(d):
         return None
     rows = list(csv.DictReader(open(files[0])))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    tag = "GemmCfg<256, 256, 2, 4, 2>, false>"
+    tag = "GemmCfg<256, 256, 2, 4, 2, 1>, false>"
     is_dom = [tag in r["Kernel_Name"] for r in rows]
     dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
     groups = {"step": [], "burst": [], "sustained": [], "other": [], "all": []}
@@ -436,6 +548,12 @@ def main():
         return
     if args.vendor_reference:
         vendor_reference()
+        return
+    if args.summarize_gemm_counters:
+        summarize_gemm_counters(*args.summarize_gemm_counters)
+        return
+    if args.profile_gemms:
+        profile_gemms()
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
@@ -592,29 +710,31 @@ def main():
     del fns, d, xc, qc, sc, ykv, kc_, vc_, ks_, vs_
     torch.cuda.empty_cache()
 
-    # The dominant kernel (the q and o GEMMs) inside steps: DOM_STEPS eager steps, each GEMM
-    # launch between two HIP events on its launch stream.  Its average duration there is
-    # `roofline.avg_us`.  For context, the same kernel in a short burst (20 launches back to
-    # back) and sustained (100 back to back), where the chip lowers its clock under the
-    # continuous matrix-core load.  Each group is a distinct launch pattern in a kernel
-    # trace of the same command (single launches between other kernels, and runs of 23 and
-    # 103 consecutive launches of which the last 20 / 100 are timed).
+    # The dominant kernel (the q and o GEMMs) inside steps: the step graph against the same
+    # step captured without those two GEMMs, replayed alternately (medians of DOM_ROUNDS
+    # rounds of `steps` replays each); half the difference per step is the average duration
+    # of one in-step launch, with no event between kernels.  For context, the same kernel in
+    # a short burst (20 launches back to back) and sustained (100 back to back).  Each group
+    # is a distinct launch pattern in a kernel trace of the same command (single launches
+    # between other kernels, and runs of 23 and 103 consecutive launches of which the last
+    # 20 / 100 are timed).
     dom_names = ("a3_gemm_q", "a3_gemm_o")
-    pairs = []
+    graph_wo = torch.cuda.CUDAGraph()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph_wo, stream=side):
+            for name, fn in calls:
+                if name not in dom_names:
+                    fn()
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    for _ in range(DOM_STEPS):
-        for name, fn in calls:
-            if name in dom_names:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                fn()
-                e1.record()
-                pairs.append((e0, e1))
-            else:
-                fn()
-    torch.cuda.synchronize()
-    dom_avg_ms = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
-    n_dom = len(pairs)
+    full, wo = [], []
+    for _ in range(DOM_ROUNDS):
+        full.append(_time_graph(torch, graph, args.steps))
+        wo.append(_time_graph(torch, graph_wo, args.steps))
+    med = lambda v: sorted(v)[len(v) // 2]
+    dom_avg_ms = (med(full) - med(wo)) / 2
+    n_dom = 2 * args.steps * DOM_ROUNDS
     dom_fn = calls[2][1]
 
     def back_to_back(n):
@@ -668,7 +788,9 @@ def main():
                 "traffic": traffic_from_profile("gemm_w8a8_4096", source_digest("gemm.hip")),
                 "kernel": "gemm_w8a8_kernel<GemmCfg<256,256,2,4,2>> M=N=K=4096 (q/o projection)",
                 "avg_us": round(dom_avg_ms * 1e3, 2), "launches_timed": n_dom,
-                "timed_as": f"q and o GEMM launches inside {DOM_STEPS} steps, each between two HIP events",
+                "timed_as": f"inside the step: (step graph - step graph without the q and o GEMMs) / 2, "
+                            f"medians of {DOM_ROUNDS} alternating rounds of {args.steps} replays",
+                "step_ms_with": round(med(full), 4), "step_ms_without": round(med(wo), 4),
                 "burst_avg_us": round(burst_ms * 1e3, 2), "burst_launches": DOM_BURST,
                 "sustained_avg_us": round(sustained_ms * 1e3, 2), "sustained_launches": DOM_SUSTAINED}
 
