@@ -859,10 +859,17 @@ static hipError_t launch_tiles(const void* a, int64_t ld_a, const float* a_s, in
 hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                        int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                        int64_t k, bool pow2, hipStream_t stream) {
-  if (pow2 && m > 64) return launch_tiles<true>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-  // (up to 64 tokens, power-of-two scales take the promotion path below: same result)
-  // few tokens: stream the weights over all CUs
-  if (m <= 64) return launch_few_tokens<false>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  // Few tokens, or few tiles: at most 64 tiles of 128x64 leave most CUs idle while each
+  // tile walks all of K (a 128x64 tile takes about 14 us at K = 4096 however many run
+  // beside it); the few-token kernel splits K over the 8 waves of every workgroup instead.
+  // Measured on 56 shapes (80 <= m <= 700, n = 512 .. 4096, k = 1024 and 4096): with 64
+  // tiles or fewer it was as fast or faster (130x1024x4096 13.9 -> 6.8 us, 256x512x4096
+  // 14.0 -> 5.9 us), from 96 tiles slower.  Power-of-two scales take its promotion path too
+  // (same result).
+  const int64_t few_tiles = ((m + 127) / 128) * (n / 64);
+  if (m <= 64 || (m < 1024 && k >= 1024 && few_tiles <= 64))
+    return launch_few_tokens<false>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  if (pow2) return launch_tiles<true>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   return launch_tiles<false>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
 }
 

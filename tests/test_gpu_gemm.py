@@ -103,7 +103,9 @@ def test_mlp_shapes_sampled():
     (1000, 1024, 512),    # 128x64 tiles (m < 1024), ragged
     (700, 1024, 640),     # 128x64 tiles, ragged
     (900, 1024, 1152),    # 128x64 tiles in two K groups, odd K-block count: one group's last step is empty
-    (200, 512, 1024),     # two K groups, four steps each
+    (200, 4096, 1024),    # two K groups, four steps each
+    (700, 512, 1024),     # few tiles (48 of 128x64): the few-token kernel, 22 tiles of 32 tokens, ragged
+    (1000, 512, 4096),    # 64 tiles: the few-token kernel at its largest tile count
     (65536, 384, 256),    # n not a multiple of 256 with enough rows for 256x256 tiles
     (4000, 4096, 128),    # 256x256 tiles, one K step: the only step is also the last
     (4000, 4096, 256),    # 256x256 tiles, two K steps

@@ -68,8 +68,9 @@ def test_quantizer_guards():
 
 @pytest.mark.parametrize("m,n,k", [
     (37, 256, 384),      # few tokens
-    (300, 512, 1152),    # 128x64 tiles in two K groups
-    (700, 256, 640),     # 128x64 tiles, one K group
+    (300, 512, 1152),    # few tiles (24 of 128x64): the few-token kernel
+    (300, 4096, 1152),   # 128x64 tiles in two K groups
+    (700, 1024, 640),    # 128x64 tiles, one K group
     (1100, 256, 384),    # 128x128 tiles
     (4000, 4096, 256),   # 256x256 tiles, ragged
 ])
