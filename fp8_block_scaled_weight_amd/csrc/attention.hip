@@ -30,8 +30,9 @@
 // combined through LDS in a fixed order, so the result does not depend on timing.
 // A chunk's key rows are loaded with 8 lanes per 128-byte row (a quarter-wave of MFMA
 // fragment loads would touch 16 rows, which measured slower) and pass through a per-wave
-// LDS stage (16-byte chunk c of row r at c ^ (r & 7), conflict-free both ways); value
-// rows already arrive as whole 128-byte lines per quarter-wave.
+// LDS stage laid out so that the 16 lanes served together by a 16-byte LDS access cover all
+// 64 banks, both in the row-wise writes and in the fragment reads (key_slot); value rows
+// already arrive as whole 128-byte lines per quarter-wave.
 #include "e4m3.hpp"
 #include "launch.hpp"
 
@@ -53,6 +54,20 @@ __device__ __forceinline__ att_v8bf fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
     o[2 * h + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
   }
   return __builtin_bit_cast(att_v8bf, o);
+}
+
+// LDS offset of 16-byte chunk c of key-stage row r (row = token * HG + head).  A fragment
+// read takes one chunk of 16 rows of one head; the bank group of a 16-byte slot is the
+// row's half of the 256-byte bank window and the chunk position.  HG = 1: rows 2i and 2i+1
+// share the position c ^ ((r >> 1) & 7) and fill the two halves.  HG = 2: the rows read
+// together have one parity, so rows are swapped in pairs (r ^ ((r >> 1) & 1)) to alternate
+// the halves, with the position c ^ ((r >> 2) & 7).  A row-wise write (one or two tokens,
+// whole rows) also covers every bank.
+template <int HG>
+__device__ __forceinline__ int key_slot(int r, int c) {
+  static_assert(HG == 1 || HG == 2, "one or two KV heads per workgroup");
+  if constexpr (HG == 1) return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+  return (r ^ ((r >> 1) & 1)) * 128 + ((c ^ ((r >> 2) & 7)) << 4);
 }
 
 constexpr int kAttnWaves = 8;
@@ -241,7 +256,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void paged_decode_attn_kernel(
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int row = (TPI * u + kt) * HG + (kcol >> 3);
-      *reinterpret_cast<uint4*>(kst + row * 128 + (((kcol & 7) ^ (row & 7)) << 4)) = R.kr[u];
+      *reinterpret_cast<uint4*>(kst + key_slot<HG>(row, kcol & 7)) = R.kr[u];
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -252,9 +267,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void paged_decode_attn_kernel(
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         const int row = (16 * i + hcol) * HG + hh;
-        const uint8_t* kb = kst + row * 128;
-        const uint4 k0 = *reinterpret_cast<const uint4*>(kb + (((2 * quad) ^ (row & 7)) << 4));
-        const uint4 k1 = *reinterpret_cast<const uint4*>(kb + (((2 * quad + 1) ^ (row & 7)) << 4));
+        const uint4 k0 = *reinterpret_cast<const uint4*>(kst + key_slot<HG>(row, 2 * quad));
+        const uint4 k1 = *reinterpret_cast<const uint4*>(kst + key_slot<HG>(row, 2 * quad + 1));
         att_v4f r = {0.f, 0.f, 0.f, 0.f};
         r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k0.x, k0.y), fq[hh][0], r, 0, 0, 0);
         r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(k0.z, k0.w), fq[hh][1], r, 0, 0, 0);

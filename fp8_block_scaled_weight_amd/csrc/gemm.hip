@@ -620,9 +620,12 @@ static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, in
 // back in the MFMA operand layout, while the loads of its next K block are in flight.
 // (Fragment loads straight from memory make every 16-lane quarter-wave touch 16 lines;
 // measured on these shapes they move the same bytes about 1.6x slower.)  A stage row is
-// 128 bytes with 16-byte chunk c of row r at c ^ (r & 7), so the row-wise writes and the
-// fragment reads are both free of bank conflicts.  The 8 partial sums are added through
-// LDS in a fixed order, so the result does not depend on timing.
+// 128 bytes with 16-byte chunk c of row r at c ^ ((r >> 1) & 7): the 16 lanes served
+// together by a 16-byte LDS access then cover all 64 banks, both in a row-wise write (two
+// whole rows) and in a fragment read (one chunk of each of 16 rows: rows 2i and 2i+1 share
+// the chunk position and lie in the two halves of the 256-byte bank window).  The 8
+// partial sums are added through LDS in a fixed order, so the result does not depend on
+// timing.
 //
 // FUSED: the token rows arrive as bf16 and are quantized where they are loaded (FP8-RL
 // summary page, "Method step details" step 1: activations are quantized dynamically on
@@ -635,7 +638,7 @@ static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, in
 constexpr int kSmallWaves = 8;
 
 // byte offset of 16-byte chunk c of row r in a stage
-__device__ __forceinline__ int stage_at(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+__device__ __forceinline__ int stage_at(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 template <int WM, bool FUSED, int D>
 __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
