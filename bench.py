@@ -9,10 +9,6 @@ call, inputs resident in HBM:
   -> FP8 KV-cache write of the k/v outputs (8 heads x 128) with scale recalibration
   -> 1x128 quantization of the attention output stand-in [4096, 4096]
   -> o GEMM (4096x4096).
-The kv GEMM and the KV write depend only on X's quantization, so the step runs them on a
-second stream beside the q GEMM and the second quantization, joined before the o GEMM (the
-q GEMM's last tiles and the kv GEMM's first ones then share the CUs); `ms_per_step_serial`
-times the same calls in order on one stream.
 `value` is the step's GEMM FLOPs divided by the measured step time (TFLOP/s).
 Side legs (not in `value`) time the full 36-layer weight sync, one MoE layer's
 grouped GEMMs (128 experts, Zipf top-8 routing of 4096 tokens) and one layer of the
@@ -666,47 +662,9 @@ def main():
             if not torch.equal(a.view(torch.uint8), b.view(torch.uint8)):
                 raise SystemExit("graph replay differs from the eager step")
 
-    # The step as an engine schedules it: the kv GEMM and the KV write (which need only X's
-    # codes) on a second stream beside the q GEMM and the attention output's quantization,
-    # joined before the o GEMM.  Its replays must reproduce the eager step byte for byte too.
-    call = dict(calls)
-    aux = torch.cuda.Stream()
-
-    def step_two_streams():
-        main = torch.cuda.current_stream()
-        call["a1_weight_sync_qkvo"]()
-        call["a2_act_quant_x"]()
-        aux.wait_stream(main)
-        with torch.cuda.stream(aux):
-            call["a3_gemm_kv"]()
-            call["a5a6_kv_recal_write"]()
-        call["a3_gemm_q"]()
-        call["a2_act_quant_o"]()
-        main.wait_stream(aux)
-        call["a3_gemm_o"]()
-
-    graph2 = torch.cuda.CUDAGraph()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step_two_streams()
-        torch.cuda.synchronize()
-        with torch.cuda.graph(graph2, stream=side):
-            step_two_streams()
-    torch.cuda.current_stream().wait_stream(side)
-    for t in outputs:
-        t.zero_()
-    for _ in range(3):
-        graph2.replay()
-        torch.cuda.synchronize()
-        for a, b in zip(outputs, eager):
-            if not torch.equal(a.view(torch.uint8), b.view(torch.uint8)):
-                raise SystemExit("graph replay of the two-stream step differs from the eager step")
-
-    # untimed replays of both graphs first: the shader clock settles over the first few
-    # tens of steps, and whichever graph ran first would otherwise carry that
+    # untimed replays first: the shader clock settles over the first few tens of steps
     for _ in range(max(args.steps, 20)):
         graph.replay()
-        graph2.replay()
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
@@ -715,17 +673,10 @@ def main():
     torch.cuda.synchronize()
     t0.record()
     for _ in range(args.steps):
-        graph2.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
         graph.replay()
     t1.record()
     torch.cuda.synchronize()
-    ms_step_serial = t0.elapsed_time(t1) / args.steps
+    ms_step = t0.elapsed_time(t1) / args.steps
 
     gemm_flops = 2 * TOKENS * HIDDEN * (HIDDEN + 2 * KV_DIM + HIDDEN)
     value = gemm_flops / (ms_step * 1e-3) / 1e12
@@ -856,7 +807,6 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "ms_per_step_serial": round(ms_step_serial, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
