@@ -249,16 +249,18 @@ static fp8q_status quant_weight(const fp8q_weight_desc* descs, int32_t count, vo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   fp8q::WeightChunk chunk;
   chunk.count = 0;
-  int64_t blocks = 0;
+  int64_t blocks = 0, quads = 0;
   for (int32_t i = 0; i < count; ++i) {
     const fp8q_weight_desc& d = descs[i];
     if (d.n == 0 || d.k == 0) continue;
     const int64_t nblk = (d.n / 128) * (d.k / 128);
+    const int64_t nquad = (d.n / 128) * ((d.k / 128 + 3) / 4);
     if (chunk.count == fp8q::kWeightChunk || blocks + nblk > (int64_t)0x7fffffff) {
-      st = launched(fp8q::launch_quant_weight_chunk(chunk, blocks, pow2, s), "quant_weight_blk128");
+      st = launched(fp8q::launch_quant_weight_chunk(chunk, blocks, quads, pow2, s), "quant_weight_blk128");
       if (st != FP8Q_OK) return st;
       chunk.count = 0;
       blocks = 0;
+      quads = 0;
     }
     fp8q::WeightDescDev& e = chunk.d[chunk.count++];
     e.w = d.w;
@@ -268,10 +270,13 @@ static fp8q_status quant_weight(const fp8q_weight_desc* descs, int32_t count, vo
     e.ld_q = d.ld_q;
     e.first_block = (int32_t)blocks;
     e.kblocks = (int32_t)(d.k / 128);
+    e.first_quad = (int32_t)quads;
+    e.kquads = (int32_t)((d.k / 128 + 3) / 4);
     blocks += nblk;
+    quads += nquad;
   }
-  return finish(launched(fp8q::launch_quant_weight_chunk(chunk, blocks, pow2, s), "quant_weight_blk128"), stream,
-                "quant_weight_blk128");
+  return finish(launched(fp8q::launch_quant_weight_chunk(chunk, blocks, quads, pow2, s), "quant_weight_blk128"),
+                stream, "quant_weight_blk128");
 }
 
 fp8q_status fp8q_quant_weight_blk128(const fp8q_weight_desc* descs, int32_t count, void* stream) {

@@ -15,16 +15,22 @@ struct WeightDescDev {
   int64_t ld_q;
   int32_t first_block;  // first block id of this tensor within the launch
   int32_t kblocks;      // k / 128
+  int32_t first_quad;   // first workgroup id of this tensor in a launch of 4-block workgroups
+  int32_t kquads;       // ceil(kblocks / 4)
 };
 
-constexpr int kWeightChunk = 64;  // descriptors per launch (3 KB of kernel arguments)
+constexpr int kWeightChunk = 64;  // descriptors per launch (3.5 KB of kernel arguments)
 
 struct WeightChunk {
   int32_t count;
   WeightDescDev d[kWeightChunk];
 };
+static_assert(sizeof(WeightChunk) <= 4096, "kernel arguments are limited to 4 KB");
 
-hipError_t launch_quant_weight_chunk(const WeightChunk& chunk, int64_t blocks, bool pow2, hipStream_t stream);
+// blocks: 128x128 blocks of the chunk; quads: workgroups of the chunk when each takes four
+// blocks of a block row (the sum of n/128 * kquads)
+hipError_t launch_quant_weight_chunk(const WeightChunk& chunk, int64_t blocks, int64_t quads, bool pow2,
+                                     hipStream_t stream);
 
 hipError_t launch_quant_act(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q, int64_t ld_q,
                             float* s, int64_t ld_s, bool pow2, hipStream_t stream);

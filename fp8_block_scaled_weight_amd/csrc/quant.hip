@@ -71,7 +71,77 @@ __global__ __launch_bounds__(256) void quant_weight_blk128_kernel(WeightChunk ch
   }
 }
 
-hipError_t launch_quant_weight_chunk(const WeightChunk& chunk, int64_t blocks, bool pow2, hipStream_t stream) {
+// Large launches: one 512-thread workgroup per four blocks side by side in a block row,
+// so every row is read and written in 1 KB runs instead of 256-byte ones.  Thread t covers
+// columns 16*(t%32) .. +15 of the four blocks' 512 (block (t%32)/8) in rows t/32 + 16*i
+// (i < 8).  A block's amax: 8 lanes of a row, the two rows of a wave, then the 8 waves
+// through LDS.  A block row's last workgroup may hold fewer than four blocks; its other
+// lanes load and store nothing.
+template <bool POW2>
+__global__ __launch_bounds__(512) void quant_weight_blk128x4_kernel(WeightChunk chunk) {
+  __shared__ uint32_t wave_max[8][4];
+  const int64_t wg = blockIdx.x;
+  int lo = 0, hi = chunk.count - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (chunk.d[mid].first_quad <= wg) lo = mid; else hi = mid - 1;
+  }
+  const WeightDescDev& d = chunk.d[lo];
+  const int64_t local = wg - d.first_quad;
+  const int64_t bi = local / d.kquads;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int c = t & 31, b = c >> 3;
+  const int64_t bj = (local - bi * d.kquads) * 4 + b;
+  const bool live = bj < d.kblocks;  // uniform over 8 lanes of a row
+  const int col = (c & 7) * 16;
+  const int row0 = t >> 5;
+  const uint16_t* w = reinterpret_cast<const uint16_t*>(d.w) + (bi * 128) * d.ld_w + bj * 128 + col;
+  uint8_t* q = reinterpret_cast<uint8_t*>(d.q) + (bi * 128) * d.ld_q + bj * 128 + col;
+
+  uint4 v[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (live) {
+      const uint4* p = reinterpret_cast<const uint4*>(w + (int64_t)(row0 + 16 * i) * d.ld_w);
+      v[2 * i] = load_plain(p);
+      v[2 * i + 1] = load_plain(p + 1);
+    } else {
+      v[2 * i] = v[2 * i + 1] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, absmax16(v[2 * i], v[2 * i + 1]));
+  m = max_over_8_lanes(m);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+  if ((lane & 39) == 0) wave_max[wave][b] = m;  // lanes 0, 8, 16, 24: blocks 0..3
+  __syncthreads();
+  m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, wave_max[i][b]);
+  const float scale = block_scale<POW2>(bf16_bits_to_float(m), kE4M3Max);
+  if (!live) return;
+  if (t < 32 && (t & 7) == 0) d.s[bi * d.kblocks + bj] = scale;
+  const Quantizer qz = make_quantizer(scale);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    store_stream(q + (int64_t)(row0 + 16 * i) * d.ld_q, quant16<false>(v[2 * i], v[2 * i + 1], qz));
+}
+
+hipError_t launch_quant_weight_chunk(const WeightChunk& chunk, int64_t blocks, int64_t quads, bool pow2,
+                                     hipStream_t stream) {
+  // four blocks per workgroup once a launch moves 1 GB or more (48 KB of traffic per block)
+#ifndef WIDE_MIN_BLOCKS
+#define WIDE_MIN_BLOCKS 21846
+#endif
+  if (blocks >= WIDE_MIN_BLOCKS) {
+    if (pow2)
+      hipLaunchKernelGGL(quant_weight_blk128x4_kernel<true>, dim3((unsigned)quads), dim3(512), 0, stream, chunk);
+    else
+      hipLaunchKernelGGL(quant_weight_blk128x4_kernel<false>, dim3((unsigned)quads), dim3(512), 0, stream, chunk);
+    return hipGetLastError();
+  }
   if (pow2)
     hipLaunchKernelGGL(quant_weight_blk128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, chunk);
   else

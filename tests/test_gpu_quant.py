@@ -159,6 +159,45 @@ def test_weight_tiny_scale_block():
     assert np.all(q[128:, 128:] == 0x80)
 
 
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_weight_wide_launch_equals_per_tensor_calls(ue8m0):
+    """A launch of 21846 blocks or more (1 GB of traffic) takes four blocks of a block row per
+    workgroup.  Its codes and scales equal per-tensor calls (each below that size: one block per
+    workgroup) byte for byte.  K of 1, 2, 3, 5, 6, 7, 24, 32 and 16 blocks covers every count of
+    live blocks in a row's last workgroup; pitches are padded and the bytes beyond k must stay
+    untouched.  Two blocks of each tensor are also checked against the oracle.  Both the fp32
+    and the power-of-two (UE8M0) scale variants."""
+    quant = fq.fp8q_quant_weight_blk128_ue8m0 if ue8m0 else fq.fp8q_quant_weight_blk128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    shapes = [(12800, 128, 192, 144), (12800, 256, 264, 272), (12800, 384, 384, 400), (12800, 640, 648, 656),
+              (8192, 768, 768, 768), (25600, 896, 904, 912), (25600, 3072, 3072, 3072),
+              (25600, 4096, 4104, 4112), (51200, 2048, 2048, 2048), (12800, 4096, 4096, 4096)]
+    assert sum((n // 128) * (k // 128) for n, k, _, _ in shapes) >= 21846
+    ws, wide, single = [], [], []
+    for n, k, ldw, ldq in shapes:
+        x = torch.randn((n, ldw), generator=g, device=DEV) * 0.02
+        x[torch.rand((n, ldw), generator=g, device=DEV) < 1e-3] *= 20.0
+        ws.append(x.to(torch.bfloat16)[:, :k])
+        for outs in (wide, single):
+            qfull = torch.full((n, ldq), 0xA5, dtype=torch.uint8, device=DEV)
+            outs.append((qfull, torch.empty((n // 128, k // 128), dtype=torch.float32, device=DEV)))
+    quant([(w, q[:, :w.shape[1]], s) for w, (q, s) in zip(ws, wide)])
+    for w, (q, s) in zip(ws, single):
+        quant([(w, q[:, :w.shape[1]], s)])
+    torch.cuda.synchronize()
+    for (n, k, _, ldq), w, (qw, sw), (q1, s1) in zip(shapes, ws, wide, single):
+        assert torch.equal(sw.view(torch.int32), s1.view(torch.int32)), f"{n}x{k}: scales differ"
+        assert torch.equal(qw, q1), f"{n}x{k}: codes differ"
+        if ldq > k:
+            assert bool(torch.all(qw[:, k:] == 0xA5)), f"{n}x{k}: bytes beyond k were written"
+        for bi, bj in ((0, k // 128 - 1), (n // 256, (k // 128) // 2)):
+            wb = w[128 * bi:128 * bi + 128, 128 * bj:128 * bj + 128].contiguous().view(torch.int16)
+            qr, sr = oracle.quant_weight_blk128(wb.cpu().numpy().view(np.uint16), ue8m0=ue8m0)
+            assert np.float32(sw[bi, bj].item()).view(np.uint32) == sr.reshape(-1)[0].view(np.uint32)
+            assert np.array_equal(u8(qw[128 * bi:128 * bi + 128, 128 * bj:128 * bj + 128]), qr)
+
+
 # ----------------------------------------------------------------------------- KV
 def gpu_kv(k_bits, v_bits, slots, pages, page_size, k_scale=1.0, v_scale=1.0, recal=True, rng=448.0):
     t, h, d = k_bits.shape
