@@ -66,6 +66,12 @@ def parse():
                         "the bf16 matmul at the dense GEMM shapes, as context for the block-scaled GEMM's rate")
     p.add_argument("--profile-gemms", action="store_true",
                    help="only launch each GEMM workload of the side legs 8 times (a target for counter passes)")
+    p.add_argument("--profile-quantizers", action="store_true",
+                   help="only run the large quantizer workloads 3 times each: the 36-layer weight sync, one MoE "
+                        "layer's expert weights, one 64 x 20,000-token KV layer (a target for counter passes)")
+    p.add_argument("--summarize-quantizer-counters", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                   help="write profiles/quantizers_large_traffic.md from FETCH_SIZE / WRITE_SIZE passes over "
+                        "--profile-quantizers and the 1 GiB copy calibration")
     p.add_argument("--summarize-gemm-counters", nargs=5,
                    metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE", "MFMA"),
                    help="write profiles/gemm_workloads_counters.md from counter passes over --profile-gemms")
@@ -239,6 +245,105 @@ def profile_gemms():
                 fq.fp8q_gemm_w8a8_blkscaled(a, asc, b, bsc, y)
         torch.cuda.synchronize()
         log(f"profiled: {label}")
+
+
+_SYNC_SHAPES = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (12288, 4096), (12288, 4096), (4096, 12288)]
+_MOE_WEIGHT_SHAPES = [(128 * 2 * 768, 2048), (128 * 2048, 768)]
+_QUANT_CALLS = 3
+
+
+def profile_quantizers():
+    """The large quantizer workloads, _QUANT_CALLS calls each, eagerly: the 36-layer weight sync
+    (one batched call), one MoE layer's expert weights, one 64 x 20,000-token KV layer with
+    recalibration (a target for counter passes)."""
+    import torch
+    import fp8_block_scaled_weight_amd as fq
+    from fp8_block_scaled_weight_amd import synth
+    dev = torch.device("cuda:0")
+    for label, shapes in (("36-layer sync", _SYNC_SHAPES * 36), ("MoE expert weights", _MOE_WEIGHT_SHAPES)):
+        descs = [(synth.device_normal_bf16((n, k), 0.02, dev, 3, i, 0, outlier_p=1e-3, outlier_mult=20.0),
+                  torch.empty((n, k), dtype=torch.uint8, device=dev),
+                  torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev)) for i, (n, k) in enumerate(shapes)]
+        for _ in range(_QUANT_CALLS):
+            fq.fp8q_quant_weight_blk128(descs)
+        torch.cuda.synchronize()
+        log(f"profiled: {label}")
+        del descs
+        torch.cuda.empty_cache()
+    slots_np, pages = synth.kv_slot_mapping()
+    t = len(slots_np)
+    k = synth.device_kv(t, dev, 5, 0, 0)
+    v = synth.device_kv(t, dev, 5, 0, 1)
+    sl = torch.from_numpy(slots_np).to(dev)
+    kc = torch.empty((pages, 16, 8, 128), dtype=torch.uint8, device=dev)
+    vc = torch.empty_like(kc)
+    ks, vs = torch.ones(1, device=dev), torch.ones(1, device=dev)
+    for _ in range(_QUANT_CALLS):
+        fq.fp8q_kv_quant(k, v, sl, kc, vc, ks, vs, 448.0, recalibrate=True)
+    torch.cuda.synchronize()
+    log("profiled: KV layer")
+
+
+def summarize_quantizer_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
+    """HBM bytes per call of the --profile-quantizers workloads (FETCH_SIZE / WRITE_SIZE scaled by
+    the 1 GiB copy calibration) against their algorithmic bytes.  Writes
+    profiles/quantizers_large_traffic.md."""
+    import csv
+    import glob
+
+    def dispatches(d):
+        per = {}
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            for r in csv.DictReader(open(f)):
+                if "fp8q" not in r["Kernel_Name"]:
+                    continue
+                e = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"].split("(")[0]})
+                e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return [per[k] for k in sorted(per)]
+
+    cf, cw = _counter_rows(cal_fetch_dir), _counter_rows(cal_write_dir)
+    kib = (1 << 30) / 1024
+    fs = kib / max(x for _, c, x in cf if c.startswith("FETCH_SIZE"))
+    ws = kib / max(x for _, c, x in cw if c.startswith("WRITE_SIZE"))
+    fd, wd = dispatches(fetch_dir), dispatches(write_dir)
+    from fp8_block_scaled_weight_amd import synth
+    t = len(synth.kv_slot_mapping()[0])
+    row = 8 * 128
+    sync_el = sum(n * k for n, k in _SYNC_SHAPES) * 36
+    moe_el = sum(n * k for n, k in _MOE_WEIGHT_SHAPES)
+    # (label, launches per call, algorithmic read and write bytes per call)
+    work = [("36-layer weight sync (252 tensors, one call)", -(-252 // 64), 2 * sync_el, sync_el + 4 * sync_el / 16384),
+            ("MoE expert weights of one layer (2 tensors)", 1, 2 * moe_el, moe_el + 4 * moe_el / 16384),
+            ("KV layer, 64 x 20,000 tokens, recalibrate + write", 3, 2 * (2 * 2 * t * row) + 2 * 8 * t,
+             2 * t * row)]
+    md = ["# HBM traffic of the large quantizer workloads", "",
+          "Counter passes over `python3 bench.py --profile-quantizers` (each workload called "
+          f"{_QUANT_CALLS} times, eagerly), one MI355X, repository root, TMPDIR=/tmp:", "",
+          "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/q_fetch -o q -- python3 bench.py --profile-quantizers",
+          "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/q_write -o q -- python3 bench.py --profile-quantizers",
+          "    python3 bench.py --summarize-quantizer-counters <out>/q_fetch <out>/q_write <out>/cal_FETCH_SIZE "
+          "<out>/cal_WRITE_SIZE", "",
+          f"FETCH_SIZE x{fs:.4f} and WRITE_SIZE x{ws:.4f} (the 1 GiB copy calibration of "
+          "`gemm_w8a8_4096_traffic.txt`).  Bytes per call, averaged over the calls after the first.", "",
+          "| workload | kernels | fetched GB | algorithmic read GB | written GB | algorithmic write GB |",
+          "|---|---|---|---|---|---|"]
+    pos = 0
+    for label, launches, alg_r, alg_w in work:
+        n = launches * _QUANT_CALLS
+        f_, w_ = fd[pos:pos + n], wd[pos:pos + n]
+        pos += n
+        if len(f_) < n or len(w_) < n:
+            continue
+        per_call = lambda lst, c: sum(x.get(c, 0.0) for x in lst[launches:]) / (_QUANT_CALLS - 1)
+        fb = per_call(f_, "FETCH_SIZE") * 1024 * fs
+        wb = per_call(w_, "WRITE_SIZE") * 1024 * ws
+        names = sorted({x["name"].replace("void fp8q::", "").replace("fp8q::", "") for x in f_})
+        md.append(f"| {label} | {', '.join('`' + x + '`' for x in names)} | {fb / 1e9:.3f} | {alg_r / 1e9:.3f} | "
+                  f"{wb / 1e9:.3f} | {alg_w / 1e9:.3f} |")
+    md += ["", "Source digests: " + ", ".join(f"{n} {source_digest(n)}" for n in ("quant.hip", "kv_quant.hip"))]
+    with open(os.path.join(ROOT, "profiles", "quantizers_large_traffic.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
 
 
 def summarize_gemm_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, mfma_dir):
@@ -554,6 +659,12 @@ def main():
         return
     if args.profile_gemms:
         profile_gemms()
+        return
+    if args.profile_quantizers:
+        profile_quantizers()
+        return
+    if args.summarize_quantizer_counters:
+        summarize_quantizer_counters(*args.summarize_quantizer_counters)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
