@@ -225,6 +225,14 @@ def test_grouped_many_groups():
     check_grouped(grouped_case(list(sizes), 256, 256, 7))
 
 
+def test_grouped_many_groups_large_tiles():
+    """300 experts (five 64-group passes of the tile search), about a third of them empty,
+    on the K >= 2048 path of 256- and 128-row tiles."""
+    g = np.random.Generator(np.random.PCG64(12))
+    sizes = g.integers(0, 30, size=300) * (g.random(300) > 0.33)
+    check_grouped(grouped_case(list(sizes), 256, 2048, 12))
+
+
 def test_grouped_moe_routing_fc2_subset():
     """Zipf-skewed top-8 routing over 128 experts (4096 tokens); fc2 shape n=2048, k=768.
     Checks a subset of groups (smallest, largest, a few others) against the oracle."""
