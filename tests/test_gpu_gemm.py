@@ -118,6 +118,25 @@ def test_tile_configs_ragged(m, n, k):
     check(xq, xs, wq, ws, rows=rows)
 
 
+@pytest.mark.parametrize("m,n,k", [
+    (64, 512, 1024),      # the last few-token size
+    (65, 512, 1024),      # 8 tiles of 128x64: the few-token kernel past 64 tokens
+    (65, 8192, 1024),     # 128 tiles: 128x64 tiles in two K groups
+    (1023, 512, 1024),    # 64 tiles: still the few-token kernel
+    (1024, 512, 1024),    # 128x128 tiles from 1024 tokens
+    (300, 512, 896),      # 24 tiles but K < 1024: 128x64 tiles, one K group
+    (129, 1024, 1024),    # 32 tiles, a 1-token last tile of 32 tokens
+])
+def test_dispatch_boundaries(m, n, k):
+    """Each side of every size rule that picks a GEMM kernel, sampled rows against the oracle."""
+    g = np.random.Generator(np.random.PCG64(m * 7 + n + k))
+    xq, xs, wq, ws = quantized_operands(m, n, k, tensor=30 + m % 7)
+    edges = [0, 1, 31, 32, 63, 64, 127, 128, m - 2, m - 1]
+    rows = np.unique(np.concatenate([np.array([r for r in edges if 0 <= r < m]),
+                                     g.choice(m, min(m, 24), replace=False)]))
+    check(xq, xs, wq, ws, rows=rows)
+
+
 def test_padded_output_pitch_untouched():
     xq, xs, wq, ws = quantized_operands(40, 256, 384, tensor=9)
     yfull = check(xq, xs, wq, ws, ld_y=264)
