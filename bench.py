@@ -667,7 +667,7 @@ def main():
         summarize_quantizer_counters(*args.summarize_quantizer_counters)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         log("bench.py: only --gpus 1 is supported (single-GPU hot path; see the sharding notes)")
         sys.exit(2)
