@@ -825,6 +825,21 @@ def main():
     cold_ms["a5a6_kv_recal_write"] = _time_rotated(torch, fns)
     del fns, d, xc, qc, sc, ykv, kc_, vc_, ks_, vs_
     torch.cuda.empty_cache()
+    # The step's GEMMs the same way, for context: each call on its own operands and output,
+    # rotated over >= 1 GB (in the step their operands were just written by a quantizer and
+    # are read warm, which the per-call GEMM rates and `roofline` report)
+    log("cold GEMM timing (operands rotated over >= 1 GB)")
+    for name, (a_, as_, b_, bs_, y_) in (("a3_gemm_q", (Xq, Xs, WQ["q"], WS["q"], Y["q"])),
+                                         ("a3_gemm_kv", (Xq, Xs, WQ["kv"], WS["kv"], Y["kv"])),
+                                         ("a3_gemm_o", (Oq, Os, WQ["o"], WS["o"], Y["o"]))):
+        per = a_.numel() + 4 * as_.numel() + b_.numel() + 4 * bs_.numel() + 2 * y_.numel()
+        fns = []
+        for _ in range(_rotation_sets(per)):
+            t = (a_.clone(), as_.clone(), b_.clone(), bs_.clone(), torch.empty_like(y_))
+            fns.append(lambda t=t: fq.fp8q_gemm_w8a8_blkscaled(*t))
+        cold_ms[name] = _time_rotated(torch, fns)
+        del fns, t
+        torch.cuda.empty_cache()
 
     # The dominant kernel (the q and o GEMMs) inside steps: the step graph against the same
     # step captured without those two GEMMs, replayed alternately (medians of DOM_ROUNDS
@@ -891,7 +906,8 @@ def main():
             d.update(GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBPS, 4))
         if name in flops_of:
             tf = flops_of[name] / (ms * 1e-3) / 1e12
-            d.update(TFLOPs=round(tf, 1), frac_fp8_peak=round(tf / FP8_PEAK_TFLOPS, 4))
+            d.update(TFLOPs=round(tf, 1), frac_fp8_peak=round(tf / FP8_PEAK_TFLOPS, 4),
+                     cold_us=round(cold_ms[name] * 1e3, 2))
         call_info[name] = d
     q_bytes = sum(bytes_of.values())
     q_ms = sum(cold_ms[n] for n in bytes_of)
