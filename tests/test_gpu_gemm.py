@@ -137,6 +137,30 @@ def test_dispatch_boundaries(m, n, k):
     check(xq, xs, wq, ws, rows=rows)
 
 
+def _random_shapes(count, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    shapes = []
+    while len(shapes) < count:
+        m = int(g.choice([g.integers(1, 65), g.integers(65, 1024), g.integers(1024, 5000)]))
+        n, k = 128 * int(g.integers(1, 65)), 128 * int(g.integers(1, 41))
+        if m * k <= 16 << 20 and n * k <= 16 << 20:
+            shapes.append((m, n, k))
+    return shapes
+
+
+@pytest.mark.parametrize("m,n,k", _random_shapes(24, 2024))
+def test_random_shapes(m, n, k):
+    """Seeded random shapes across every kernel-selection branch (few tokens, few tiles,
+    128x64 tiles with one or two K groups, 128x128 and 256x256 tiles), sampled rows
+    against the oracle."""
+    g = np.random.Generator(np.random.PCG64(m + 3 * n + 7 * k))
+    xq, xs, wq, ws = quantized_operands(m, n, k, tensor=40 + (m + n + k) % 9)
+    edges = [0, 1, 127, 128, 255, 256, m - 1]
+    rows = np.unique(np.concatenate([np.array([r for r in edges if 0 <= r < m]),
+                                     g.choice(m, min(m, 16), replace=False)]))
+    check(xq, xs, wq, ws, rows=rows)
+
+
 def test_padded_output_pitch_untouched():
     xq, xs, wq, ws = quantized_operands(40, 256, 384, tensor=9)
     yfull = check(xq, xs, wq, ws, ld_y=264)
