@@ -276,6 +276,26 @@ def test_grouped_many_groups_large_tiles():
     check_grouped(grouped_case(list(sizes), 256, 2048, 12))
 
 
+def _random_grouped_cases(count, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for c in range(count):
+        groups = int(g.integers(1, 41))
+        sizes = [int(x) for x in g.integers(0, 300, size=groups) * (g.random(groups) > 0.2)]
+        n = int(g.choice([128, 256, 384, 512]))
+        k = int(g.choice([128, 256, 768, 1024, 2048, 2560]))
+        cases.append((tuple(sizes), n, k, 100 + c))
+    return cases
+
+
+@pytest.mark.parametrize("sizes,n,k,seed", _random_grouped_cases(10, 31))
+def test_grouped_random(sizes, n, k, seed):
+    """Seeded random expert counts, group sizes (a fifth of them empty), N and K: both tile
+    paths (128x128, and 256/128-row tiles for K >= 2048 with N a multiple of 256), every row
+    against the oracle."""
+    check_grouped(grouped_case(list(sizes), n, k, seed))
+
+
 def test_grouped_moe_routing_fc2_subset():
     """Zipf-skewed top-8 routing over 128 experts (4096 tokens); fc2 shape n=2048, k=768.
     Checks a subset of groups (smallest, largest, a few others) against the oracle."""

@@ -116,6 +116,45 @@ def gpu_weight(tensors):
     return [(u8(qf), f32(s)) for qf, s in outs]
 
 
+def test_act_random_shapes_and_pitches():
+    """Seeded random activation shapes with padded row pitches and scale rows: codes and
+    scales bit-exact against the oracle, padding untouched."""
+    g = np.random.Generator(np.random.PCG64(77))
+    for case in range(12):
+        m, k = int(g.integers(1, 3000)), 128 * int(g.integers(1, 33))
+        ldx, ldq, lds = k + 8 * int(g.integers(0, 5)), k + 16 * int(g.integers(0, 5)), m + int(g.integers(0, 9))
+        x_bits = synth.activation(2, 1, case, m, k)
+        xfull = np.zeros((m, ldx), np.uint16)
+        xfull[:, :k] = x_bits
+        x = to_dev_bf16(xfull)[:, :k]
+        qfull = torch.full((m, ldq), 0xA5, dtype=torch.uint8, device=DEV)
+        sfull = torch.full((k // 128, lds), -7.0, dtype=torch.float32, device=DEV)
+        fq.fp8q_quant_act_g128(x, qfull[:, :k], sfull)
+        torch.cuda.synchronize()
+        q, sc = u8(qfull), f32(sfull)
+        qr, sr = oracle.quant_act_g128(x_bits)
+        assert np.array_equal(sc[:, :m].view(np.uint32), sr[:, :m].view(np.uint32)), f"case {case}: scales"
+        assert np.array_equal(q[:, :k], qr), f"case {case}: codes"
+        assert np.all(q[:, k:] == 0xA5) and np.all(sc[:, m:] == -7.0), f"case {case}: padding written"
+
+
+def test_weight_random_batches():
+    """Seeded random batches of weight tensors (1 to 9 per call, random shapes and padded
+    pitches): codes and scales bit-exact against the oracle."""
+    g = np.random.Generator(np.random.PCG64(78))
+    for call in range(6):
+        specs = []
+        for t in range(int(g.integers(1, 10))):
+            n, k = 128 * int(g.integers(1, 13)), 128 * int(g.integers(1, 13))
+            specs.append((synth.weight(3, 5 + call, t, n, k), k + 8 * int(g.integers(0, 4)), k + 16 * int(g.integers(0, 4))))
+        for (w, _, _), (q, sc) in zip(specs, gpu_weight(specs)):
+            k = w.shape[1]
+            qr, sr = oracle.quant_weight_blk128(w)
+            assert np.array_equal(sc.view(np.uint32), sr.view(np.uint32))
+            assert np.array_equal(q[:, :k], qr)
+            assert np.all(q[:, k:] == 0xA5)
+
+
 def test_weight_tiny():
     w, _ = synth.tiny()
     (q, s), = gpu_weight([(w, 256, 256)])
