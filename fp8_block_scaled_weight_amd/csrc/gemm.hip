@@ -613,9 +613,9 @@ static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, in
 
 // ----------------------------------------------------------------------------
 // Few tokens (decode, short prefill): the GEMM streams the weight matrix once and is
-// HBM-bound, so it is spread over as many CUs as possible.  A workgroup owns 16 weight
-// rows and up to 16*WM token rows; its 8 waves take the K blocks round-robin.  For each
-// K block a wave loads the 16 weight rows (non-temporal) and its live token rows (from
+// HBM-bound, so it is spread over as many CUs as possible.  A workgroup owns 16 or 32
+// weight rows and up to 16*WM token rows; its 8 waves take the K blocks round-robin.  For each
+// K block a wave loads the weight rows (non-temporal) and its live token rows (from
 // L2) with 8 lanes per 128-byte line, writes them to its own LDS stage and reads them
 // back in the MFMA operand layout, while the loads of its next K block are in flight.
 // (Fragment loads straight from memory make every 16-lane quarter-wave touch 16 lines;
@@ -640,25 +640,27 @@ constexpr int kSmallWaves = 8;
 // byte offset of 16-byte chunk c of row r in a stage
 __device__ __forceinline__ int stage_at(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
-template <int WM, bool FUSED, int D>
+template <int WM, bool FUSED, int D, int WN = 1>
 __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
     const void* __restrict__ a_, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
     const uint8_t* __restrict__ b, int64_t ld_b, const float* __restrict__ bs, uint16_t* __restrict__ y,
     int64_t ld_y, int64_t m, int64_t n16, int kblocks) {
   constexpr int RT = 16 * WM;                                    // token rows of the tile
-  constexpr int kStage = (16 + RT) * 128 + (FUSED ? RT * 4 : 0);  // weight rows, token rows, scales
+  constexpr int RW = 16 * WN;                                    // weight rows of the tile
+  constexpr int kStage = (RW + RT) * 128 + (FUSED ? RT * 4 : 0);  // weight rows, token rows, scales
   constexpr int TP = RT / 8;                                     // row-wise token loads per lane
   constexpr int P = 4 * WM;                                      // FUSED: 64-lane passes over a tile's chunks
-  static_assert(kStage >= WM * 64 * 16, "the partial sums reuse the stage");
+  static_assert(kStage >= WN * WM * 64 * 16, "the partial sums reuse the stage");
+  static_assert(WN * WM <= kSmallWaves, "one wave per output sub-tile in the final sum");
   __shared__ __align__(16) uint8_t stages[kSmallWaves * kStage];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   uint8_t* wst = stages + wave * kStage;
-  uint8_t* tst = wst + 16 * 128;
-  float* sst = reinterpret_cast<float*>(wst + (16 + RT) * 128);
+  uint8_t* tst = wst + RW * 128;
+  float* sst = reinterpret_cast<float*>(wst + (RW + RT) * 128);
   const int64_t tn = blockIdx.x % n16;
   const int64_t m0 = (blockIdx.x / n16) * RT;
-  const int64_t n0 = tn * 16;
+  const int64_t n0 = tn * RW;
   const int q = lane >> 4;
   const int fr = lane & 15;  // fragment row
   const int lr = lane >> 3, lc = lane & 7;  // row-wise lanes: row lr (+8i), chunk lc
@@ -677,12 +679,16 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
   }
 
   // D K blocks in registers: slot d holds the wave's d-th, (d + D)-th, ... K block
-  u32x4 rw[D][2];
+  u32x4 rw[D][2 * WN];
   uint4 rt[D][FUSED ? P : TP];
   float rsa[D][FUSED ? 1 : WM], rsb[D];
   auto load = [&](int d, int kb) {
-    rw[d][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w0 + (int64_t)kb * 128));
-    rw[d][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w1 + (int64_t)kb * 128));
+#pragma unroll
+    for (int wb = 0; wb < WN; ++wb) {
+      const int64_t o = (int64_t)wb * 16 * ld_b + (int64_t)kb * 128;
+      rw[d][2 * wb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w0 + o));
+      rw[d][2 * wb + 1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w1 + o));
+    }
     rsb[d] = bsrow[kb];
     if constexpr (FUSED) {
 #pragma unroll
@@ -704,9 +710,11 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
     }
   };
 
-  v4f acc[WM];
+  v4f acc[WN][WM];
 #pragma unroll
-  for (int j = 0; j < WM; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int wb = 0; wb < WN; ++wb)
+#pragma unroll
+    for (int j = 0; j < WM; ++j) acc[wb][j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (wave + d * kSmallWaves < kblocks) load(d, wave + d * kSmallWaves);
@@ -716,8 +724,11 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
       const int kb = kb0 + d * kSmallWaves;
       if (kb >= kblocks) break;
       // stage this K block
-      *reinterpret_cast<u32x4*>(wst + stage_at(lr, lc)) = rw[d][0];
-      *reinterpret_cast<u32x4*>(wst + stage_at(lr + 8, lc)) = rw[d][1];
+#pragma unroll
+      for (int wb = 0; wb < WN; ++wb) {
+        *reinterpret_cast<u32x4*>(wst + stage_at(16 * wb + lr, lc)) = rw[d][2 * wb];
+        *reinterpret_cast<u32x4*>(wst + stage_at(16 * wb + lr + 8, lc)) = rw[d][2 * wb + 1];
+      }
       float sa[WM];
       const float sb = rsb[d];
       if constexpr (FUSED) {
@@ -751,8 +762,11 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
       // this slot's next K block flies while this one is multiplied
       if (kb + kSmallWaves * D < kblocks) load(d, kb + kSmallWaves * D);
       __builtin_amdgcn_wave_barrier();
-      const v8i fw = join(*reinterpret_cast<const u32x4*>(wst + stage_at(fr, 2 * q)),
-                          *reinterpret_cast<const u32x4*>(wst + stage_at(fr, 2 * q + 1)));
+      v8i fw[WN];
+#pragma unroll
+      for (int wb = 0; wb < WN; ++wb)
+        fw[wb] = join(*reinterpret_cast<const u32x4*>(wst + stage_at(16 * wb + fr, 2 * q)),
+                      *reinterpret_cast<const u32x4*>(wst + stage_at(16 * wb + fr, 2 * q + 1)));
 #pragma unroll
       for (int j = 0; j < WM; ++j) {
         const int r = 16 * j + fr;
@@ -763,8 +777,11 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
                     *reinterpret_cast<const u32x4*>(tst + stage_at(r, 2 * q + 1)));
           s = FUSED ? sst[r] : sa[j];
         }
-        const v4f p = mfma_fp8(fw, ft);
-        acc[j] = p * (s * sb) + acc[j];
+#pragma unroll
+        for (int wb = 0; wb < WN; ++wb) {
+          const v4f p = mfma_fp8(fw[wb], ft);
+          acc[wb][j] = p * (s * sb) + acc[wb][j];
+        }
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -772,17 +789,19 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
   // the partial sums go through the wave's own stage
   v4f* part = reinterpret_cast<v4f*>(wst);
 #pragma unroll
-  for (int j = 0; j < WM; ++j) part[j * 64 + lane] = acc[j];
-  __syncthreads();
-  // wave j < WM adds the 8 partial sums of token tile j (fixed order) and stores it
-  if (wave < WM) {
-    const int j = wave;
-    v4f t = reinterpret_cast<const v4f*>(stages)[j * 64 + lane];
+  for (int wb = 0; wb < WN; ++wb)
 #pragma unroll
-    for (int w = 1; w < kSmallWaves; ++w) t += reinterpret_cast<const v4f*>(stages + w * kStage)[j * 64 + lane];
+    for (int j = 0; j < WM; ++j) part[(wb * WM + j) * 64 + lane] = acc[wb][j];
+  __syncthreads();
+  // wave wb * WM + j adds the 8 partial sums of sub-tile (wb, j) (fixed order) and stores it
+  if (wave < WN * WM) {
+    const int j = wave % WM, wb = wave / WM;
+    v4f t = reinterpret_cast<const v4f*>(stages)[wave * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < kSmallWaves; ++w) t += reinterpret_cast<const v4f*>(stages + w * kStage)[wave * 64 + lane];
     const int64_t row = m0 + 16 * j + (lane & 15);
     if (row < m) {
-      const int64_t col = n0 + 4 * q;
+      const int64_t col = n0 + 16 * wb + 4 * q;
       uint2 o;
       o.x = bf16_rne(t[0]) | (bf16_rne(t[1]) << 16);
       o.y = bf16_rne(t[2]) | (bf16_rne(t[3]) << 16);
@@ -791,13 +810,19 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
   }
 }
 
-template <int WM, bool FUSED = false>
+template <int WM, bool FUSED = false, int WN = 1>
 static hipError_t launch_smallm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                                 int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                                 int64_t k, hipStream_t stream) {
   const int64_t n16 = n / 16;
   const int64_t groups = (m + 16 * WM - 1) / (16 * WM);
   const unsigned grid = (unsigned)(n16 * groups);
+  if constexpr (WN == 2) {
+    hipLaunchKernelGGL((gemm_smallm_kernel<WM, FUSED, 1, 2>), dim3((unsigned)((n / 32) * groups)),
+                       dim3(64 * kSmallWaves), 0, stream, a, ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b),
+                       ld_b, b_s, reinterpret_cast<uint16_t*>(y), ld_y, m, n / 32, (int)(k / 128));
+    return hipGetLastError();
+  }
   // K blocks in flight per wave: one, except two for a 16-token tile whose grid fits on the
   // CUs at once (measured: 1-4 tokens, N = K = 4096, 5.7 -> 4.9 us; deeper rings cost more in
   // occupancy than they gain wherever the grid is larger)
@@ -822,6 +847,16 @@ static hipError_t launch_few_tokens(const void* a, int64_t ld_a, const float* a_
                                     int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                                     int64_t k, hipStream_t stream) {
   const int64_t n16 = n / 16;
+  // 32 weight rows per workgroup where that still gives 192 workgroups or more: a token row
+  // loaded into a workgroup then serves twice the weights, and the tokens, read once per
+  // workgroup from L2, are most of the traffic.  Measured (interleaved, byte-identical):
+  // 64x4096x4096 9.4 -> 8.3 us (32 x 32), 64x12288x4096 24.6 -> 21.2 us and 512x1024x4096
+  // 13.1 -> 10.0 us (64 x 32), 256x1024x4096 8.0 -> 6.9 us; with 128 such workgroups slower
+  // (64x4096x4096 9.4 -> 11.0 us).
+  if (!FUSED && m > 32 && (n / 32) * ((m + 63) / 64) >= 192)
+    return launch_smallm<4, FUSED, 2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  if (!FUSED && m > 16 && (n / 32) * ((m + 31) / 32) >= 192)
+    return launch_smallm<2, FUSED, 2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   if (m > 32 && n16 >= 256)
     return launch_smallm<4, FUSED>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   if (m > 16 && n16 * ((m + 31) / 32) >= 256)
