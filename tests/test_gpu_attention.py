@@ -69,6 +69,39 @@ def test_small_contexts(hq, hkv, ps):
         assert ok, f"recal={recal}: worst err/bound {ratio:.3f}"
 
 
+def _random_attention_cases(count, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for c in range(count):
+        hkv = int(g.choice([1, 2, 4, 8]))
+        hq = hkv * int(g.choice([1, 2, 3, 4, 8, 16]))
+        cases.append((int(g.integers(1, 13)), hq, hkv, int(g.choice([1, 5, 16])), 300 + c))
+    return cases
+
+
+@pytest.mark.parametrize("seqs,hq,hkv,ps,seed", _random_attention_cases(8, 17))
+def test_random_contexts(seqs, hq, hkv, ps, seed):
+    """Seeded random sequence counts and lengths (empty ones included), query / KV head
+    counts, page sizes and scales, with and without query recalibration."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    lens = g.integers(0, 900, size=seqs).astype(np.int32)
+    per = max(1, -(-int(lens.max()) // ps))
+    pages = seqs * per + int(g.integers(0, 5))
+    bt = g.permutation(pages)[:seqs * per].reshape(seqs, per).astype(np.int32)
+    kc, vc = _codes(seed, (pages, ps, hkv, 128)), _codes(seed + 1, (pages, ps, hkv, 128))
+    q = synth.activation(5, 2, seed, seqs, hq * 128).reshape(seqs, hq, 128)
+    ks, vs = float(g.choice([0.005, 0.02, 0.08])), float(g.choice([0.01, 0.03]))
+    sm = 128 ** -0.5
+    recal = bool(g.integers(0, 2))
+    qs = float(oracle.q_scale(q)) if recal else 0.01
+    got, qs_dev = _run(q, kc, vc, bt, lens, 0.01, ks, vs, sm, recal)
+    if recal:
+        assert np.float32(qs_dev) == np.float32(qs)
+    ref = oracle.paged_decode_attention(q, kc, vc, bt, lens, qs, ks, vs, sm)
+    ok, ratio = _gate(got, ref)
+    assert ok, f"worst err/bound {ratio:.3f}"
+
+
 @pytest.mark.parametrize("ps", [16, 5])
 def test_many_sequences_pair_kv_heads(ps):
     """64 sequences x 8 KV heads with groups of 4 query heads: the kernel reads two KV heads

@@ -300,6 +300,23 @@ def test_kv_sequences_pages():
     check_kv(synth.kv_values(5, 1, 0, t), synth.kv_values(5, 1, 1, t), slots, pages, 16)
 
 
+def test_kv_random_cases():
+    """Seeded random token counts, head counts, page sizes, skipped slots, stored or
+    recalibrated scales and E4M3 ranges: cache bytes and scales bit-exact."""
+    g = np.random.Generator(np.random.PCG64(31))
+    for case in range(10):
+        t, h = int(g.integers(1, 2500)), int(g.integers(1, 9))
+        ps = int(g.choice([1, 5, 8, 16]))
+        pages = -(-t // ps) + int(g.integers(0, 4))
+        slots = g.permutation(pages * ps)[:t].astype(np.int64)
+        slots[g.random(t) < 0.1] = -1
+        k = synth.to_bf16_bits(float(g.choice([0.1, 1.0, 30.0])) * g.standard_normal((t, h, 128), dtype=np.float32))
+        v = synth.to_bf16_bits(g.standard_normal((t, h, 128), dtype=np.float32))
+        recal = bool(g.integers(0, 2))
+        check_kv(k, v, slots, pages, ps, recal=recal, rng=float(g.choice([448.0, 240.0])),
+                 k_scale=float(g.choice([0.01, 0.25, 2.0])), v_scale=float(g.choice([0.005, 0.125])))
+
+
 def test_kv_empty_call_recalibrates_to_one():
     k = np.zeros((0, 8, 128), np.uint16)
     kc, vc, ks, vs = gpu_kv(k, k, np.zeros(0, np.int64), 1, 16, k_scale=3.0, v_scale=3.0)

@@ -113,6 +113,27 @@ def test_gemm_matches_oracle(m, n, k):
     assert nrm < 4e-3
 
 
+def _random_shapes(count, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(count):
+        m = int(g.choice([int(g.integers(1, 65)), int(g.integers(65, 1100)), int(g.integers(1100, 5000))]))
+        out.append((m, 128 * int(g.integers(1, 33)), 128 * int(g.integers(1, 25))))
+    return out
+
+
+@pytest.mark.parametrize("m,n,k", _random_shapes(12, 88))
+def test_gemm_random_shapes(m, n, k):
+    """Seeded random shapes over every tile configuration, sampled rows against the oracle."""
+    xq, xs, wq, ws = _operands(m, n, k, tensor=(m + n + k) % 11)
+    y = _gpu_gemm(fq.fp8q_gemm_w8a8_ue8m0, xq, xs, wq, ws)
+    g = np.random.Generator(np.random.PCG64(m + n))
+    rows = np.unique(np.concatenate([[0, m - 1], g.choice(m, min(m, 40), replace=False)]))
+    ok, ratio, nrm = gemm_gate(y[rows], oracle.gemm_w8a8(xq[rows], xs[:, rows], wq, ws))
+    assert ok, f"worst err/bound {ratio:.3f}"
+    assert nrm < 4e-3
+
+
 def test_gemm_agrees_with_fp32_scale_path():
     """Power-of-two scales are valid FP32 scales: both GEMMs pass the same gate."""
     xq, xs, wq, ws = _operands(512, 1024, 2048, tensor=3)
