@@ -214,6 +214,10 @@ __device__ __forceinline__ void store_stream(void* p, uint4 v) {
   u32x4 w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
 }
+typedef unsigned int u32x2e __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store8_stream(void* p, uint2 v) {
+  __builtin_nontemporal_store(u32x2e{v.x, v.y}, reinterpret_cast<u32x2e*>(p));
+}
 __device__ __forceinline__ uint4 load_plain(const void* p) {
   const u32x4 v = *reinterpret_cast<const u32x4*>(p);
   return make_uint4(v.x, v.y, v.z, v.w);
