@@ -317,6 +317,19 @@ def test_kv_random_cases():
                  k_scale=float(g.choice([0.01, 0.25, 2.0])), v_scale=float(g.choice([0.005, 0.125])))
 
 
+@pytest.mark.parametrize("heads", [9, 12, 16])
+def test_kv_rows_longer_than_one_pass(heads):
+    """Token rows of more than 1024 elements take several passes of the lane layout."""
+    g = np.random.Generator(np.random.PCG64(heads))
+    t, pages = 700, 50
+    k = synth.to_bf16_bits(g.standard_normal((t, heads, 128), dtype=np.float32))
+    v = synth.to_bf16_bits(3 * g.standard_normal((t, heads, 128), dtype=np.float32))
+    slots = g.permutation(pages * 16)[:t].astype(np.int64)
+    slots[g.random(t) < 0.05] = -1
+    check_kv(k, v, slots, pages, 16)
+    check_kv(k, v, slots, pages, 16, recal=False, k_scale=0.004, v_scale=0.02)
+
+
 def test_kv_empty_call_recalibrates_to_one():
     k = np.zeros((0, 8, 128), np.uint16)
     kc, vc, ks, vs = gpu_kv(k, k, np.zeros(0, np.int64), 1, 16, k_scale=3.0, v_scale=3.0)
