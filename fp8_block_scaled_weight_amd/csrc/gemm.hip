@@ -613,7 +613,7 @@ static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, in
 
 // ----------------------------------------------------------------------------
 // Few tokens (decode, short prefill): the GEMM streams the weight matrix once and is
-// HBM-bound, so it is spread over as many CUs as possible.  A workgroup owns 16 or 32
+// HBM-bound, so it is spread over as many CUs as possible.  A workgroup owns 16, 32 or 48
 // weight rows and up to 16*WM token rows; its 8 waves take the K blocks round-robin.  For each
 // K block a wave loads the weight rows (non-temporal) and its live token rows (from
 // L2) with 8 lanes per 128-byte line, writes them to its own LDS stage and reads them
@@ -651,7 +651,6 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
   constexpr int TP = RT / 8;                                     // row-wise token loads per lane
   constexpr int P = 4 * WM;                                      // FUSED: 64-lane passes over a tile's chunks
   static_assert(kStage >= WN * WM * 64 * 16, "the partial sums reuse the stage");
-  static_assert(WN * WM <= kSmallWaves, "one wave per output sub-tile in the final sum");
   __shared__ __align__(16) uint8_t stages[kSmallWaves * kStage];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -670,7 +669,6 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
   const uint16_t* x = reinterpret_cast<const uint16_t*>(a_);
   const uint8_t* w0 = b + (n0 + lr) * ld_b + lc * 16;
   const uint8_t* w1 = w0 + 8 * ld_b;
-  const float* bsrow = bs + (n0 / 128) * kblocks;
   int64_t srow[WM];  // token row of this lane's fragments (row 0 stands in for rows past m)
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
@@ -681,7 +679,9 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
   // D K blocks in registers: slot d holds the wave's d-th, (d + D)-th, ... K block
   u32x4 rw[D][2 * WN];
   uint4 rt[D][FUSED ? P : TP];
-  float rsa[D][FUSED ? 1 : WM], rsb[D];
+  // weight scales: one per 16-row block where a tile can straddle two 128-row blocks
+  constexpr int NSB = (128 % RW) ? WN : 1;
+  float rsa[D][FUSED ? 1 : WM], rsb[D][NSB];
   auto load = [&](int d, int kb) {
 #pragma unroll
     for (int wb = 0; wb < WN; ++wb) {
@@ -689,7 +689,8 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
       rw[d][2 * wb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w0 + o));
       rw[d][2 * wb + 1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w1 + o));
     }
-    rsb[d] = bsrow[kb];
+#pragma unroll
+    for (int wb = 0; wb < NSB; ++wb) rsb[d][wb] = bs[((n0 + 16 * wb) / 128) * kblocks + kb];
     if constexpr (FUSED) {
 #pragma unroll
       for (int p = 0; p < P; ++p) {
@@ -730,7 +731,9 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
         *reinterpret_cast<u32x4*>(wst + stage_at(16 * wb + lr + 8, lc)) = rw[d][2 * wb + 1];
       }
       float sa[WM];
-      const float sb = rsb[d];
+      float sb[WN];
+#pragma unroll
+      for (int wb = 0; wb < WN; ++wb) sb[wb] = rsb[d][NSB > 1 ? wb : 0];
       if constexpr (FUSED) {
         // group amax over the 16 lanes of a row, then the activation quantizer's scale and
         // encoder; codes and scales into the stage
@@ -780,7 +783,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
 #pragma unroll
         for (int wb = 0; wb < WN; ++wb) {
           const v4f p = mfma_fp8(fw[wb], ft);
-          acc[wb][j] = p * (s * sb) + acc[wb][j];
+          acc[wb][j] = p * (s * sb[wb]) + acc[wb][j];
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -793,12 +796,13 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
 #pragma unroll
     for (int j = 0; j < WM; ++j) part[(wb * WM + j) * 64 + lane] = acc[wb][j];
   __syncthreads();
-  // wave wb * WM + j adds the 8 partial sums of sub-tile (wb, j) (fixed order) and stores it
-  if (wave < WN * WM) {
-    const int j = wave % WM, wb = wave / WM;
-    v4f t = reinterpret_cast<const v4f*>(stages)[wave * 64 + lane];
+  // wave w adds the 8 partial sums of sub-tiles w, w + 8, ... (sub-tile wb * WM + j) in a
+  // fixed order and stores them
+  for (int st = wave; st < WN * WM; st += kSmallWaves) {
+    const int j = st % WM, wb = st / WM;
+    v4f t = reinterpret_cast<const v4f*>(stages)[st * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < kSmallWaves; ++w) t += reinterpret_cast<const v4f*>(stages + w * kStage)[wave * 64 + lane];
+    for (int w = 1; w < kSmallWaves; ++w) t += reinterpret_cast<const v4f*>(stages + w * kStage)[st * 64 + lane];
     const int64_t row = m0 + 16 * j + (lane & 15);
     if (row < m) {
       const int64_t col = n0 + 16 * wb + 4 * q;
@@ -817,10 +821,10 @@ static hipError_t launch_smallm(const void* a, int64_t ld_a, const float* a_s, i
   const int64_t n16 = n / 16;
   const int64_t groups = (m + 16 * WM - 1) / (16 * WM);
   const unsigned grid = (unsigned)(n16 * groups);
-  if constexpr (WN == 2) {
-    hipLaunchKernelGGL((gemm_smallm_kernel<WM, FUSED, 1, 2>), dim3((unsigned)((n / 32) * groups)),
+  if constexpr (WN > 1) {
+    hipLaunchKernelGGL((gemm_smallm_kernel<WM, FUSED, 1, WN>), dim3((unsigned)((n / (16 * WN)) * groups)),
                        dim3(64 * kSmallWaves), 0, stream, a, ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b),
-                       ld_b, b_s, reinterpret_cast<uint16_t*>(y), ld_y, m, n / 32, (int)(k / 128));
+                       ld_b, b_s, reinterpret_cast<uint16_t*>(y), ld_y, m, n / (16 * WN), (int)(k / 128));
     return hipGetLastError();
   }
   // K blocks in flight per wave: one, except two for a 16-token tile whose grid fits on the
@@ -847,16 +851,24 @@ static hipError_t launch_few_tokens(const void* a, int64_t ld_a, const float* a_
                                     int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                                     int64_t k, hipStream_t stream) {
   const int64_t n16 = n / 16;
-  // 32 weight rows per workgroup where that still gives 192 workgroups or more: a token row
-  // loaded into a workgroup then serves twice the weights, and the tokens, read once per
-  // workgroup from L2, are most of the traffic.  Measured (interleaved, byte-identical):
-  // 64x4096x4096 9.4 -> 8.3 us (32 x 32), 64x12288x4096 24.6 -> 21.2 us and 512x1024x4096
-  // 13.1 -> 10.0 us (64 x 32), 256x1024x4096 8.0 -> 6.9 us; with 128 such workgroups slower
+  // 48 or 32 weight rows per workgroup where that still gives 192 workgroups or more: a
+  // token row loaded into a workgroup then serves more weights, and the tokens, read once
+  // per workgroup from L2, are most of the traffic.  Measured against 16 rows (interleaved,
+  // byte-identical): 64x4096x4096 9.4 -> 8.3 us (32 tokens x 32 rows), 512x1024x4096
+  // 13.1 -> 10.0 us (64 x 32), 256x1024x4096 8.0 -> 6.9 us; 64x12288x4096 24.6 -> 21.2 us
+  // with 64 x 32 (384 workgroups: one and a half rounds of the CUs), 15.8 us with 64 x 48
+  // (256), 32x12288x4096 15.1 -> 12.0 us with 32 x 48.  With 128 workgroups slower
   // (64x4096x4096 9.4 -> 11.0 us).
-  if (!FUSED && m > 32 && (n / 32) * ((m + 63) / 64) >= 192)
-    return launch_smallm<4, FUSED, 2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-  if (!FUSED && m > 16 && (n / 32) * ((m + 31) / 32) >= 192)
-    return launch_smallm<2, FUSED, 2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  if constexpr (!FUSED) {
+    if (m > 32 && n % 48 == 0 && (n / 48) * ((m + 63) / 64) >= 192)
+      return launch_smallm<4, FUSED, 3>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+    if (m > 32 && (n / 32) * ((m + 63) / 64) >= 192)
+      return launch_smallm<4, FUSED, 2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+    if (m > 16 && n % 48 == 0 && (n / 48) * ((m + 31) / 32) >= 192)
+      return launch_smallm<2, FUSED, 3>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+    if (m > 16 && (n / 32) * ((m + 31) / 32) >= 192)
+      return launch_smallm<2, FUSED, 2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  }
   if (m > 32 && n16 >= 256)
     return launch_smallm<4, FUSED>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   if (m > 16 && n16 * ((m + 31) / 32) >= 256)

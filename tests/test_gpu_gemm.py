@@ -138,18 +138,25 @@ def test_dispatch_boundaries(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [
-    (40, 12288, 1024),    # 64 tokens x 32 weight rows, 384 workgroups, 40 live rows
+    (40, 12288, 1024),    # 64 tokens x 48 weight rows, 256 workgroups, 40 live rows
     (500, 1024, 1024),    # 64 x 32, 256 workgroups, a 52-row last token tile
     (64, 6144, 1024),     # 64 x 32 at exactly 192 workgroups
     (64, 6016, 1024),     # 188 such workgroups: 32 x 32 instead
     (33, 4096, 1024),     # 32 x 32, 256 workgroups, a 1-row last token tile
-    (17, 12288, 1024),    # 32 x 32 from 17 tokens
+    (17, 12288, 1024),    # 32 x 48 from 17 tokens
     (320, 1024, 2048),    # 160 workgroups of 64 x 32: 32 x 32
     (16, 12288, 1024),    # 16 tokens: 16 weight rows per workgroup
+    (64, 12288, 1024),    # 64 x 48: 256 workgroups, tiles straddling 128-row scale blocks
+    (50, 12288, 256),     # 64 x 48, a 50-row token tile
+    (64, 9216, 512),      # 64 x 48 at exactly 192 workgroups
+    (64, 9600, 512),      # 64 x 48, 200 workgroups
+    (64, 6272, 512),      # n not a multiple of 48: 64 x 32
+    (20, 12288, 1024),    # 32 x 48
 ])
 def test_few_token_weight_row_pairs(m, n, k):
-    """The few-token kernel with 32 weight rows per workgroup, both token heights and each
-    side of the workgroup-count rule: every output against the oracle."""
+    """The few-token kernel with 32 or 48 weight rows per workgroup (48-row tiles straddle
+    128-row scale blocks), both token heights and each side of the workgroup-count rules:
+    every output against the oracle."""
     check(*quantized_operands(m, n, k, tensor=40 + m % 5))
 
 

@@ -68,8 +68,10 @@ def test_quantizer_guards():
 
 @pytest.mark.parametrize("m,n,k", [
     (37, 256, 384),      # few tokens
-    (40, 12288, 256),    # few tokens, 64 tokens x 32 weight rows per workgroup
-    (20, 12288, 256),    # few tokens, 32 x 32
+    (40, 12288, 256),    # few tokens, 64 tokens x 48 weight rows per workgroup
+    (40, 6272, 256),     # few tokens, 64 x 32
+    (20, 12288, 256),    # few tokens, 32 x 48
+    (20, 6272, 256),     # few tokens, 32 x 32
     (300, 512, 1152),    # few tiles (24 of 128x64): the few-token kernel
     (500, 1024, 1024),   # few tiles, 64 x 32
     (300, 4096, 1152),   # 128x64 tiles in two K groups
