@@ -614,10 +614,10 @@ static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, in
 // ----------------------------------------------------------------------------
 // Few tokens (decode, short prefill): the GEMM streams the weight matrix once and is
 // HBM-bound, so it is spread over as many CUs as possible.  A workgroup owns 16, 32 or 48
-// weight rows and up to 16*WM token rows; its 8 waves take the K blocks round-robin.  For each
-// K block a wave loads the weight rows (non-temporal) and its live token rows (from
-// L2) with 8 lanes per 128-byte line, writes them to its own LDS stage and reads them
-// back in the MFMA operand layout, while the loads of its next K block are in flight.
+// weight rows and up to 16*WM token rows; its 8 waves take the K blocks round-robin.
+// For each K block a wave loads the weight rows (non-temporal) and its live token rows
+// (from L2) with 8 lanes per 128-byte line, writes them to its own LDS stage and reads
+// them back in the MFMA operand layout, while the loads of its next K block are in flight.
 // (Fragment loads straight from memory make every 16-lane quarter-wave touch 16 lines;
 // measured on these shapes they move the same bytes about 1.6x slower.)  A stage row is
 // 128 bytes with 16-byte chunk c of row r at c ^ ((r >> 1) & 7): the 16 lanes served

@@ -121,8 +121,8 @@ __global__ __launch_bounds__(kKvBlock) void kv_write_kernel(const uint16_t* __re
     int64_t sl[NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u) sl[u] = (t0 + u * waves < tokens) ? slots[t0 + u * waves] : -1;
-    // the amax pass's lane layout: elements 8l .. and 512 + 8l .. of each 1024-element pass,
-    // 8 codes stored per lane and half (whole 512-byte runs per instruction)
+    // the amax pass's lane layout: elements 8l .. and 512 + 8l .. of each 1024-element pass;
+    // each store instruction writes 8 codes per lane, a 512-byte run
     for (int64_t e0 = 0; e0 < row; e0 += kElemsPerWavePass) {
       const int64_t ea = e0 + lane * 8, eb = ea + kElemsPerWavePass / 2;
       const bool va = ea < row, vb = eb < row;
