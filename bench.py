@@ -259,7 +259,7 @@ _QUANT_CALLS = 3
 def profile_quantizers():
     """The large quantizer workloads, _QUANT_CALLS calls each, eagerly: the 36-layer weight sync
     (one batched call), one MoE layer's expert weights, one 64 x 20,000-token KV layer with
-    recalibration (a target for counter passes)."""
+    recalibration, then FP8 decode attention over that cache (a target for counter passes)."""
     import torch
     import fp8_block_scaled_weight_amd as fq
     from fp8_block_scaled_weight_amd import synth
@@ -286,6 +286,18 @@ def profile_quantizers():
         fq.fp8q_kv_quant(k, v, sl, kc, vc, ks, vs, 448.0, recalibrate=True)
     torch.cuda.synchronize()
     log("profiled: KV layer")
+    # FP8 decode attention over the cache just written (the bench leg's shape, stored query scale)
+    import numpy as np
+    seqs, hq = 64, 32
+    bt = torch.from_numpy((slots_np.reshape(seqs, -1)[:, ::16] // 16).astype(np.int32)).to(dev)
+    lens = torch.full((seqs,), t // seqs, dtype=torch.int32, device=dev)
+    qd = synth.device_activation(seqs, hq * 128, dev, 5, 0, 50).view(seqs, hq, 128)
+    od = torch.empty((seqs, hq, 128), dtype=torch.bfloat16, device=dev)
+    qsc = torch.full((1,), 0.01, device=dev)
+    for _ in range(_QUANT_CALLS):
+        fq.fp8q_paged_decode_attention(qd, kc, vc, bt, lens, qsc, ks, vs, 128 ** -0.5, od)
+    torch.cuda.synchronize()
+    log("profiled: decode attention")
 
 
 def summarize_quantizer_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir):
@@ -319,8 +331,10 @@ def summarize_quantizer_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_
     work = [("36-layer weight sync (252 tensors, one call)", -(-252 // 64), 2 * sync_el, sync_el + 4 * sync_el / 16384),
             ("MoE expert weights of one layer (2 tensors)", 1, 2 * moe_el, moe_el + 4 * moe_el / 16384),
             ("KV layer, 64 x 20,000 tokens, recalibrate + write", 3, 2 * (2 * 2 * t * row) + 2 * 8 * t,
-             2 * t * row)]
-    md = ["# HBM traffic of the large quantizer workloads", "",
+             2 * t * row),
+            ("FP8 decode attention over that cache (64 sequences, 32 query heads)", 1,
+             2 * t * row + 2 * 64 * 32 * 128 + 4 * (t // 16) + 4 * 64, 2 * 64 * 32 * 128)]
+    md = ["# HBM traffic of the large quantizer workloads and the decode attention", "",
           "Counter passes over `python3 bench.py --profile-quantizers` (each workload called "
           f"{_QUANT_CALLS} times, eagerly), one MI355X, repository root, TMPDIR=/tmp:", "",
           "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/q_fetch -o q -- python3 bench.py --profile-quantizers",
@@ -344,7 +358,8 @@ def summarize_quantizer_counters(fetch_dir, write_dir, cal_fetch_dir, cal_write_
         names = sorted({x["name"].replace("void fp8q::", "").replace("fp8q::", "") for x in f_})
         md.append(f"| {label} | {', '.join('`' + x + '`' for x in names)} | {fb / 1e9:.3f} | {alg_r / 1e9:.3f} | "
                   f"{wb / 1e9:.3f} | {alg_w / 1e9:.3f} |")
-    md += ["", "Source digests: " + ", ".join(f"{n} {source_digest(n)}" for n in ("quant.hip", "kv_quant.hip"))]
+    md += ["", "Source digests: " + ", ".join(f"{n} {source_digest(n)}" for n in ("quant.hip", "kv_quant.hip",
+                                                                                   "attention.hip"))]
     with open(os.path.join(ROOT, "profiles", "quantizers_large_traffic.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     print("\n".join(md))
