@@ -597,6 +597,195 @@ __global__ __launch_bounds__(C::THREADS) void gemm_w8a8_kernel(const uint8_t* __
                (uint8_t FP8Q_LDS*)lds);
 }
 
+
+// Ping-pong 256x256 tile for power-of-two scales.  The 8 waves form two groups of 4, each
+// owning 128 token rows x 256 weight rows (128 x 64 per wave, as in CfgLarge).  A step is
+// a memory phase (read every fragment of the K block into registers, start the next
+// block's copies) and a compute phase (16 scaled MFMAs, nothing else).  The groups run
+// half a step apart, one barrier out of phase: while one group computes, the other reads
+// LDS, so the matrix core and LDS are busy at the same time instead of in bursts shared
+// by all 8 waves.  Only power-of-two scales leave room for it: the fp32-scale tile's
+// per-chain partial products (32 more registers) do not fit beside a whole step of
+// fragments.  Copy rings: group 0 copies the weight rows (two stages shared by both
+// groups), each group its own token rows and scales (two stages per group).
+// Summation order per output is that of gemm_tile<CfgLarge, true>: K blocks in order,
+// K halves 0 and 1 within a block; the results are bit-identical.
+struct PingPongCfg {
+  static constexpr int W_STAGE = 256 * 128;        // a step's 256 weight rows
+  static constexpr int T_SCALE = 128 * 128;        // token scales, after a group's 128 rows
+  static constexpr int T_WSC = T_SCALE + 128 * 4;  // per wave: the tile's two weight scales
+  static constexpr int T_STAGE = 17408;
+  static constexpr int T_BASE = 2 * W_STAGE;
+  static constexpr int LDS_BYTES = T_BASE + 4 * T_STAGE;
+};
+static_assert(PingPongCfg::T_WSC + 4 * 8 <= PingPongCfg::T_STAGE && PingPongCfg::LDS_BYTES <= 160 * 1024 &&
+                  8 * 128 * 64 * 2 <= PingPongCfg::LDS_BYTES,
+              "ping-pong LDS: stages, and the epilogue's 8 wave blocks");
+
+__device__ __forceinline__ void gemm_tile_pingpong_pow2(const uint8_t* __restrict__ a, int64_t ld_a,
+                                                        int64_t a_rows, const float* __restrict__ as,
+                                                        int64_t ld_as, const uint8_t* __restrict__ b,
+                                                        int64_t ld_b, const float* __restrict__ bs, int kblocks,
+                                                        uint16_t* __restrict__ y, int64_t ld_y, int64_t m0,
+                                                        int64_t m_end, int64_t n0, uint8_t FP8Q_LDS* lds) {
+  using Q = PingPongCfg;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = wave >> 2, w4 = wave & 3;  // group; wave within it
+  const int wn = w4 * 64;
+  const int64_t tm0 = m0 + G * 128;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  // Row copies: lane l of wave w4 copies chunk l%8 of rows 8*w4 + l/8 + 32i (weights: i < 8,
+  // group 0 only; tokens: i < 4, clamped to the last valid row), swizzled as in gemm_tile.
+  const int rl = w4 * 8 + (lane >> 3);
+  const int chunk = (lane & 7) ^ swz(rl);  // swz(rl + 32i) == swz(rl)
+  const uint32_t wsrc = (uint32_t)((n0 + rl) * ld_b) + chunk * 16;
+  const uint32_t wstride = (uint32_t)(32 * ld_b);
+  const uint32_t tsrc0 = (uint32_t)((tm0 + rl) * ld_a) + chunk * 16;
+  const uint32_t tclamp = (uint32_t)((m_end - 1) * ld_a) + chunk * 16;
+  const uint32_t tstride = (uint32_t)(32 * ld_a);
+  // Scales: lanes 0..31 copy token scales into slots w4*32 + l (slot p holds token row
+  // 32 * (p % 4) + p / 4 of the group, so a lane's four scales are contiguous); lanes 32
+  // and 33 copy the tile's two weight scales into the wave's own pair of slots.
+  const bool tok_lane = lane < 32;
+  const int slot = w4 * 32 + (lane & 31);
+  int64_t srow = tm0 + 32 * (slot & 3) + (slot >> 2);
+  srow = srow < m_end ? srow : m_end - 1;
+  const bool wsc_lane = lane == 32 || lane == 33;
+  const uint32_t scsrc = tok_lane ? (uint32_t)(srow * 4) : (uint32_t)((n0 / 128 + (lane & 1)) * kblocks * 4);
+
+  const v4i ra = make_rsrc(a, (uint32_t)(a_rows * ld_a));
+  const v4i rb = make_rsrc(b, (uint32_t)((n0 + 256) * ld_b));
+  const v4i rsa = make_rsrc(as, (uint32_t)(ld_as * kblocks * 4));
+  const v4i rsb = make_rsrc(bs, (uint32_t)((n0 / 128 + 2) * kblocks * 4));
+
+  auto issue = [&](int kb, int st) {
+    const uint32_t tdst = lds_base + Q::T_BASE + (uint32_t)((G * 2 + st) * Q::T_STAGE);
+    if (G == 0) {
+      const uint32_t wdst = lds_base + (uint32_t)(st * Q::W_STAGE);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        dma16(rb, wsrc, (uint32_t)kb * 128u + (uint32_t)i * wstride, wdst + (uint32_t)((i * 4 + w4) * 1024));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = tsrc0 + (uint32_t)i * tstride;
+      dma16(ra, o < tclamp ? o : tclamp, (uint32_t)kb * 128u, tdst + (uint32_t)((i * 4 + w4) * 1024));
+    }
+    if (tok_lane) dma4(rsa, scsrc, (uint32_t)(kb * ld_as * 4), tdst + Q::T_SCALE + (uint32_t)(w4 * 128));
+    if (wsc_lane) dma4(rsb, scsrc, (uint32_t)kb * 4u, tdst + Q::T_WSC + (uint32_t)(w4 * 8) - 128u);
+  };
+
+  const int r32 = lane & 31, g = lane >> 5;
+  uint32_t fo[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) fo[h][e] = (uint32_t)(r32 * 128 + (((4 * h + 2 * g + e) ^ swz(r32)) << 4));
+
+  v16f acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  v8i fa[2][2];  // weight fragments [sub-tile][K half]
+  v8i fb[4][2];  // token fragments
+
+  // Barriers: every wave passes 2 + 2 * kblocks before the epilogue's; group 1 takes its
+  // extra one first (so it trails by one), group 0 last.  Between consecutive barriers
+  // one group is in its memory phase and the other in its compute phase.  A stage is
+  // rewritten only after both groups' reads of it have completed (lgkmcnt(0) before the
+  // barrier that ends each memory phase), and a group's copies have landed (vmcnt(0)
+  // before the barrier that ends its compute phase) before any wave reads them.
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if (G == 1) asm volatile("s_barrier" ::: "memory");
+  for (int s = 0; s < kblocks; ++s) {
+    const int cur = s & 1;
+    const uint8_t FP8Q_LDS* stw = lds + cur * Q::W_STAGE + wn * 128;
+    const uint8_t FP8Q_LDS* stt = lds + Q::T_BASE + (G * 2 + cur) * Q::T_STAGE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        fa[i][h] = join(lds_ld<u32x4>(stw, fo[h][0] + i * 4096), lds_ld<u32x4>(stw, fo[h][1] + i * 4096));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        fb[j][h] = join(lds_ld<u32x4>(stt, fo[h][0] + j * 4096), lds_ld<u32x4>(stt, fo[h][1] + j * 4096));
+    const u32x4 t4 = lds_ld<u32x4>(stt, Q::T_SCALE + r32 * 16);
+    const int ea = e8m0_of(lds_ld<float>(stt, Q::T_WSC + (w4 * 2 + (wn >> 7)) * 4));
+    const int eb[4] = {(int)(t4.x >> 23), (int)(t4.y >> 23), (int)(t4.z >> 23), (int)(t4.w >> 23)};
+    if (s + 1 < kblocks) issue(s + 1, cur ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // K half 0 of all 8 sub-tiles, then half 1: no MFMA waits for the one just before it
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][j] = mfma32_scaled(fa[i][h], fb[j][h], acc[i][j], ea, eb[j]);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (G == 0) asm volatile("s_barrier" ::: "memory");
+
+  // epilogue as in gemm_tile: each wave stages its 128 x 64 bf16 block in LDS, swizzled,
+  // and stores whole 128-byte row segments
+  constexpr int TM = 128, TN = 64;
+  constexpr int CPR = TN / 8, RPW = 16 / CPR, RPI = 64 / CPR;
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  uint8_t FP8Q_LDS* ep = lds + wave * (TM * TN * 2);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int row = 32 * j + r32;
+        const int ck = (4 * i + q4) ^ ((row / RPW) & (CPR - 1));
+        u32x2 o;
+        o.x = bf16_rne(acc[i][j][4 * q4 + 0]) | (bf16_rne(acc[i][j][4 * q4 + 1]) << 16);
+        o.y = bf16_rne(acc[i][j][4 * q4 + 2]) | (bf16_rne(acc[i][j][4 * q4 + 3]) << 16);
+        *reinterpret_cast<u32x2 FP8Q_LDS*>(ep + row * (TN * 2) + ck * 16 + 8 * g) = o;
+      }
+  const int c_in = lane % CPR;
+#pragma unroll
+  for (int t = 0; t < TM / RPI; ++t) {
+    const int row = t * RPI + lane / CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4 FP8Q_LDS*>(ep + row * (TN * 2) +
+                                                           ((c_in ^ ((row / RPW) & (CPR - 1))) * 16));
+    const int64_t m = tm0 + row;
+    if (m < m_end) *reinterpret_cast<u32x4*>(y + m * ld_y + n0 + wn + 8 * c_in) = v;
+  }
+}
+
+__global__ __launch_bounds__(512) void gemm_w8a8_pingpong_pow2_kernel(
+    const uint8_t* __restrict__ a, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
+    const uint8_t* __restrict__ b, int64_t ld_b, const float* __restrict__ bs, uint16_t* __restrict__ y,
+    int64_t ld_y, int64_t m, int64_t m_tiles, int64_t n_tiles, int kblocks) {
+  __shared__ __align__(1024) uint8_t lds[PingPongCfg::LDS_BYTES];
+  const int64_t tiles = m_tiles * n_tiles;
+  const int64_t t = xcd_tile(blockIdx.x, tiles);
+  if (t >= tiles) return;
+  int64_t tm, tn;
+  tile_coords<4>(t, m_tiles, n_tiles, tm, tn);
+  const int64_t m0 = tm * 256;
+  const int64_t m_end = (m0 + 256) < m ? (m0 + 256) : m;
+  gemm_tile_pingpong_pow2(a, ld_a, m, as, ld_as, b, ld_b, bs, kblocks, y, ld_y, m0, m_end, tn * 256,
+                          (uint8_t FP8Q_LDS*)lds);
+}
+
 template <class C, bool POW2 = false>
 static hipError_t launch_dense(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                                int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
@@ -896,6 +1085,19 @@ static hipError_t launch_tiles(const void* a, int64_t ld_a, const float* a_s, in
   }
   // large tiles when they cover n exactly and still give every CU a tile
   const int64_t large_tiles = ((m + CfgLarge::BM - 1) / CfgLarge::BM) * (n / CfgLarge::BN);
+  if constexpr (POW2) {
+    // ping-pong tile from 16 K steps on (interleaved medians, base -> ping-pong: 4096^3
+    // 60.3 -> 57.2 us, 4096x12288x4096 164.6 -> 156.1, 8192^3 421 -> 396; even at
+    // K = 1024, slower at K = 512: 8192x4096x512 28.0 -> 30.3)
+    if (n % CfgLarge::BN == 0 && large_tiles >= 256 && k >= 2048) {
+      const int64_t n_tiles = n / 256, m_tiles = (m + 255) / 256, tiles = m_tiles * n_tiles;
+      const int64_t grid = ((tiles + kXcds - 1) / kXcds) * kXcds;
+      hipLaunchKernelGGL(gemm_w8a8_pingpong_pow2_kernel, dim3((unsigned)grid), dim3(512), 0, stream,
+                         reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b),
+                         ld_b, b_s, reinterpret_cast<uint16_t*>(y), ld_y, m, m_tiles, n_tiles, (int)(k / 128));
+      return hipGetLastError();
+    }
+  }
   if (n % CfgLarge::BN == 0 && large_tiles >= 256)
     return launch_dense<CfgLarge, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   // with at least two tiles per CU, two co-resident workgroups hide each other's waits

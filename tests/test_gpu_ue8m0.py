@@ -101,6 +101,9 @@ def _gpu_gemm(fn, xq, xs, wq, ws):
     (4000, 4096, 1024),  # 256x256 tiles, ragged
     (4000, 4096, 128),   # 256x256 tiles, one K step
     (4000, 4096, 256),   # 256x256 tiles, two K steps
+    (4000, 4096, 2048),  # ping-pong 256x256 tiles, ragged: the last tile's second half 32 rows
+    (1030, 16384, 2048),  # ping-pong 256x256 tiles, the last tile's second half empty
+    (4096, 2048, 4096),  # ping-pong 256x256 tiles, whole
 ])
 def test_gemm_matches_oracle(m, n, k):
     xq, xs, wq, ws = _operands(m, n, k, tensor=n // 128 + m % 7)
