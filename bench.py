@@ -211,6 +211,7 @@ _GEMM_WORKLOADS = [
     ("dense 4096x12288x4096 (gate/up)", "dense", 4096, 12288, 4096),
     ("dense 64x4096x4096 (q, o at 64 tokens)", "dense", 64, 4096, 4096),
     ("dense 64x12288x4096 (gate/up at 64 tokens)", "dense", 64, 12288, 4096),
+    ("dense UE8M0 4096x4096x4096 (q, o; power-of-two scales)", "ue8m0", 4096, 4096, 4096),
     ("grouped MoE fc1 (128 experts, 32768 rows, 1536x2048)", "grouped", 32768, 1536, 2048),
     ("grouped MoE fc2 (128 experts, 32768 rows, 2048x768)", "grouped", 32768, 2048, 768),
 ]
@@ -241,10 +242,14 @@ def profile_gemms():
         asc = torch.rand((k // 128, m), device=dev, generator=gen)
         b = torch.randint(0, 0x77, (e * n, k), dtype=torch.uint8, device=dev, generator=gen)
         bsc = torch.rand((e * n // 128, k // 128), device=dev, generator=gen)
+        if kind == "ue8m0":
+            asc, bsc = torch.exp2(torch.round(torch.log2(asc))), torch.exp2(torch.round(torch.log2(bsc)))
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         for _ in range(8):
             if kind == "grouped":
                 fq.fp8q_grouped_gemm_w8a8(a, asc, b.view(e, n, k), bsc.view(e, n // 128, k // 128), offs, y)
+            elif kind == "ue8m0":
+                fq.fp8q_gemm_w8a8_ue8m0(a, asc, b, bsc, y)
             else:
                 fq.fp8q_gemm_w8a8_blkscaled(a, asc, b, bsc, y)
         torch.cuda.synchronize()

@@ -78,6 +78,7 @@ def test_quantizer_guards():
     (700, 1024, 640),    # 128x64 tiles, one K group
     (1100, 256, 384),    # 128x128 tiles
     (4000, 4096, 256),   # 256x256 tiles, ragged
+    (4000, 4096, 2048),  # 256x256 tiles, ragged; power-of-two scales: the ping-pong tile
 ])
 def test_gemm_guards(m, n, k):
     a, b = _codes((m, k), 1), _codes((n, k), 2)
@@ -212,3 +213,22 @@ def test_gemm_independent_of_tile_configuration():
     fq.fp8q_gemm_w8a8_blkscaled(a2[300:1400], a2_s[:, 300:1400].contiguous(), b2[1], b2_s[1], yd)
     torch.cuda.synchronize()
     assert torch.equal(yg[300:1400].view(torch.int16), yd.view(torch.int16))
+
+
+def test_ue8m0_gemm_independent_of_tile_configuration():
+    """Power-of-two scales, K = 2048: rows of a 4096-row GEMM (ping-pong 256x256 tiles) equal
+    a 4000-row one (the same, ragged), a 2048-row one (128x128 tiles, two-stage ring) and a
+    1100-row one (128x128, four-stage ring), bit for bit."""
+    n, k = 4096, 2048
+    a, b = _codes((4096, k), 21), _codes((n, k), 22)
+    a_s = torch.exp2(torch.round(torch.log2(_scales((k // 128, 4096), 23))))
+    b_s = torch.exp2(torch.round(torch.log2(_scales((n // 128, k // 128), 24))))
+    ys = {}
+    for m in (4096, 4000, 2048, 1100):
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+        fq.fp8q_gemm_w8a8_ue8m0(a[:m], a_s[:, :m].contiguous(), b, b_s, y)
+        ys[m] = y
+    torch.cuda.synchronize()
+    assert torch.equal(ys[4096][:4000].view(torch.int16), ys[4000].view(torch.int16))
+    assert torch.equal(ys[4096][:2048].view(torch.int16), ys[2048].view(torch.int16))
+    assert torch.equal(ys[2048][:1100].view(torch.int16), ys[1100].view(torch.int16))
