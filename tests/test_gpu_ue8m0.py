@@ -165,3 +165,23 @@ def test_grouped_with_empty_groups():
     ref = oracle.grouped_gemm_w8a8(aq, as_, bq, bs, off)
     ok, ratio, _ = gemm_gate(bf16_bits(y), ref)
     assert ok, f"worst err/bound {ratio:.3f}"
+
+
+def test_pingpong_padded_pitches():
+    """The ping-pong 256x256 tile (K >= 2048) with every pitch padded (a, b, y rows; the token
+    scale rows) gives the bytes it gives on contiguous buffers and leaves y's padding alone."""
+    m, n, k = 1100, 16384, 2048
+    g = torch.Generator(device=DEV)
+    g.manual_seed(31)
+    a_pad = torch.randint(0, 0x77, (m, k + 128), dtype=torch.uint8, device=DEV, generator=g)
+    b_pad = torch.randint(0, 0x77, (n, k + 256), dtype=torch.uint8, device=DEV, generator=g)
+    as_pad = torch.exp2(torch.randint(-12, -4, (k // 128, m + 5), device=DEV, generator=g).float())
+    b_s = torch.exp2(torch.randint(-12, -4, (n // 128, k // 128), device=DEV, generator=g).float())
+    a, b, a_s = a_pad[:, :k], b_pad[:, :k], as_pad[:, :m]
+    y_pad = torch.full((m, n + 64), float("nan"), dtype=torch.bfloat16, device=DEV)
+    fq.fp8q_gemm_w8a8_ue8m0(a, a_s, b, b_s, y_pad[:, :n])
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    fq.fp8q_gemm_w8a8_ue8m0(a.contiguous(), a_s.contiguous(), b.contiguous(), b_s, y)
+    torch.cuda.synchronize()
+    assert torch.equal(y_pad[:, :n].view(torch.int16), y.view(torch.int16))
+    assert torch.isnan(y_pad[:, n:].float()).all()
