@@ -89,10 +89,12 @@ def lib():
                                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
                                                     ctypes.c_float, ctypes.c_float, ctypes.c_double, _f64p]
         L.oracle_swiglu_quant_g128.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p, _i64, _f64p]
+        L.oracle_swiglu_quant_g128_ue8m0.argtypes = L.oracle_swiglu_quant_g128.argtypes
         L.oracle_silu_times_up.argtypes = [ctypes.c_double, ctypes.c_double]
         L.oracle_silu_times_up.restype = ctypes.c_double
         for f in ("oracle_kv_scales", "oracle_quant_weight_blk128", "oracle_quant_act_g128", "oracle_gemm_w8a8",
-                  "oracle_swiglu_quant_g128", "oracle_q_scale", "oracle_paged_decode_attention",
+                  "oracle_swiglu_quant_g128", "oracle_swiglu_quant_g128_ue8m0", "oracle_q_scale",
+                  "oracle_paged_decode_attention",
                   "oracle_quant_weight_blk128_ue8m0", "oracle_quant_act_g128_ue8m0",
                   "oracle_grouped_gemm_w8a8", "oracle_kv_quant", "oracle_num_threads"):
             getattr(L, f).restype = ctypes.c_int
@@ -289,10 +291,12 @@ def moe_dispatch(xq: np.ndarray, xs: np.ndarray, topk_ids: np.ndarray, num_exper
     return aq, as_, offsets, row_of.reshape(t, topk)
 
 
-def swiglu_quant_g128(h_bits: np.ndarray, ld_s: int | None = None, with_amax: bool = False):
+def swiglu_quant_g128(h_bits: np.ndarray, ld_s: int | None = None, with_amax: bool = False,
+                      ue8m0: bool = False):
     """silu(gate) * up of a bf16 fc1 output [m, 2n] (gate = first n columns), quantized
     in 1x128 groups -> (codes [m, n], scales [n/128, ld_s]) and, with_amax, the fp64
-    group maxima [n/128, m]."""
+    group maxima [n/128, m].  ue8m0=True takes the power-of-two scale of each group's fp64
+    maximum instead of fl32(amax/448)."""
     h = _u16(h_bits)
     m, n2 = h.shape
     n = n2 // 2
@@ -300,7 +304,8 @@ def swiglu_quant_g128(h_bits: np.ndarray, ld_s: int | None = None, with_amax: bo
     q = np.empty((m, n), dtype=np.uint8)
     s = np.zeros((n // 128, ld_s), dtype=np.float32)
     amax = np.zeros((n // 128, m), dtype=np.float64)
-    _check(lib().oracle_swiglu_quant_g128(h, m, n, n2, q, n, s, ld_s, amax), "swiglu_quant_g128")
+    f = lib().oracle_swiglu_quant_g128_ue8m0 if ue8m0 else lib().oracle_swiglu_quant_g128
+    _check(f(h, m, n, n2, q, n, s, ld_s, amax), "swiglu_quant_g128")
     return (q, s, amax) if with_amax else (q, s)
 
 

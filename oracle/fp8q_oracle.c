@@ -252,8 +252,21 @@ int oracle_quant_act_g128_ue8m0(const uint16_t* x, int64_t m, int64_t k, int64_t
  * to an fp32 rounding boundary. */
 static double silu_times_up(double g, double u) { return g / (1.0 + exp(-g)) * u; }
 
-int oracle_swiglu_quant_g128(const uint16_t* h, int64_t m, int64_t n, int64_t ld_h, uint8_t* q,
-                             int64_t ld_q, float* s, int64_t ld_s, double* amax_out) {
+/* The power-of-two rule of oracle_scale_ue8m0 for an fp64 amax: 2^e for the smallest
+ * integer e with range * 2^e >= amax (exact fp64 comparisons), limited to [-127, 127];
+ * 1 for amax == 0. */
+static float scale_ue8m0_f64(double amax, double range) {
+  if (amax == 0.0) return 1.0f;
+  int e = ilogb(amax) - ilogb(range);
+  while (range * ldexp(1.0, e) < amax) ++e;
+  while (range * ldexp(1.0, e - 1) >= amax) --e;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return ldexpf(1.0f, e);
+}
+
+static int swiglu_quant_rule(const uint16_t* h, int64_t m, int64_t n, int64_t ld_h, uint8_t* q,
+                             int64_t ld_q, float* s, int64_t ld_s, double* amax_out, int ue8m0) {
   if (m < 0 || n < 0 || n % 128 || ld_h < 2 * n || ld_q < n || ld_s < m) return -2;
   int64_t groups = n / 128;
   int bad = 0;
@@ -269,13 +282,26 @@ int oracle_swiglu_quant_g128(const uint16_t* h, int64_t m, int64_t n, int64_t ld
         a[c] = silu_times_up((double)gv, (double)uv);
         if (fabs(a[c]) > amax) amax = fabs(a[c]);
       }
-      float sc = (amax == 0.0) ? 1.0f : (float)(amax / E4M3_MAX);
+      float sc = ue8m0 ? scale_ue8m0_f64(amax, E4M3_MAX) : (amax == 0.0) ? 1.0f : (float)(amax / E4M3_MAX);
       s[g * ld_s + row] = sc;
       if (amax_out) amax_out[g * m + row] = amax;
       for (int64_t c = 0; c < 128; ++c) q[row * ld_q + g * 128 + c] = oracle_e4m3_encode(a[c] / (double)sc);
     }
   }
   return bad ? -1 : 0;
+}
+
+int oracle_swiglu_quant_g128(const uint16_t* h, int64_t m, int64_t n, int64_t ld_h, uint8_t* q,
+                             int64_t ld_q, float* s, int64_t ld_s, double* amax_out) {
+  return swiglu_quant_rule(h, m, n, ld_h, q, ld_q, s, ld_s, amax_out, 0);
+}
+
+/* The same with the power-of-two (UE8M0) scale of the fp64 group maximum
+ * [FP8-RL, "Experimental results", scale-format ablation]; the code is then the E4M3
+ * nearest of the exact quotient a / 2^e. */
+int oracle_swiglu_quant_g128_ue8m0(const uint16_t* h, int64_t m, int64_t n, int64_t ld_h, uint8_t* q,
+                                   int64_t ld_q, float* s, int64_t ld_s, double* amax_out) {
+  return swiglu_quant_rule(h, m, n, ld_h, q, ld_q, s, ld_s, amax_out, 1);
 }
 
 /* SiLU(g) * u of one element, as above (exposed for the tests' pins). */

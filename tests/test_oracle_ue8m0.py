@@ -105,3 +105,42 @@ def test_power_of_two_blocks_agree_with_fp32_scales():
     q8, s8 = oracle.quant_weight_blk128(w, ue8m0=True)
     q32, s32 = oracle.quant_weight_blk128(w)
     assert np.array_equal(s8, s32) and np.array_equal(q8, q32)
+
+
+# ------------------------------------------------- SwiGLU + 1x128 quantization, UE8M0
+def test_swiglu_saturated_gate_reduces_to_activation_quantizer():
+    """Every gate >= 40 makes the SiLU factor exactly 1 in fp64, so up = 1 turns the
+    power-of-two SwiGLU quantization into the power-of-two activation quantizer of the
+    gate values (pinned above against torch's cast), and up = -1 flips every sign."""
+    m, n = 6, 384
+    g = synth.bf16_bits_to_f32(synth.activation(4, 2, 17, m, n)).astype(np.float64)
+    gate = synth.to_bf16_bits((40.0 + np.abs(g) * 30.0).astype(np.float32))
+    for up, flip in ((1.0, 0x00), (-1.0, 0x80)):
+        h = np.concatenate([gate, synth.to_bf16_bits(np.full((m, n), up, np.float32))], axis=1)
+        q, s = oracle.swiglu_quant_g128(h, ue8m0=True)
+        q_ref, s_ref = oracle.quant_act_g128(gate, ue8m0=True)
+        assert np.array_equal(s, s_ref)
+        assert np.array_equal(q, q_ref ^ flip)
+
+
+def test_swiglu_scales_and_codes_exact_rational():
+    """Each group's scale is the rule's power of two for the exact fp64 group maximum
+    (brute force in rationals), and every code is the E4M3 nearest of a / scale."""
+    from tests.test_oracle_bruteforce import brute_code
+    m, n = 10, 256
+    h = np.concatenate([synth.activation(4, 3, 11, m, n), synth.activation(4, 3, 12, m, n)], axis=1)
+    h[0, :128] = 0                                                  # zero gate group: scale 1
+    h[1, n:n + 128] = synth.to_bf16_bits(np.full(128, 2.0 ** -130, np.float32))  # tiny: clamped
+    q, s, amax = oracle.swiglu_quant_g128(h, ld_s=m + 1, with_amax=True, ue8m0=True)
+    x = synth.bf16_bits_to_f32(h).astype(np.float64)
+    a = np.array([[oracle.silu_times_up(x[r, c], x[r, n + c]) for c in range(n)] for r in range(m)])
+    assert s[0, 0] == 1.0 and np.all(q[0, :128] & 0x7F == 0)
+    assert s[0, 1] == np.float32(2.0 ** -127)
+    for r in range(m):
+        for gi in range(n // 128):
+            grp = a[r, gi * 128:(gi + 1) * 128]
+            am = float(np.abs(grp).max())
+            assert amax[gi, r] == am
+            assert Fraction(float(s[gi, r])) == _rule(am)
+            for c in range(128):
+                assert q[r, gi * 128 + c] == brute_code(grp[c], float(s[gi, r]))
