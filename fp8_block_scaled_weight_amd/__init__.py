@@ -37,7 +37,7 @@ EXPORTED = (
     "fp8q_quant_weight_blk128_ue8m0", "fp8q_quant_act_g128_ue8m0", "fp8q_gemm_w8a8_ue8m0",
     "fp8q_grouped_gemm_w8a8_ue8m0", "fp8q_moe_dispatch", "fp8q_swiglu_quant_g128", "fp8q_moe_combine",
     "fp8q_gemm_w8a8_bf16act", "fp8q_paged_decode_attention", "fp8q_grouped_gemm_swiglu_quant",
-    "fp8q_moe_route",
+    "fp8q_moe_route", "fp8q_swiglu_quant_g128_ue8m0", "fp8q_grouped_gemm_swiglu_quant_ue8m0",
 )
 
 
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.fp8q_swiglu_quant_g128.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp]
         L.fp8q_grouped_gemm_swiglu_quant.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, vp, i32, i64, vp, i64,
                                                      vp, i64, i64, i64, vp]
+        L.fp8q_swiglu_quant_g128_ue8m0.argtypes = L.fp8q_swiglu_quant_g128.argtypes
+        L.fp8q_grouped_gemm_swiglu_quant_ue8m0.argtypes = L.fp8q_grouped_gemm_swiglu_quant.argtypes
         L.fp8q_moe_route.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
         L.fp8q_moe_combine.argtypes = [vp, i64, vp, vp, i64, i32, i64, vp, i64, vp]
         for name in EXPORTED[3:]:
@@ -302,12 +304,21 @@ def fp8q_moe_route(topk_ids: torch.Tensor, num_experts: int, offsets: torch.Tens
 def fp8q_swiglu_quant_g128(h: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
     """silu(gate) * up of h = [gate | up] ([m, 2n] bf16), quantized per 1x128 group:
     q [m, n] fp8, s [n/128, ld_s] fp32."""
+    _swiglu("fp8q_swiglu_quant_g128", h, q, s, stream)
+
+
+def fp8q_swiglu_quant_g128_ue8m0(h: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
+    """As fp8q_swiglu_quant_g128 with power-of-two (UE8M0) scales."""
+    _swiglu("fp8q_swiglu_quant_g128_ue8m0", h, q, s, stream)
+
+
+def _swiglu(fn, h, q, s, stream) -> None:
     m, n2 = h.shape
     n = n2 // 2
     if tuple(q.shape) != (m, n) or s.dim() != 2 or s.shape[0] != n // 128 or s.stride(1) != 1:
         raise ValueError("q must be [m, n] and s [n/128, ld_s] with unit column stride")
-    _check(lib().fp8q_swiglu_quant_g128(_dev(h, "h", BF16), m, n, _rows(h, "h"), _dev(q, "q", FP8), _rows(q, "q"),
-                                        _dev(s, "s", F32), s.stride(0), _stream(stream)), "fp8q_swiglu_quant_g128")
+    _check(getattr(lib(), fn)(_dev(h, "h", BF16), m, n, _rows(h, "h"), _dev(q, "q", FP8), _rows(q, "q"),
+                              _dev(s, "s", F32), s.stride(0), _stream(stream)), fn)
 
 
 def fp8q_grouped_gemm_swiglu_quant(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
@@ -318,6 +329,19 @@ def fp8q_grouped_gemm_swiglu_quant(a: torch.Tensor, a_s: torch.Tensor, b: torch.
     bf16 [total_m, 2*n_half] buffer followed by fp8q_swiglu_quant_g128 on it: q [total_m, n_half]
     fp8, s [n_half/128, ld_s] fp32.  With row_token (fp8q_moe_route's), a [T, k] and a_s are the
     token rows and dispatched row r reads token row_token[r]."""
+    _grouped_swiglu("fp8q_grouped_gemm_swiglu_quant", a, a_s, b, b_s, group_offsets, q, s, row_token, stream)
+
+
+def fp8q_grouped_gemm_swiglu_quant_ue8m0(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,
+                                         group_offsets: torch.Tensor, q: torch.Tensor, s: torch.Tensor,
+                                         row_token: Optional[torch.Tensor] = None, stream=None) -> None:
+    """As fp8q_grouped_gemm_swiglu_quant for power-of-two (UE8M0) scales: equal, bit for bit, to
+    fp8q_grouped_gemm_w8a8_ue8m0 followed by fp8q_swiglu_quant_g128_ue8m0."""
+    _grouped_swiglu("fp8q_grouped_gemm_swiglu_quant_ue8m0", a, a_s, b, b_s, group_offsets, q, s, row_token,
+                    stream)
+
+
+def _grouped_swiglu(fn, a, a_s, b, b_s, group_offsets, q, s, row_token, stream) -> None:
     a_rows, k = a.shape
     total_m = q.shape[0]
     g, n2, kb = b.shape
@@ -331,11 +355,10 @@ def fp8q_grouped_gemm_swiglu_quant(a: torch.Tensor, a_s: torch.Tensor, b: torch.
     if group_offsets.numel() != g + 1:
         raise ValueError("group_offsets must have G+1 entries")
     tok = 0 if row_token is None else _dev(row_token, "row_token", (torch.int32,))
-    _check(lib().fp8q_grouped_gemm_swiglu_quant(
+    _check(getattr(lib(), fn)(
         _dev(a, "a", FP8), _rows(a, "a"), _dev(a_s, "a_s", F32), a_s.stride(0), tok, a_rows, _dev(b, "b", FP8),
         _dev(b_s, "b_s", F32), _dev(group_offsets, "group_offsets", (torch.int32,)), g, total_m,
-        _dev(q, "q", FP8), _rows(q, "q"), _dev(s, "s", F32), s.stride(0), n_half, k, _stream(stream)),
-        "fp8q_grouped_gemm_swiglu_quant")
+        _dev(q, "q", FP8), _rows(q, "q"), _dev(s, "s", F32), s.stride(0), n_half, k, _stream(stream)), fn)
 
 
 def fp8q_moe_combine(y: torch.Tensor, row_of: torch.Tensor, weights: torch.Tensor, out: torch.Tensor,

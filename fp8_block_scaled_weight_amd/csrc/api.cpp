@@ -476,11 +476,11 @@ fp8q_status fp8q_grouped_gemm_w8a8_ue8m0(const void* a, int64_t ld_a, const floa
   return grouped_gemm(a, ld_a, a_s, ld_as, b, b_s, group_offsets, num_groups, total_m, y, ld_y, n, k, stream, true);
 }
 
-fp8q_status fp8q_grouped_gemm_swiglu_quant(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
-                                           const int32_t* row_token, int64_t token_rows, const void* b,
-                                           const float* b_s, const int32_t* group_offsets, int32_t num_groups,
-                                           int64_t total_m, void* q, int64_t ld_q, float* s, int64_t ld_s,
-                                           int64_t n_half, int64_t k, void* stream) {
+static fp8q_status grouped_swiglu(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
+                                  const int32_t* row_token, int64_t token_rows, const void* b, const float* b_s,
+                                  const int32_t* group_offsets, int32_t num_groups, int64_t total_m, void* q,
+                                  int64_t ld_q, float* s, int64_t ld_s, int64_t n_half, int64_t k, void* stream,
+                                  bool pow2) {
   if (num_groups < 1) return fail(FP8Q_ERR_SHAPE, "num_groups must be >= 1 (got %d)", num_groups);
   if (total_m < 0 || n_half < 0 || k < 0 || token_rows < 0) return fail(FP8Q_ERR_SHAPE, "negative shape");
   const int64_t a_rows = row_token ? token_rows : total_m;  // rows of a (and columns of a_s)
@@ -532,15 +532,33 @@ fp8q_status fp8q_grouped_gemm_swiglu_quant(const void* a, int64_t ld_a, const fl
     }
     if (st == FP8Q_OK) st = no_nan_codes(a, a_rows, k, ld_a, "a");
     if (st == FP8Q_OK) st = no_nan_codes(b, num_groups * 2 * n_half, k, k, "b");
-    if (st == FP8Q_OK) st = check_f32(a_s, k / 128, a_rows, ld_as, "a_s", false, false);
-    if (st == FP8Q_OK) st = check_f32(b_s, num_groups * (2 * n_half / 128), k / 128, k / 128, "b_s", false, false);
+    if (st == FP8Q_OK) st = check_f32(a_s, k / 128, a_rows, ld_as, "a_s", pow2, false);
+    if (st == FP8Q_OK) st = check_f32(b_s, num_groups * (2 * n_half / 128), k / 128, k / 128, "b_s", pow2, false);
     if (st != FP8Q_OK) return st;
   }
   return finish(launched(fp8q::launch_grouped_swiglu(a, ld_a, a_s, ld_as, b, b_s, group_offsets, num_groups, total_m,
-                                                     n_half, k, q, ld_q, s, ld_s, row_token, token_rows,
+                                                     n_half, k, q, ld_q, s, ld_s, row_token, token_rows, pow2,
                                                      reinterpret_cast<hipStream_t>(stream)),
                          "grouped_gemm_swiglu_quant"),
                 stream, "grouped_gemm_swiglu_quant");
+}
+
+fp8q_status fp8q_grouped_gemm_swiglu_quant(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
+                                           const int32_t* row_token, int64_t token_rows, const void* b,
+                                           const float* b_s, const int32_t* group_offsets, int32_t num_groups,
+                                           int64_t total_m, void* q, int64_t ld_q, float* s, int64_t ld_s,
+                                           int64_t n_half, int64_t k, void* stream) {
+  return grouped_swiglu(a, ld_a, a_s, ld_as, row_token, token_rows, b, b_s, group_offsets, num_groups, total_m, q,
+                        ld_q, s, ld_s, n_half, k, stream, false);
+}
+
+fp8q_status fp8q_grouped_gemm_swiglu_quant_ue8m0(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
+                                                 const int32_t* row_token, int64_t token_rows, const void* b,
+                                                 const float* b_s, const int32_t* group_offsets,
+                                                 int32_t num_groups, int64_t total_m, void* q, int64_t ld_q,
+                                                 float* s, int64_t ld_s, int64_t n_half, int64_t k, void* stream) {
+  return grouped_swiglu(a, ld_a, a_s, ld_as, row_token, token_rows, b, b_s, group_offsets, num_groups, total_m, q,
+                        ld_q, s, ld_s, n_half, k, stream, true);
 }
 
 fp8q_status fp8q_kv_quant(const void* k, int64_t ld_k, const void* v, int64_t ld_v, int64_t num_tokens,
@@ -667,8 +685,8 @@ fp8q_status fp8q_moe_route(const int16_t* topk_ids, int64_t num_tokens, int32_t 
                 stream, "moe_route");
 }
 
-fp8q_status fp8q_swiglu_quant_g128(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q, int64_t ld_q,
-                                   float* s, int64_t ld_s, void* stream) {
+static fp8q_status swiglu_quant(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q, int64_t ld_q, float* s,
+                                int64_t ld_s, void* stream, bool pow2) {
   if (m < 0 || n < 0) return fail(FP8Q_ERR_SHAPE, "negative shape");
   if (n % 128) return fail(FP8Q_ERR_SHAPE, "n=%lld must be a multiple of 128", (long long)n);
   if (m == 0 || n == 0) {
@@ -701,16 +719,26 @@ fp8q_status fp8q_swiglu_quant_g128(const void* h, int64_t m, int64_t n, int64_t 
           break;
         }
         const double g = dec(gb), a = g / (1.0 + std::exp(-g)) * dec(ub);
-        if (std::fabs(a) / 448.0 > 3.4028234663852886e38)
+        if (!pow2 && std::fabs(a) / 448.0 > 3.4028234663852886e38)
           st = fail(FP8Q_ERR_PRECONDITION, "silu(h[%lld][%lld]) * up = %g: its group's amax / 448 exceeds binary32",
                     (long long)r, (long long)c, a);
       }
     if (st != FP8Q_OK) return st;
   }
-  return finish(launched(fp8q::launch_swiglu_quant(h, m, n, ld_h, q, ld_q, s, ld_s,
+  return finish(launched(fp8q::launch_swiglu_quant(h, m, n, ld_h, q, ld_q, s, ld_s, pow2,
                                                    reinterpret_cast<hipStream_t>(stream)),
                          "swiglu_quant_g128"),
                 stream, "swiglu_quant_g128");
+}
+
+fp8q_status fp8q_swiglu_quant_g128(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q, int64_t ld_q,
+                                   float* s, int64_t ld_s, void* stream) {
+  return swiglu_quant(h, m, n, ld_h, q, ld_q, s, ld_s, stream, false);
+}
+
+fp8q_status fp8q_swiglu_quant_g128_ue8m0(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q, int64_t ld_q,
+                                         float* s, int64_t ld_s, void* stream) {
+  return swiglu_quant(h, m, n, ld_h, q, ld_q, s, ld_s, stream, true);
 }
 
 fp8q_status fp8q_moe_combine(const void* y, int64_t ld_y, const int32_t* row_of, const float* weights,

@@ -524,7 +524,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a, int64_t
       const int64_t m = m0 + r;
       uint32_t o[4];
       float scale;
-      if (swiglu_quant16(gw, uw, m < m_end, o, scale)) {
+      if (swiglu_quant16<POW2>(gw, uw, m < m_end, o, scale)) {
         if (cc == 0) sw.s[jt * sw.ld_s + m] = scale;
         store_plain(sw.q + m * sw.ld_q + jt * 128 + cc * 16, make_uint4(o[0], o[1], o[2], o[3]));
       }
@@ -1336,12 +1336,13 @@ static hipError_t launch_grouped(const void* a, int64_t ld_a, const float* a_s, 
 hipError_t launch_grouped_swiglu(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                                  const float* b_s, const int32_t* offsets, int32_t groups, int64_t total_m,
                                  int64_t half, int64_t k, void* q, int64_t ld_q, float* s, int64_t ld_s,
-                                 const int32_t* row_token, int64_t token_rows, hipStream_t stream) {
+                                 const int32_t* row_token, int64_t token_rows, bool pow2, hipStream_t stream) {
   using C = CfgLarge;
   const int64_t n_tiles = half / 128;
   // 256-row tiles: at most total_m / 256 + one per group; 128-row tiles: at most one per group
   const int64_t m_tiles = (total_m + 255) / 256 + 2 * (int64_t)groups;
-  hipLaunchKernelGGL(grouped_swiglu_kernel<false>, dim3((unsigned)(n_tiles * m_tiles)), dim3(C::THREADS), 0, stream,
+  auto kernel = pow2 ? grouped_swiglu_kernel<true> : grouped_swiglu_kernel<false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)(n_tiles * m_tiles)), dim3(C::THREADS), 0, stream,
                      reinterpret_cast<const uint8_t*>(a), ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b), b_s,
                      offsets, groups, half, k, n_tiles, reinterpret_cast<uint8_t*>(q), ld_q, s, ld_s, row_token,
                      token_rows);

@@ -51,7 +51,7 @@ hipError_t launch_gemm_bf16act(const void* x, int64_t ld_x, const void* b, int64
 hipError_t launch_grouped_swiglu(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                                  const float* b_s, const int32_t* offsets, int32_t groups, int64_t total_m,
                                  int64_t half, int64_t k, void* q, int64_t ld_q, float* s, int64_t ld_s,
-                                 const int32_t* row_token, int64_t token_rows, hipStream_t stream);
+                                 const int32_t* row_token, int64_t token_rows, bool pow2, hipStream_t stream);
 hipError_t launch_grouped_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as,
                                const void* b, const float* b_s, const int32_t* offsets, int32_t groups,
                                int64_t total_m, void* y, int64_t ld_y, int64_t n, int64_t k, bool pow2,
@@ -63,7 +63,7 @@ hipError_t launch_moe_dispatch(const void* xq, int64_t ld_xq, const float* xs, i
 hipError_t launch_moe_route(const int16_t* ids, int64_t tokens, int32_t topk, int32_t experts, int32_t* offsets,
                             int32_t* row_of, int32_t* row_token, hipStream_t stream);
 hipError_t launch_swiglu_quant(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q, int64_t ld_q, float* s,
-                               int64_t ld_s, hipStream_t stream);
+                               int64_t ld_s, bool pow2, hipStream_t stream);
 hipError_t launch_moe_combine(const void* y, int64_t ld_y, const int32_t* row_of, const float* w, int64_t tokens,
                               int32_t topk, int64_t hidden, void* out, int64_t ld_out, hipStream_t stream);
 hipError_t launch_decode_attention(const void* q, int64_t ld_q, const void* k_cache, const void* v_cache,

@@ -178,6 +178,7 @@ hipError_t launch_moe_dispatch(const void* xq, int64_t ld_xq, const float* xs, i
 // (row, 128-column group), 16 values each (the activation quantizer's lane mapping); the
 // arithmetic is swiglu_quant16 (swiglu.hpp), which the fc1 GEMM's fused epilogue shares.
 // ----------------------------------------------------------------------------
+template <bool POW2>
 __global__ __launch_bounds__(256) void swiglu_quant_g128_kernel(const uint16_t* __restrict__ h, int64_t m,
                                                                 int64_t groups, int64_t n, int64_t ld_h,
                                                                 uint8_t* __restrict__ q, int64_t ld_q,
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(256) void swiglu_quant_g128_kernel(const uint16_t* 
 
   uint32_t o[4];
   float scale;
-  if (!swiglu_quant16(gw, uw, live, o, scale)) return;
+  if (!swiglu_quant16<POW2>(gw, uw, live, o, scale)) return;
   if ((lane & 7) == 0) s[g * ld_s + row] = scale;
   store_plain(q + row * ld_q + g * 128 + col, make_uint4(o[0], o[1], o[2], o[3]));
 }
@@ -231,11 +232,12 @@ hipError_t launch_moe_route(const int16_t* ids, int64_t tokens, int32_t topk, in
 }
 
 hipError_t launch_swiglu_quant(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q, int64_t ld_q, float* s,
-                               int64_t ld_s, hipStream_t stream) {
+                               int64_t ld_s, bool pow2, hipStream_t stream) {
   const int64_t groups = n / 128;
   const int64_t group_tiles = (groups + 3) / 4;
   const int64_t wgs = ((m + 7) / 8) * group_tiles;
-  hipLaunchKernelGGL(swiglu_quant_g128_kernel, dim3((unsigned)wgs), dim3(256), 0, stream,
+  auto kernel = pow2 ? swiglu_quant_g128_kernel<true> : swiglu_quant_g128_kernel<false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)wgs), dim3(256), 0, stream,
                      reinterpret_cast<const uint16_t*>(h), m, groups, n, ld_h, reinterpret_cast<uint8_t*>(q), ld_q,
                      s, ld_s, group_tiles);
   return hipGetLastError();

@@ -81,6 +81,19 @@ __device__ __forceinline__ double swiglu_at(const uint32_t (&gw)[8], const uint3
   return silu_times_up((double)g, (double)u);
 }
 
+// Power-of-two (UE8M0) scale of an fp64 group maximum: the smallest 2^e with
+// 448 * 2^e >= amax (exact fp64 comparisons), e limited to the E8M0 range [-127, 127];
+// 1 for amax == 0.  The start is within a few steps of the answer.
+__device__ __forceinline__ float scale_pow2_from_amax_f64(double amax) {
+  if (amax == 0.0) return 1.0f;
+  const int biased = (int)((__double_as_longlong(amax) >> 52) & 0x7ff);
+  int e = (biased ? biased - 1023 : -1074) - 8;
+  while ((double)kE4M3Max * ldexp(1.0, e) < amax) ++e;
+  while ((double)kE4M3Max * ldexp(1.0, e - 1) >= amax) --e;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  return __builtin_ldexpf(1.0f, e);
+}
+
 constexpr float kSwigluCodeSlack = 0x1p-15f;   // relative move of the fp32 quotient
 constexpr double kSwigluMaxSlack = 0x1p-14;     // values this close to the maximum are recomputed
 
@@ -88,7 +101,9 @@ constexpr double kSwigluMaxSlack = 0x1p-14;     // values this close to the maxi
 // i in half i & 1 of word i >> 1); the 8 lanes of a group (lane & 7 = 0..7, aligned)
 // call together, dead lanes included, since the group maximum is reduced by shuffles.
 // Returns false for a dead lane; otherwise sets the group's scale and the lane's 16
-// codes (o[w] byte e = value 4w + e).
+// codes (o[w] byte e = value 4w + e).  POW2: the group's scale is the power of two above
+// (the codes then follow from the same exact quotient rule).
+template <bool POW2 = false>
 __device__ __forceinline__ bool swiglu_quant16(const uint32_t (&gw)[8], const uint32_t (&uw)[8], bool live,
                                                uint32_t (&o)[4], float& scale) {
   // fp32 values, and the values that need fp64 from the start
@@ -125,7 +140,7 @@ __device__ __forceinline__ bool swiglu_quant16(const uint32_t (&gw)[8], const ui
   }
   amax = max_over_8_lanes_f64(amax);
   if (!live) return false;
-  scale = (amax == 0.0) ? 1.0f : (float)(amax / (double)kE4M3Max);
+  scale = POW2 ? scale_pow2_from_amax_f64(amax) : (amax == 0.0) ? 1.0f : (float)(amax / (double)kE4M3Max);
 
   // codes: fp32 quotient moved both ways; the fp64 quotient where they disagree
 #pragma unroll

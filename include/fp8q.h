@@ -268,6 +268,19 @@ fp8q_status fp8q_grouped_gemm_swiglu_quant(const void* a, int64_t ld_a, const fl
                                            float* s, int64_t ld_s, int64_t n_half, int64_t k,
                                            void* stream);
 
+/* The same for power-of-two (UE8M0) scales: a_s and b_s as for
+ * fp8q_grouped_gemm_w8a8_ue8m0 (precondition: every value is 2^e, -127 <= e <= 127), and
+ * the epilogue quantizes as fp8q_swiglu_quant_g128_ue8m0.  The results equal, bit for bit,
+ *   fp8q_grouped_gemm_w8a8_ue8m0(...) then fp8q_swiglu_quant_g128_ue8m0(...)
+ * with the arguments of the fp32-scale composition above. */
+fp8q_status fp8q_grouped_gemm_swiglu_quant_ue8m0(const void* a, int64_t ld_a, const float* a_s,
+                                                 int64_t ld_as, const int32_t* row_token,
+                                                 int64_t token_rows, const void* b, const float* b_s,
+                                                 const int32_t* group_offsets, int32_t num_groups,
+                                                 int64_t total_m, void* q, int64_t ld_q, float* s,
+                                                 int64_t ld_s, int64_t n_half, int64_t k,
+                                                 void* stream);
+
 /* The grouped GEMM for power-of-two scales; arguments as fp8q_grouped_gemm_w8a8, scale
  * precondition as fp8q_gemm_w8a8_ue8m0. */
 fp8q_status fp8q_grouped_gemm_w8a8_ue8m0(const void* a, int64_t ld_a, const float* a_s,
@@ -388,6 +401,15 @@ fp8q_status fp8q_moe_route(const int16_t* topk_ids, int64_t num_tokens, int32_t 
  * h, q 16-byte aligned.  Precondition: amax / 448 fits binary32. */
 fp8q_status fp8q_swiglu_quant_g128(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q,
                                    int64_t ld_q, float* s, int64_t ld_s, void* stream);
+
+/* The same with power-of-two (UE8M0) scales [FP8-RL, "Experimental results", scale-format
+ * ablation], so that fc2 can run as fp8q_grouped_gemm_w8a8_ue8m0: scale = the smallest
+ * 2^e with 448 * 2^e >= amax (exact comparison with the fp64 amax), e limited to
+ * [-127, 127], 1.0 if amax == 0; code = the E4M3FN value nearest the exact quotient
+ * a / scale (saturating).  Arguments, layouts and errors as fp8q_swiglu_quant_g128,
+ * without the binary32 precondition. */
+fp8q_status fp8q_swiglu_quant_g128_ue8m0(const void* h, int64_t m, int64_t n, int64_t ld_h, void* q,
+                                         int64_t ld_q, float* s, int64_t ld_s, void* stream);
 
 /* fp8q_moe_combine: out[t][c] = bf16( sum_{j < topk, row_of[t*topk+j] >= 0}
  *   weights[t*topk+j] * y[row_of[t*topk+j]][c] ), the sum in fp32 in the order of j

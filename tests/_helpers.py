@@ -73,7 +73,8 @@ def swiglu_near_decisions(h_bits: np.ndarray, scales: np.ndarray, rel: float = 2
         a = g / (1.0 + np.exp(-g)) * u
     amax = np.abs(a).reshape(m, n // 128, 128).max(axis=2)
     v = amax / 448.0
-    f32 = v.astype(np.float32)
+    with np.errstate(over="ignore"):  # a power-of-two call's group maximum may exceed 448 * FLT_MAX
+        f32 = v.astype(np.float32)
     up = np.nextafter(f32, np.float32(np.inf)).astype(np.float64)
     dn = np.nextafter(f32, np.float32(0)).astype(np.float64)
     f = f32.astype(np.float64)

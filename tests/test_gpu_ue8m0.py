@@ -185,3 +185,130 @@ def test_pingpong_padded_pitches():
     torch.cuda.synchronize()
     assert torch.equal(y_pad[:, :n].view(torch.int16), y.view(torch.int16))
     assert torch.isnan(y_pad[:, n:].float()).all()
+
+
+# ------------------------------------------------- SwiGLU + 1x128 quantization, UE8M0
+def _near_pow2_boundary(amax, rel=2.0 ** -44):
+    """Groups whose fp64 amax lies within rel (relative) of 448 * 2^k for some k: there an
+    exp result a few ulps away could move the power-of-two scale."""
+    v = np.asarray(amax, np.float64) / 448.0
+    with np.errstate(divide="ignore"):
+        k = np.round(np.log2(np.where(v > 0, v, 1.0)))
+    return (v > 0) & (np.abs(v - np.exp2(k)) <= v * rel)
+
+
+def _check_swiglu_ue8m0(h, ld_s=None):
+    from tests._helpers import swiglu_near_decisions
+    m, n2 = h.shape
+    n = n2 // 2
+    ld_s = m if ld_s is None else ld_s
+    q = torch.empty((m, n), dtype=torch.uint8, device=DEV)
+    s = torch.full((n // 128, ld_s), -5.0, dtype=torch.float32, device=DEV)
+    fq.fp8q_swiglu_quant_g128_ue8m0(to_dev_bf16(h), q, s)
+    torch.cuda.synchronize()
+    gq, gs = u8(q), f32(s)
+    rq, rs, amax = oracle.swiglu_quant_g128(h, ld_s=ld_s, with_amax=True, ue8m0=True)
+    assert np.all(gs[:, m:] == -5.0)
+    assert not np.any(_near_pow2_boundary(amax)), "a group maximum sits on a power-of-two boundary"
+    assert swiglu_near_decisions(h, rs)[1] == 0, "a quotient sits on an E4M3 midpoint"
+    assert np.array_equal(gs[:, :m].view(np.uint32), rs[:, :m].view(np.uint32)), "scales differ"
+    bad = gq != rq
+    assert not np.any(bad), f"{int(bad.sum())} codes differ"
+    return rs
+
+
+def test_swiglu_moe_fc2_input_shape():
+    """fc1 output of the MoE layer: 32768 rows of [gate | up], 768 columns each."""
+    g = synth.activation(4, 0, 80, 32768, 768, outlier_channels=0)
+    u = synth.activation(4, 0, 81, 32768, 768)
+    rs = _check_swiglu_ue8m0(np.concatenate([g, u], axis=1))
+    e = np.log2(rs)
+    assert np.all(e == np.round(e))
+
+
+def test_swiglu_ragged_and_edges():
+    m, n = 13, 384
+    g = synth.activation(4, 1, 82, m, n)
+    u = synth.activation(4, 1, 83, m, n)
+    g[0, :128] = 0                                                            # zero group: scale 1
+    g[1, 128:256] = synth.to_bf16_bits(np.full(128, 60.0, np.float32))      # saturated gate: a = g*u
+    g[2, :128] = synth.to_bf16_bits(np.full(128, -900.0, np.float32))        # exp overflows: a = -0
+    u[3, 256:] = synth.to_bf16_bits(np.full(128, 2.0 ** -130, np.float32))   # tiny group: the 2^-127 clamp
+    g[4, 256:] = synth.to_bf16_bits(np.linspace(-3e38, 3e38, 128, dtype=np.float32))
+    u[4, 256:] = synth.to_bf16_bits(np.full(128, 2.0 ** 100, np.float32))    # beyond 448 * 2^127: clamp, saturate
+    rs = _check_swiglu_ue8m0(np.concatenate([g, u], axis=1), ld_s=m + 3)
+    assert rs[0, 0] == 1.0 and rs[2, 3] == np.float32(2.0 ** -127) and rs[2, 4] == np.float32(2.0 ** 127)
+
+
+def _fused_operands(sizes, n_half, k, seed):
+    """fc1 inputs quantized with power-of-two scales: tokens ~N(0,1) with an outlier channel,
+    expert weights ~N(0,0.02)."""
+    g = len(sizes)
+    off = np.zeros(g + 1, np.int32)
+    off[1:] = np.cumsum(sizes)
+    m = int(off[-1])
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    x = torch.randn((max(m, 1), k), device=DEV, generator=gen)
+    x[:, 7] *= 40.0
+    x = x.to(torch.bfloat16)[:m]
+    w = (torch.randn((g * 2 * n_half, k), device=DEV, generator=gen) * 0.02).to(torch.bfloat16)
+    aq = torch.empty((m, k), dtype=torch.uint8, device=DEV)
+    a_s = torch.empty((k // 128, max(m, 1)), dtype=torch.float32, device=DEV)
+    if m:
+        fq.fp8q_quant_act_g128_ue8m0(x, aq, a_s)
+    bq = torch.empty((g * 2 * n_half, k), dtype=torch.uint8, device=DEV)
+    b_s = torch.empty((g * 2 * n_half // 128, k // 128), dtype=torch.float32, device=DEV)
+    fq.fp8q_quant_weight_blk128_ue8m0([(w, bq, b_s)])
+    return (aq, a_s, bq.view(g, 2 * n_half, k), b_s.view(g, 2 * n_half // 128, k // 128),
+            torch.from_numpy(off).to(DEV), m)
+
+
+@pytest.mark.parametrize("sizes,n_half,k", [
+    ([3, 0, 300, 1, 0, 513, 64, 256], 256, 2048),   # empty, sub-tile, ragged multi-tile groups
+    ([5, 130, 0, 77], 128, 256),                    # short K, one 128-output tile column
+    ([200, 128, 129, 0, 384, 255, 1], 256, 2048),   # 256- and 128-row tiles
+])
+def test_fused_swiglu_equals_gemm_then_swiglu_and_the_oracle(sizes, n_half, k):
+    """fp8q_grouped_gemm_swiglu_quant_ue8m0 = fp8q_grouped_gemm_w8a8_ue8m0 (bf16 output) then
+    fp8q_swiglu_quant_g128_ue8m0, bit for bit; the latter against the oracle on that output."""
+    from tests._helpers import swiglu_near_decisions
+    aq, a_s, bq, b_s, off, m = _fused_operands(sizes, n_half, k, seed=len(sizes) * 5 + k)
+    y = torch.empty((m, 2 * n_half), dtype=torch.bfloat16, device=DEV)
+    fq.fp8q_grouped_gemm_w8a8_ue8m0(aq, a_s, bq, b_s, off, y)
+    q1 = torch.full((m, n_half), 0x5A, dtype=torch.uint8, device=DEV)
+    s1 = torch.full((n_half // 128, m + 3), -1.0, device=DEV)
+    fq.fp8q_swiglu_quant_g128_ue8m0(y, q1, s1)
+    q2 = torch.full((m, n_half), 0xA5, dtype=torch.uint8, device=DEV)
+    s2 = torch.full((n_half // 128, m + 3), -2.0, device=DEV)
+    fq.fp8q_grouped_gemm_swiglu_quant_ue8m0(aq, a_s, bq, b_s, off, q2, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2), f"codes differ at {int((q1 != q2).sum())} places"
+    assert torch.equal(s1[:, :m].view(torch.int32), s2[:, :m].view(torch.int32)), "scales differ"
+    assert torch.all(s2[:, m:] == -2.0), "scale columns past total_m are not written"
+    q_ref, s_ref, amax = oracle.swiglu_quant_g128(bf16_bits(y), with_amax=True, ue8m0=True)
+    assert not np.any(_near_pow2_boundary(amax))
+    assert swiglu_near_decisions(bf16_bits(y), s_ref)[1] == 0
+    assert np.array_equal(q2.cpu().numpy(), q_ref)
+    assert np.array_equal(s2[:, :m].cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_fused_swiglu_at_the_moe_layer_shape_with_token_rows():
+    """128 experts, 4096 tokens routed top-8: the fused call reading the token rows through
+    fp8q_moe_route's row_token equals the dispatched-row composition, every byte."""
+    _, off_np, _ = synth.moe_routing(0)
+    sizes = list(np.diff(off_np))
+    aq, a_s, bq, b_s, off, m = _fused_operands(sizes, 768, 2048, seed=13)
+    y = torch.empty((m, 1536), dtype=torch.bfloat16, device=DEV)
+    fq.fp8q_grouped_gemm_w8a8_ue8m0(aq, a_s, bq, b_s, off, y)
+    q1 = torch.empty((m, 768), dtype=torch.uint8, device=DEV)
+    s1 = torch.empty((6, m), device=DEV)
+    fq.fp8q_swiglu_quant_g128_ue8m0(y, q1, s1)
+    # the same rows held once each as "token rows", read through an identity row_token
+    q2 = torch.empty_like(q1)
+    s2 = torch.empty_like(s1)
+    tok = torch.arange(m, dtype=torch.int32, device=DEV)
+    fq.fp8q_grouped_gemm_swiglu_quant_ue8m0(aq, a_s, bq, b_s, off, q2, s2, row_token=tok)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2), f"codes differ at {int((q1 != q2).sum())} places"
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32)), "scales differ"
