@@ -1260,6 +1260,34 @@ def legs(torch, fq, synth, dev):
     res["f1_moe_layer_fused"] = {"tokens": T, "rows": n, "us": round(ms_lf * 1e3, 1),
                                  "TFLOPs": round((f1 + f2) / (ms_lf * 1e-3) / 1e12, 1),
                                  "steps": "route, fc1 + swiglu-quant fused reading the token rows, fc2, combine"}
+
+    # the same fused layer with power-of-two (UE8M0) scales throughout: expert weights, tokens
+    # and fc2's input (the fc1 epilogue's quantization) all take the UE8M0 rule
+    fc1u, fc2u = torch.empty_like(fc1q), torch.empty_like(fc2q)
+    fc1us, fc2us = torch.empty_like(fc1s), torch.empty_like(fc2s)
+    fq.fp8q_quant_weight_blk128_ue8m0([(fc1, fc1u, fc1us), (fc2, fc2u, fc2us)])
+    b1u, b1us = fc1u.view(E, 2 * I, H), fc1us.view(E, 2 * I // 128, H // 128)
+    b2u, b2us = fc2u.view(E, H, I), fc2us.view(E, H // 128, I // 128)
+    xqu, xscu = torch.empty_like(xq), torch.empty_like(xsc)
+    fq.fp8q_quant_act_g128_ue8m0(x, xqu, xscu)
+    ms_swu = _time(torch, lambda: fq.fp8q_swiglu_quant_g128_ue8m0(y1, q2, s2), 10)
+    ms_f1u = _time(torch, lambda: fq.fp8q_grouped_gemm_swiglu_quant_ue8m0(xqu, xscu, b1u, b1us, doff, q2f, s2f,
+                                                                          row_token=rtok), 10)
+
+    def layer_fused_ue8m0():
+        fq.fp8q_moe_route(ids, E, doff, row_of, rtok)
+        fq.fp8q_grouped_gemm_swiglu_quant_ue8m0(xqu, xscu, b1u, b1us, doff, q2f, s2f, row_token=rtok)
+        fq.fp8q_grouped_gemm_w8a8_ue8m0(q2f, s2f, b2u, b2us, doff, y2)
+        fq.fp8q_moe_combine(y2, row_of, rw, out)
+
+    ms_lfu = _time(torch, layer_fused_ue8m0, 5, reps=2)
+    res["f2_ue8m0_moe_layer_fused"] = {"tokens": T, "rows": n, "us": round(ms_lfu * 1e3, 1),
+                                       "TFLOPs": round((f1 + f2) / (ms_lfu * 1e-3) / 1e12, 1),
+                                       "fc1_swiglu_fused_token_rows_us": round(ms_f1u * 1e3, 1),
+                                       "swiglu_quant_us": round(ms_swu * 1e3, 1),
+                                       "steps": "route, UE8M0 fc1 + swiglu-quant fused reading the token rows, "
+                                                "UE8M0 fc2, combine"}
+    del fc1u, fc2u, fc1us, fc2us, xqu, xscu
     del xq, dq, q2, out, q2f, s2f, rtok
     del fc1, fc2, fc1q, fc2q, x, xs_rows, a1q, a2, a2q, y1, y2
     torch.cuda.empty_cache()
