@@ -38,6 +38,7 @@ EXPORTED = (
     "fp8q_grouped_gemm_w8a8_ue8m0", "fp8q_moe_dispatch", "fp8q_swiglu_quant_g128", "fp8q_moe_combine",
     "fp8q_gemm_w8a8_bf16act", "fp8q_paged_decode_attention", "fp8q_grouped_gemm_swiglu_quant",
     "fp8q_moe_route", "fp8q_swiglu_quant_g128_ue8m0", "fp8q_grouped_gemm_swiglu_quant_ue8m0",
+    "fp8q_gemm_w8a8_bf16act_ue8m0",
 )
 
 
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
         L.fp8q_paged_decode_attention.argtypes = [vp, i64, vp, vp, vp, i64, vp, i32, i32, i32, i32, i32, i64, vp,
                                                   vp, vp, f32, f32, u32, vp, i64, vp]
         L.fp8q_gemm_w8a8_bf16act.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp]
+        L.fp8q_gemm_w8a8_bf16act_ue8m0.argtypes = L.fp8q_gemm_w8a8_bf16act.argtypes
         L.fp8q_kv_quant.argtypes = [vp, i64, vp, i64, i64, i32, i32, vp, vp, vp, i32, i64, vp, vp, f32, u32, vp]
         L.fp8q_moe_dispatch.argtypes = [vp, i64, vp, i64, vp, i64, i32, i32, i64, vp, i64, vp, i64, vp, vp, vp]
         L.fp8q_swiglu_quant_g128.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp]
@@ -212,13 +214,23 @@ def fp8q_gemm_w8a8_bf16act(x: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor, 
                            stream=None) -> None:
     """y [m,n] bf16 = the block-scaled GEMM of x [m,k] bf16 (m <= 64), quantized per 1x128 group
     inside the kernel, with b [n,k] fp8 (b_s [n/128,k/128])."""
+    _bf16act("fp8q_gemm_w8a8_bf16act", x, b, b_s, y, stream)
+
+
+def fp8q_gemm_w8a8_bf16act_ue8m0(x: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor, y: torch.Tensor,
+                                 stream=None) -> None:
+    """As fp8q_gemm_w8a8_bf16act with power-of-two (UE8M0) scales."""
+    _bf16act("fp8q_gemm_w8a8_bf16act_ue8m0", x, b, b_s, y, stream)
+
+
+def _bf16act(fn, x, b, b_s, y, stream) -> None:
     m, k = x.shape
     n = b.shape[0]
     if b.shape[1] != k or tuple(y.shape) != (m, n) or not b_s.is_contiguous():
         raise ValueError("shape mismatch between x, b and y")
-    _check(lib().fp8q_gemm_w8a8_bf16act(_dev(x, "x", BF16), _rows(x, "x"), _dev(b, "b", FP8), _rows(b, "b"),
-                                        _dev(b_s, "b_s", F32), _dev(y, "y", BF16), _rows(y, "y"), m, n, k,
-                                        _stream(stream)), "fp8q_gemm_w8a8_bf16act")
+    _check(getattr(lib(), fn)(_dev(x, "x", BF16), _rows(x, "x"), _dev(b, "b", FP8), _rows(b, "b"),
+                              _dev(b_s, "b_s", F32), _dev(y, "y", BF16), _rows(y, "y"), m, n, k, _stream(stream)),
+           fn)
 
 
 def fp8q_grouped_gemm_w8a8(a: torch.Tensor, a_s: torch.Tensor, b: torch.Tensor, b_s: torch.Tensor,

@@ -385,8 +385,8 @@ fp8q_status fp8q_gemm_w8a8_ue8m0(const void* a, int64_t ld_a, const float* a_s, 
   return gemm(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream, true);
 }
 
-fp8q_status fp8q_gemm_w8a8_bf16act(const void* x, int64_t ld_x, const void* b, int64_t ld_b, const float* b_s,
-                                   void* y, int64_t ld_y, int64_t m, int64_t n, int64_t k, void* stream) {
+static fp8q_status gemm_bf16act(const void* x, int64_t ld_x, const void* b, int64_t ld_b, const float* b_s, void* y,
+                                int64_t ld_y, int64_t m, int64_t n, int64_t k, void* stream, bool pow2) {
   if (m < 0 || n < 0 || k < 0) return fail(FP8Q_ERR_SHAPE, "negative shape");
   if (m > 64) return fail(FP8Q_ERR_SHAPE, "m=%lld: the fused activation quantization takes at most 64 tokens",
                           (long long)m);
@@ -409,13 +409,24 @@ fp8q_status fp8q_gemm_w8a8_bf16act(const void* x, int64_t ld_x, const void* b, i
     if (st == FP8Q_OK) st = debug_sync(stream);
     if (st == FP8Q_OK) st = finite_bf16(x, m, k, ld_x, "x");
     if (st == FP8Q_OK) st = no_nan_codes(b, n, k, ld_b, "b");
-    if (st == FP8Q_OK) st = check_f32(b_s, n / 128, k / 128, k / 128, "b_s", false, false);
+    if (st == FP8Q_OK) st = check_f32(b_s, n / 128, k / 128, k / 128, "b_s", pow2, false);
     if (st != FP8Q_OK) return st;
   }
-  return finish(launched(fp8q::launch_gemm_bf16act(x, ld_x, b, ld_b, b_s, y, ld_y, m, n, k,
+  return finish(launched(fp8q::launch_gemm_bf16act(x, ld_x, b, ld_b, b_s, y, ld_y, m, n, k, pow2,
                                                    reinterpret_cast<hipStream_t>(stream)),
                          "gemm_w8a8_bf16act"),
                 stream, "gemm_w8a8_bf16act");
+}
+
+fp8q_status fp8q_gemm_w8a8_bf16act(const void* x, int64_t ld_x, const void* b, int64_t ld_b, const float* b_s,
+                                   void* y, int64_t ld_y, int64_t m, int64_t n, int64_t k, void* stream) {
+  return gemm_bf16act(x, ld_x, b, ld_b, b_s, y, ld_y, m, n, k, stream, false);
+}
+
+fp8q_status fp8q_gemm_w8a8_bf16act_ue8m0(const void* x, int64_t ld_x, const void* b, int64_t ld_b,
+                                         const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n, int64_t k,
+                                         void* stream) {
+  return gemm_bf16act(x, ld_x, b, ld_b, b_s, y, ld_y, m, n, k, stream, true);
 }
 
 static fp8q_status grouped_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,

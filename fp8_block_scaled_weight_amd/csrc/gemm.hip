@@ -830,7 +830,7 @@ constexpr int kSmallWaves = 8;
 // byte offset of 16-byte chunk c of row r in a stage
 __device__ __forceinline__ int stage_at(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
-template <int WM, bool FUSED, int D, int WN = 1>
+template <int WM, bool FUSED, int D, int WN = 1, bool POW2 = false>
 __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
     const void* __restrict__ a_, int64_t ld_a, const float* __restrict__ as, int64_t ld_as,
     const uint8_t* __restrict__ b, int64_t ld_b, const float* __restrict__ bs, uint16_t* __restrict__ y,
@@ -934,7 +934,8 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
           const uint4 v = rt[d][p];
           uint32_t mx = max_over_8_lanes(absmax8(v));
           mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x140, 0xf, 0xf, false));  // row mirror
-          const float scale = scale_from_amax(bf16_bits_to_float(mx), kE4M3Max);
+          const float scale = POW2 ? scale_pow2_from_amax(bf16_bits_to_float(mx), kE4M3Max)
+                                   : scale_from_amax(bf16_bits_to_float(mx), kE4M3Max);
           const Quantizer qz = make_quantizer(scale);
           const uint2 code = (qz.xm == 1.0f) ? quant8<false>(v, qz, false) : quant8<false>(v, qz, true);
           if (c < chunks) {
@@ -1004,7 +1005,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void gemm_smallm_kernel(
   }
 }
 
-template <int WM, bool FUSED = false, int WN = 1>
+template <int WM, bool FUSED = false, int WN = 1, bool POW2 = false>
 static hipError_t launch_smallm(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                                 int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                                 int64_t k, hipStream_t stream) {
@@ -1012,7 +1013,7 @@ static hipError_t launch_smallm(const void* a, int64_t ld_a, const float* a_s, i
   const int64_t groups = (m + 16 * WM - 1) / (16 * WM);
   const unsigned grid = (unsigned)(n16 * groups);
   if constexpr (WN > 1) {
-    hipLaunchKernelGGL((gemm_smallm_kernel<WM, FUSED, 1, WN>), dim3((unsigned)((n / (16 * WN)) * groups)),
+    hipLaunchKernelGGL((gemm_smallm_kernel<WM, FUSED, 1, WN, POW2>), dim3((unsigned)((n / (16 * WN)) * groups)),
                        dim3(64 * kSmallWaves), 0, stream, a, ld_a, a_s, ld_as, reinterpret_cast<const uint8_t*>(b),
                        ld_b, b_s, reinterpret_cast<uint16_t*>(y), ld_y, m, n / (16 * WN), (int)(k / 128));
     return hipGetLastError();
@@ -1028,7 +1029,7 @@ static hipError_t launch_smallm(const void* a, int64_t ld_a, const float* a_s, i
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_smallm_kernel<WM, FUSED, 1>), dim3(grid), dim3(64 * kSmallWaves), 0, stream, a, ld_a, a_s,
+  hipLaunchKernelGGL((gemm_smallm_kernel<WM, FUSED, 1, 1, POW2>), dim3(grid), dim3(64 * kSmallWaves), 0, stream, a, ld_a, a_s,
                      ld_as, reinterpret_cast<const uint8_t*>(b), ld_b, b_s, reinterpret_cast<uint16_t*>(y), ld_y, m,
                      n16, (int)(k / 128));
   return hipGetLastError();
@@ -1036,7 +1037,7 @@ static hipError_t launch_smallm(const void* a, int64_t ld_a, const float* a_s, i
 
 // Token groups per workgroup for few tokens: 16*WM tokens, WM shrinking (more
 // workgroups, each re-reading its weight rows from L2) until the grid covers every CU.
-template <bool FUSED>
+template <bool FUSED, bool POW2 = false>
 static hipError_t launch_few_tokens(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                                     int64_t ld_b, const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                                     int64_t k, hipStream_t stream) {
@@ -1060,14 +1061,18 @@ static hipError_t launch_few_tokens(const void* a, int64_t ld_a, const float* a_
       return launch_smallm<2, FUSED, 2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   }
   if (m > 32 && n16 >= 256)
-    return launch_smallm<4, FUSED>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+    return launch_smallm<4, FUSED, 1, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   if (m > 16 && n16 * ((m + 31) / 32) >= 256)
-    return launch_smallm<2, FUSED>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-  return launch_smallm<1, FUSED>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+    return launch_smallm<2, FUSED, 1, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  return launch_smallm<1, FUSED, 1, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
 }
 
+// FUSED with POW2: the tokens are quantized with the power-of-two rule, as the UE8M0
+// activation quantizer would; the GEMM is the same promotion path (the products of
+// power-of-two scales are the fp32 numbers the block-scaled MFMA would apply).
 hipError_t launch_gemm_bf16act(const void* x, int64_t ld_x, const void* b, int64_t ld_b, const float* b_s, void* y,
-                               int64_t ld_y, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+                               int64_t ld_y, int64_t m, int64_t n, int64_t k, bool pow2, hipStream_t stream) {
+  if (pow2) return launch_few_tokens<true, true>(x, ld_x, nullptr, 0, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   return launch_few_tokens<true>(x, ld_x, nullptr, 0, b, ld_b, b_s, y, ld_y, m, n, k, stream);
 }
 

@@ -47,7 +47,7 @@ hipError_t launch_gemm(const void* a, int64_t ld_a, const float* a_s, int64_t ld
 
 // few tokens (m <= 64) with bf16 activations quantized inside the GEMM
 hipError_t launch_gemm_bf16act(const void* x, int64_t ld_x, const void* b, int64_t ld_b, const float* b_s, void* y,
-                               int64_t ld_y, int64_t m, int64_t n, int64_t k, hipStream_t stream);
+                               int64_t ld_y, int64_t m, int64_t n, int64_t k, bool pow2, hipStream_t stream);
 hipError_t launch_grouped_swiglu(const void* a, int64_t ld_a, const float* a_s, int64_t ld_as, const void* b,
                                  const float* b_s, const int32_t* offsets, int32_t groups, int64_t total_m,
                                  int64_t half, int64_t k, void* q, int64_t ld_q, float* s, int64_t ld_s,

@@ -237,6 +237,14 @@ fp8q_status fp8q_gemm_w8a8_bf16act(const void* x, int64_t ld_x, const void* b, i
                                    const float* b_s, void* y, int64_t ld_y, int64_t m, int64_t n,
                                    int64_t k, void* stream);
 
+/* The same for power-of-two (UE8M0) scales: the token groups are quantized as
+ * fp8q_quant_act_g128_ue8m0 would, and the result is bit-identical to that call followed
+ * by fp8q_gemm_w8a8_ue8m0.  b_s precondition as fp8q_gemm_w8a8_ue8m0; other arguments,
+ * limits and errors as fp8q_gemm_w8a8_bf16act. */
+fp8q_status fp8q_gemm_w8a8_bf16act_ue8m0(const void* x, int64_t ld_x, const void* b, int64_t ld_b,
+                                         const float* b_s, void* y, int64_t ld_y, int64_t m,
+                                         int64_t n, int64_t k, void* stream);
+
 /* fp8q_grouped_gemm_swiglu_quant: MoE fc1 with the SwiGLU activation and fc2's 1x128
  * input quantization fused into the GEMM's epilogue [R3, section 4: the grouped expert
  * GEMM over the recorded routing; Rounding, the SwiGLU fusion region: silu(gate) is

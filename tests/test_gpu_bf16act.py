@@ -69,3 +69,27 @@ def test_fused_zero_tokens_is_a_no_op():
     fq.fp8q_gemm_w8a8_bf16act(torch.empty((0, 256), dtype=torch.bfloat16, device=DEV), b, bs,
                               torch.empty((0, 256), dtype=torch.bfloat16, device=DEV))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 4096, 4096), (17, 1024, 512), (33, 4096, 4096), (64, 1024, 4096)])
+def test_fused_ue8m0_equals_quantize_then_gemm(m, n, k):
+    """Power-of-two scales: the fused call equals fp8q_quant_act_g128_ue8m0 followed by
+    fp8q_gemm_w8a8_ue8m0 bit for bit, and passes the GEMM gate of the oracle's UE8M0 path."""
+    x_bits = synth.activation(2, 0, 300 + m, m, k)
+    wq, ws = oracle.quant_weight_blk128(synth.weight(2, 0, n // 128 + m + 1, n, k), ue8m0=True)
+    b, bs = torch.from_numpy(wq).to(DEV), torch.from_numpy(ws).to(DEV)
+    x = to_dev_bf16(x_bits)
+    y_fused = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
+    fq.fp8q_gemm_w8a8_bf16act_ue8m0(x, b, bs, y_fused)
+    xq = torch.empty((m, k), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((k // 128, m), dtype=torch.float32, device=DEV)
+    fq.fp8q_quant_act_g128_ue8m0(x, xq, xs)
+    y_two = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    fq.fp8q_gemm_w8a8_ue8m0(xq, xs, b, bs, y_two)
+    torch.cuda.synchronize()
+    got = bf16_bits(y_fused)
+    assert np.array_equal(got, bf16_bits(y_two)), "fused result differs from quantize + GEMM"
+    rq, rs = oracle.quant_act_g128(x_bits, ue8m0=True)
+    assert np.array_equal(xq.cpu().numpy(), rq) and np.array_equal(xs.cpu().numpy(), rs)
+    ok, ratio, _ = gemm_gate(got, oracle.gemm_w8a8(rq, rs, wq, ws))
+    assert ok, f"worst err/bound {ratio:.3f}"
