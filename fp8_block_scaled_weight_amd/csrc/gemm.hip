@@ -1050,6 +1050,17 @@ static hipError_t launch_few_tokens(const void* a, int64_t ld_a, const float* a_
   // with 64 x 32 (384 workgroups: one and a half rounds of the CUs), 15.8 us with 64 x 48
   // (256), 32x12288x4096 15.1 -> 12.0 us with 32 x 48.  With 128 workgroups slower
   // (64x4096x4096 9.4 -> 11.0 us).
+  // Fused activation quantization: every workgroup quantizes its token rows again, so 32
+  // weight rows per workgroup halve that work (64 tokens x 32 rows spills; 32 x 32 and 16 x
+  // 32 do not).  Interleaved medians, 16 -> 32 rows, byte-identical: 64x4096x4096 39.2 ->
+  // 23.0 us, 33x4096x4096 25.4 -> 23.0, 64x12288x4096 113.2 -> 66.3, 16x12288x4096 27.5 ->
+  // 20.6; with fewer than 192 workgroups no faster (16x4096x4096 12.9 -> 13.3).
+  if constexpr (FUSED) {
+    if (m > 16 && (n / 32) * ((m + 31) / 32) >= 192)
+      return launch_smallm<2, FUSED, 2, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+    if (m > 8 && n / 32 >= 192)
+      return launch_smallm<1, FUSED, 2, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
+  }
   if constexpr (!FUSED) {
     if (m > 32 && n % 48 == 0 && (n / 48) * ((m + 63) / 64) >= 192)
       return launch_smallm<4, FUSED, 3>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);

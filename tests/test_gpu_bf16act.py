@@ -25,7 +25,8 @@ def _weight(n, k, tensor):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 4096, 4096), (5, 1024, 4096), (16, 4096, 4096), (17, 1024, 512),
-                                   (33, 4096, 4096), (64, 1024, 4096), (64, 12288, 4096), (16, 256, 256)])
+                                   (33, 4096, 4096), (64, 1024, 4096), (64, 12288, 4096), (16, 256, 256),
+                                   (12, 6144, 1024), (40, 12288, 1024)])  # last two: 32 weight rows per workgroup
 def test_fused_equals_quantize_then_gemm(m, n, k):
     x_bits = synth.activation(2, 0, 200 + m, m, k)
     b, bs, wq, ws = _weight(n, k, n // 128 + m)
@@ -71,7 +72,8 @@ def test_fused_zero_tokens_is_a_no_op():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 4096, 4096), (17, 1024, 512), (33, 4096, 4096), (64, 1024, 4096)])
+@pytest.mark.parametrize("m,n,k", [(1, 4096, 4096), (17, 1024, 512), (33, 4096, 4096), (64, 1024, 4096),
+                                   (12, 6144, 1024)])
 def test_fused_ue8m0_equals_quantize_then_gemm(m, n, k):
     """Power-of-two scales: the fused call equals fp8q_quant_act_g128_ue8m0 followed by
     fp8q_gemm_w8a8_ue8m0 bit for bit, and passes the GEMM gate of the oracle's UE8M0 path."""

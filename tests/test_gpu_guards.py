@@ -72,6 +72,7 @@ def test_quantizer_guards():
     (40, 6272, 256),     # few tokens, 64 x 32
     (20, 12288, 256),    # few tokens, 32 x 48
     (20, 6272, 256),     # few tokens, 32 x 32
+    (12, 6144, 256),     # few tokens, 16 x 16 (fused activation quantization: 16 x 32)
     (300, 512, 1152),    # few tiles (24 of 128x64): the few-token kernel
     (500, 1024, 1024),   # few tiles, 64 x 32
     (300, 4096, 1152),   # 128x64 tiles in two K groups
