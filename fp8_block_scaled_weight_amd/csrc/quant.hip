@@ -182,10 +182,7 @@ __global__ __launch_bounds__(256) void quant_act_g128_kernel(const uint16_t* __r
   if ((lane & 7) == 0) s[g * ld_s + row] = scale;
   const Quantizer qz = make_quantizer(scale);
   uint4 o = quant16<false>(a, b, qz);
-  // non-temporal: cold-rotation medians 4096 x 4096 13.3-13.5 -> 12.3-12.4 us, 32768 x 768
-  // 18.4 -> 17.9, 4096 x 12288 32.1-33.6 -> 31.1-33.2 (plain loads stay: non-temporal ones
-  // were slower at 4096 x 12288)
-  store_stream(q + row * ld_q + g * 128 + col, o);
+  store_plain(q + row * ld_q + g * 128 + col, o);
 }
 
 hipError_t launch_quant_act(const void* x, int64_t m, int64_t k, int64_t ld_x, void* q, int64_t ld_q,
