@@ -575,7 +575,7 @@ using CfgLarge = GemmCfg<256, 256, 2, 4, 2>;   // 128 x 64 per wave, 132 KB LDS
 using CfgLargeHalf = GemmCfg<128, 256, 2, 4, 2>;  // 64 x 64 per wave: a group's last <= 128 rows
 using CfgMid = GemmCfg<128, 128, 2, 4, 4>;     // 64 x 32 per wave, 132 KB LDS
 using CfgMid2 = GemmCfg<128, 128, 2, 4, 2>;    // two workgroups per CU when tiles are plenty
-using CfgMid2W4 = GemmCfg<128, 128, 2, 2, 2>;  // the same with 4 waves of 64 x 64 (power-of-two scales)
+using CfgMid2W4 = GemmCfg<128, 128, 2, 2, 2>;  // the same with 4 waves of 64 x 64
 using CfgSmall = GemmCfg<128, 64, 2, 2, 4>;    // 64 x 32 per wave, 100 KB LDS
 using CfgSmallK2 = GemmCfg<128, 64, 2, 2, 3, 2>;  // two K groups of 4 waves, 3-stage rings, 150 KB LDS
 
@@ -1120,14 +1120,14 @@ static hipError_t launch_tiles(const void* a, int64_t ld_a, const float* a_s, in
   // with at least two tiles per CU, two co-resident workgroups hide each other's waits
   // better than deeper copy rings
   const int64_t mid_tiles = ((m + CfgMid::BM - 1) / CfgMid::BM) * (n / CfgMid::BN);
-  // Power-of-two scales: four waves of 64 x 64 read 25 % fewer LDS bytes per FLOP than
-  // eight of 64 x 32 (interleaved medians, 8 -> 4 waves: 4096x2048x4096 40.6 -> 38.0 us,
-  // 2048x4096x4096 38.2 -> 36.5, 8192x1024x4096 42.6 -> 40.4, 65536x384x256 20.7 -> 20.9).
-  // With FP32 scales the same change moved these shapes by -3 to +3 %, so they keep 8 waves.
-  if constexpr (POW2) {
-    if (mid_tiles >= 512)
-      return launch_dense<CfgMid2W4, true>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
-  }
+  // Four waves of 64 x 64 read 25 % fewer LDS bytes per FLOP than eight of 64 x 32.
+  // Interleaved medians, 8 -> 4 waves, byte-identical: power-of-two scales 4096x2048x4096
+  // 40.6 -> 38.0 us, 2048x4096x4096 38.2 -> 36.5, 8192x1024x4096 42.6 -> 40.4, 65536x384x256
+  // 20.7 -> 20.9; FP32 scales 4096x2048x4096 42.0 -> 40.8 and 40.4 -> 38.4, 2048x4096x4096
+  // 41.8 -> 40.1, 4096x2048x2048 24.1 -> 23.2, but 8192x1024x4096 40.6 -> 41.8 and
+  // 65536x384x256 19.1 -> 19.5, hence N >= 2048 there.
+  if (mid_tiles >= 512 && (POW2 || n >= 2048))
+    return launch_dense<CfgMid2W4, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   if (mid_tiles >= 512)
     return launch_dense<CfgMid2, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
   return launch_dense<CfgMid, POW2>(a, ld_a, a_s, ld_as, b, ld_b, b_s, y, ld_y, m, n, k, stream);
